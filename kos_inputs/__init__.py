@@ -1,0 +1,303 @@
+"""Seeded synthetic inputs for the fused GEMM+collective kernels and their oracle.
+
+This module is shared by the tests, the bench and the oracle's callers.  It
+holds no arithmetic of the method itself: it only draws seeded random tensors
+of the shapes, dtypes and value distributions of the workloads, and emulates
+what the *other* ranks would have produced (their shards, partial sums, the
+rows they send and return), because only one GPU's share is run.
+
+Workloads (shapes from the KOSMOS pages' problem statement: an all-gather
+before a column-parallel GEMM, a reduce-scatter after a row-parallel GEMM, and
+an expert layer whose tokens travel to their expert's rank and back):
+
+* ``AG_TINY``  -- 4 ranks, shards 64x256 bf16, weight 256x256.
+* ``AG_QKV``   -- 8 ranks, shards 512x8192 bf16, weight 8192x3072 (QKV
+  column-parallel projection, sequence 4096, hidden 8192).
+* ``RS_MLP``   -- 8 ranks, A 4096x3584 bf16, W 3584x8192, reduce-scattered
+  into 512x8192 fp32 chunks (MLP down projection).
+* ``MOE_DSV3`` -- DeepSeek-V3-shaped expert layer: 4096 tokens, hidden 7168,
+  256 experts, top-8, 32 local experts, SwiGLU 7168->2048->7168.
+* ``MOE_QWEN3`` -- Qwen3-235B-shaped: 8192 tokens, hidden 4096, 128 experts,
+  top-8, 16 local experts, SwiGLU 4096->1536->4096, router logits N(0,1) plus a
+  per-expert Zipf(s=1.1) bias (skewed routing).
+
+Distributions: N(0, v) means variance v (a fan-in initialiser keeps unit
+output variance).  bf16 tensors are drawn in fp32 and rounded to nearest even
+by torch's own conversion.  Integer-valued variants draw uniformly from
+[-4, 4] so that every fp32 sum of the small cases is exact.
+
+Every tensor is drawn from its own ``torch.Generator`` seeded from
+(workload id, tensor id, rank), on the device it is requested for.  CPU and
+GPU generators give different streams; a test that compares both sides draws
+once and copies.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+# ---------------------------------------------------------------------------
+# workload descriptions
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class AgShape:
+    name: str
+    wid: int          # workload id, part of every seed
+    world: int
+    m_local: int
+    k: int
+    n: int
+
+    @property
+    def m(self) -> int:
+        return self.world * self.m_local
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.m * self.n * self.k
+
+
+@dataclasses.dataclass(frozen=True)
+class RsShape:
+    name: str
+    wid: int
+    world: int
+    m: int
+    k: int
+    n: int
+
+    @property
+    def m_chunk(self) -> int:
+        return self.m // self.world
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.m * self.n * self.k
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeShape:
+    name: str
+    wid: int
+    world: int
+    tokens: int
+    hidden: int
+    experts: int
+    topk: int
+    ffn: int
+    zipf_s: Optional[float] = None   # per-expert bias (e+1)^-s added to logits
+
+    @property
+    def e_local(self) -> int:
+        return self.experts // self.world
+
+    @property
+    def peer_cap(self) -> int:
+        """Rows one rank can send to one peer: each token reaches a peer's
+        experts at most min(topk, e_local) times (one row per pair)."""
+        return self.tokens * min(self.topk, self.e_local)
+
+    @property
+    def flops_per_row(self) -> float:
+        # gate + up (2 GEMMs of H x F) and down (F x H), 2 flops per MAC
+        return 6.0 * self.hidden * self.ffn
+
+
+AG_TINY = AgShape("ag_tiny_4r_256x256x256", 1, 4, 64, 256, 256)
+AG_QKV = AgShape("ag_qkv_8r_4096x8192x3072", 2, 8, 512, 8192, 3072)
+RS_MLP = RsShape("rs_mlpdown_8r_4096x3584x8192", 3, 8, 4096, 3584, 8192)
+MOE_DSV3 = MoeShape("moe_dsv3_8r_t4096_h7168_e256_k8_f2048", 4, 8, 4096, 7168,
+                    256, 8, 2048)
+MOE_QWEN3 = MoeShape("moe_qwen3_8r_t8192_h4096_e128_k8_f1536_zipf1.1", 5, 8,
+                     8192, 4096, 128, 8, 1536, zipf_s=1.1)
+
+# small shapes for the CPU oracle tests and the fast GPU parity cases: several
+# tiles in each direction and a ragged expert tail
+MOE_TINY = MoeShape("moe_tiny_4r_t96_h256_e16_k4_f128", 6, 4, 96, 256, 16, 4,
+                    128)
+MOE_TINY_SKEW = MoeShape("moe_tiny_skew_4r_t160_h256_e16_k4_f192", 7, 4, 160,
+                         256, 16, 4, 192, zipf_s=1.1)
+
+
+# ---------------------------------------------------------------------------
+# seeded draws
+# ---------------------------------------------------------------------------
+
+# tensor ids (stable: part of the seed)
+T_A, T_W, T_PEER, T_X, T_LOGITS, T_WG, T_WU, T_WD, T_SEND, T_RET, T_PLOG = range(11)
+
+
+def _gen(wid: int, tid: int, rank: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(((wid * 97 + tid) * 131 + rank) * 1_000_003 + 12345)
+    return g
+
+
+def normal(shape, var, wid, tid, rank, device, dtype=torch.bfloat16):
+    """N(0, var) drawn in fp32 and converted to ``dtype``."""
+    g = _gen(wid, tid, rank, device)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if var != 1.0:
+        t.mul_(math.sqrt(var))
+    return t.to(dtype)
+
+
+def integers(shape, lo, hi, wid, tid, rank, device, dtype=torch.bfloat16):
+    """Uniform integers in [lo, hi] (exact in bf16 for |v| <= 256)."""
+    g = _gen(wid, tid, rank, device)
+    t = torch.randint(lo, hi + 1, shape, generator=g, device=device,
+                      dtype=torch.int32)
+    return t.to(dtype)
+
+
+# ---------------------------------------------------------------------------
+# all-gather + GEMM
+# ---------------------------------------------------------------------------
+
+def ag_inputs(s: AgShape, rank: int, device="cpu", integer=False):
+    """Shards of every rank (shard p is the same whichever rank asks) and the
+    column-parallel weight shard.  Returns dict(a_local, a_peers, w) with
+    ``a_peers[rank] is None``."""
+    shards = []
+    for p in range(s.world):
+        if integer:
+            shards.append(integers((s.m_local, s.k), -4, 4, s.wid, T_A, p, device))
+        else:
+            shards.append(normal((s.m_local, s.k), 1.0, s.wid, T_A, p, device))
+    if integer:
+        w = integers((s.k, s.n), -4, 4, s.wid, T_W, 0, device)
+    else:
+        w = normal((s.k, s.n), 1.0 / s.k, s.wid, T_W, 0, device)
+    peers = [None if p == rank else shards[p] for p in range(s.world)]
+    return dict(a_local=shards[rank], a_peers=peers, w=w)
+
+
+# ---------------------------------------------------------------------------
+# GEMM + reduce-scatter
+# ---------------------------------------------------------------------------
+
+def rs_inputs(s: RsShape, rank: int, device="cpu", integer=False):
+    """A, W and the fp32 rows of chunk ``rank`` that every peer p computed
+    (``peer_slices[rank] is None``).  Same law as the local partial's entries:
+    N(0,1) (K * 1 * 1/K)."""
+    if integer:
+        a = integers((s.m, s.k), -4, 4, s.wid, T_A, rank, device)
+        w = integers((s.k, s.n), -4, 4, s.wid, T_W, 0, device)
+    else:
+        a = normal((s.m, s.k), 1.0, s.wid, T_A, rank, device)
+        w = normal((s.k, s.n), 1.0 / s.k, s.wid, T_W, 0, device)
+    peers = []
+    for p in range(s.world):
+        if p == rank:
+            peers.append(None)
+        elif integer:
+            peers.append(integers((s.m_chunk, s.n), -4096, 4096, s.wid,
+                                  T_PEER, p * 64 + rank, device,
+                                  dtype=torch.float32))
+        else:
+            peers.append(normal((s.m_chunk, s.n), 1.0, s.wid, T_PEER,
+                                p * 64 + rank, device, dtype=torch.float32))
+    return dict(a=a, w=w, peer_slices=peers)
+
+
+# ---------------------------------------------------------------------------
+# expert layer
+# ---------------------------------------------------------------------------
+
+def zipf_bias(s: MoeShape, device="cpu") -> torch.Tensor:
+    """Unnormalised Zipf weight (e+1)^-s per expert, in fp32."""
+    e = torch.arange(s.experts, device=device, dtype=torch.float64)
+    return (e + 1.0).pow(-s.zipf_s).to(torch.float32)
+
+
+def router_logits(s: MoeShape, rank: int, device="cpu", tid=T_LOGITS):
+    lg = normal((s.tokens, s.experts), 1.0, s.wid, tid, rank, device,
+                dtype=torch.float32)
+    if s.zipf_s is not None:
+        lg = lg + zipf_bias(s, device)[None, :]
+    return lg
+
+
+def emulated_peer_counts(s: MoeShape, rank: int, device="cpu"):
+    """Rows each peer p sends to ``rank``, per local expert of ``rank``.
+
+    A peer's routing is emulated from its own seeded logits of the same law by
+    a library top-k: only how many of its tokens land on each of our experts
+    matters here (the rows themselves are seeded), so the tie rule is
+    irrelevant.  Returns int32 [world, e_local] with row ``rank`` zero."""
+    counts = torch.zeros((s.world, s.e_local), dtype=torch.int32)
+    lo = rank * s.e_local
+    for p in range(s.world):
+        if p == rank:
+            continue
+        lg = router_logits(s, p, "cpu", tid=T_PLOG)
+        sel = torch.topk(lg, s.topk, dim=1).indices.reshape(-1)
+        hist = torch.bincount(sel, minlength=s.experts)
+        counts[p] = hist[lo:lo + s.e_local].to(torch.int32)
+    return counts.to(device)
+
+
+def moe_inputs(s: MoeShape, rank: int, device="cpu", with_weights=True):
+    """Everything one rank's expert layer reads.
+
+    x [T,H] bf16 N(0,1); logits [T,E] fp32 N(0,1) (+ Zipf bias);
+    local expert weights wg, wu [E_loc,H,F] N(0,1/H), wd [E_loc,F,H] N(0,1/F);
+    peer_counts [R,E_loc] int32 (emulated routing of the peers);
+    peer_send[p] [n_p,H] bf16 N(0,1): rows p sends us, expert-major;
+    peer_return[d] [peer_cap,H] bf16 N(0,1): results d returns for the rows we
+    send it, in our packed order (only the first send-count rows are read)."""
+    out = {}
+    out["x"] = normal((s.tokens, s.hidden), 1.0, s.wid, T_X, rank, device)
+    out["logits"] = router_logits(s, rank, device)
+    pc = emulated_peer_counts(s, rank, "cpu")
+    out["peer_counts"] = pc.to(device)
+    peer_send, peer_ret = [], []
+    for p in range(s.world):
+        if p == rank:
+            peer_send.append(None)
+            peer_ret.append(None)
+            continue
+        n_p = int(pc[p].sum())
+        peer_send.append(normal((max(n_p, 1), s.hidden), 1.0, s.wid, T_SEND,
+                                p * 64 + rank, device)[:n_p])
+        peer_ret.append(normal((s.peer_cap, s.hidden), 1.0, s.wid, T_RET,
+                               p * 64 + rank, device))
+    out["peer_send"] = peer_send
+    out["peer_return"] = peer_ret
+    if with_weights:
+        out.update(moe_weights(s, rank, device))
+    return out
+
+
+def moe_weights(s: MoeShape, rank: int, device="cpu"):
+    H, F, El = s.hidden, s.ffn, s.e_local
+    wg = torch.empty((El, H, F), dtype=torch.bfloat16, device=device)
+    wu = torch.empty_like(wg)
+    wd = torch.empty((El, F, H), dtype=torch.bfloat16, device=device)
+    for e in range(El):
+        ge = rank * El + e
+        wg[e] = normal((H, F), 1.0 / H, s.wid, T_WG, ge, device)
+        wu[e] = normal((H, F), 1.0 / H, s.wid, T_WU, ge, device)
+        wd[e] = normal((F, H), 1.0 / F, s.wid, T_WD, ge, device)
+    return dict(wg=wg, wu=wu, wd=wd)
+
+
+# ---------------------------------------------------------------------------
+# conversions for handing torch tensors to the NumPy oracle
+# ---------------------------------------------------------------------------
+
+def bf16_bits(t: torch.Tensor):
+    """bf16 tensor -> NumPy uint16 bit patterns (a copy on the host)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view("uint16")
+
+
+def from_bf16_bits(a, device="cpu") -> torch.Tensor:
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(device)

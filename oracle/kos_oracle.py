@@ -1,0 +1,316 @@
+"""CPU oracle for the fused GEMM+collective kernels -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  The product path (the HIP
+library and its Python binding) never does, and shares no code with it.
+
+What it computes are the plain definitions of the collectives and products
+that the KOSMOS persistent kernels fuse.  The kernels only change *when* and
+*by whom* each piece is computed (self-scheduling workgroups, consumer-ordered
+queues, ready flags); the values they must produce are those of the unfused
+operations, which is what is written out here, one step at a time, in the
+order the pages describe them:
+
+* all-gather of sequence shards before a column-parallel GEMM, and scatter and
+  add of the partial results after a row-parallel GEMM [KOSMOS explainer,
+  "Start with the problem" paragraph];
+* the expert layer "from router to fold": tokens travel to the rank that holds
+  their expert, results travel back [same paragraph; KOSMOS arXiv abstract].
+
+Arithmetic is float64 (NumPy/BLAS), which is exact for every integer-valued
+case and more accurate than the kernels' fp32 accumulation otherwise.  bf16
+values enter as uint16 bit patterns and are widened exactly; a bf16 result is
+the round-to-nearest-even of the float64 value.
+
+Readings where the pages are silent (rank-order gather, K x N weights, top-k
+then softmax over the k, ties to the lowest expert index, expert-major
+permutation, contiguous expert->rank map, no dedup, SwiGLU rounding points)
+are stated at each function.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` (brute force, closed forms, invariants).
+``expert_ffn`` is pinned only to a float64 brute-force loop and to closed-form
+special cases (there is no printed example), which fixes its definition but
+not a value from the pages.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float
+# ---------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float values to the nearest bf16, ties to even; returns uint16.
+
+    The rounding is done on the exact float64 value (no double rounding via
+    fp32): x = m * 2^e with 0.5 <= |m| < 1, bf16 keeps 8 significant bits, so
+    the quantum is 2^(e-8), or 2^-133 in bf16's subnormal range.  Values past
+    the largest finite bf16 become infinities.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.exp2(np.maximum(e - 8, -133).astype(np.float64))
+    r = np.rint(x / q) * q          # np.rint rounds half to even
+    with np.errstate(over="ignore"):
+        f = r.astype(np.float32)    # exact: r has <= 8 significant bits
+        big = np.abs(r) > 3.3895313892515355e38   # 0x7F7F, largest finite bf16
+    f = np.where(big, np.copysign(np.float32(np.inf), f), f)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# all-gather + GEMM
+# ---------------------------------------------------------------------------
+
+
+def gather(shards) -> np.ndarray:
+    """The gathered input: shard p's rows at rows [p*m, (p+1)*m), rank order.
+
+    Sequence-parallel shards split the sequence into contiguous pieces, so
+    gathering them is concatenation in rank order [KOSMOS explainer, "Start
+    with the problem"].  Bit copy: the result is the input bytes."""
+    return np.concatenate([np.asarray(s, dtype=np.uint16) for s in shards], axis=0)
+
+
+def gemm(a_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """C = A . W in float64 for bf16 A [M,K] and bf16 W [K,N] (row-major,
+    weight stored K x N)."""
+    return bf16_to_f64(a_bits) @ bf16_to_f64(w_bits)
+
+
+def ag_gemm(a_local, a_peers, w_bits, rank: int, out_dtype: str = "bf16"):
+    """All-gather then GEMM: returns (gathered uint16 [R*m,K], C).
+
+    ``a_peers[p]`` is rank p's shard (entry ``rank`` ignored).  C is bf16 bits
+    (nearest even of the exact product) or float32."""
+    shards = [a_local if p == rank else a_peers[p] for p in range(len(a_peers))]
+    g = gather(shards)
+    c = gemm(g, w_bits)
+    if out_dtype == "bf16":
+        return g, round_bf16(c)
+    return g, c.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# GEMM + reduce-scatter
+# ---------------------------------------------------------------------------
+
+
+def gemm_rs(a_bits, w_bits, peer_slices, rank: int):
+    """GEMM then reduce-scatter, seen from rank ``rank`` of R.
+
+    P = A . W is this rank's partial sum of the full [M,N] output.  Chunk c is
+    rows [c*M/R, (c+1)*M/R); the scatter sends chunk c to rank c, which adds
+    the R partials of its chunk [KOSMOS explainer, "Start with the problem"].
+    ``peer_slices[p]`` (fp32 [M/R,N]) is rank p's partial for chunk ``rank``.
+
+    Returns (partial fp32 [M,N], y fp32 [M/R,N]) with
+    y = sum over p = 0..R-1, ascending, of X_p, X_rank = P[chunk rank]."""
+    R = len(peer_slices)
+    p_full = gemm(a_bits, w_bits)
+    partial = p_full.astype(np.float32)          # what the builders store
+    M = partial.shape[0]
+    mc = M // R
+    acc = np.zeros((mc, partial.shape[1]), dtype=np.float64)
+    for p in range(R):
+        if p == rank:
+            acc += partial[rank * mc:(rank + 1) * mc].astype(np.float64)
+        else:
+            acc += np.asarray(peer_slices[p], dtype=np.float32).astype(np.float64)
+    return partial, acc.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# expert layer: router, permutation, dispatch, FFN, push, fold
+# ---------------------------------------------------------------------------
+
+
+def router(logits: np.ndarray, k: int):
+    """Top-k experts per token and their combine weights.
+
+    Selection: experts in order of descending logit, ties to the lowest
+    expert index (a stable sort of the negated logits; -0.0 ties +0.0).
+    Weights: softmax over the k selected logits, which equals the full
+    softmax renormalised over the k, so they sum to 1.  Returns
+    (idx int32 [T,k], w float32 [T,k])."""
+    lg = np.asarray(logits, dtype=np.float32)
+    order = np.argsort(-lg, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(lg, idx, axis=1).astype(np.float64)
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+    return idx, w.astype(np.float32)
+
+
+def expert_counts(idx: np.ndarray, n_experts: int) -> np.ndarray:
+    """counts[e] = number of (token, slot) pairs routed to expert e."""
+    return np.bincount(np.asarray(idx).reshape(-1), minlength=n_experts).astype(np.int32)
+
+
+def permute(idx: np.ndarray, n_experts: int):
+    """Expert-major packed order of the (token, slot) pairs.
+
+    Pair (t, j) routed to e gets position offset[e] + (number of tokens t' < t
+    routed to e), offset the exclusive scan of the counts (a token reaches an
+    expert at most once).  Returns (perm int32 [T*k], offsets int32 [E+1]);
+    perm[t*k+j] is the pair's position."""
+    flat = np.asarray(idx).reshape(-1)
+    counts = expert_counts(idx, n_experts)
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")     # by (expert, t, j)
+    perm = np.empty(flat.size, dtype=np.int64)
+    perm[order] = np.arange(flat.size)
+    return perm.astype(np.int32), offsets.astype(np.int32)
+
+
+def send_offsets(offsets: np.ndarray, world: int, e_local: int) -> np.ndarray:
+    """Destination d holds experts [d*E_loc, (d+1)*E_loc) (contiguous map), so
+    its rows are packed positions [offsets[d*E_loc], offsets[(d+1)*E_loc])."""
+    return np.array([offsets[d * e_local] for d in range(world + 1)], dtype=np.int64)
+
+
+def dispatch(x_bits, logits, peer_send, peer_counts, world: int, rank: int, k: int):
+    """Router -> permutation -> token movement, for rank ``rank``.
+
+    Returns a dict with idx, w, counts, perm, offsets, send (list: rows for
+    each destination d != rank, in our packed order), grouped (rows of our
+    local experts, expert-major, then by source rank, then in the source's
+    packed order), grouped_offsets [E_loc+1] and row_src [rows, 2] = (source
+    rank, row index in what that source sends us)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, E = logits.shape
+    el = E // world
+    idx, w = router(logits, k)
+    counts = expert_counts(idx, E)
+    perm, offsets = permute(idx, E)
+    token_of = np.empty(T * k, dtype=np.int64)
+    token_of[perm] = np.arange(T * k) // k
+    packed = x_bits[token_of]
+    so = send_offsets(offsets, world, el)
+    send = [None if d == rank else packed[so[d]:so[d + 1]] for d in range(world)]
+    pc = np.asarray(peer_counts, dtype=np.int64)
+    rows, src = [], []
+    gofs = [0]
+    for e in range(el):
+        ge = rank * el + e
+        for p in range(world):
+            if p == rank:
+                lo, hi = offsets[ge], offsets[ge + 1]
+                rows.append(packed[lo:hi])
+                src += [(p, i - so[rank]) for i in range(lo, hi)]
+            else:
+                lo = int(pc[p, :e].sum())
+                n = int(pc[p, e])
+                rows.append(np.asarray(peer_send[p], dtype=np.uint16)[lo:lo + n])
+                src += [(p, i) for i in range(lo, lo + n)]
+        gofs.append(sum(r.shape[0] for r in rows))
+    grouped = np.concatenate(rows, axis=0) if rows else np.zeros((0, x_bits.shape[1]), np.uint16)
+    return dict(idx=idx, w=w, counts=counts, perm=perm, offsets=offsets,
+                send_off=so, send=send, grouped=grouped,
+                grouped_offsets=np.array(gofs, dtype=np.int32),
+                row_src=np.array(src, dtype=np.int32).reshape(-1, 2))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_bits, wg_bits, wu_bits, wd_bits) -> np.ndarray:
+    """SwiGLU expert on rows X (bf16 [n,H]):
+    h = bf16(silu(X.Wg) * (X.Wu)), Y = bf16(h.Wd); returns uint16 [n,H].
+
+    Rows are independent, so any subset of rows can be evaluated alone."""
+    x = bf16_to_f64(x_bits)
+    g = x @ bf16_to_f64(wg_bits)
+    u = x @ bf16_to_f64(wu_bits)
+    h = round_bf16(silu(g) * u)
+    return round_bf16(bf16_to_f64(h) @ bf16_to_f64(wd_bits))
+
+
+def expert_hidden(x_bits, wg_bits, wu_bits) -> np.ndarray:
+    """The rounded SwiGLU hidden h = bf16(silu(X.Wg) * (X.Wu))."""
+    x = bf16_to_f64(x_bits)
+    return round_bf16(silu(x @ bf16_to_f64(wg_bits)) * (x @ bf16_to_f64(wu_bits)))
+
+
+def grouped_ffn(grouped, grouped_offsets, wg, wu, wd) -> np.ndarray:
+    """Expert FFN over every local expert's rows (expert e: rows
+    [grouped_offsets[e], grouped_offsets[e+1]))."""
+    out = np.zeros_like(np.asarray(grouped, dtype=np.uint16))
+    for e in range(len(grouped_offsets) - 1):
+        lo, hi = int(grouped_offsets[e]), int(grouped_offsets[e + 1])
+        if hi > lo:
+            out[lo:hi] = expert_ffn(grouped[lo:hi], wg[e], wu[e], wd[e])
+    return out
+
+
+def push(y_grouped, row_src, world: int, rank: int, peer_rows):
+    """Results travel back: row r of the grouped output whose source is
+    (p, i), p != rank, goes to row i of what we return to p.  ``peer_rows[p]``
+    is how many rows p sent us.  Returns a list (None at ``rank``)."""
+    out = [None if p == rank else np.zeros((int(peer_rows[p]), y_grouped.shape[1]), np.uint16)
+           for p in range(world)]
+    for r, (p, i) in enumerate(np.asarray(row_src)):
+        if p != rank:
+            out[p][i] = y_grouped[r]
+    return out
+
+
+def local_row(e, pos, rank, e_local, offsets, grouped_offsets, peer_counts):
+    """Grouped row holding our own pair at packed position ``pos`` of expert
+    ``e`` (a local expert): after the rows of sources p < rank."""
+    el = e - rank * e_local
+    before = int(np.asarray(peer_counts)[:rank, el].sum())
+    return int(grouped_offsets[el]) + before + int(pos - offsets[e])
+
+
+def fold(idx, w, perm, offsets, y_grouped, grouped_offsets, peer_counts,
+         peer_return, world: int, rank: int, tokens=None):
+    """y[t] = bf16(sum_j w[t,j] * res[t,j]), j ascending.
+
+    res[t,j] is the local expert output when expert idx[t,j] lives here,
+    otherwise row perm[t*k+j] - send_off[d] of what rank d returned.
+    ``tokens`` restricts the evaluation to a subset (rows are independent).
+    ``y_grouped`` must hold the local results the chosen tokens need."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    E = int(len(offsets) - 1)
+    el = E // world
+    so = send_offsets(offsets, world, el)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    out = np.zeros((len(toks), np.asarray(y_grouped).shape[1]), dtype=np.float64)
+    for n, t in enumerate(toks):
+        for j in range(k):
+            e = int(idx[t, j])
+            d = e // el
+            pos = int(perm[t * k + j])
+            if d == rank:
+                r = local_row(e, pos, rank, el, offsets, grouped_offsets, peer_counts)
+                res = bf16_to_f64(y_grouped[r])
+            else:
+                res = bf16_to_f64(peer_return[d][pos - so[d]])
+            out[n] += float(w[t, j]) * res
+    return round_bf16(out)
+
+
+def moe_layer(x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return,
+              world: int, rank: int, k: int):
+    """The whole expert layer for one rank: dispatch, expert FFN, push, fold."""
+    d = dispatch(x_bits, logits, peer_send, peer_counts, world, rank, k)
+    yg = grouped_ffn(d["grouped"], d["grouped_offsets"], wg, wu, wd)
+    pc = np.asarray(peer_counts)
+    out_return = push(yg, d["row_src"], world, rank, pc.sum(axis=1))
+    y = fold(d["idx"], d["w"], d["perm"], d["offsets"], yg, d["grouped_offsets"],
+             pc, peer_return, world, rank)
+    d.update(y_grouped=yg, out_return=out_return, y=y)
+    return d
