@@ -1,0 +1,126 @@
+"""torch-tensor front end of the C ABI (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from ._binding import KOS_BF16, KOS_F32, MoeShape, Opts, check, lib, opts as make_opts, ptr_array
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {ndim}-d tensor")
+
+
+class Workspace:
+    """Device workspace of kos_workspace_bytes() bytes, zeroed once."""
+
+    def __init__(self, device="cuda", stream=None):
+        self.nbytes = int(lib.kos_workspace_bytes())
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        check(lib.kos_workspace_init(self.ptr, self.nbytes, _stream(stream)))
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def status(self, stream=None) -> None:
+        """Synchronizes and raises KosError if a device-side error was recorded."""
+        check(lib.kos_workspace_status(self.ptr, _stream(stream)))
+
+
+def ag_gemm(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w: torch.Tensor,
+            a_gathered: torch.Tensor, c: torch.Tensor, rank: int, ws: Workspace,
+            o: Optional[Opts] = None, stream=None) -> None:
+    """kos_ag_gemm: a_gathered = concat(shards); c = a_gathered @ w."""
+    world = len(a_peers)
+    _need(a_local, torch.bfloat16, "a_local", 2)
+    _need(w, torch.bfloat16, "w", 2)
+    _need(a_gathered, torch.bfloat16, "a_gathered", 2)
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("c must be bf16 or fp32")
+    _need(c, c.dtype, "c", 2)
+    for p, t in enumerate(a_peers):
+        if p != rank:
+            _need(t, torch.bfloat16, f"a_peers[{p}]", 2)
+    m_local, k = a_local.shape
+    n = w.shape[1]
+    peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(a_peers)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_ag_gemm(world, rank, m_local, k, n, _p(a_local), peers, _p(w), _p(a_gathered),
+                          _p(c), KOS_BF16 if c.dtype == torch.bfloat16 else KOS_F32,
+                          ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def gemm_rs(a: torch.Tensor, w: torch.Tensor, peer_slices: Sequence[Optional[torch.Tensor]],
+            partial: torch.Tensor, y: torch.Tensor, rank: int, ws: Workspace,
+            o: Optional[Opts] = None, stream=None) -> None:
+    """kos_gemm_rs: partial = a @ w (fp32); y = reduce of chunk `rank`."""
+    world = len(peer_slices)
+    _need(a, torch.bfloat16, "a", 2)
+    _need(w, torch.bfloat16, "w", 2)
+    _need(partial, torch.float32, "partial", 2)
+    _need(y, torch.float32, "y", 2)
+    for p, t in enumerate(peer_slices):
+        if p != rank:
+            _need(t, torch.float32, f"peer_slices[{p}]", 2)
+    m, k = a.shape
+    n = w.shape[1]
+    peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(peer_slices)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_gemm_rs(world, rank, m, k, n, _p(a), _p(w), peers, _p(partial), _p(y),
+                          ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def moe_shape(world, rank, tokens, hidden, experts, topk, ffn) -> MoeShape:
+    return MoeShape(world, rank, tokens, hidden, experts, topk, ffn, 0)
+
+
+def moe_dispatch(s: MoeShape, x, logits, peer_send, peer_counts, topk_idx, topk_w, counts, perm,
+                 out_send, x_grouped, grouped_offsets, row_src, ws: Workspace,
+                 o: Optional[Opts] = None, stream=None) -> None:
+    """kos_moe_dispatch (see include/kos.h for every buffer's layout)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(logits, torch.float32, "logits", 2)
+    _need(peer_counts, torch.int32, "peer_counts", 2)
+    _need(x_grouped, torch.bfloat16, "x_grouped", 2)
+    send = ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(peer_send)])
+    osend = ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(out_send)])
+    send_cap = max((t.shape[0] for p, t in enumerate(out_send) if p != s.rank), default=0)
+    o = o if o is not None else make_opts()
+    check(lib.kos_moe_dispatch(ctypes.byref(s), _p(x), _p(logits), send, _p(peer_counts),
+                               _p(topk_idx), _p(topk_w), _p(counts), _p(perm), osend, send_cap,
+                               _p(x_grouped), x_grouped.shape[0], _p(grouped_offsets), _p(row_src),
+                               ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def moe_combine(s: MoeShape, x_grouped, grouped_offsets, row_src, w_gate, w_up, w_down,
+                topk_idx, topk_w, counts, perm, peer_counts, peer_return, h, y_grouped,
+                out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+    """kos_moe_combine (see include/kos.h for every buffer's layout)."""
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, torch.bfloat16, name, 3)
+    _need(h, torch.bfloat16, "h", 2)
+    _need(y_grouped, torch.bfloat16, "y_grouped", 2)
+    _need(y, torch.bfloat16, "y", 2)
+    pret = ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(peer_return)])
+    oret = ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(out_return)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_moe_combine(ctypes.byref(s), _p(x_grouped), _p(grouped_offsets), _p(row_src),
+                              x_grouped.shape[0], _p(w_gate), _p(w_up), _p(w_down), _p(topk_idx),
+                              _p(topk_w), _p(counts), _p(perm), _p(peer_counts), pret, _p(h),
+                              _p(y_grouped), oret, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes,
+                              _stream(stream)))

@@ -1,0 +1,222 @@
+// All-gather + GEMM as one persistent kernel (one rank's share).
+//
+// [KOSMOS explainer, "Start with the problem"]: every layer gathers pieces
+// of its input from the other GPUs before a matrix multiplication.
+// ["Role switching only works if ..."]: builders compute their own local
+// shard first while movers fetch remote shards in the order the
+// multiplication needs them.  ["KOSMOS removes the manager"]: movers become
+// builders once their transfers finish (one-way switch).
+//
+// Queues (heads in the workspace):
+//   head[0]  move entries: remote shards in consumption order (rank+1,
+//            rank+2, ... mod world), row blocks ascending, each row block cut
+//            into equal slices; then the local shard's copy into the
+//            gathered output (nobody waits for it).
+//   head[1]  tiles: local shard first, then the remote shards in the same
+//            order; within a shard row block ascending, then column tile.
+// Ready counter per (shard, row block): the number of its slices landed.
+#include "kos_host.h"
+#include "kos_tile.h"
+
+namespace kos {
+
+struct AgParams {
+  int32_t world, rank;
+  int32_t m_local, k, n;
+  const uint16_t* a_local;
+  const uint16_t* peers[8];
+  const uint16_t* w;
+  uint16_t* gathered;
+  void* c;
+  int32_t c_f32;
+  int32_t n_movers;       // tickets below this start as movers
+  int32_t movers_switch;  // movers become builders when moves run out
+  int32_t do_build;       // this launch builds tiles
+  int32_t wait_flags;     // builders wait for remote row blocks
+  uint32_t spin_limit;
+  int32_t rb_per_shard;   // m_local / BM
+  int32_t tiles_n;        // n / BN
+  int32_t rows_per_move;  // rows of one move entry (divides BM)
+  int32_t moves_per_rb;   // BM / rows_per_move
+  int32_t n_move;         // move entries (remote + local)
+  int32_t n_tiles;
+  WsHeader* ws;
+  uint32_t* ready;
+};
+
+template <class S>
+__global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
+  constexpr int BM = S::BM, BN = S::BN;
+  __shared__ uint4 lds[S::LDS_BYTES / 16];
+  __shared__ WgSlots slots;
+  WsHeader* h = p.ws;
+  const int64_t K = p.k, N = p.n;
+  const uint32_t ticket = wg_ticket(h, &slots);
+
+  // ---- mover role -------------------------------------------------------
+  if (ticket < (uint32_t)p.n_movers) {
+    const int32_t per_shard = p.rb_per_shard * p.moves_per_rb;
+    const int32_t n_remote = (p.world - 1) * per_shard;
+    for (;;) {
+      const uint32_t i = wg_claim(&h->head[0], h, &slots);
+      if (i >= (uint32_t)p.n_move) break;
+      int shard, rem;
+      const uint16_t* src_shard;
+      if ((int32_t)i < n_remote) {
+        const int q = 1 + (int)i / per_shard;
+        rem = (int)i % per_shard;
+        shard = (p.rank + q) % p.world;
+        src_shard = p.peers[shard];
+      } else {
+        rem = (int)i - n_remote;
+        shard = p.rank;
+        src_shard = p.a_local;
+      }
+      const int rb = rem / p.moves_per_rb;
+      const int64_t row = (int64_t)rb * BM + (int64_t)(rem % p.moves_per_rb) * p.rows_per_move;
+      wg_copy(p.gathered + ((int64_t)shard * p.m_local + row) * K, src_shard + row * K,
+              (size_t)p.rows_per_move * K * 2);
+      wg_signal(&p.ready[shard * p.rb_per_shard + rb], 1u);
+    }
+    if (!p.movers_switch) {
+      wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
+      return;
+    }
+  }
+
+  // ---- builder role -----------------------------------------------------
+  if (p.do_build) {
+    f32x16 acc[S::TM][S::TN];
+    const int32_t per_q = p.rb_per_shard * p.tiles_n;
+    for (;;) {
+      const uint32_t j = wg_claim(&h->head[1], h, &slots);
+      if (j >= (uint32_t)p.n_tiles) break;
+      const int q = (int)j / per_q;
+      const int rem = (int)j % per_q;
+      const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
+      const int shard = (p.rank + q) % p.world;
+      const uint16_t* A;
+      if (q == 0) {
+        A = p.a_local + (int64_t)rb * BM * K;
+      } else {
+        if (p.wait_flags &&
+            !wg_wait(&p.ready[shard * p.rb_per_shard + rb], (uint32_t)p.moves_per_rb, h, p.spin_limit, j, &slots))
+          break;
+        A = p.gathered + ((int64_t)shard * p.m_local + (int64_t)rb * BM) * K;
+      }
+      BSrc b{p.w + (int64_t)nt * BN, nullptr, N, 0};
+      tile_mainloop<S>(acc, A, K, BM, b, p.k, lds);
+      const int64_t row0 = (int64_t)shard * p.m_local + (int64_t)rb * BM;
+      const int64_t col0 = (int64_t)nt * BN;
+      if (p.c_f32) {
+        float* C = reinterpret_cast<float*>(p.c) + row0 * N + col0;
+        tile_foreach<S>(acc, [&](int r, int c, float v) { C[r * N + c] = v; });
+      } else {
+        uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + row0 * N + col0;
+        tile_foreach<S>(acc, [&](int r, int c, float v) { C[r * N + c] = f32_to_bf16_bits(v); });
+      }
+    }
+  }
+  wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
+}
+
+template <class S>
+static kos_status launch_ag(const AgParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((ag_gemm_kernel<S>), dim3(grid), dim3(S::NT), 0, stream, p);
+  return launch_status("ag_gemm launch");
+}
+
+static kos_status launch_ag_tile(int bm, int bn, const AgParams& p, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256, 2, 4>>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128, 2, 2>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128, 2, 2>>(p, grid, s);
+  return launch_ag<TileShape<64, 64, 2, 2>>(p, grid, s);
+}
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                                  const void* a_local, const void* const* a_peers, const void* w,
+                                  void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (world < 1 || world > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", world);
+  if (rank < 0 || rank >= world) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", rank, world);
+  if (c_dtype != KOS_BF16 && c_dtype != KOS_F32) return fail(KOS_ERR_ARG, "bad c_dtype %d", c_dtype);
+  if (!a_local || !w || !a_gathered || !c) return fail(KOS_ERR_ARG, "null buffer");
+  if (world > 1 && !a_peers) return fail(KOS_ERR_ARG, "a_peers is NULL");
+  for (int p = 0; p < world; ++p)
+    if (p != rank && !a_peers[p]) return fail(KOS_ERR_ARG, "a_peers[%d] is NULL", p);
+  if (m_local <= 0 || k <= 0 || n <= 0 || m_local % 64 || k % 64 || n % 64)
+    return fail(KOS_ERR_SHAPE, "m_local %lld, k %lld, n %lld must be positive multiples of 64", (long long)m_local,
+                (long long)k, (long long)n);
+  if (m_local * world > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20))
+    return fail(KOS_ERR_SHAPE, "sizes too large");
+  if (!aligned16(a_local) || !aligned16(w) || !aligned16(a_gathered) || !aligned16(c))
+    return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  for (int p = 0; p < world; ++p)
+    if (p != rank && !aligned16(a_peers[p])) return fail(KOS_ERR_ALIGN, "a_peers[%d] not 16-byte aligned", p);
+  kos_status st = check_workspace(ws, ws_bytes);
+  if (st != KOS_OK) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != KOS_OK) return st;
+  kos_opts o;
+  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+
+  // Tile: the largest supported tile that divides the shard rows and columns.
+  int bm = 64, bn = 64;
+  if (m_local % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
+  else if (m_local % 128 == 0 && n % 128 == 0) bm = 128, bn = 128;
+
+  AgParams p{};
+  p.world = world;
+  p.rank = rank;
+  p.m_local = (int32_t)m_local;
+  p.k = (int32_t)k;
+  p.n = (int32_t)n;
+  p.a_local = static_cast<const uint16_t*>(a_local);
+  for (int q = 0; q < world; ++q) p.peers[q] = q == rank ? nullptr : static_cast<const uint16_t*>(a_peers[q]);
+  p.w = static_cast<const uint16_t*>(w);
+  p.gathered = static_cast<uint16_t*>(a_gathered);
+  p.c = c;
+  p.c_f32 = c_dtype == KOS_F32;
+  p.spin_limit = o.spin_limit;
+  p.rb_per_shard = (int32_t)(m_local / bm);
+  p.tiles_n = (int32_t)(n / bn);
+  // Move entries of about 512 KiB: whole rows, dividing the row block.
+  int rows = (int)((512 * 1024) / (k * 2));
+  if (rows < 1) rows = 1;
+  if (rows > bm) rows = bm;
+  while (bm % rows) --rows;
+  p.rows_per_move = rows;
+  p.moves_per_rb = bm / rows;
+  p.n_move = world * p.rb_per_shard * p.moves_per_rb;
+  p.n_tiles = world * p.rb_per_shard * p.tiles_n;
+  p.ws = static_cast<WsHeader*>(ws);
+  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = o.grid;
+  if (o.mode == KOS_MODE_UNFUSED) {
+    AgParams mv = p;           // launch 1: the whole all-gather
+    mv.n_movers = grid;
+    mv.movers_switch = 0;
+    mv.do_build = 0;
+    if ((st = launch_ag_tile(bm, bn, mv, grid, s)) != KOS_OK) return st;
+    AgParams gm = p;           // launch 2: the whole GEMM
+    gm.n_movers = 0;
+    gm.n_move = 0;
+    gm.do_build = 1;
+    gm.wait_flags = 0;
+    return launch_ag_tile(bm, bn, gm, grid, s);
+  }
+  if (o.n_movers < 1 || o.n_movers >= grid)
+    return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, grid);
+  p.n_movers = o.n_movers;
+  p.movers_switch = o.mode == KOS_MODE_FUSED;
+  p.do_build = 1;
+  p.wait_flags = 1;
+  return launch_ag_tile(bm, bn, p, grid, s);
+}

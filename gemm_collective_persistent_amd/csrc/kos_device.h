@@ -1,0 +1,182 @@
+// Device runtime of the persistent self-scheduling kernels (gfx950).
+//
+// One workgroup (4 or 8 wave64s) per compute unit.  Workgroups
+// take entries from atomic queue heads ("ticket rail"), publish finished
+// pieces through ready counters, and wait on them with a bounded poll
+// [KOSMOS explainer, "KOSMOS removes the manager" and "Role switching only
+// works if ..." paragraphs].
+//
+// Memory ordering: the MI355X's eight XCDs each have their own L2, which is
+// not coherent with the others for ordinary accesses.  A producer therefore
+// makes its stores visible at agent scope (release fence in every thread,
+// which waits for the stores and writes the L2 back) before one thread bumps
+// the counter; a consumer polls the counter with relaxed agent-scope loads
+// and then issues an agent-scope acquire fence in every thread (which
+// invalidates the stale lines) before it reads the data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kos_common.h"
+
+namespace kos {
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// atomics and fences (agent scope = the whole GPU)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Records the first device-side error and tells every workgroup to drain.
+__device__ inline void raise_error(WsHeader* h, uint32_t code, uint32_t info) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&h->status, &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    st_relaxed(&h->err_info, info);
+  }
+  st_relaxed(&h->abort, 1u);
+}
+
+__device__ __forceinline__ bool aborted(WsHeader* h) { return ld_relaxed(&h->abort) != 0; }
+
+// Per-workgroup LDS slots used by the helpers below.
+struct WgSlots {
+  uint32_t claim;
+  int32_t ok;
+  uint32_t aux[6];
+};
+
+constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
+
+// Thread 0 takes the next entry of a queue; every thread gets it.  Returns
+// kNoEntry once an error has been recorded, so that the decision to stop is
+// the same in every wave.
+__device__ __forceinline__ uint32_t wg_claim(uint32_t* head, WsHeader* h, WgSlots* s) {
+  __syncthreads();
+  if (threadIdx.x == 0) s->claim = aborted(h) ? kNoEntry : add_relaxed(head, 1u);
+  __syncthreads();
+  return s->claim;
+}
+
+// Makes this workgroup's global stores visible GPU-wide, then adds `v` to a
+// ready counter.
+__device__ __forceinline__ void wg_signal(uint32_t* counter, uint32_t v) {
+  fence_release();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until *counter >= target.  Bounded: after `limit` polls it records
+// KOS_ERR_TIMEOUT (with `info`) and returns false; it also returns false as
+// soon as another workgroup has recorded an error.
+__device__ inline bool wg_wait(const uint32_t* counter, uint32_t target, WsHeader* h,
+                               uint32_t limit, uint32_t info, WgSlots* s) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint32_t it = 0;
+    while (ld_relaxed(counter) < target) {
+      if (aborted(h)) { ok = 0; break; }
+      if (++it >= limit) { raise_error(h, KOS_ERR_TIMEOUT, info); ok = 0; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s->ok = ok;
+  }
+  __syncthreads();
+  const bool ok = s->ok != 0;
+  fence_acquire();
+  return ok;
+}
+
+// Non-blocking readiness test by thread 0, broadcast (no fence: callers that
+// act on `true` must still call wg_wait or fence_acquire before reading).
+__device__ __forceinline__ bool wg_ready(const uint32_t* counter, uint32_t target, WgSlots* s) {
+  __syncthreads();
+  if (threadIdx.x == 0) s->ok = ld_relaxed(counter) >= target ? 1 : 0;
+  __syncthreads();
+  return s->ok != 0;
+}
+
+// Role assignment ticket: arrival order of the workgroups.
+__device__ __forceinline__ uint32_t wg_ticket(WsHeader* h, WgSlots* s) {
+  __syncthreads();
+  if (threadIdx.x == 0) s->claim = add_relaxed(&h->ticket, 1u);
+  __syncthreads();
+  return s->claim;
+}
+
+// Departure: the last workgroup out returns the workspace to all-zero (queue
+// heads, tickets, the first `n_counters` ready counters), keeping only the
+// sticky error word, so the next call needs no clearing launch.
+__device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_counters, WgSlots* s) {
+  fence_release();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s->claim = __hip_atomic_fetch_add(&h->exit_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s->claim != gridDim.x - 1) return;
+  fence_acquire();
+  for (uint32_t i = threadIdx.x; i < n_counters; i += blockDim.x) st_relaxed(&counters[i], 0u);
+  if (threadIdx.x < kNumHeads) st_relaxed(&h->head[threadIdx.x], 0u);
+  if (threadIdx.x == 0) {
+    st_relaxed(&h->ticket, 0u);
+    st_relaxed(&h->abort, 0u);
+    st_relaxed(&h->exit_count, 0u);
+  }
+  fence_release();
+}
+
+// ---------------------------------------------------------------------------
+// movers: coalesced 128-bit copies
+// ---------------------------------------------------------------------------
+
+// Copies `bytes` (a multiple of 16) from src to dst with the whole
+// workgroup; consecutive threads touch consecutive 16-byte chunks and each
+// thread keeps 8 loads in flight.
+__device__ inline void wg_copy(void* __restrict__ dst, const void* __restrict__ src, size_t bytes) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const size_t n = bytes >> 4;
+  const size_t nt = blockDim.x;
+  size_t i = threadIdx.x;
+  constexpr int U = 8;
+  for (; i + (U - 1) * nt < n; i += U * nt) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + u * nt]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + u * nt] = v[u];
+  }
+  for (; i < n; i += nt) d[i] = __builtin_nontemporal_load(&s[i]);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);   // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+
+}  // namespace kos

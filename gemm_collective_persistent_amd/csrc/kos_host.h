@@ -1,0 +1,35 @@
+// Host-side helpers shared by the entry points: error reporting, device
+// properties, workspace and option checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kos_common.h"
+
+namespace kos {
+
+// Records a thread-local message for kos_last_error() and returns `s`.
+kos_status fail(kos_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+struct DeviceInfo {
+  int device = -1;
+  int cus = 0;
+  bool gfx950 = false;
+};
+
+// Properties of the current device (cached per device).
+kos_status current_device(DeviceInfo* out);
+
+// Validates a workspace pointer/size.
+kos_status check_workspace(const void* ws, size_t ws_bytes);
+
+// Fills `o` from `in` (NULL -> defaults), resolving the default crew size
+// for the peer link and the grid.  Validates enums and ranges.
+kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, kos_opts* o);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Maps a launch error to a status.
+kos_status launch_status(const char* what);
+
+}  // namespace kos

@@ -1,0 +1,276 @@
+/*
+ * kos.h -- C ABI of the KOSMOS-style self-scheduling persistent kernels for
+ * MI355X (gfx950): collectives fused into their GEMMs, run on one GPU's share.
+ *
+ * Sources of the operations (the two KOSMOS pages that describe the method):
+ *   [explainer]  "KOSMOS -- Self-scheduling persistent kernels -- What does it
+ *                mean?" (learnaivisually.com), paragraphs "Start with the
+ *                problem", "KOSMOS removes the manager", "Role switching only
+ *                works if ...", "A worked example".
+ *   [abstract]   "KOSMOS: Self-scheduling Persistent Kernels for
+ *                Communication-Compute Overlap", arXiv 2611.07477, abstract.
+ *
+ * Every entry point launches ONE persistent kernel (two for the unfused
+ * baseline) with one workgroup per compute unit.  Workgroups take entries
+ * from atomic queues laid out in the order consumers need them and switch
+ * roles as ready flags show which data has landed [explainer, "KOSMOS
+ * removes the manager"; "Role switching only works if ..."].
+ *
+ * One rank's share is computed.  The other ranks of a world of `world`
+ * ranks are emulated: what they would send arrives as ordinary buffers
+ * (device memory, or host memory mapped for the device to model a slower
+ * link); what this rank would send them is written to output buffers.
+ *
+ * Conventions
+ *   - Matrices are row-major and dense (leading dimension = column count).
+ *   - bf16 is IEEE bfloat16; products accumulate in fp32; bf16 results are
+ *     rounded to nearest even.
+ *   - Every pointer argument not called "host array" is a device-accessible
+ *     address (device memory, or pinned host memory mapped for the device
+ *     where stated).  "host array" arguments are small host-side arrays of
+ *     such pointers, read during the call only.
+ *   - The caller allocates every buffer.  The library allocates nothing on
+ *     the call path and keeps no pointer after the call returns.
+ *   - All calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Inputs must stay valid and outputs untouched until
+ *     the stream reaches the call.
+ *   - `ws` is a workspace of `kos_workspace_bytes()` bytes, zeroed once with
+ *     kos_workspace_init().  Every call leaves it zeroed again (the last
+ *     workgroup to finish resets it), except for the sticky error word that
+ *     kos_workspace_status() reads and clears.  Calls that share one
+ *     workspace must be ordered on one stream; concurrent calls need
+ *     separate workspaces.
+ *
+ * Errors
+ *   - Argument errors are detected before any launch and returned
+ *     synchronously; nothing is launched then.  kos_last_error() gives a
+ *     thread-local message for the last non-OK status.
+ *   - Device-side errors (a ready flag that never arrives within the spin
+ *     limit, a capacity overflow) cannot be returned synchronously: the
+ *     kernel records the first one in the workspace, every workgroup drains
+ *     and exits (no hang), and kos_workspace_status() reports it.  Outputs of
+ *     such a call are undefined.
+ */
+#ifndef KOS_H_
+#define KOS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kos_status {
+  KOS_OK = 0,
+  KOS_ERR_ARG = 1,          /* null pointer, bad enum, world/rank out of range   */
+  KOS_ERR_SHAPE = 2,        /* sizes not supported (see each entry point)        */
+  KOS_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned                   */
+  KOS_ERR_WORKSPACE = 4,    /* ws null or smaller than kos_workspace_bytes()     */
+  KOS_ERR_HIP = 5,          /* a HIP runtime call failed (launch, sync, copy)    */
+  KOS_ERR_UNSUPPORTED = 6,  /* no gfx950 device, or a mode this op lacks         */
+  KOS_ERR_TIMEOUT = 7,      /* device: a ready flag did not arrive in time       */
+  KOS_ERR_CAPACITY = 8      /* device: routed rows exceed a caller capacity      */
+} kos_status;
+
+typedef enum kos_dtype { KOS_BF16 = 0, KOS_F32 = 1 } kos_dtype;
+
+/* How the collective and the GEMM share the GPU.
+ *   FUSED   one persistent launch; roles switch as readiness dictates.
+ *   FIXED   one persistent launch; a fixed crew of `n_movers` workgroups
+ *           only communicates (or only reduces), the rest only compute:
+ *           the "manager who assigns the crew at opening time" baseline
+ *           [explainer, "Picture a restaurant kitchen" paragraph].
+ *   UNFUSED two launches: the whole collective step, then the whole GEMM
+ *           (or GEMM then reduction), same tile code. */
+typedef enum kos_mode { KOS_MODE_FUSED = 0, KOS_MODE_FIXED = 1, KOS_MODE_UNFUSED = 2 } kos_mode;
+
+/* GEMM+reduce-scatter output order: band by band across every rank's chunk
+ * (the consumer order), or chunk after chunk, row by row (the ablation the
+ * explainer reports as 1.41-1.45x slower) ["Role switching only works if"]. */
+typedef enum kos_rs_order { KOS_RS_BAND = 0, KOS_RS_ROW = 1 } kos_rs_order;
+
+typedef struct kos_opts {
+  int32_t mode;         /* kos_mode                                            */
+  int32_t n_movers;     /* workgroups that START in the communication role (and,
+                           under FIXED, stay there); < 0 = the library's default
+                           for the peer link.  Never tuned per shape.          */
+  int32_t rs_order;     /* kos_rs_order (kos_gemm_rs only)                     */
+  int32_t grid;         /* workgroups; 0 = one per compute unit.  Must not
+                           exceed the compute-unit count (all co-resident).    */
+  uint32_t spin_limit;  /* polls of a ready flag before KOS_ERR_TIMEOUT; 0 =
+                           default (about a few seconds).                      */
+  int32_t peer_link;    /* 0: peers' buffers in device memory; 1: in pinned,
+                           device-mapped host memory (PCIe).  Only picks the
+                           default crew size.                                  */
+  int32_t reserved[2];  /* must be 0                                            */
+} kos_opts;
+
+/* Fills `o` with the defaults (FUSED, default crew, band order, full grid). */
+void kos_opts_default(kos_opts* o);
+
+/* Bytes of workspace every entry point needs (a fixed size). */
+size_t kos_workspace_bytes(void);
+
+/* Zeroes a workspace on `stream` (asynchronous).  Call once after allocating. */
+kos_status kos_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronizes `stream`, then returns the first device-side error recorded
+ * in `ws` since the last call of this function (KOS_OK if none) and clears
+ * it.  KOS_ERR_HIP if the synchronization itself fails. */
+kos_status kos_workspace_status(void* ws, void* stream);
+
+/* Thread-local description of the last non-OK status returned on this
+ * thread ("" if none).  Valid until the next library call on the thread. */
+const char* kos_last_error(void);
+
+/* Number of compute units of the current device (0 if none). */
+int32_t kos_device_cu_count(void);
+
+/*
+ * All-gather + GEMM, one rank's share [explainer, "Start with the problem":
+ * every layer gathers pieces of its input from the other GPUs before a
+ * matrix multiplication; "Role switching only works if": the local shard is
+ * computed first while movers fetch remote shards in the order the
+ * multiplication needs them; "KOSMOS removes the manager": movers become
+ * builders once their transfers finish].
+ *
+ *   G = [S_0; S_1; ...; S_{world-1}]   (rank-order concatenation of shards)
+ *   C = G . W
+ *
+ * world      ranks, 1..8;   rank: this rank, 0..world-1
+ * m_local    rows per shard (> 0);  k: columns of a shard = rows of W;
+ *            n: columns of W and C
+ * a_local    bf16 [m_local, k]: S_rank
+ * a_peers    host array[world]: a_peers[p] = S_p, bf16 [m_local, k], for
+ *            p != rank (a_peers[rank] is ignored and may be NULL); device
+ *            memory or pinned device-mapped host memory
+ * w          bf16 [k, n] (the weight shard, stored K x N)
+ * a_gathered out bf16 [world*m_local, k]: G, a bit copy of the shards
+ * c          out [world*m_local, n] of c_dtype (KOS_BF16 or KOS_F32)
+ * Shapes: k % 64 == 0, n % 64 == 0 and m_local % 64 == 0 (KOS_ERR_SHAPE
+ * otherwise); all pointers 16-byte aligned (KOS_ERR_ALIGN).
+ */
+kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                       const void* a_local, const void* const* a_peers, const void* w,
+                       void* a_gathered, void* c, int32_t c_dtype,
+                       const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * GEMM + reduce-scatter, one rank's share [explainer, "Start with the
+ * problem": scatter and add the partial results after the multiplication;
+ * "Role switching only works if": output produced band by band across every
+ * GPU's chunk so every GPU's reducers start after the first band; "KOSMOS
+ * removes the manager": builders join the reduction when the tiles run out].
+ *
+ *   P = A . W                     (this rank's fp32 partial of the output)
+ *   chunk c = rows [c*m/world, (c+1)*m/world)
+ *   y = sum_{p=0..world-1, ascending} X_p,  X_rank = P[chunk rank],
+ *       X_p = peer_slices[p] (p's partial of chunk `rank`), fp32 adds.
+ *
+ * world, rank  as above;  m, k, n: A is [m, k], W is [k, n]
+ * a            bf16 [m, k];  w: bf16 [k, n]
+ * peer_slices  host array[world] of fp32 [m/world, n] (entry `rank` ignored)
+ * partial      out fp32 [m, n]: P.  Rows of chunk c != rank stand for the
+ *              pushes into peer c's inbox; rows of chunk `rank` are staging.
+ * y            out fp32 [m/world, n]
+ * Band height = the builder tile height; a band of chunk `rank` is reduced
+ * once this rank's tiles of that band are stored (peers run the same order
+ * at the same pace, so their slices of the band are taken as ready then).
+ * Shapes: m % world == 0, (m/world) % 64 == 0, k % 64 == 0, n % 64 == 0.
+ */
+kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n,
+                       const void* a, const void* w, const float* const* peer_slices,
+                       float* partial, float* y,
+                       const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/* Shape of an expert layer seen from one rank.  Experts are spread over the
+ * ranks contiguously: rank d holds experts [d*E_loc, (d+1)*E_loc),
+ * E_loc = experts / world. */
+typedef struct kos_moe_shape {
+  int32_t world, rank;
+  int32_t tokens;   /* T: this rank's tokens                                 */
+  int32_t hidden;   /* H                                                      */
+  int32_t experts;  /* E (global), a multiple of world, <= 1024              */
+  int32_t topk;     /* k, 1..min(E, 16)                                       */
+  int32_t ffn;      /* F: expert hidden width                                 */
+  int32_t reserved; /* must be 0                                              */
+} kos_moe_shape;
+
+/*
+ * Expert layer, dispatch direction: router -> permutation -> token movement
+ * [abstract: an entire expert layer "from router to fold"; explainer, "Start
+ * with the problem": tokens travel to the GPU that holds their expert].
+ *
+ * Router: per token, the k experts of largest logit in descending order,
+ * ties to the lowest expert index; weights = softmax over the k selected
+ * logits (fp32).  Packed order: pairs (t, j) sorted by (expert, t); pair
+ * (t, j) of expert e sits at offset[e] + #{t' < t routed to e}.  One row per
+ * pair (a token sent twice to one rank is sent twice).
+ *
+ * x            bf16 [T, H];  logits: fp32 [T, E]
+ * peer_send    host array[world]: rows peer p sends us (p != rank), bf16,
+ *              expert-major over our local experts, in p's packed order
+ * peer_counts  int32 [world, E_loc] (device): rows p sends us per local
+ *              expert; row `rank` must be 0
+ * topk_idx     out int32 [T, k];  topk_w: out fp32 [T, k]
+ * counts       out int32 [E]: pairs routed to each expert (global)
+ * perm         out int32 [T*k]: packed position of pair (t, j)
+ * out_send     host array[world] of out bf16 [send_cap, H]: rows for peer
+ *              d != rank, i.e. our packed rows of d's experts, in order
+ * x_grouped    out bf16 [grouped_cap, H]: rows of our local experts,
+ *              expert-major, then by source rank, then in source order
+ * grouped_offsets out int32 [E_loc + 1]: expert e's rows start here
+ * row_src      out int32 [grouped_cap, 2]: (source rank, row index in what
+ *              that source sends us) of every grouped row
+ * Capacities overflow -> KOS_ERR_CAPACITY (device, see kos_workspace_status);
+ * send_cap >= T*min(k, E_loc) and grouped_cap >= sum(peer_counts) +
+ * T*min(k, E_loc) never overflow.  Shapes: H % 64 == 0.
+ */
+kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* logits,
+                            const void* const* peer_send, const int32_t* peer_counts,
+                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* perm,
+                            void* const* out_send, int64_t send_cap,
+                            void* x_grouped, int64_t grouped_cap, int32_t* grouped_offsets,
+                            int32_t* row_src,
+                            const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert layer, combine direction: grouped SwiGLU expert GEMMs, results
+ * pushed back to their source ranks, and the weighted fold of this rank's
+ * tokens [abstract; explainer, "KOSMOS removes the manager": in the combine
+ * step a workgroup pushes any ready result and otherwise builds a tile].
+ *
+ *   h  = bf16( silu(X_e . Wg_e) * (X_e . Wu_e) )      fp32 silu and product
+ *   Yg = bf16( h . Wd_e )                              per local expert e
+ *   out_return[p][i] = Yg[r] for the grouped row r with row_src (p, i), p != rank
+ *   y[t] = bf16( sum_{j ascending} topk_w[t,j] * res(t,j) ), fp32 accumulate,
+ *   res(t,j) = Yg row of pair (t,j) if its expert is local, else row
+ *              perm[t*k+j] - send_off[d] of peer_return[d], d = expert's rank.
+ *
+ * x_grouped, grouped_offsets, row_src, topk_idx, topk_w, counts, perm,
+ * peer_counts: as produced / consumed by kos_moe_dispatch (device)
+ * w_gate, w_up bf16 [E_loc, H, F];  w_down bf16 [E_loc, F, H]
+ * peer_return  host array[world] of bf16 [>= rows we sent d, H] (entry
+ *              `rank` ignored): results d returns, in our packed order
+ * h            out bf16 [grouped_cap, F] (the SwiGLU hidden, kept for
+ *              inspection);  y_grouped: out bf16 [grouped_cap, H]
+ * out_return   host array[world] of out bf16 [rows p sent us, H]
+ * y            out bf16 [T, H]
+ * Shapes: H % 128 == 0, F % 128 == 0.
+ */
+kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
+                           const int32_t* grouped_offsets, const int32_t* row_src,
+                           int64_t grouped_cap,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* counts, const int32_t* perm,
+                           const int32_t* peer_counts,
+                           const void* const* peer_return,
+                           void* h, void* y_grouped, void* const* out_return, void* y,
+                           const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KOS_H_ */

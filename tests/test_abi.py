@@ -1,0 +1,56 @@
+"""The C-ABI library: loads, exports every declared symbol, validates
+arguments before touching a device (CPU only: no compute calls)."""
+import ctypes
+import os
+
+import pytest
+
+from kos_testutil import header_symbols
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kos.h")
+
+
+def test_library_exports_every_declared_symbol():
+    import gemm_collective_persistent_amd as kos
+    declared = header_symbols(HEADER)
+    assert declared, "no declarations parsed"
+    missing = [s for s in declared if not hasattr(kos.lib, s)]
+    assert not missing, f"declared in kos.h but not exported: {missing}"
+    assert sorted(kos.EXPORTS) == declared
+
+
+def test_opts_defaults_and_workspace_size():
+    import gemm_collective_persistent_amd as kos
+    o = kos.opts()
+    assert (o.mode, o.n_movers, o.rs_order, o.grid, o.spin_limit, o.peer_link) == (0, -1, 0, 0, 0, 0)
+    assert kos.lib.kos_workspace_bytes() >= 16 << 20
+
+
+def _ag(kos, **over):
+    lib = kos.lib
+    fake = ctypes.c_void_p(0x10000)           # never dereferenced: validation fails first
+    peers = kos._binding.ptr_array([None, 0x10000, 0x10000, 0x10000])
+    args = dict(world=4, rank=0, m=64, k=256, n=256, a=fake, peers=peers, w=fake, g=fake, c=fake,
+                dt=0, ws=fake, wsb=lib.kos_workspace_bytes())
+    args.update(over)
+    o = kos.opts()
+    return lib.kos_ag_gemm(args["world"], args["rank"], args["m"], args["k"], args["n"], args["a"],
+                           args["peers"], args["w"], args["g"], args["c"], args["dt"], ctypes.byref(o),
+                           args["ws"], args["wsb"], None)
+
+
+def test_ag_gemm_argument_validation():
+    import gemm_collective_persistent_amd as kos
+    from gemm_collective_persistent_amd._binding import (KOS_ERR_ALIGN, KOS_ERR_ARG, KOS_ERR_SHAPE,
+                                                         KOS_ERR_WORKSPACE)
+    assert _ag(kos, world=9) == KOS_ERR_ARG
+    assert _ag(kos, rank=4) == KOS_ERR_ARG
+    assert _ag(kos, dt=7) == KOS_ERR_ARG
+    assert _ag(kos, a=None) == KOS_ERR_ARG
+    assert _ag(kos, peers=kos._binding.ptr_array([None, None, 0x10000, 0x10000])) == KOS_ERR_ARG
+    assert _ag(kos, k=100) == KOS_ERR_SHAPE
+    assert _ag(kos, m=0) == KOS_ERR_SHAPE
+    assert _ag(kos, a=ctypes.c_void_p(0x10008)) == KOS_ERR_ALIGN
+    assert _ag(kos, wsb=1024) == KOS_ERR_WORKSPACE
+    assert b"workspace" in kos.lib.kos_last_error()
