@@ -1,0 +1,223 @@
+// GEMM + reduce-scatter as one persistent kernel (one rank's share).
+//
+// [KOSMOS explainer, "Start with the problem"]: after a row-parallel matrix
+// multiplication the partial results are scattered and added.
+// ["Role switching only works if ..."]: output is produced band by band
+// across every GPU's chunk, so every GPU's reducers can start after the
+// first band is ready; producing it row by row instead is the slower
+// ablation.  ["KOSMOS removes the manager"]: builders join the reduction
+// when the multiplication tiles run out (one-way switch).
+//
+// Chunk c = rows [c*mc, (c+1)*mc), mc = m/world; band b of a chunk = its
+// rows [b*BM, (b+1)*BM).
+// Queues:
+//   head[1]  tiles.  Band order: band b, then chunk c ascending, then
+//            column tile.  Row order: chunk c, then band, then column tile.
+//            Every tile stores its fp32 partial into `partial` (rows of
+//            chunk c != rank stand for the push into rank c's inbox); tiles
+//            of our own chunk then bump ready[band * tiles_n + col].
+//   head[2]  reduce entries (band b, column tile) of our own chunk, b
+//            ascending then column: y = sum_p X_p in ascending p (fp32),
+//            X_rank = partial[chunk rank], X_p = peer_slices[p].  Gated on
+//            the ready counter of our own tile at (b, column).  The peers'
+//            slices of a band are taken as ready together with ours: every
+//            rank runs the same order at the same pace.
+#include "kos_host.h"
+#include "kos_tile.h"
+
+namespace kos {
+
+struct RsParams {
+  int32_t world, rank;
+  int32_t m, k, n, mc;
+  const uint16_t* a;
+  const uint16_t* w;
+  const float* peers[8];
+  float* partial;
+  float* y;
+  int32_t row_order;
+  int32_t n_reducers;       // tickets below this start as reducers
+  int32_t builders_switch;  // builders become reducers when tiles run out
+  int32_t do_build, do_reduce, wait_flags;
+  uint32_t spin_limit;
+  int32_t bands;            // mc / BM
+  int32_t tiles_n;          // n / BN
+  int32_t n_tiles, n_reduce;
+  WsHeader* ws;
+  uint32_t* ready;
+};
+
+// y[rows, cols] of one reduce entry: BM x BN floats, float4 per thread.
+template <int BM, int BN>
+__device__ inline void reduce_entry(const RsParams& p, int band, int col_tile) {
+  const int64_t N = p.n;
+  const int64_t r0 = (int64_t)band * BM;                 // row inside the chunk
+  const int64_t c0 = (int64_t)col_tile * BN;
+  constexpr int V = BN / 4;                              // float4 per row
+  const float* own = p.partial + ((int64_t)p.rank * p.mc + r0) * N + c0;
+  for (int e = threadIdx.x; e < BM * V; e += blockDim.x) {
+    const int row = e / V, v = e % V;
+    const int64_t off = row * N + v * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q >= p.world) break;
+      f32x4 x;
+      if (q == p.rank)
+        x = *reinterpret_cast<const f32x4*>(own + off);
+      else
+        x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.peers[q] + (r0 * N + c0) + off));
+      acc += x;
+    }
+    *reinterpret_cast<f32x4*>(p.y + (r0 * N + c0) + off) = acc;
+  }
+}
+
+template <class S>
+__global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
+  constexpr int BM = S::BM, BN = S::BN;
+  __shared__ uint4 lds[S::LDS_BYTES / 16];
+  __shared__ WgSlots slots;
+  WsHeader* h = p.ws;
+  const int64_t K = p.k, N = p.n;
+  const uint32_t ticket = wg_ticket(h, &slots);
+  const bool starts_reducer = p.do_reduce && ticket < (uint32_t)p.n_reducers;
+
+  // ---- builder role -----------------------------------------------------
+  if (p.do_build && !starts_reducer) {
+    f32x16 acc[S::TM][S::TN];
+    const int32_t per_band = p.world * p.tiles_n;  // band order: tiles of one band
+    const int32_t per_chunk = p.bands * p.tiles_n; // row order: tiles of one chunk
+    for (;;) {
+      const uint32_t j = wg_claim(&h->head[1], h, &slots);
+      if (j >= (uint32_t)p.n_tiles) break;
+      int band, chunk, col;
+      if (!p.row_order) {
+        band = (int)j / per_band;
+        const int rem = (int)j % per_band;
+        chunk = rem / p.tiles_n;
+        col = rem % p.tiles_n;
+      } else {
+        chunk = (int)j / per_chunk;
+        const int rem = (int)j % per_chunk;
+        band = rem / p.tiles_n;
+        col = rem % p.tiles_n;
+      }
+      const int64_t row0 = (int64_t)chunk * p.mc + (int64_t)band * BM;
+      BSrc b{p.w + (int64_t)col * BN, nullptr, N, 0};
+      tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k, lds);
+      float* P = p.partial + row0 * N + (int64_t)col * BN;
+      tile_foreach<S>(acc, [&](int r, int c, float v) { P[r * N + c] = v; });
+      if (chunk == p.rank) wg_signal(&p.ready[band * p.tiles_n + col], 1u);
+    }
+    if (!p.builders_switch || !p.do_reduce) {
+      wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
+      return;
+    }
+  }
+
+  // ---- reducer role -----------------------------------------------------
+  if (p.do_reduce) {
+    for (;;) {
+      const uint32_t i = wg_claim(&h->head[2], h, &slots);
+      if (i >= (uint32_t)p.n_reduce) break;
+      const int band = (int)i / p.tiles_n, col = (int)i % p.tiles_n;
+      if (p.wait_flags && !wg_wait(&p.ready[i], 1u, h, p.spin_limit, i, &slots)) break;
+      reduce_entry<BM, BN>(p, band, col);
+    }
+  }
+  wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
+}
+
+template <class S>
+static kos_status launch_rs(const RsParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_rs_kernel<S>), dim3(grid), dim3(S::NT), 0, stream, p);
+  return launch_status("gemm_rs launch");
+}
+
+static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128, 2, 2>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128, 2, 2>>(p, grid, s);
+  return launch_rs<TileShape<64, 64, 2, 2>>(p, grid, s);
+}
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
+                                  const void* w, const float* const* peer_slices, float* partial, float* y,
+                                  const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+  if (world < 1 || world > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", world);
+  if (rank < 0 || rank >= world) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", rank, world);
+  if (!a || !w || !partial || !y) return fail(KOS_ERR_ARG, "null buffer");
+  if (world > 1 && !peer_slices) return fail(KOS_ERR_ARG, "peer_slices is NULL");
+  for (int p = 0; p < world; ++p)
+    if (p != rank && !peer_slices[p]) return fail(KOS_ERR_ARG, "peer_slices[%d] is NULL", p);
+  if (m <= 0 || k <= 0 || n <= 0 || m % world || (m / world) % 64 || k % 64 || n % 64)
+    return fail(KOS_ERR_SHAPE, "m %lld (m/world a multiple of 64), k %lld, n %lld (multiples of 64) unsupported",
+                (long long)m, (long long)k, (long long)n);
+  if (m > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20)) return fail(KOS_ERR_SHAPE, "sizes too large");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(partial) || !aligned16(y))
+    return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  for (int p = 0; p < world; ++p)
+    if (p != rank && !aligned16(peer_slices[p])) return fail(KOS_ERR_ALIGN, "peer_slices[%d] not aligned", p);
+  kos_status st = check_workspace(ws, ws_bytes);
+  if (st != KOS_OK) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != KOS_OK) return st;
+  kos_opts o;
+  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+
+  const int64_t mc = m / world;
+  int bm = 64, bn = 64;
+  if (mc % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
+  else if (mc % 128 == 0 && n % 128 == 0) bm = 128, bn = 128;
+
+  RsParams p{};
+  p.world = world;
+  p.rank = rank;
+  p.m = (int32_t)m;
+  p.k = (int32_t)k;
+  p.n = (int32_t)n;
+  p.mc = (int32_t)mc;
+  p.a = static_cast<const uint16_t*>(a);
+  p.w = static_cast<const uint16_t*>(w);
+  for (int q = 0; q < world; ++q) p.peers[q] = q == rank ? nullptr : peer_slices[q];
+  p.partial = partial;
+  p.y = y;
+  p.row_order = o.rs_order == KOS_RS_ROW;
+  p.spin_limit = o.spin_limit;
+  p.bands = (int32_t)(mc / bm);
+  p.tiles_n = (int32_t)(n / bn);
+  p.n_tiles = world * p.bands * p.tiles_n;
+  p.n_reduce = p.bands * p.tiles_n;
+  p.ws = static_cast<WsHeader*>(ws);
+  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  if ((size_t)p.n_reduce > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many output tiles");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = o.grid;
+  if (o.mode == KOS_MODE_UNFUSED) {
+    RsParams gm = p;            // launch 1: the whole GEMM
+    gm.do_build = 1;
+    gm.do_reduce = 0;
+    gm.n_reducers = 0;
+    if ((st = launch_rs_tile(bm, bn, gm, grid, s)) != KOS_OK) return st;
+    RsParams rd = p;            // launch 2: the whole reduction
+    rd.do_build = 0;
+    rd.do_reduce = 1;
+    rd.n_reducers = grid;
+    rd.wait_flags = 0;
+    return launch_rs_tile(bm, bn, rd, grid, s);
+  }
+  // The crew that starts reducing (FUSED) or only reduces (FIXED).
+  if (o.n_movers < 1 || o.n_movers >= grid)
+    return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, grid);
+  p.n_reducers = o.n_movers;
+  p.builders_switch = o.mode == KOS_MODE_FUSED;
+  p.do_build = 1;
+  p.do_reduce = 1;
+  p.wait_flags = 1;
+  return launch_rs_tile(bm, bn, p, grid, s);
+}

@@ -1,0 +1,480 @@
+// Expert layer, combine direction, as one persistent kernel: grouped SwiGLU
+// expert GEMMs, results pushed back to the ranks that sent the rows, and the
+// weighted fold of our own tokens [KOSMOS arXiv abstract: "from router to
+// fold", one launch per direction; KOSMOS explainer, "KOSMOS removes the
+// manager": in the combine step a workgroup pushes any ready result and
+// otherwise builds a tile (two-way switching)].
+//
+// Work units: (local expert e, row block of BM grouped rows), expert-major.
+// Per unit: G gate/up tiles (each BN/2 columns of h = bf16(silu(X.Wg) *
+// (X.Wu)), gate and up computed in one MFMA tile) and D down tiles (BN
+// columns of Y = bf16(h.Wd)), the down tiles gated on the unit's G gate/up
+// tiles.
+// Queues:
+//   head[1]  tiles, consumer-ordered with a lag of L units: the gate/up
+//            tiles of units 0..L-1, then for each unit i the gate/up tiles
+//            of unit i+L followed by the down tiles of unit i -- a down tile
+//            is claimed about a wave of tiles after the tiles it needs.
+//   head[2]  push entries, one per unit, in unit order: rows whose source is
+//            another rank are copied to that rank's return buffer once the
+//            unit's D down tiles are done.  Between tiles a workgroup takes
+//            the head entry if it is ready, else builds the next tile.
+//   head[3]  fold entries, 16 tokens each: y[t] = bf16(sum_j w[t,j] *
+//            res(t,j)), fp32, j ascending; local results gated on their
+//            unit's down tiles, remote results read from what the peers
+//            returned.
+#include "kos_host.h"
+#include "kos_moe.h"
+#include "kos_tile.h"
+
+namespace kos {
+
+constexpr int kFoldTokens = 16;
+
+struct CombineParams {
+  int32_t world, rank, T, H, E, k, F, E_loc;
+  const uint16_t* xg;
+  const int32_t* go_in;
+  const int32_t* row_src;
+  const uint16_t* wg;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* counts;
+  const int32_t* perm;
+  const int32_t* peer_counts;
+  const uint16_t* peer_return[8];
+  uint16_t* h;
+  uint16_t* yg;
+  uint16_t* out_return[8];
+  uint16_t* y;
+  int32_t G, D, L;        // gate/up tiles per unit, down tiles per unit, lag (units)
+  int32_t u_max;          // bound on units: size of each counter array
+  int32_t do_gu, do_dn, do_push, do_fold;
+  int32_t two_way;        // builders take ready pushes between tiles
+  int32_t n_crew;         // > 0: tickets below it only push and fold
+  int32_t wait_flags;
+  uint32_t spin_limit;
+  WsHeader* ws;
+  uint32_t* ctr;          // gu_done[u_max], then dn_done[u_max]
+};
+
+struct CombineMeta {
+  int32_t go[kMoeMaxLocal + 1];     // grouped offsets
+  int32_t ub[kMoeMaxLocal + 1];     // first unit of each local expert
+  int32_t before[kMoeMaxLocal];     // grouped rows of sources < rank, per local expert
+  int32_t off[kMoeMaxExperts + 1];  // our packed offsets
+};
+
+template <int BM>
+__device__ inline void load_combine_meta(const CombineParams& p, CombineMeta& M) {
+  for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) M.go[el] = p.go_in[el];
+  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
+    int run = 0;
+    for (int q = 0; q < p.rank; ++q) run += p.peer_counts[q * p.E_loc + el];
+    M.before[el] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    M.off[0] = 0;
+    for (int e = 0; e < p.E; ++e) M.off[e + 1] = M.off[e] + p.counts[e];
+    M.ub[0] = 0;
+    for (int el = 0; el < p.E_loc; ++el) {
+      const int n = M.go[el + 1] - M.go[el];
+      M.ub[el + 1] = M.ub[el] + (n + BM - 1) / BM;
+    }
+  }
+  __syncthreads();
+}
+
+struct Unit {
+  int el, rb, row0, m_valid;
+};
+
+template <int BM>
+__device__ __forceinline__ Unit unit_of(const CombineMeta& M, int E_loc, int u) {
+  int el = 0;
+  while (el + 1 < E_loc && M.ub[el + 1] <= u) ++el;
+  Unit x;
+  x.el = el;
+  x.rb = u - M.ub[el];
+  x.row0 = M.go[el] + x.rb * BM;
+  const int n = M.go[el + 1] - M.go[el];
+  x.m_valid = min(BM, n - x.rb * BM);
+  return x;
+}
+
+// Tile entry j of the queue -> (is_down, unit, column tile).
+__device__ __forceinline__ void decode_tile(const CombineParams& p, int U, int j, bool& down, int& u, int& nt) {
+  if (p.do_gu && !p.do_dn) {
+    down = false;
+    u = j / p.G;
+    nt = j % p.G;
+    return;
+  }
+  if (!p.do_gu) {
+    down = true;
+    u = j / p.D;
+    nt = j % p.D;
+    return;
+  }
+  const int L = min(p.L, U);
+  const int head = L * p.G;
+  if (j < head) {
+    down = false;
+    u = j / p.G;
+    nt = j % p.G;
+    return;
+  }
+  const int jj = j - head;
+  const int nfull = max(U - p.L, 0);
+  const int GD = p.G + p.D;
+  if (jj < nfull * GD) {
+    const int i = jj / GD, r = jj % GD;
+    if (r < p.G) {
+      down = false;
+      u = i + p.L;
+      nt = r;
+    } else {
+      down = true;
+      u = i;
+      nt = r - p.G;
+    }
+    return;
+  }
+  const int jj2 = jj - nfull * GD;
+  down = true;
+  u = nfull + jj2 / p.D;
+  nt = jj2 % p.D;
+}
+
+template <class S>
+__device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN], uint4* lds) {
+  constexpr int HN = S::BN / 2;    // h columns per tile
+  const int64_t H = p.H, F = p.F;
+  BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
+         S::BN / 4};
+  tile_mainloop<S>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H, lds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  uint16_t* hb = p.h + (int64_t)x.row0 * F + (int64_t)nt * HN;
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN / 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * S::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = wn * (S::BN / 4) + j * 32 + (lane & 31);
+        if (row < x.m_valid) {
+          const float g = acc[i][j][r], u = acc[i][j + S::TN / 2][r];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          hb[(int64_t)row * F + col] = f32_to_bf16_bits(hv);
+        }
+      }
+}
+
+template <class S>
+__device__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN], uint4* lds) {
+  const int64_t H = p.H, F = p.F;
+  BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
+  tile_mainloop<S>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F, lds);
+  uint16_t* yb = p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN;
+  const int mv = x.m_valid;
+  tile_foreach<S>(acc, [&](int r, int c, float v) {
+    if (r < mv) yb[(int64_t)r * H + c] = f32_to_bf16_bits(v);
+  });
+}
+
+__device__ void push_unit(const CombineParams& p, const Unit& x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  (void)lane;
+  for (int r = wave; r < x.m_valid; r += nw) {
+    const int64_t grow = (int64_t)x.row0 + r;
+    const int src = p.row_src[grow * 2];
+    if (src == p.rank) continue;
+    const int64_t i = p.row_src[grow * 2 + 1];
+    wave_copy_row(p.out_return[src] + i * p.H, p.yg + grow * p.H, p.H * 2);
+  }
+}
+
+// Thread 0 polls a counter (bounded); others idle.  Returns the outcome in
+// thread 0 only.
+__device__ inline bool t0_poll(const uint32_t* c, uint32_t target, WsHeader* h, uint32_t limit, uint32_t info) {
+  uint32_t it = 0;
+  while (ld_relaxed(c) < target) {
+    if (aborted(h)) return false;
+    if (++it >= limit) {
+      raise_error(h, KOS_ERR_TIMEOUT, info);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
+
+template <int BM>
+__device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb, WgSlots* s) {
+  const int t0 = fb * kFoldTokens;
+  const int t1 = min(p.T, t0 + kFoldTokens);
+  const uint32_t* dn_done = p.ctr + p.u_max;
+  // wait for every local result these tokens read
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (p.wait_flags) {
+      for (int t = t0; t < t1 && ok; ++t)
+        for (int j = 0; j < p.k && ok; ++j) {
+          const int e = p.topk_idx[(int64_t)t * p.k + j];
+          if (e / p.E_loc != p.rank) continue;
+          const int el = e - p.rank * p.E_loc;
+          const int grow = M.go[el] + M.before[el] + (p.perm[(int64_t)t * p.k + j] - M.off[e]);
+          const int u = M.ub[el] + (grow - M.go[el]) / BM;
+          if (!t0_poll(&dn_done[u], (uint32_t)p.D, p.ws, p.spin_limit, 0x40000000u | (uint32_t)fb)) ok = 0;
+        }
+    }
+    s->ok = ok;
+  }
+  __syncthreads();
+  if (!s->ok) return false;
+  fence_acquire();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int E_loc = p.E_loc;
+  for (int t = t0 + wave; t < t1; t += nw) {
+    const uint16_t* src[kMoeMaxTopk];
+    float w[kMoeMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMoeMaxTopk; ++j) {
+      if (j >= p.k) break;
+      const int e = p.topk_idx[(int64_t)t * p.k + j];
+      const int pos = p.perm[(int64_t)t * p.k + j];
+      const int d = e / E_loc;
+      w[j] = p.topk_w[(int64_t)t * p.k + j];
+      if (d == p.rank) {
+        const int el = e - p.rank * E_loc;
+        src[j] = p.yg + ((int64_t)M.go[el] + M.before[el] + (pos - M.off[e])) * p.H;
+      } else {
+        src[j] = p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H;
+      }
+    }
+    for (int c = lane; c < p.H / 8; c += 64) {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMoeMaxTopk; ++j) {
+        if (j >= p.k) break;
+        const uint4 v = reinterpret_cast<const uint4*>(src[j])[c];
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          a[2 * m] += w[j] * __builtin_bit_cast(float, q[m] << 16);
+          a[2 * m + 1] += w[j] * __builtin_bit_cast(float, q[m] & 0xFFFF0000u);
+        }
+      }
+      uint4 o;
+      o.x = (uint32_t)f32_to_bf16_bits(a[0]) | ((uint32_t)f32_to_bf16_bits(a[1]) << 16);
+      o.y = (uint32_t)f32_to_bf16_bits(a[2]) | ((uint32_t)f32_to_bf16_bits(a[3]) << 16);
+      o.z = (uint32_t)f32_to_bf16_bits(a[4]) | ((uint32_t)f32_to_bf16_bits(a[5]) << 16);
+      o.w = (uint32_t)f32_to_bf16_bits(a[6]) | ((uint32_t)f32_to_bf16_bits(a[7]) << 16);
+      reinterpret_cast<uint4*>(p.y + (int64_t)t * p.H)[c] = o;
+    }
+  }
+  return true;
+}
+
+template <class S>
+__global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) {
+  constexpr int BM = S::BM;
+  __shared__ uint4 lds[S::LDS_BYTES / 16];
+  __shared__ CombineMeta M;
+  __shared__ WgSlots slots;
+  WsHeader* h = p.ws;
+  load_combine_meta<BM>(p, M);
+  const int U = M.ub[p.E_loc];
+  uint32_t* gu_done = p.ctr;
+  uint32_t* dn_done = p.ctr + p.u_max;
+  const uint32_t ticket = wg_ticket(h, &slots);
+  const bool crew = p.n_crew > 0 && ticket < (uint32_t)p.n_crew;
+  bool failed = false;
+
+  // ---- builder role (two-way: push any ready result between tiles) -------
+  if (!crew && (p.do_gu || p.do_dn)) {
+    f32x16 acc[S::TM][S::TN];
+    const int n_entries = (p.do_gu && p.do_dn) ? U * (p.G + p.D) : (p.do_gu ? U * p.G : U * p.D);
+    for (;;) {
+      if (p.two_way && p.do_push) {
+        for (;;) {   // push while the head of the push queue is ready
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            uint32_t hd = ld_relaxed(&h->head[2]);
+            uint32_t got = kNoEntry;
+            if (hd < (uint32_t)U && ld_relaxed(&dn_done[hd]) >= (uint32_t)p.D &&
+                __hip_atomic_compare_exchange_strong(&h->head[2], &hd, hd + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+              got = hd;
+            slots.claim = got;
+          }
+          __syncthreads();
+          const uint32_t got = slots.claim;
+          if (got == kNoEntry) break;
+          fence_acquire();
+          push_unit(p, unit_of<BM>(M, p.E_loc, (int)got));
+        }
+      }
+      const uint32_t j = wg_claim(&h->head[1], h, &slots);
+      if (j >= (uint32_t)n_entries) break;
+      bool down;
+      int u, nt;
+      decode_tile(p, U, (int)j, down, u, nt);
+      const Unit x = unit_of<BM>(M, p.E_loc, u);
+      if (!down) {
+        gate_up_tile<S>(p, x, nt, acc, lds);
+        wg_signal(&gu_done[u], 1u);
+      } else {
+        if (p.wait_flags && p.do_gu && !wg_wait(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
+          failed = true;
+          break;
+        }
+        down_tile<S>(p, x, nt, acc, lds);
+        wg_signal(&dn_done[u], 1u);
+      }
+    }
+    if (p.n_crew > 0) {   // fixed crew: builders only build
+      wg_exit(h, p.ctr, 2 * p.u_max, &slots);
+      return;
+    }
+  }
+
+  // ---- pusher role (drain, in unit order) --------------------------------
+  if (!failed && p.do_push) {
+    for (;;) {
+      const uint32_t i = wg_claim(&h->head[2], h, &slots);
+      if (i >= (uint32_t)U) break;
+      if (p.wait_flags && !wg_wait(&dn_done[i], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
+      push_unit(p, unit_of<BM>(M, p.E_loc, (int)i));
+    }
+  }
+
+  // ---- fold role ---------------------------------------------------------
+  if (!failed && p.do_fold) {
+    const int nfb = (p.T + kFoldTokens - 1) / kFoldTokens;
+    for (;;) {
+      const uint32_t i = wg_claim(&h->head[3], h, &slots);
+      if (i >= (uint32_t)nfb) break;
+      if (!fold_block<BM>(p, M, (int)i, &slots)) break;
+    }
+  }
+  wg_exit(h, p.ctr, 2 * p.u_max, &slots);
+}
+
+using CombineTile = TileShape<256, 128, 2, 2>;
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped, const int32_t* grouped_offsets,
+                                      const int32_t* row_src, int64_t grouped_cap, const void* w_gate,
+                                      const void* w_up, const void* w_down, const int32_t* topk_idx,
+                                      const float* topk_w, const int32_t* counts, const int32_t* perm,
+                                      const int32_t* peer_counts, const void* const* peer_return, void* h,
+                                      void* y_grouped, void* const* out_return, void* y, const kos_opts* opts,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  using S = CombineTile;
+  if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
+  const int R = s->world, r = s->rank;
+  if (R < 1 || R > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", R);
+  if (r < 0 || r >= R) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", r, R);
+  if (s->reserved) return fail(KOS_ERR_ARG, "reserved must be 0");
+  if (s->tokens < 0 || s->hidden <= 0 || s->hidden % S::BN || s->ffn <= 0 || s->ffn % (S::BN / 2) ||
+      s->experts <= 0 || s->experts > kMoeMaxExperts || s->experts % R || s->experts / R > kMoeMaxLocal ||
+      s->topk < 1 || s->topk > kMoeMaxTopk || s->topk > s->experts)
+    return fail(KOS_ERR_SHAPE, "unsupported expert-layer shape (hidden %% %d, ffn %% %d)", S::BN, S::BN / 2);
+  if (!x_grouped || !grouped_offsets || !row_src || !w_gate || !w_up || !w_down || !topk_idx || !topk_w ||
+      !counts || !perm || !peer_counts || !h || !y_grouped || !y)
+    return fail(KOS_ERR_ARG, "null buffer");
+  if (R > 1 && (!peer_return || !out_return)) return fail(KOS_ERR_ARG, "peer_return / out_return is NULL");
+  for (int q = 0; q < R; ++q) {
+    if (q == r) continue;
+    if (!peer_return[q] || !out_return[q]) return fail(KOS_ERR_ARG, "peer buffers of rank %d are NULL", q);
+    if (!aligned16(peer_return[q]) || !aligned16(out_return[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
+  }
+  if (!aligned16(x_grouped) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(h) ||
+      !aligned16(y_grouped) || !aligned16(y))
+    return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
+  kos_status st = check_workspace(ws, ws_bytes);
+  if (st != KOS_OK) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != KOS_OK) return st;
+  kos_opts o;
+  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+
+  CombineParams p{};
+  p.world = R;
+  p.rank = r;
+  p.T = s->tokens;
+  p.H = s->hidden;
+  p.E = s->experts;
+  p.k = s->topk;
+  p.F = s->ffn;
+  p.E_loc = s->experts / R;
+  p.xg = static_cast<const uint16_t*>(x_grouped);
+  p.go_in = grouped_offsets;
+  p.row_src = row_src;
+  p.wg = static_cast<const uint16_t*>(w_gate);
+  p.wu = static_cast<const uint16_t*>(w_up);
+  p.wd = static_cast<const uint16_t*>(w_down);
+  p.topk_idx = topk_idx;
+  p.topk_w = topk_w;
+  p.counts = counts;
+  p.perm = perm;
+  p.peer_counts = peer_counts;
+  for (int q = 0; q < R; ++q) {
+    p.peer_return[q] = q == r ? nullptr : static_cast<const uint16_t*>(peer_return[q]);
+    p.out_return[q] = q == r ? nullptr : static_cast<uint16_t*>(out_return[q]);
+  }
+  p.h = static_cast<uint16_t*>(h);
+  p.yg = static_cast<uint16_t*>(y_grouped);
+  p.y = static_cast<uint16_t*>(y);
+  p.G = s->ffn / (S::BN / 2);
+  p.D = s->hidden / S::BN;
+  p.L = (o.grid + p.G - 1) / p.G;
+  p.u_max = (int32_t)((grouped_cap + S::BM - 1) / S::BM) + p.E_loc;
+  if ((size_t)2 * p.u_max > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
+  p.spin_limit = o.spin_limit;
+  p.ws = static_cast<WsHeader*>(ws);
+  p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  auto launch = [&](const CombineParams& q, const char* what) {
+    hipLaunchKernelGGL((moe_combine_kernel<S>), dim3(o.grid), dim3(S::NT), 0, strm, q);
+    return launch_status(what);
+  };
+  if (o.mode == KOS_MODE_UNFUSED) {
+    // four launches: gate/up GEMMs, down GEMMs, push, fold
+    CombineParams a = p;
+    a.do_gu = 1;
+    if ((st = launch(a, "moe_combine gate/up launch")) != KOS_OK) return st;
+    CombineParams b = p;
+    b.do_dn = 1;
+    if ((st = launch(b, "moe_combine down launch")) != KOS_OK) return st;
+    CombineParams c = p;
+    c.do_push = 1;
+    if ((st = launch(c, "moe_combine push launch")) != KOS_OK) return st;
+    CombineParams d = p;
+    d.do_fold = 1;
+    return launch(d, "moe_combine fold launch");
+  }
+  p.do_gu = p.do_dn = p.do_push = p.do_fold = 1;
+  p.wait_flags = 1;
+  if (o.mode == KOS_MODE_FIXED) {
+    if (o.n_movers < 1 || o.n_movers >= o.grid)
+      return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, o.grid);
+    p.n_crew = o.n_movers;
+    p.two_way = 0;
+  } else {
+    p.two_way = 1;
+  }
+  return launch(p, "moe_combine launch");
+}

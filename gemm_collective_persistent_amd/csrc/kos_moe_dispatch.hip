@@ -1,0 +1,436 @@
+// Expert layer, dispatch direction, as one persistent kernel: router ->
+// permutation -> token movement [KOSMOS arXiv abstract: an entire expert
+// layer "from router to fold", one launch per direction; KOSMOS explainer,
+// "Start with the problem": tokens travel to the GPU that holds their
+// expert].
+//
+// Queues and counters:
+//   head[0]      router entries, one per block of 64 tokens: top-k of each
+//                token's logits (descending, ties to the lowest expert
+//                index), softmax over the k, and a 64-bit mask per expert of
+//                the block's tokens routed to it (order-free, so the result
+//                is deterministic).
+//   counter[0]   routed blocks.  The workgroup that routes the last block
+//                runs the scan: per-expert counts, the exclusive scan over
+//                experts (packed offsets), per-(block, expert) bases, the
+//                grouped offsets of our local experts, capacity checks; then
+//                sets counter[1].
+//   head[1]      mover entries (after counter[1]): a quarter block of our
+//                tokens -- pair (t, j) of expert e lands at base[block][e] +
+//                popcount(mask & tokens before t); the row goes to the send
+//                buffer of e's rank, or straight into the grouped input when
+//                e is local -- then 64-row chunks of each peer's rows, pulled
+//                into the grouped input.
+#include "kos_host.h"
+#include "kos_moe.h"
+
+namespace kos {
+
+struct DispatchParams {
+  int32_t world, rank, T, H, E, k, E_loc;
+  const uint16_t* x;
+  const float* logits;
+  const uint16_t* peer_send[8];
+  const int32_t* peer_counts;   // [world, E_loc]
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* perm;
+  uint16_t* out_send[8];
+  int64_t send_cap;
+  uint16_t* x_grouped;
+  int64_t grouped_cap;
+  int32_t* grouped_offsets;
+  int32_t* row_src;
+  int32_t nblk;
+  int32_t do_route, do_copy, wait_scan;
+  uint32_t spin_limit;
+  WsHeader* ws;
+  uint32_t* ctr;                 // [0] routed blocks, [1] scan done
+  unsigned long long* masks;     // scratch [nblk, E]
+  int32_t* base;                 // scratch [nblk, E]: histogram, then bases
+  int32_t* off;                  // scratch [E + 1]
+};
+
+struct DispatchLds {
+  unsigned long long m[kMoeMaxExperts];
+  int32_t off[kMoeMaxExperts + 1];
+  int32_t pc[8][kMoeMaxLocal];          // peer counts (row `rank` = our own local counts after the scan)
+  int32_t cum[8][kMoeMaxLocal + 1];     // per-source prefix over local experts
+  int32_t before[8][kMoeMaxLocal];      // rows of sources < p, per local expert
+  int32_t go[kMoeMaxLocal + 1];         // grouped offsets
+  int32_t chunk_base[9];                // first peer entry of each source
+  int32_t meta_loaded;
+};
+
+// Wave-wide argmax of (value, index) pairs: larger value wins, equal values
+// go to the lower index; idx == INT_MAX marks "no candidate".
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(i, off);
+    const bool take = oi != INT_MAX && (i == INT_MAX || ov > v || (ov == v && oi < i));
+    if (take) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ void route_block(const DispatchParams& p, int b, DispatchLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.m[e] = 0ull;
+  __syncthreads();
+  const int nv = (p.E + 63) / 64;
+  for (int tl = wave; tl < kMoeTokBlock; tl += nw) {
+    const int t = b * kMoeTokBlock + tl;
+    if (t >= p.T) break;
+    float v[kMoeMaxExperts / 64];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < kMoeMaxExperts / 64; ++i) {
+      if (i < nv) {
+        const int e = lane + 64 * i;
+        if (e < p.E) v[i] = p.logits[(int64_t)t * p.E + e];
+        else taken |= 1u << i;
+      }
+    }
+    float sel_v[kMoeMaxTopk];
+    int sel_i[kMoeMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMoeMaxTopk; ++j) {
+      if (j < p.k) {
+        float bv = 0.f;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < kMoeMaxExperts / 64; ++i) {
+          if (i < nv && !((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
+            bv = v[i];
+            bi = lane + 64 * i;
+          }
+        }
+        wave_argmax(bv, bi);
+        sel_v[j] = bv;
+        sel_i[j] = bi;
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      }
+    }
+    // softmax over the k selected logits (largest first)
+    float z[kMoeMaxTopk];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMoeMaxTopk; ++j)
+      if (j < p.k) {
+        z[j] = expf(sel_v[j] - sel_v[0]);
+        s += z[j];
+      }
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < kMoeMaxTopk; ++j)
+      if (j < p.k && lane == j) {
+        p.topk_idx[(int64_t)t * p.k + j] = sel_i[j];
+        p.topk_w[(int64_t)t * p.k + j] = z[j] * inv;
+        atomicOr(&L.m[sel_i[j]], 1ull << tl);
+      }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    const unsigned long long m = L.m[e];
+    p.masks[(int64_t)b * p.E + e] = m;
+    p.base[(int64_t)b * p.E + e] = __popcll(m);
+  }
+}
+
+// Run once, by the workgroup that routed the last block.  Returns false
+// (for every thread) when a capacity would overflow; the error is recorded
+// and the movers are never released.
+__device__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < p.nblk; ++b) {
+      const int h = p.base[(int64_t)b * p.E + e];
+      p.base[(int64_t)b * p.E + e] = run;
+      run += h;
+    }
+    p.counts[e] = run;
+    L.off[e + 1] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    L.off[0] = 0;
+    for (int e = 0; e < p.E; ++e) L.off[e + 1] += L.off[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= p.E; e += blockDim.x) p.off[e] = L.off[e];
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
+    for (int b = 0; b < p.nblk; ++b) p.base[(int64_t)b * p.E + e] += L.off[e];
+  if (threadIdx.x == 0) {
+    bool over = false;
+    for (int d = 0; d < p.world; ++d) {
+      if (d == p.rank) continue;
+      const int sent = L.off[(d + 1) * p.E_loc] - L.off[d * p.E_loc];
+      if (sent > p.send_cap) over = true;
+    }
+    int64_t go = 0;
+    for (int el = 0; el < p.E_loc; ++el) {
+      p.grouped_offsets[el] = (int32_t)go;
+      const int ge = p.rank * p.E_loc + el;
+      go += L.off[ge + 1] - L.off[ge];
+      for (int q = 0; q < p.world; ++q)
+        if (q != p.rank) go += p.peer_counts[q * p.E_loc + el];
+    }
+    p.grouped_offsets[p.E_loc] = (int32_t)go;
+    if (go > p.grouped_cap) over = true;
+    if (over) raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)go);
+    slots->ok = over ? 0 : 1;
+  }
+  __syncthreads();
+  return slots->ok != 0;
+}
+
+// Loads the scan's results into LDS (after counter[1]).
+__device__ void load_meta(const DispatchParams& p, DispatchLds& L) {
+  for (int e = threadIdx.x; e <= p.E; e += blockDim.x) L.off[e] = p.off[e];
+  for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) L.go[el] = p.grouped_offsets[el];
+  __syncthreads();
+  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
+    const int ge = p.rank * p.E_loc + el;
+    L.pc[p.rank][el] = L.off[ge + 1] - L.off[ge];
+    int run = 0;
+    for (int q = 0; q < p.world; ++q) {
+      L.before[q][el] = run;
+      run += L.pc[q][el];
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
+  __shared__ DispatchLds L;
+  __shared__ WgSlots slots;
+  WsHeader* h = p.ws;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NT / 64;
+  wg_ticket(h, &slots);
+
+  // peer counts (inputs) and the per-source prefixes
+  for (int i = threadIdx.x; i < p.world * p.E_loc; i += NT) {
+    const int q = i / p.E_loc, el = i % p.E_loc;
+    L.pc[q][el] = q == p.rank ? 0 : p.peer_counts[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < p.world) {
+    const int q = threadIdx.x;
+    int run = 0;
+    for (int el = 0; el < p.E_loc; ++el) {
+      L.cum[q][el] = run;
+      run += L.pc[q][el];
+    }
+    L.cum[q][p.E_loc] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int nb = p.nblk * 4;
+    for (int q = 0; q < p.world; ++q) {
+      L.chunk_base[q] = nb;
+      if (q != p.rank) nb += (L.cum[q][p.E_loc] + 63) / 64;
+    }
+    L.chunk_base[p.world] = nb;
+  }
+  __syncthreads();
+
+  // ---- router role ------------------------------------------------------
+  if (p.do_route) {
+    if (p.nblk == 0 && slots.claim == 0) {   // no tokens: the first arrival scans
+      if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
+    }
+    for (;;) {
+      const uint32_t b = wg_claim(&h->head[0], h, &slots);
+      if (b >= (uint32_t)p.nblk) break;
+      route_block(p, (int)b, L);
+      fence_release();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        slots.aux[0] = __hip_atomic_fetch_add(&p.ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (slots.aux[0] == (uint32_t)p.nblk - 1) {   // the last block: scan
+        fence_acquire();
+        if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
+      }
+    }
+  }
+
+  // ---- mover role -------------------------------------------------------
+  if (p.do_copy) {
+    const int n_entries = L.chunk_base[p.world];
+    bool have_meta = false;
+    for (;;) {
+      const uint32_t i = wg_claim(&h->head[1], h, &slots);
+      if (i >= (uint32_t)n_entries) break;
+      if (!have_meta) {
+        if (p.wait_scan && !wg_wait(&p.ctr[1], 1u, h, p.spin_limit, 0xFFFF0000u, &slots)) break;
+        fence_acquire();
+        load_meta(p, L);
+        have_meta = true;
+      }
+      const int H = p.H;
+      const int row_bytes = H * 2;
+      if ((int)i < p.nblk * 4) {
+        // our own tokens: a quarter block, one token per wave at a time
+        const int b = (int)i >> 2, q = (int)i & 3;
+        for (int tq = wave; tq < kMoeTokBlock / 4; tq += nw) {
+          const int tl = q * (kMoeTokBlock / 4) + tq;
+          const int t = b * kMoeTokBlock + tl;
+          if (t >= p.T) break;
+          uint16_t* dst[kMoeMaxTopk];
+#pragma unroll
+          for (int j = 0; j < kMoeMaxTopk; ++j) {
+            if (j >= p.k) break;
+            const int e = p.topk_idx[(int64_t)t * p.k + j];
+            const unsigned long long m = p.masks[(int64_t)b * p.E + e];
+            const int pos = p.base[(int64_t)b * p.E + e] + __popcll(m & ((1ull << tl) - 1ull));
+            const int d = e / p.E_loc;
+            if (lane == j) p.perm[(int64_t)t * p.k + j] = pos;
+            if (d != p.rank) {
+              dst[j] = p.out_send[d] + (int64_t)(pos - L.off[d * p.E_loc]) * H;
+            } else {
+              const int el = e - p.rank * p.E_loc;
+              const int64_t grow = (int64_t)L.go[el] + L.before[p.rank][el] + (pos - L.off[e]);
+              dst[j] = p.x_grouped + grow * H;
+              if (lane == 0) {
+                p.row_src[grow * 2] = p.rank;
+                p.row_src[grow * 2 + 1] = pos - L.off[p.rank * p.E_loc];
+              }
+            }
+          }
+          const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * H);
+          for (int c = lane; c < row_bytes / 16; c += 64) {
+            const u32x4 v = src[c];
+#pragma unroll
+            for (int j = 0; j < kMoeMaxTopk; ++j) {
+              if (j >= p.k) break;
+              reinterpret_cast<u32x4*>(dst[j])[c] = v;
+            }
+          }
+        }
+      } else {
+        // a chunk of 64 rows peer q sent us, pulled into the grouped input
+        int q = 0;
+        while (q + 1 <= p.world && L.chunk_base[q + 1] <= (int)i) ++q;
+        const int r0 = ((int)i - L.chunk_base[q]) * 64;
+        const int n_q = L.cum[q][p.E_loc];
+        for (int rr = wave; rr < 64; rr += nw) {
+          const int r = r0 + rr;
+          if (r >= n_q) break;
+          int el = 0;
+          while (el + 1 < p.E_loc && L.cum[q][el + 1] <= r) ++el;
+          const int64_t grow = (int64_t)L.go[el] + L.before[q][el] + (r - L.cum[q][el]);
+          wave_copy_row(p.x_grouped + grow * H, p.peer_send[q] + (int64_t)r * H, row_bytes);
+          if (lane == 0) {
+            p.row_src[grow * 2] = q;
+            p.row_src[grow * 2 + 1] = r;
+          }
+        }
+      }
+    }
+  }
+  wg_exit(h, p.ctr, 2, &slots);
+}
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* logits,
+                                       const void* const* peer_send, const int32_t* peer_counts, int32_t* topk_idx,
+                                       float* topk_w, int32_t* counts, int32_t* perm, void* const* out_send,
+                                       int64_t send_cap, void* x_grouped, int64_t grouped_cap,
+                                       int32_t* grouped_offsets, int32_t* row_src, const kos_opts* opts, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
+  const int R = s->world, r = s->rank;
+  if (R < 1 || R > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", R);
+  if (r < 0 || r >= R) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", r, R);
+  if (s->reserved) return fail(KOS_ERR_ARG, "reserved must be 0");
+  if (s->tokens < 0 || s->hidden <= 0 || s->hidden % 64 || s->experts <= 0 || s->experts > kMoeMaxExperts ||
+      s->experts % R || s->experts / R > kMoeMaxLocal || s->topk < 1 || s->topk > kMoeMaxTopk ||
+      s->topk > s->experts || s->ffn <= 0)
+    return fail(KOS_ERR_SHAPE, "unsupported expert-layer shape");
+  if (!x || !logits || !peer_counts || !topk_idx || !topk_w || !counts || !perm || !x_grouped ||
+      !grouped_offsets || !row_src)
+    return fail(KOS_ERR_ARG, "null buffer");
+  if (R > 1 && (!peer_send || !out_send)) return fail(KOS_ERR_ARG, "peer_send / out_send is NULL");
+  for (int q = 0; q < R; ++q) {
+    if (q == r) continue;
+    if (!peer_send[q] || !out_send[q]) return fail(KOS_ERR_ARG, "peer buffers of rank %d are NULL", q);
+    if (!aligned16(peer_send[q]) || !aligned16(out_send[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
+  }
+  if (!aligned16(x) || !aligned16(x_grouped)) return fail(KOS_ERR_ALIGN, "row buffers must be 16-byte aligned");
+  if (send_cap < 0 || grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1)
+    return fail(KOS_ERR_ARG, "bad capacity");
+  kos_status st = check_workspace(ws, ws_bytes);
+  if (st != KOS_OK) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != KOS_OK) return st;
+  kos_opts o;
+  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+  if (o.mode == KOS_MODE_FIXED) return fail(KOS_ERR_UNSUPPORTED, "dispatch has no compute role to split from");
+
+  DispatchParams p{};
+  p.world = R;
+  p.rank = r;
+  p.T = s->tokens;
+  p.H = s->hidden;
+  p.E = s->experts;
+  p.k = s->topk;
+  p.E_loc = s->experts / R;
+  p.x = static_cast<const uint16_t*>(x);
+  p.logits = logits;
+  for (int q = 0; q < R; ++q) {
+    p.peer_send[q] = q == r ? nullptr : static_cast<const uint16_t*>(peer_send[q]);
+    p.out_send[q] = q == r ? nullptr : static_cast<uint16_t*>(out_send[q]);
+  }
+  p.peer_counts = peer_counts;
+  p.topk_idx = topk_idx;
+  p.topk_w = topk_w;
+  p.counts = counts;
+  p.perm = perm;
+  p.send_cap = send_cap;
+  p.x_grouped = static_cast<uint16_t*>(x_grouped);
+  p.grouped_cap = grouped_cap;
+  p.grouped_offsets = grouped_offsets;
+  p.row_src = row_src;
+  p.nblk = (s->tokens + kMoeTokBlock - 1) / kMoeTokBlock;
+  p.spin_limit = o.spin_limit;
+  p.ws = static_cast<WsHeader*>(ws);
+  p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  char* scratch = static_cast<char*>(ws) + kScratchOffset;
+  const size_t mask_bytes = (size_t)p.nblk * p.E * 8, base_bytes = (size_t)p.nblk * p.E * 4;
+  if (mask_bytes + base_bytes + (size_t)(p.E + 1) * 4 > kScratchBytes)
+    return fail(KOS_ERR_SHAPE, "too many tokens x experts for the workspace");
+  p.masks = reinterpret_cast<unsigned long long*>(scratch);
+  p.base = reinterpret_cast<int32_t*>(scratch + mask_bytes);
+  p.off = reinterpret_cast<int32_t*>(scratch + mask_bytes + base_bytes);
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  constexpr int NT = 256;
+  if (o.mode == KOS_MODE_UNFUSED) {
+    DispatchParams a = p;   // launch 1: router + scan
+    a.do_route = 1;
+    a.do_copy = 0;
+    hipLaunchKernelGGL(moe_dispatch_kernel<NT>, dim3(o.grid), dim3(NT), 0, strm, a);
+    if ((st = launch_status("moe_dispatch route launch")) != KOS_OK) return st;
+    DispatchParams b = p;   // launch 2: token movement
+    b.do_route = 0;
+    b.do_copy = 1;
+    b.wait_scan = 0;
+    hipLaunchKernelGGL(moe_dispatch_kernel<NT>, dim3(o.grid), dim3(NT), 0, strm, b);
+    return launch_status("moe_dispatch copy launch");
+  }
+  p.do_route = 1;
+  p.do_copy = 1;
+  p.wait_scan = 1;
+  hipLaunchKernelGGL(moe_dispatch_kernel<NT>, dim3(o.grid), dim3(NT), 0, strm, p);
+  return launch_status("moe_dispatch launch");
+}

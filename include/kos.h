@@ -257,7 +257,7 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
  *              inspection);  y_grouped: out bf16 [grouped_cap, H]
  * out_return   host array[world] of out bf16 [rows p sent us, H]
  * y            out bf16 [T, H]
- * Shapes: H % 128 == 0, F % 128 == 0.
+ * Shapes: H % 128 == 0, F % 64 == 0.
  */
 kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
                            const int32_t* grouped_offsets, const int32_t* row_src,

@@ -116,6 +116,9 @@ MOE_DSV3 = MoeShape("moe_dsv3_8r_t4096_h7168_e256_k8_f2048", 4, 8, 4096, 7168,
 MOE_QWEN3 = MoeShape("moe_qwen3_8r_t8192_h4096_e128_k8_f1536_zipf1.1", 5, 8,
                      8192, 4096, 128, 8, 1536, zipf_s=1.1)
 
+RS_TINY = RsShape("rs_tiny_4r_256x256x256", 8, 4, 256, 256, 256)
+RS_MID = RsShape("rs_mid_4r_2048x192x384", 9, 4, 2048, 192, 384)
+
 # small shapes for the CPU oracle tests and the fast GPU parity cases: several
 # tiles in each direction and a ragged expert tail
 MOE_TINY = MoeShape("moe_tiny_4r_t96_h256_e16_k4_f128", 6, 4, 96, 256, 16, 4,
