@@ -1,0 +1,278 @@
+#!/usr/bin/env python
+"""Benchmark of the fused GEMM+collective persistent kernels on one MI355X.
+
+One step = one pass of the whole hot path on one rank's share of an
+8-rank job, peers emulated in HBM:
+  1. all-gather + GEMM   (QKV column-parallel: 8 x 512x8192 shards, W 8192x3072)
+  2. GEMM + reduce-scatter (MLP down: A 4096x3584, W 3584x8192 -> 512x8192 chunk)
+  3. expert layer, DeepSeek-V3 shape (4096 tokens, H 7168, 256 experts top-8,
+     32 local SwiGLU experts 7168->2048->7168): dispatch, then combine.
+Each op is one persistent launch (fused mode).  `value` is the step's
+algorithmic GEMM FLOPs (AG + RS + expert FFN) / step time, in TFLOP/s; the
+MoE layer's tokens/s and each op's own TFLOP/s are reported beside it.
+
+Also reported: the same-GPU baselines (unfused launches, best fixed crew),
+the GEMM throughput on 224 of 256 compute units, the roofline of the
+dominant kernel, and the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+collective TFLOP/s (% bf16 MFMA peak); MoE layer tokens/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def crew_model(t_gemm_full, cus_total, cus_reserved, frac_on_rest, tail_fixed, tail_switch):
+    """The explainer's worked example as a model: a GEMM taking t_gemm_full
+    on the whole GPU runs at `frac_on_rest` of full throughput on the CUs left
+    after reserving a crew, then a reduction tail follows; with switching the
+    tail shrinks.  Returns (t_fixed, t_switch, speedup).  (cus_* are kept for
+    the record; the page states the throughput fraction directly.)"""
+    t_rest = t_gemm_full / frac_on_rest
+    t_fixed = t_rest + tail_fixed
+    t_switch = t_rest + tail_switch
+    return t_fixed, t_switch, t_fixed / t_switch
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def build_inputs(torch, KI, kos, moe_shape):
+    dev = "cuda"
+    inp = {}
+    ag = KI.ag_inputs(KI.AG_QKV, 0, dev)
+    s = KI.AG_QKV
+    ag["g"] = torch.empty((s.m, s.k), dtype=torch.bfloat16, device=dev)
+    ag["c"] = torch.empty((s.m, s.n), dtype=torch.bfloat16, device=dev)
+    inp["ag"] = ag
+    rs = KI.rs_inputs(KI.RS_MLP, 7, dev)
+    s = KI.RS_MLP
+    rs["partial"] = torch.empty((s.m, s.n), dtype=torch.float32, device=dev)
+    rs["y"] = torch.empty((s.m_chunk, s.n), dtype=torch.float32, device=dev)
+    inp["rs"] = rs
+    s = moe_shape
+    m = KI.moe_inputs(s, 0, dev)
+    pc = m["peer_counts"].cpu()
+    cap = int(pc.sum()) + s.tokens * min(s.topk, s.e_local)
+    m.update(
+        idx=torch.empty((s.tokens, s.topk), dtype=torch.int32, device=dev),
+        w=torch.empty((s.tokens, s.topk), dtype=torch.float32, device=dev),
+        counts=torch.empty((s.experts,), dtype=torch.int32, device=dev),
+        perm=torch.empty((s.tokens * s.topk,), dtype=torch.int32, device=dev),
+        send=[None if p == 0 else torch.empty((s.peer_cap, s.hidden), dtype=torch.bfloat16, device=dev)
+              for p in range(s.world)],
+        grouped=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
+        goff=torch.empty((s.e_local + 1,), dtype=torch.int32, device=dev),
+        row_src=torch.empty((cap, 2), dtype=torch.int32, device=dev),
+        h=torch.empty((cap, s.ffn), dtype=torch.bfloat16, device=dev),
+        yg=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
+        y=torch.empty((s.tokens, s.hidden), dtype=torch.bfloat16, device=dev),
+        ret=[None if p == 0 else torch.empty((max(int(pc[p].sum()), 1), s.hidden), dtype=torch.bfloat16,
+                                             device=dev) for p in range(s.world)],
+    )
+    inp["moe"] = m
+    return inp
+
+
+def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0):
+    from gemm_collective_persistent_amd.api import moe_shape as mk_shape
+    o = kos.opts(mode=mode, n_movers=n_movers, grid=grid)
+    ag, rs, m = inp["ag"], inp["rs"], inp["moe"]
+    s = moe_shape
+    shp = mk_shape(s.world, 0, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
+
+    def op_ag():
+        kos.ag_gemm(ag["a_local"], ag["a_peers"], ag["w"], ag["g"], ag["c"], 0, ws, o)
+
+    def op_rs():
+        kos.gemm_rs(rs["a"], rs["w"], rs["peer_slices"], rs["partial"], rs["y"], 7, ws, o)
+
+    def op_dispatch():
+        od = o if mode != 1 else kos.opts(mode=0, grid=grid)
+        kos.moe_dispatch(shp, m["x"], m["logits"], m["peer_send"], m["peer_counts"], m["idx"], m["w"],
+                         m["counts"], m["perm"], m["send"], m["grouped"], m["goff"], m["row_src"], ws, od)
+
+    def op_combine():
+        kos.moe_combine(shp, m["grouped"], m["goff"], m["row_src"], m["wg"], m["wu"], m["wd"], m["idx"], m["w"],
+                        m["counts"], m["perm"], m["peer_counts"], m["peer_return"], m["h"], m["yg"], m["ret"],
+                        m["y"], ws, o)
+
+    return [("ag_gemm", op_ag), ("gemm_rs", op_rs), ("moe_dispatch", op_dispatch), ("moe_combine", op_combine)]
+
+
+def time_ops(torch, ops, reps, ws):
+    """Runs `reps` steps; returns (per-op mean ms from events, wall ms/step)."""
+    n = len(ops)
+    ev = [_events(torch, n + 1) for _ in range(reps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(reps):
+        ev[r][0].record()
+        for i, (_, fn) in enumerate(ops):
+            fn()
+            ev[r][i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / reps
+    ws.status()
+    per = [sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps for i in range(n)]
+    return per, wall
+
+
+def cpu_baseline(inp, moe_shape, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    all-gather+GEMM of 8 rows of each of the 8 shards, the GEMM+reduce-scatter
+    of 8 rows of each of the 8 chunks, and the whole expert layer for the
+    first 128 tokens (no rows from peers).  FLOPs of the sample / time,
+    repeated until `budget_s` has elapsed."""
+    import numpy as np
+    import kos_inputs as KI
+    from oracle import kos_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    ag, rs, m = inp["ag"], inp["rs"], inp["moe"]
+    s2, s3, s4 = KI.AG_QKV, KI.RS_MLP, moe_shape
+    r = 8
+    ag_local = KI.bf16_bits(ag["a_local"][:r])
+    ag_peers = [None if t is None else KI.bf16_bits(t[:r]) for t in ag["a_peers"]]
+    w_ag = KI.bf16_bits(ag["w"])
+    a_rs = np.concatenate([KI.bf16_bits(rs["a"][c * s3.m_chunk:c * s3.m_chunk + r]) for c in range(s3.world)])
+    w_rs = KI.bf16_bits(rs["w"])
+    rs_peers = [None if t is None else t[:r].cpu().numpy() for t in rs["peer_slices"]]
+    ts = 128
+    x = KI.bf16_bits(m["x"][:ts])
+    lg = m["logits"][:ts].cpu().numpy()
+    wg, wu, wd = (KI.bf16_bits(m[k]) for k in ("wg", "wu", "wd"))
+    no_counts = np.zeros((s4.world, s4.e_local), np.int32)
+    no_rows = [np.zeros((0, s4.hidden), np.uint16)] * s4.world
+    cap = ts * min(s4.topk, s4.e_local)
+    pret = [None if t is None else KI.bf16_bits(t[:cap]) for t in m["peer_return"]]
+    flops, done, t0 = 0.0, 0, time.perf_counter()
+    while True:
+        O.ag_gemm(ag_local, ag_peers, w_ag, 0)
+        O.gemm_rs(a_rs, w_rs, rs_peers, 7)
+        out = O.moe_layer(x, lg, wg, wu, wd, no_rows, no_counts, pret, s4.world, 0, s4.topk)
+        flops += 2.0 * (8 * r) * s2.n * s2.k + 2.0 * (8 * r) * s3.n * s3.k
+        flops += int(out["grouped_offsets"][-1]) * s4.flops_per_row
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{done} x [AG+GEMM: 8 rows of each of 8 shards (64x{s2.k} . {s2.k}x{s2.n}); "
+                       f"GEMM+RS: 8 rows of each of 8 chunks (64x{s3.k} . {s3.k}x{s3.n}) + 8 partials; "
+                       f"expert layer on the first {ts} tokens ({s4.name}, no peer rows)], float64 NumPy, "
+                       f"{dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--moe", choices=["dsv3", "qwen3"], default="dsv3")
+    ap.add_argument("--no-baselines", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's share only (emulated peers); --gpus {args.gpus} is not supported: "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kos_inputs as KI
+    import gemm_collective_persistent_amd as kos
+
+    moe_shape = KI.MOE_DSV3 if args.moe == "dsv3" else KI.MOE_QWEN3
+    torch.cuda.set_device(0)
+    ws = kos.Workspace("cuda")
+    inp = build_inputs(torch, KI, kos, moe_shape)
+    ops = make_ops(kos, KI, inp, ws, moe_shape)
+    for _ in range(args.warmup):
+        for _, fn in ops:
+            fn()
+    torch.cuda.synchronize()
+    ws.status()
+    per, wall = time_ops(torch, ops, args.steps, ws)
+    ms_step = sum(per)
+    names = [n for n, _ in ops]
+    rows = int(inp["moe"]["goff"][-1].item())
+    fl = {"ag_gemm": KI.AG_QKV.flops, "gemm_rs": KI.RS_MLP.flops, "moe_dispatch": 0.0,
+          "moe_combine": rows * moe_shape.flops_per_row}
+    total_flops = sum(fl.values())
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    per_op = {}
+    for n, t in zip(names, per):
+        d = {"ms": round(t, 4)}
+        if fl[n] > 0:
+            tf = fl[n] / (t * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), pct_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+        per_op[n] = d
+    t_moe = per[names.index("moe_dispatch")] + per[names.index("moe_combine")]
+    moe_tok_s = moe_shape.tokens / (t_moe * 1e-3)
+    dom = max(range(len(per)), key=lambda i: per[i] if fl[names[i]] > 0 else -1)
+    ach = fl[names[dom]] / (per[dom] * 1e-3) / 1e12
+    roofline = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    extra = {"per_op": per_op, "moe_tokens_per_s": round(moe_tok_s, 1), "moe_grouped_rows": rows,
+             "wall_ms_per_step": round(wall, 3)}
+    if not args.no_baselines:
+        base = {}
+        reps = max(3, args.steps // 4)
+        for label, mode, crew in [("unfused", 2, -1)] + [(f"fixed_crew{m}", 1, m) for m in (8, 16, 32, 64)]:
+            ops_b = make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew)
+            for _, fn in ops_b:
+                fn()
+            pb, _ = time_ops(torch, ops_b, reps, ws)
+            base[label] = {n: round(t, 4) for n, t in zip(names, pb)}
+        fixed = {n: min(base[k][n] for k in base if k.startswith("fixed")) for n in names}
+        extra["baselines_ms"] = base
+        extra["speedup_vs_unfused"] = {n: round(base["unfused"][n] / t, 3) for n, t in zip(names, per)}
+        extra["speedup_vs_best_fixed"] = {n: round(fixed[n] / t, 3) for n, t in zip(names, per)
+                                          if n != "moe_dispatch"}
+        # GEMM throughput on 224 of 256 CUs (plain GEMM: the unfused GEMM launch at world 1)
+        ag = inp["ag"]
+        a_all = ag["g"]
+        cfull = torch.empty((a_all.shape[0], ag["w"].shape[1]), dtype=torch.bfloat16, device="cuda")
+        res = {}
+        for grid in (256, 224):
+            o = kos.opts(mode=2, grid=grid)
+            fn = lambda: kos.ag_gemm(a_all, [None], ag["w"], a_all, cfull, 0, ws, o)  # noqa: E731
+            fn()
+            t, _ = time_ops(torch, [("gemm", fn)], reps, ws)
+            res[grid] = t[0]
+        extra["gemm_224_vs_256_cu_throughput"] = round(res[256] / res[224], 3)
+        extra["gemm_256cu_ms"] = round(res[256], 4)
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, moe_shape)
+    else:
+        cpu = None
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"kosmos layer pass: ag_gemm {KI.AG_QKV.name} + gemm_rs {KI.RS_MLP.name} + "
+                               f"moe {moe_shape.name}", "emulated_ranks": 8, "mode": "fused",
+                   "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 1)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

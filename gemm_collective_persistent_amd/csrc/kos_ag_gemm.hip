@@ -197,8 +197,19 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
 
+  // A single rank whose gathered output is its own shard has nothing to move.
+  const bool nothing_to_move = world == 1 && a_gathered == a_local;
+  if (nothing_to_move) p.n_move = 0;
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = o.grid;
+  if (o.mode == KOS_MODE_UNFUSED && nothing_to_move) {
+    AgParams gm = p;           // the GEMM alone
+    gm.n_movers = 0;
+    gm.do_build = 1;
+    gm.wait_flags = 0;
+    return launch_ag_tile(bm, bn, gm, grid, s);
+  }
   if (o.mode == KOS_MODE_UNFUSED) {
     AgParams mv = p;           // launch 1: the whole all-gather
     mv.n_movers = grid;

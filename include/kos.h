@@ -146,7 +146,8 @@ int32_t kos_device_cu_count(void);
  *            p != rank (a_peers[rank] is ignored and may be NULL); device
  *            memory or pinned device-mapped host memory
  * w          bf16 [k, n] (the weight shard, stored K x N)
- * a_gathered out bf16 [world*m_local, k]: G, a bit copy of the shards
+ * a_gathered out bf16 [world*m_local, k]: G, a bit copy of the shards; with
+ *            world == 1 it may alias a_local (then nothing is moved)
  * c          out [world*m_local, n] of c_dtype (KOS_BF16 or KOS_F32)
  * Shapes: k % 64 == 0, n % 64 == 0 and m_local % 64 == 0 (KOS_ERR_SHAPE
  * otherwise); all pointers 16-byte aligned (KOS_ERR_ALIGN).
