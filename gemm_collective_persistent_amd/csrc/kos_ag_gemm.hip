@@ -47,7 +47,6 @@ struct AgParams {
 template <class S>
 __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
   constexpr int BM = S::BM, BN = S::BN;
-  __shared__ uint4 lds[S::LDS_BYTES / 16];
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
         A = p.gathered + ((int64_t)shard * p.m_local + (int64_t)rb * BM) * K;
       }
       BSrc b{p.w + (int64_t)nt * BN, nullptr, N, 0};
-      tile_mainloop<S>(acc, A, K, BM, b, p.k, lds);
+      tile_mainloop<S>(acc, A, K, BM, b, p.k);
       const int64_t row0 = (int64_t)shard * p.m_local + (int64_t)rb * BM;
       const int64_t col0 = (int64_t)nt * BN;
       if (p.c_f32) {
@@ -127,10 +126,10 @@ static kos_status launch_ag(const AgParams& p, int grid, hipStream_t stream) {
 }
 
 static kos_status launch_ag_tile(int bm, int bn, const AgParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256, 2, 4>>(p, grid, s);
-  if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128, 2, 2>>(p, grid, s);
-  if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128, 2, 2>>(p, grid, s);
-  return launch_ag<TileShape<64, 64, 2, 2>>(p, grid, s);
+  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256>>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128>>(p, grid, s);
+  return launch_ag<TileShape<64, 64>>(p, grid, s);
 }
 
 }  // namespace kos

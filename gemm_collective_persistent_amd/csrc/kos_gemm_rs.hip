@@ -76,7 +76,6 @@ __device__ inline void reduce_entry(const RsParams& p, int band, int col_tile) {
 template <class S>
 __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
   constexpr int BM = S::BM, BN = S::BN;
-  __shared__ uint4 lds[S::LDS_BYTES / 16];
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
       }
       const int64_t row0 = (int64_t)chunk * p.mc + (int64_t)band * BM;
       BSrc b{p.w + (int64_t)col * BN, nullptr, N, 0};
-      tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k, lds);
+      tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k);
       float* P = p.partial + row0 * N + (int64_t)col * BN;
       tile_foreach<S>(acc, [&](int r, int c, float v) { P[r * N + c] = v; });
       if (chunk == p.rank) wg_signal(&p.ready[band * p.tiles_n + col], 1u);
@@ -136,9 +135,9 @@ static kos_status launch_rs(const RsParams& p, int grid, hipStream_t stream) {
 }
 
 static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128, 2, 2>>(p, grid, s);
-  if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128, 2, 2>>(p, grid, s);
-  return launch_rs<TileShape<64, 64, 2, 2>>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128>>(p, grid, s);
+  return launch_rs<TileShape<64, 64>>(p, grid, s);
 }
 
 }  // namespace kos

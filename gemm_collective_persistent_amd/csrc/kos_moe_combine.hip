@@ -150,12 +150,12 @@ __device__ __forceinline__ void decode_tile(const CombineParams& p, int U, int j
 }
 
 template <class S>
-__device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN], uint4* lds) {
+__device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   constexpr int HN = S::BN / 2;    // h columns per tile
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
          S::BN / 4};
-  tile_mainloop<S>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H, lds);
+  tile_mainloop<S>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   uint16_t* hb = p.h + (int64_t)x.row0 * F + (int64_t)nt * HN;
@@ -176,10 +176,10 @@ __device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x
 }
 
 template <class S>
-__device__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN], uint4* lds) {
+__device__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
-  tile_mainloop<S>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F, lds);
+  tile_mainloop<S>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
   uint16_t* yb = p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN;
   const int mv = x.m_valid;
   tile_foreach<S>(acc, [&](int r, int c, float v) {
@@ -285,7 +285,6 @@ __device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb,
 template <class S>
 __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) {
   constexpr int BM = S::BM;
-  __shared__ uint4 lds[S::LDS_BYTES / 16];
   __shared__ CombineMeta M;
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
@@ -328,14 +327,14 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
       decode_tile(p, U, (int)j, down, u, nt);
       const Unit x = unit_of<BM>(M, p.E_loc, u);
       if (!down) {
-        gate_up_tile<S>(p, x, nt, acc, lds);
+        gate_up_tile<S>(p, x, nt, acc);
         wg_signal(&gu_done[u], 1u);
       } else {
         if (p.wait_flags && p.do_gu && !wg_wait(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
           failed = true;
           break;
         }
-        down_tile<S>(p, x, nt, acc, lds);
+        down_tile<S>(p, x, nt, acc);
         wg_signal(&dn_done[u], 1u);
       }
     }
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
   wg_exit(h, p.ctr, 2 * p.u_max, &slots);
 }
 
-using CombineTile = TileShape<256, 128, 2, 2>;
+using CombineTile = TileShape<256, 128>;
 
 }  // namespace kos
 

@@ -1,16 +1,26 @@
-// The builders' bf16 MFMA tile (gfx950): C[BM x BN] += A[BM x K] . B[K x BN],
-// fp32 accumulate, operands staged through LDS with double buffering.
+// The builders' bf16 MFMA tile (gfx950): C[BM x BN] = A[BM x K] . B[K x BN],
+// fp32 accumulate.
 //
-// Workgroup of WGM x WGN wave64s; each wave owns a (BM/WGM) x (BN/WGN)
-// sub-tile made of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16.
+// Workgroup of 4 wave64s arranged 2 x 2; each wave owns a (BM/2) x (BN/2)
+// sub-tile of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16, the
+// accumulators held in registers for the whole K loop.
 //
-// LDS layout (per stage): A as BM rows x 8 chunks of 16 bytes (k contiguous),
-// B transposed as BN rows x 8 chunks (k contiguous, one row per output
-// column), both with the 16-byte chunk index XOR-swizzled by the row so that
-// the MFMA operand reads (32 consecutive rows, one chunk) and the stores hit
-// distinct banks.  B arrives K x N row-major from HBM and is transposed in
-// registers: each thread loads an 8 x 8 block (8 rows of 16 bytes) and
-// repacks it into 8 k-contiguous columns with byte permutes.
+// Operands go straight from HBM/L2 into LDS (global_load_lds_dwordx4: each
+// lane's 16 bytes land at lds_base + 16*lane, so the lanes' global addresses
+// are chosen to realise the swizzled layouts below), through a ring of
+// STAGES buffers of BK = 32 k-columns, loads issued STAGES-1 stages ahead.
+//
+// LDS layouts per stage:
+//   A: BM rows x 4 chunks of 16 bytes (8 k values), chunk c of row m stored
+//      at position c ^ ((m >> 2) & 3).  The A operand of lane l (row l%32,
+//      8 k values from 8*(l/32)) is one ds_read_b128.
+//   B: BK rows (k) x BN/8 chunks, K x N as in HBM, chunk c of row k stored at
+//      position c ^ (4 * (k & 3)) (XOR kept inside the row).  The B operand
+//      (8 consecutive k of one column) is two ds_read_b64_tr_b16: in each
+//      16-lane group, lane j receives element j%4 of source lanes j/4 + 4v,
+//      v = 0..3, so source lane i = 4v + q points at row k0+v, columns
+//      n0 + 4q .. +4, and lane 4q + c receives column n0 + 4q + c, rows
+//      k0 .. k0+3.
 //
 // MFMA operand layout (32x32x16): lane l holds A[row l%32][k 8*(l/32) .. +8]
 // and B[k 8*(l/32) .. +8][col l%32]; accumulator register r of lane l is
@@ -21,20 +31,29 @@
 
 namespace kos {
 
-template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int BM_, int BN_, int STAGES_ = 4>
 struct TileShape {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int WGM = WGM_, WGN = WGN_;
-  static constexpr int NT = 64 * WGM * WGN;             // threads
+  static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
+  static constexpr int WGM = 2, WGN = 2;
+  static constexpr int NT = 256;                        // threads (4 waves)
   static constexpr int WM = BM / WGM, WN = BN / WGN;    // wave sub-tile
   static constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 blocks per wave
-  static constexpr int A_PER_T = BM * 8 / NT;           // A chunks per thread per stage
-  static constexpr int B_PER_T = (BN + NT - 1) / NT;    // 8x8 B blocks per thread
-  static constexpr int STAGE_CHUNKS = (BM + BN) * 8;    // 16-byte chunks per stage
-  static constexpr int LDS_BYTES = 2 * STAGE_CHUNKS * 16;
+  static constexpr int A_BYTES = BM * BK * 2;           // per stage
+  static constexpr int B_BYTES = BK * BN * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;    // 1 KiB wave loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int BROW_CHUNKS = BN / 8;            // 16-byte chunks per B row
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave sub-tile sides are multiples of 32");
-  static_assert(A_PER_T >= 1 && (BM * 8) % NT == 0, "A stage must spread evenly");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "each wave loads at least 1 KiB of A and of B");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(3 * LOADS <= 63, "vmcnt range");
 };
 
 // Where the B tile's columns come from.  Plain: BN consecutive columns of
@@ -54,152 +73,253 @@ struct BSrc {
   }
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Packs 16-bit lanes: low halves (sel 0x05040100) or high halves (0x07060302)
-// of lo_src and hi_src into one dword (lo_src's half in bits 0..15).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t lo_src, uint32_t hi_src) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t lo_src, uint32_t hi_src) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
-}
-
+__device__ __forceinline__ int a_swz(int m) { return (m >> 2) & 3; }
 template <class S>
-struct TileRegs {
-  uint4 a[S::A_PER_T];
-  uint4 b[S::B_PER_T][8];
+__device__ __forceinline__ int b_swz(int k) { return (4 * (k & 3)) & (S::BROW_CHUNKS - 1); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Per-lane source offsets of this wave's direct loads, fixed for a tile:
+// every stage reads base + k0 (A) or base + k0*ld (B) plus these.
+template <class S>
+struct LoadPlan {
+  const char* a_base;              // uniform
+  const char* b_base;              // uniform (plain B)
+  uint32_t a_off[S::A_LOADS];      // bytes from a_base
+  uint32_t b_off[S::B_LOADS];      // bytes from b_base (plain B)
+  const char* b_ptr[S::B_LOADS];   // per-lane pointers (dual B)
+  int64_t b_stride;                // bytes per k row of B
+  bool dual;
 };
 
-// Global -> registers for the stage starting at k0.
+// A rows are clamped to m_valid-1: rows past the valid ones only feed
+// accumulator rows that are never stored.
 template <class S>
-__device__ __forceinline__ void tile_gload(TileRegs<S>& r, const uint16_t* __restrict__ A, int64_t lda,
-                                           int m_valid, const BSrc& b, int k0) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void plan_loads(LoadPlan<S>& P, const uint16_t* __restrict__ A, int64_t lda, int m_valid,
+                                           const BSrc& b) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  P.a_base = reinterpret_cast<const char*>(A);
 #pragma unroll
-  for (int i = 0; i < S::A_PER_T; ++i) {
-    const int c = tid + i * S::NT;
-    const int row = c >> 3, kc = c & 7;
-    if (row < m_valid)
-      r.a[i] = *reinterpret_cast<const uint4*>(A + row * lda + k0 + kc * 8);
-    else
-      r.a[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < S::A_LOADS; ++i) {
+    const int slot = (wave * S::A_LOADS + i) * 64 + lane;   // 16-byte slot in the A stage
+    const int m = slot >> 2, p = slot & 3;
+    const int c = p ^ a_swz(m);
+    const int mr = m < m_valid ? m : m_valid - 1;
+    P.a_off[i] = (uint32_t)(mr * lda * 2 + c * 16);
   }
+  P.dual = b.seg != 0;
+  P.b_stride = b.ld * 2;
+  P.b_base = reinterpret_cast<const char*>(b.p0);
 #pragma unroll
-  for (int i = 0; i < S::B_PER_T; ++i) {
-    const int blk = tid + i * S::NT;
-    if (S::BN % S::NT == 0 || blk < S::BN) {
-      const int kb = blk & 7, nb = blk >> 3;
-      const uint16_t* src = b.col8(nb) + (int64_t)(k0 + kb * 8) * b.ld;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) r.b[i][q] = *reinterpret_cast<const uint4*>(src + q * b.ld);
-    }
+  for (int i = 0; i < S::B_LOADS; ++i) {
+    const int slot = (wave * S::B_LOADS + i) * 64 + lane;
+    const int k = slot / S::BROW_CHUNKS, p = slot % S::BROW_CHUNKS;
+    const int c = p ^ b_swz<S>(k);
+    const char* g = reinterpret_cast<const char*>(b.col8(c)) + (int64_t)k * P.b_stride;
+    P.b_ptr[i] = g;
+    P.b_off[i] = (uint32_t)(g - P.b_base);
   }
 }
 
-// Registers -> LDS stage (A as is, B transposed).
+// Issues this wave's direct loads of the stage starting at k0.
 template <class S>
-__device__ __forceinline__ void tile_lstore(const TileRegs<S>& r, uint4* __restrict__ stage) {
-  const int tid = threadIdx.x;
-  uint4* As = stage;
-  uint4* Bs = stage + S::BM * 8;
+__device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S>& P, int k0) {
+  const int wave = wave_id();
+  const char* a = P.a_base + (int64_t)k0 * 2;
 #pragma unroll
-  for (int i = 0; i < S::A_PER_T; ++i) {
-    const int c = tid + i * S::NT;
-    const int row = c >> 3, kc = c & 7;
-    As[row * 8 + (kc ^ swz(row))] = r.a[i];
-  }
+  for (int i = 0; i < S::A_LOADS; ++i)
+    __builtin_amdgcn_global_load_lds(a + P.a_off[i], (lds_void*)(lds_stage + (wave * S::A_LOADS + i) * 1024), 16,
+                                     0, 0);
+  char* bst = lds_stage + S::A_BYTES;
+  const int64_t kb = (int64_t)k0 * P.b_stride;
+  if (!P.dual) {
+    const char* bb = P.b_base + kb;
 #pragma unroll
-  for (int i = 0; i < S::B_PER_T; ++i) {
-    const int blk = tid + i * S::NT;
-    if (S::BN % S::NT == 0 || blk < S::BN) {
-      const int kb = blk & 7, nb = blk >> 3;
-      const uint32_t* in = reinterpret_cast<const uint32_t*>(&r.b[i][0]);  // in[q*4 + d]
+    for (int i = 0; i < S::B_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(bb + P.b_off[i], (lds_void*)(bst + (wave * S::B_LOADS + i) * 1024), 16, 0,
+                                       0);
+  } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = j >> 1;
-        uint4 o;
-        if ((j & 1) == 0) {
-          o.x = pack_lo(in[0 * 4 + d], in[1 * 4 + d]);
-          o.y = pack_lo(in[2 * 4 + d], in[3 * 4 + d]);
-          o.z = pack_lo(in[4 * 4 + d], in[5 * 4 + d]);
-          o.w = pack_lo(in[6 * 4 + d], in[7 * 4 + d]);
-        } else {
-          o.x = pack_hi(in[0 * 4 + d], in[1 * 4 + d]);
-          o.y = pack_hi(in[2 * 4 + d], in[3 * 4 + d]);
-          o.z = pack_hi(in[4 * 4 + d], in[5 * 4 + d]);
-          o.w = pack_hi(in[6 * 4 + d], in[7 * 4 + d]);
-        }
-        const int n = nb * 8 + j;
-        Bs[n * 8 + (kb ^ swz(n))] = o;
-      }
-    }
+    for (int i = 0; i < S::B_LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(P.b_ptr[i] + kb, (lds_void*)(bst + (wave * S::B_LOADS + i) * 1024), 16, 0,
+                                       0);
   }
 }
 
-// MFMAs over one LDS stage (BK = 64: four k16 steps).
+// Operand fragments of one k16 step.
 template <class S>
-__device__ __forceinline__ void tile_compute(f32x16 (&acc)[S::TM][S::TN], const uint4* __restrict__ stage) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+struct Frags {
+  bf16x8 a[S::TM];
+  bf16x8 b[S::TN];
+};
+
+// LDS -> registers for k16 step s (0 or 1) of a stage.
+template <class S>
+__device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, int s) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave / S::WGN, wn = wave % S::WGN;
-  const uint4* As = stage;
-  const uint4* Bs = stage + S::BM * 8;
+  const char* ast = lds_stage;
+  const char* bst = lds_stage + S::A_BYTES;
+  const int g = lane >> 4, jj = lane & 15, v = jj >> 2, q = jj & 3;
+  const int kc = 2 * s + (lane >> 5);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int kc = 2 * s + (lane >> 5);
-    bf16x8 af[S::TM], bfr[S::TN];
+  for (int i = 0; i < S::TM; ++i) {
+    const int m = wm * S::WM + i * 32 + (lane & 31);
+    f.a[i] = *reinterpret_cast<const bf16x8*>(ast + m * 64 + ((kc ^ a_swz(m)) << 4));
+  }
 #pragma unroll
-    for (int i = 0; i < S::TM; ++i) {
-      const int row = wm * S::WM + i * 32 + (lane & 31);
-      af[i] = __builtin_bit_cast(bf16x8, As[row * 8 + (kc ^ swz(row))]);
+  for (int j = 0; j < S::TN; ++j) {
+    const int n = wn * S::WN + j * 32 + 16 * (g & 1) + 4 * q;
+    s16x4 h[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k = s * 16 + 8 * (g >> 1) + 4 * r + v;
+      const int c = (n >> 3) ^ b_swz<S>(k);
+      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(bst + k * (S::BN * 2) + (c << 4) + ((n & 7) << 1)));
     }
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const int n = wn * S::WN + j * 32 + (lane & 31);
-      bfr[j] = __builtin_bit_cast(bf16x8, Bs[n * 8 + (kc ^ swz(n))]);
-    }
-#pragma unroll
-    for (int i = 0; i < S::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < S::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 both = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    f.b[j] = __builtin_bit_cast(bf16x8, both);
   }
 }
 
-// Full K loop: acc = A[0:m_valid rows] . B over k in [0, K).  Rows >= m_valid
-// read as zero.  `lds` holds two stages.  Begins and ends with the LDS free.
+template <class S>
+__device__ __forceinline__ void frag_mfma(f32x16 (&acc)[S::TM][S::TN], const Frags<S>& f) {
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt immediate: vmcnt <= v, lgkmcnt <= l (expcnt untouched).
+#define KOS_WAITCNT(v, l) __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (0x7 << 4) | ((l) << 8))
+
+// Waits until at most `n` stages of this wave's loads are in flight and all
+// its LDS reads have completed.
+template <class S>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 2) {
+    KOS_WAITCNT(2 * S::LOADS, 0);
+  } else if (n == 1) {
+    KOS_WAITCNT(S::LOADS, 0);
+  } else {
+    KOS_WAITCNT(0, 0);
+  }
+}
+
+// Workgroup barrier without a memory fence (the waits above are explicit);
+// the asm memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The LDS ring: one __shared__ array per stage, so the compiler can tell a
+// stage being read from the stages being filled and does not wait for them.
+template <class S, int I>
+__device__ __forceinline__ char* ring() {
+  __shared__ __attribute__((aligned(1024))) char buf[S::STAGE_BYTES];
+  return buf;
+}
+
+// One iteration of the K loop on stage kt, which sits in ring buffer `cur`
+// (`nxt` holds stage kt+1).  On entry f0 holds (kt, step 0); leaves f0 =
+// (kt+1, step 0).  `steady`: the look-ahead load is always issued (past the
+// end it re-reads the last stage: cache hits, never used), so the counts in
+// flight stay uniform and the loop body has no branches.
+template <class S, bool steady>
+__device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0, Frags<S>& f1, int kt, int nk,
+                                       const LoadPlan<S>& P, char* cur, char* nxt) {
+#if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
+  constexpr int ST = S::STAGES;
+  frag_load<S>(f1, cur, 1);
+  frag_mfma<S>(acc, f0);
+  // stage kt+1 must have landed (all waves) and stage kt must be read by all
+  // waves before its buffer takes stage kt+ST
+  if (steady) {
+    KOS_WAITCNT(2 * S::LOADS, 0);
+  } else {
+    wait_stages<S>(nk - 2 - kt < ST - 2 ? nk - 2 - kt : ST - 2);
+  }
+  lds_barrier();
+  if (steady) {
+    stage_load<S>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
+    frag_load<S>(f0, nxt, 0);
+  } else {
+    if (kt + ST < nk) stage_load<S>(cur, P, (kt + ST) * S::BK);
+    if (kt + 1 < nk) frag_load<S>(f0, nxt, 0);
+  }
+  frag_mfma<S>(acc, f1);
+#endif
+}
+
+// Full K loop: acc = A[0:m_valid rows] . B over k in [0, K) (K a multiple of
+// 32).  Begins and ends with the LDS ring free.
 template <class S>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const uint16_t* __restrict__ A,
-                                              int64_t lda, int m_valid, const BSrc& b, int K,
-                                              uint4* __restrict__ lds) {
+                                              int64_t lda, int m_valid, const BSrc& b, int K) {
+  constexpr int ST = S::STAGES;
+  static_assert(ST == 4, "the ring is unrolled for four stages");
 #pragma unroll
   for (int i = 0; i < S::TM; ++i)
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   const int nk = K / S::BK;
-  TileRegs<S> regs;
-  tile_gload<S>(regs, A, lda, m_valid, b, 0);
-  __syncthreads();  // LDS free from the previous user
-  tile_lstore<S>(regs, lds);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint4* cur = lds + (kt & 1) * S::STAGE_CHUNKS;
-    uint4* nxt = lds + ((kt + 1) & 1) * S::STAGE_CHUNKS;
-    const bool more = kt + 1 < nk;
-    if (more) tile_gload<S>(regs, A, lda, m_valid, b, (kt + 1) * S::BK);
-    tile_compute<S>(acc, cur);
-    if (more) tile_lstore<S>(regs, nxt);
-    __syncthreads();
+  LoadPlan<S> P;
+  plan_loads<S>(P, A, lda, m_valid, b);
+  char* r0 = ring<S, 0>();
+  char* r1 = ring<S, 1>();
+  char* r2 = ring<S, 2>();
+  char* r3 = ring<S, 3>();
+  KOS_WAITCNT(0, 0);
+  lds_barrier();   // the ring is free (previous user done)
+  if (nk >= ST && nk % ST == 0) {
+    stage_load<S>(r0, P, 0);
+    stage_load<S>(r1, P, 1 * S::BK);
+    stage_load<S>(r2, P, 2 * S::BK);
+    stage_load<S>(r3, P, 3 * S::BK);
+    KOS_WAITCNT(3 * S::LOADS, 0);
+    lds_barrier();
+    Frags<S> f0, f1;
+    frag_load<S>(f0, r0, 0);
+    for (int kt = 0; kt < nk; kt += ST) {
+      k_iter<S, true>(acc, f0, f1, kt, nk, P, r0, r1);
+      k_iter<S, true>(acc, f0, f1, kt + 1, nk, P, r1, r2);
+      k_iter<S, true>(acc, f0, f1, kt + 2, nk, P, r2, r3);
+      k_iter<S, true>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+    }
+    KOS_WAITCNT(0, 0);
+    lds_barrier();
+    return;
   }
+  stage_load<S>(r0, P, 0);
+  if (1 < nk) stage_load<S>(r1, P, 1 * S::BK);
+  if (2 < nk) stage_load<S>(r2, P, 2 * S::BK);
+  if (3 < nk) stage_load<S>(r3, P, 3 * S::BK);
+  // stage 0 landed; up to three later stages may still fly
+  if (nk >= 4) {
+    KOS_WAITCNT(3 * S::LOADS, 0);
+  } else {
+    wait_stages<S>(nk - 1);
+  }
+  lds_barrier();
+  Frags<S> f0, f1;
+  frag_load<S>(f0, r0, 0);
+  for (int kt = 0; kt < nk; kt += ST) {
+    k_iter<S, false>(acc, f0, f1, kt, nk, P, r0, r1);
+    if (kt + 1 < nk) k_iter<S, false>(acc, f0, f1, kt + 1, nk, P, r1, r2);
+    if (kt + 2 < nk) k_iter<S, false>(acc, f0, f1, kt + 2, nk, P, r2, r3);
+    if (kt + 3 < nk) k_iter<S, false>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+  }
+  KOS_WAITCNT(0, 0);
+  lds_barrier();
 }
 
 // Visits every accumulator element with its tile-relative (row, col).
 template <class S, class F>
 __device__ __forceinline__ void tile_foreach(const f32x16 (&acc)[S::TM][S::TN], F&& f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave / S::WGN, wn = wave % S::WGN;
 #pragma unroll
   for (int i = 0; i < S::TM; ++i)
