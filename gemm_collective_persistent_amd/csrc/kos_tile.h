@@ -221,6 +221,20 @@ __device__ __forceinline__ char* ring() {
   return buf;
 }
 
+// Scheduling hints for one basic block: interleave the block's MFMAs with
+// its LDS reads (and direct loads), so that operand reads for the next step
+// travel while the matrix cores work on this one.
+template <int N_MFMA, int N_DS, int N_VMEM>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int MFMA = 0x008, DS_READ = 0x100, VMEM = 0x020;
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    if (i < N_VMEM) __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+    if (i < N_DS) __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+  }
+}
+
 // One iteration of the K loop on stage kt, which sits in ring buffer `cur`
 // (`nxt` holds stage kt+1).  On entry f0 holds (kt, step 0); leaves f0 =
 // (kt+1, step 0).  `steady`: the look-ahead load is always issued (past the
@@ -231,8 +245,10 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
                                        const LoadPlan<S>& P, char* cur, char* nxt) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
+  constexpr int NM = S::TM * S::TN, ND = S::TM + 2 * S::TN;
   frag_load<S>(f1, cur, 1);
   frag_mfma<S>(acc, f0);
+  if (steady) sched_interleave<NM, ND, 0>();
   // stage kt+1 must have landed (all waves) and stage kt must be read by all
   // waves before its buffer takes stage kt+ST
   if (steady) {
@@ -244,11 +260,13 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
   if (steady) {
     stage_load<S>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
     frag_load<S>(f0, nxt, 0);
+    frag_mfma<S>(acc, f1);
+    sched_interleave<NM, ND, S::LOADS>();
   } else {
     if (kt + ST < nk) stage_load<S>(cur, P, (kt + ST) * S::BK);
     if (kt + 1 < nk) frag_load<S>(f0, nxt, 0);
+    frag_mfma<S>(acc, f1);
   }
-  frag_mfma<S>(acc, f1);
 #endif
 }
 
