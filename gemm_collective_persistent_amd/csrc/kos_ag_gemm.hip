@@ -73,9 +73,9 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       }
       const int rb = rem / p.moves_per_rb;
       const int64_t row = (int64_t)rb * BM + (int64_t)(rem % p.moves_per_rb) * p.rows_per_move;
-      wg_copy(p.gathered + ((int64_t)shard * p.m_local + row) * K, src_shard + row * K,
-              (size_t)p.rows_per_move * K * 2);
-      wg_signal(&p.ready[shard * p.rb_per_shard + rb], 1u);
+      wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * K, src_shard + row * K,
+                  (size_t)p.rows_per_move * K * 2);
+      wg_publish(&p.ready[shard * p.rb_per_shard + rb], 1u);
     }
     if (!p.movers_switch) {
       wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
@@ -94,17 +94,21 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       const int rem = (int)j % per_q;
       const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
       const int shard = (p.rank + q) % p.world;
-      const uint16_t* A;
-      if (q == 0) {
-        A = p.a_local + (int64_t)rb * BM * K;
-      } else {
-        if (p.wait_flags &&
-            !wg_wait(&p.ready[shard * p.rb_per_shard + rb], (uint32_t)p.moves_per_rb, h, p.spin_limit, j, &slots))
-          break;
-        A = p.gathered + ((int64_t)shard * p.m_local + (int64_t)rb * BM) * K;
-      }
       BSrc b{p.w + (int64_t)nt * BN, nullptr, N, 0};
-      tile_mainloop<S>(acc, A, K, BM, b, p.k);
+      if (q == 0) {
+        tile_mainloop<S>(acc, p.a_local + (int64_t)rb * BM * K, K, BM, b, p.k);
+      } else {
+        const uint16_t* A = p.gathered + ((int64_t)shard * p.m_local + (int64_t)rb * BM) * K;
+        if (p.wait_flags) {
+          // rows written by movers of this launch: wait for them, read device-coherent
+          if (!wg_observe(&p.ready[shard * p.rb_per_shard + rb], (uint32_t)p.moves_per_rb, h, p.spin_limit, j,
+                          &slots))
+            break;
+          tile_mainloop<S, false, true>(acc, A, K, BM, b, p.k);
+        } else {
+          tile_mainloop<S>(acc, A, K, BM, b, p.k);
+        }
+      }
       const int64_t row0 = (int64_t)shard * p.m_local + (int64_t)rb * BM;
       const int64_t col0 = (int64_t)nt * BN;
       if (p.c_f32) {
@@ -127,9 +131,32 @@ static kos_status launch_ag(const AgParams& p, int grid, hipStream_t stream) {
 
 static kos_status launch_ag_tile(int bm, int bn, const AgParams& p, int grid, hipStream_t s) {
   if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256>>(p, grid, s);
+  if (bm == 256 && bn == 192) return launch_ag<TileShape<256, 192>>(p, grid, s);
   if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128>>(p, grid, s);
   if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128>>(p, grid, s);
   return launch_ag<TileShape<64, 64>>(p, grid, s);
+}
+
+// The largest tile (fewest operand re-reads) that divides the shard rows and
+// the columns and still gives every workgroup at least one tile.
+static void pick_ag_tile(int64_t world, int64_t m_local, int64_t n, int grid, int* bm, int* bn) {
+  static const int cand[][2] = {{256, 256}, {256, 192}, {256, 128}, {128, 128}, {64, 64}};
+  for (const auto& c : cand) {
+    if (m_local % c[0] || n % c[1]) continue;
+    const int64_t tiles = world * (m_local / c[0]) * (n / c[1]);
+    if (tiles >= grid || (c[0] == 64 && c[1] == 64)) {
+      *bm = c[0];
+      *bn = c[1];
+      return;
+    }
+  }
+  // no tile gives one per workgroup: the largest that divides
+  for (const auto& c : cand)
+    if (m_local % c[0] == 0 && n % c[1] == 0) {
+      *bm = c[0];
+      *bn = c[1];
+      return;
+    }
 }
 
 }  // namespace kos
@@ -163,10 +190,8 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   kos_opts o;
   if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
 
-  // Tile: the largest supported tile that divides the shard rows and columns.
   int bm = 64, bn = 64;
-  if (m_local % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
-  else if (m_local % 128 == 0 && n % 128 == 0) bm = 128, bn = 128;
+  pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
 
   AgParams p{};
   p.world = world;
@@ -183,8 +208,8 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   p.spin_limit = o.spin_limit;
   p.rb_per_shard = (int32_t)(m_local / bm);
   p.tiles_n = (int32_t)(n / bn);
-  // Move entries of about 512 KiB: whole rows, dividing the row block.
-  int rows = (int)((512 * 1024) / (k * 2));
+  // Move entries of about 128 KiB: whole rows, dividing the row block.
+  int rows = (int)((128 * 1024) / (k * 2));
   if (rows < 1) rows = 1;
   if (rows > bm) rows = bm;
   while (bm % rows) --rows;

@@ -7,12 +7,17 @@
 // works if ..." paragraphs].
 //
 // Memory ordering: the MI355X's eight XCDs each have their own L2, which is
-// not coherent with the others for ordinary accesses.  A producer therefore
-// makes its stores visible at agent scope (release fence in every thread,
-// which waits for the stores and writes the L2 back) before one thread bumps
-// the counter; a consumer polls the counter with relaxed agent-scope loads
-// and then issues an agent-scope acquire fence in every thread (which
-// invalidates the stale lines) before it reads the data.
+// not coherent with the others for ordinary accesses.  Two protocols:
+//  * coherent exchange (the hot paths): data that another workgroup of the
+//    same launch reads is stored with device-scope (sc1) stores; the
+//    producer waits for its stores to complete (vmcnt(0)) in every thread,
+//    then one thread bumps the ready counter (wg_publish); the consumer
+//    polls the counter and reads the data with device-scope (sc1) loads
+//    (wg_observe).  No L2 write-back or invalidation is needed, so the L2
+//    keeps serving every other workgroup's operands.
+//  * fenced exchange (small metadata): agent-scope release fence in every
+//    thread before the bump (wg_signal), acquire fence after the poll
+//    (wg_wait).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -105,6 +110,62 @@ __device__ inline bool wg_wait(const uint32_t* counter, uint32_t target, WsHeade
   return ok;
 }
 
+// Coherent exchange, producer side: this workgroup's device-scope stores
+// have completed (every thread waits), then `v` is added to the counter.
+__device__ __forceinline__ void wg_publish(uint32_t* counter, uint32_t v) {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) add_relaxed(counter, v);
+}
+
+// Coherent exchange, consumer side: waits until *counter >= target (same
+// bound and error behaviour as wg_wait); the caller then reads the data with
+// device-scope loads.
+__device__ inline bool wg_observe(const uint32_t* counter, uint32_t target, WsHeader* h, uint32_t limit,
+                                  uint32_t info, WgSlots* s) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint32_t it = 0;
+    while (ld_relaxed(counter) < target) {
+      if (aborted(h)) { ok = 0; break; }
+      if (++it >= limit) { raise_error(h, KOS_ERR_TIMEOUT, info); ok = 0; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s->ok = ok;
+  }
+  __syncthreads();
+  return s->ok != 0;
+}
+
+// Device-scope (sc1) stores and loads for the coherent exchange.
+__device__ __forceinline__ void st_dev_b16(uint16_t* p, uint16_t v) {
+  asm volatile("global_store_short %0, %1, off sc1" : : "v"(p), "v"((uint32_t)v) : "memory");
+}
+__device__ __forceinline__ void st_dev_b32(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_b128(void* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+// Issues a device-scope 16-byte load; the value is valid only after
+// wait_dev_loads() names it.
+__device__ __forceinline__ u32x4 ld_dev_b128_issue(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void wait_dev_loads(u32x4& a) { asm volatile("s_waitcnt vmcnt(0)" : "+v"(a)); }
+__device__ __forceinline__ void wait_dev_loads(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void wait_dev_loads(u32x4 (&v)[16]) {
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                 "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                 "+v"(v[15]));
+}
+
 // Non-blocking readiness test by thread 0, broadcast (no fence: callers that
 // act on `true` must still call wg_wait or fence_acquire before reading).
 __device__ __forceinline__ bool wg_ready(const uint32_t* counter, uint32_t target, WgSlots* s) {
@@ -146,6 +207,26 @@ __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_count
 // ---------------------------------------------------------------------------
 // movers: coalesced 128-bit copies
 // ---------------------------------------------------------------------------
+
+// Copies `bytes` (a multiple of 16) from src to dst with the whole
+// workgroup, stores device-coherent (see wg_publish); consecutive threads
+// touch consecutive 16-byte chunks and each thread keeps 8 loads in flight.
+__device__ inline void wg_copy_dev(void* __restrict__ dst, const void* __restrict__ src, size_t bytes) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const size_t n = bytes >> 4;
+  const size_t nt = blockDim.x;
+  size_t i = threadIdx.x;
+  constexpr int U = 8;
+  for (; i + (U - 1) * nt < n; i += U * nt) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + u * nt]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st_dev_b128(&d[i + u * nt], v[u]);
+  }
+  for (; i < n; i += nt) st_dev_b128(&d[i], __builtin_nontemporal_load(&s[i]));
+}
 
 // Copies `bytes` (a multiple of 16) from src to dst with the whole
 // workgroup; consecutive threads touch consecutive 16-byte chunks and each

@@ -16,8 +16,8 @@
 //            Every tile stores its fp32 partial into `partial` (rows of
 //            chunk c != rank stand for the push into rank c's inbox); tiles
 //            of our own chunk then bump ready[band * tiles_n + col].
-//   head[2]  reduce entries (band b, column tile) of our own chunk, b
-//            ascending then column: y = sum_p X_p in ascending p (fp32),
+//   head[2]  reduce entries (band b, column tile, 32-row slab) of our own
+//            chunk, in that order: y = sum_p X_p in ascending p (fp32),
 //            X_rank = partial[chunk rank], X_p = peer_slices[p].  Gated on
 //            the ready counter of our own tile at (b, column).  The peers'
 //            slices of a band are taken as ready together with ours: every
@@ -47,29 +47,56 @@ struct RsParams {
   uint32_t* ready;
 };
 
-// y[rows, cols] of one reduce entry: BM x BN floats, float4 per thread.
-template <int BM, int BN>
-__device__ inline void reduce_entry(const RsParams& p, int band, int col_tile) {
+// Rows of one reduce entry: a slab of kSlabRows rows of one output tile.
+constexpr int kSlabRows = 32;
+
+// y[slab rows, tile cols] = sum over ranks, ascending, in fp32; two float4
+// per thread per pass so that 2 x world loads are in flight.
+template <int BN>
+__device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int col_tile) {
   const int64_t N = p.n;
-  const int64_t r0 = (int64_t)band * BM;                 // row inside the chunk
   const int64_t c0 = (int64_t)col_tile * BN;
   constexpr int V = BN / 4;                              // float4 per row
-  const float* own = p.partial + ((int64_t)p.rank * p.mc + r0) * N + c0;
-  for (int e = threadIdx.x; e < BM * V; e += blockDim.x) {
-    const int row = e / V, v = e % V;
-    const int64_t off = row * N + v * 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int E = kSlabRows * V;                       // float4 per slab
+  const float* src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    src[q] = q >= p.world ? nullptr
+                          : (q == p.rank ? p.partial + ((int64_t)p.rank * p.mc + r0) * N + c0
+                                         : p.peers[q] + r0 * N + c0);
+  float* dst = p.y + r0 * N + c0;
+  for (int e = threadIdx.x; e < E; e += 2 * blockDim.x) {
+    const int e2 = e + blockDim.x;
+    const int64_t o1 = (int64_t)(e / V) * N + (e % V) * 4;
+    const int64_t o2 = (int64_t)(e2 / V) * N + (e2 % V) * 4;
+    const bool two = e2 < E;
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 x1[8], x2[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q >= p.world) break;
-      f32x4 x;
-      if (q == p.rank)
-        x = *reinterpret_cast<const f32x4*>(own + off);
-      else
-        x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.peers[q] + (r0 * N + c0) + off));
-      acc += x;
+      if (q == p.rank) {   // written by builders of this launch: device-coherent loads
+        const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src[q] + o1);
+        const uint32_t* s2 = reinterpret_cast<const uint32_t*>(src[q] + o2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x1[q][c] = __builtin_bit_cast(float, __hip_atomic_load(s1 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (two)
+            x2[q][c] = __builtin_bit_cast(float, __hip_atomic_load(s2 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+      } else {
+        x1[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + o1));
+        if (two) x2[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + o2));
+      }
     }
-    *reinterpret_cast<f32x4*>(p.y + (r0 * N + c0) + off) = acc;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q >= p.world) break;
+      a1 += x1[q];
+      if (two) a2 += x2[q];
+    }
+    *reinterpret_cast<f32x4*>(dst + o1) = a1;
+    if (two) *reinterpret_cast<f32x4*>(dst + o2) = a2;
   }
 }
 
@@ -106,8 +133,12 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
       BSrc b{p.w + (int64_t)col * BN, nullptr, N, 0};
       tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k);
       float* P = p.partial + row0 * N + (int64_t)col * BN;
-      tile_foreach<S>(acc, [&](int r, int c, float v) { P[r * N + c] = v; });
-      if (chunk == p.rank) wg_signal(&p.ready[band * p.tiles_n + col], 1u);
+      if (chunk == p.rank) {   // read by this launch's reducers: device-coherent stores
+        tile_foreach<S>(acc, [&](int r, int c, float v) { st_dev_b32(&P[r * N + c], __builtin_bit_cast(uint32_t, v)); });
+        wg_publish(&p.ready[band * p.tiles_n + col], 1u);
+      } else {
+        tile_foreach<S>(acc, [&](int r, int c, float v) { P[r * N + c] = v; });
+      }
     }
     if (!p.builders_switch || !p.do_reduce) {
       wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
@@ -117,12 +148,14 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
 
   // ---- reducer role -----------------------------------------------------
   if (p.do_reduce) {
+    constexpr int SLABS = BM / kSlabRows;
     for (;;) {
       const uint32_t i = wg_claim(&h->head[2], h, &slots);
-      if (i >= (uint32_t)p.n_reduce) break;
-      const int band = (int)i / p.tiles_n, col = (int)i % p.tiles_n;
-      if (p.wait_flags && !wg_wait(&p.ready[i], 1u, h, p.spin_limit, i, &slots)) break;
-      reduce_entry<BM, BN>(p, band, col);
+      if (i >= (uint32_t)p.n_reduce * SLABS) break;
+      const int tile = (int)i / SLABS, slab = (int)i % SLABS;
+      const int band = tile / p.tiles_n, col = tile % p.tiles_n;
+      if (p.wait_flags && !wg_observe(&p.ready[tile], 1u, h, p.spin_limit, i, &slots)) break;
+      reduce_entry<BN>(p, (int64_t)band * BM + slab * kSlabRows, col);
     }
   }
   wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
@@ -135,6 +168,7 @@ static kos_status launch_rs(const RsParams& p, int grid, hipStream_t stream) {
 }
 
 static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 256) return launch_rs<TileShape<256, 256>>(p, grid, s);
   if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128>>(p, grid, s);
   if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128>>(p, grid, s);
   return launch_rs<TileShape<64, 64>>(p, grid, s);
@@ -170,7 +204,8 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
 
   const int64_t mc = m / world;
   int bm = 64, bn = 64;
-  if (mc % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
+  if (mc % 256 == 0 && n % 256 == 0) bm = 256, bn = 256;
+  else if (mc % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
   else if (mc % 128 == 0 && n % 128 == 0) bm = 128, bn = 128;
 
   RsParams p{};

@@ -27,4 +27,28 @@ __device__ __forceinline__ void wave_copy_row(void* __restrict__ dst, const void
   for (; i < n; i += 64) d[i] = s[i];
 }
 
+// Same, reading the source with device-scope loads (rows written by other
+// workgroups of the same launch).
+__device__ __forceinline__ void wave_copy_row_dev_src(void* __restrict__ dst, const void* __restrict__ src, int bytes) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const int lane = threadIdx.x & 63;
+  const int n = bytes >> 4;
+  int i = lane;
+  for (; i + 3 * 64 < n; i += 4 * 64) {
+    u32x4 v0 = ld_dev_b128_issue(&s[i]), v1 = ld_dev_b128_issue(&s[i + 64]);
+    u32x4 v2 = ld_dev_b128_issue(&s[i + 128]), v3 = ld_dev_b128_issue(&s[i + 192]);
+    wait_dev_loads(v0, v1, v2, v3);
+    d[i] = v0;
+    d[i + 64] = v1;
+    d[i + 128] = v2;
+    d[i + 192] = v3;
+  }
+  for (; i < n; i += 64) {
+    u32x4 v = ld_dev_b128_issue(&s[i]);
+    wait_dev_loads(v);
+    d[i] = v;
+  }
+}
+
 }  // namespace kos

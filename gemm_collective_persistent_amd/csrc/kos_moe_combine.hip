@@ -68,7 +68,7 @@ struct CombineMeta {
 };
 
 template <int BM>
-__device__ inline void load_combine_meta(const CombineParams& p, CombineMeta& M) {
+__device__ __forceinline__ void load_combine_meta(const CombineParams& p, CombineMeta& M) {
   for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) M.go[el] = p.go_in[el];
   for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
     int run = 0;
@@ -150,12 +150,12 @@ __device__ __forceinline__ void decode_tile(const CombineParams& p, int U, int j
 }
 
 template <class S>
-__device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
+__device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   constexpr int HN = S::BN / 2;    // h columns per tile
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
          S::BN / 4};
-  tile_mainloop<S>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
+  tile_mainloop<S, true>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   uint16_t* hb = p.h + (int64_t)x.row0 * F + (int64_t)nt * HN;
@@ -167,27 +167,28 @@ __device__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x
       for (int r = 0; r < 16; ++r) {
         const int row = wm * S::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int col = wn * (S::BN / 4) + j * 32 + (lane & 31);
-        if (row < x.m_valid) {
+        if (row < x.m_valid) {   // read by this launch's down tiles: device-coherent stores
           const float g = acc[i][j][r], u = acc[i][j + S::TN / 2][r];
           const float hv = g / (1.0f + expf(-g)) * u;
-          hb[(int64_t)row * F + col] = f32_to_bf16_bits(hv);
+          st_dev_b16(&hb[(int64_t)row * F + col], f32_to_bf16_bits(hv));
         }
       }
 }
 
-template <class S>
-__device__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
+// COH: h was written by this launch's gate/up tiles (read device-coherent).
+template <class S, bool COH>
+__device__ __forceinline__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
-  tile_mainloop<S>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
+  tile_mainloop<S, false, COH>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
   uint16_t* yb = p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN;
   const int mv = x.m_valid;
-  tile_foreach<S>(acc, [&](int r, int c, float v) {
-    if (r < mv) yb[(int64_t)r * H + c] = f32_to_bf16_bits(v);
+  tile_foreach<S>(acc, [&](int r, int c, float v) {   // read by pushes and folds: device-coherent
+    if (r < mv) st_dev_b16(&yb[(int64_t)r * H + c], f32_to_bf16_bits(v));
   });
 }
 
-__device__ void push_unit(const CombineParams& p, const Unit& x) {
+__device__ __forceinline__ void push_unit(const CombineParams& p, const Unit& x) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   (void)lane;
   for (int r = wave; r < x.m_valid; r += nw) {
@@ -195,7 +196,7 @@ __device__ void push_unit(const CombineParams& p, const Unit& x) {
     const int src = p.row_src[grow * 2];
     if (src == p.rank) continue;
     const int64_t i = p.row_src[grow * 2 + 1];
-    wave_copy_row(p.out_return[src] + i * p.H, p.yg + grow * p.H, p.H * 2);
+    wave_copy_row_dev_src(p.out_return[src] + i * p.H, p.yg + grow * p.H, p.H * 2);
   }
 }
 
@@ -215,7 +216,7 @@ __device__ inline bool t0_poll(const uint32_t* c, uint32_t target, WsHeader* h, 
 }
 
 template <int BM>
-__device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb, WgSlots* s) {
+__device__ __forceinline__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb, WgSlots* s) {
   const int t0 = fb * kFoldTokens;
   const int t1 = min(p.T, t0 + kFoldTokens);
   const uint32_t* dn_done = p.ctr + p.u_max;
@@ -238,7 +239,6 @@ __device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb,
   }
   __syncthreads();
   if (!s->ok) return false;
-  fence_acquire();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int E_loc = p.E_loc;
   for (int t = t0 + wave; t < t1; t += nw) {
@@ -260,10 +260,15 @@ __device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb,
     }
     for (int c = lane; c < p.H / 8; c += 64) {
       float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      u32x4 vj[kMoeMaxTopk];
+#pragma unroll
+      for (int j = 0; j < kMoeMaxTopk; ++j)   // local rows come from this launch: device-coherent
+        if (j < p.k) vj[j] = ld_dev_b128_issue(reinterpret_cast<const u32x4*>(src[j]) + c);
+      wait_dev_loads(vj);
 #pragma unroll
       for (int j = 0; j < kMoeMaxTopk; ++j) {
         if (j >= p.k) break;
-        const uint4 v = reinterpret_cast<const uint4*>(src[j])[c];
+        const u32x4 v = vj[j];
         const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -282,11 +287,18 @@ __device__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb,
   return true;
 }
 
-template <class S>
-__global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) {
+// COH: one launch produces and consumes h and Y (fused and fixed-crew modes).
+template <class S, bool COH>
+__global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams args) {
   constexpr int BM = S::BM;
   __shared__ CombineMeta M;
   __shared__ WgSlots slots;
+  // The parameter block lives in LDS: the role code reads the fields it needs
+  // when it needs them instead of pinning ~40 pointers in scalar registers.
+  __shared__ CombineParams ps;
+  if (threadIdx.x == 0) ps = args;
+  __syncthreads();
+  const CombineParams& p = ps;
   WsHeader* h = p.ws;
   load_combine_meta<BM>(p, M);
   const int U = M.ub[p.E_loc];
@@ -316,7 +328,6 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
           __syncthreads();
           const uint32_t got = slots.claim;
           if (got == kNoEntry) break;
-          fence_acquire();
           push_unit(p, unit_of<BM>(M, p.E_loc, (int)got));
         }
       }
@@ -328,14 +339,14 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
       const Unit x = unit_of<BM>(M, p.E_loc, u);
       if (!down) {
         gate_up_tile<S>(p, x, nt, acc);
-        wg_signal(&gu_done[u], 1u);
+        wg_publish(&gu_done[u], 1u);
       } else {
-        if (p.wait_flags && p.do_gu && !wg_wait(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
+        if (p.wait_flags && p.do_gu && !wg_observe(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
           failed = true;
           break;
         }
-        down_tile<S>(p, x, nt, acc);
-        wg_signal(&dn_done[u], 1u);
+        down_tile<S, COH>(p, x, nt, acc);
+        wg_publish(&dn_done[u], 1u);
       }
     }
     if (p.n_crew > 0) {   // fixed crew: builders only build
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
     for (;;) {
       const uint32_t i = wg_claim(&h->head[2], h, &slots);
       if (i >= (uint32_t)U) break;
-      if (p.wait_flags && !wg_wait(&dn_done[i], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
+      if (p.wait_flags && !wg_observe(&dn_done[i], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
       push_unit(p, unit_of<BM>(M, p.E_loc, (int)i));
     }
   }
@@ -366,7 +377,9 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams p) 
   wg_exit(h, p.ctr, 2 * p.u_max, &slots);
 }
 
-using CombineTile = TileShape<256, 128>;
+// Big tile when the widths allow it (hidden % 256, ffn % 128), else 128 x 128.
+using CombineTileBig = TileShape<256, 256>;
+using CombineTileSmall = TileShape<128, 128>;
 
 }  // namespace kos
 
@@ -379,8 +392,9 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
                                       const int32_t* peer_counts, const void* const* peer_return, void* h,
                                       void* y_grouped, void* const* out_return, void* y, const kos_opts* opts,
                                       void* ws, size_t ws_bytes, void* stream) {
-  using S = CombineTile;
   if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
+  const bool big = s->hidden % CombineTileBig::BN == 0 && s->ffn % (CombineTileBig::BN / 2) == 0;
+  using S = CombineTileSmall;   // the checks below use the small tile's divisibility
   const int R = s->world, r = s->rank;
   if (R < 1 || R > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", R);
   if (r < 0 || r >= R) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", r, R);
@@ -436,10 +450,12 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   p.h = static_cast<uint16_t*>(h);
   p.yg = static_cast<uint16_t*>(y_grouped);
   p.y = static_cast<uint16_t*>(y);
-  p.G = s->ffn / (S::BN / 2);
-  p.D = s->hidden / S::BN;
+  const int BMt = big ? CombineTileBig::BM : CombineTileSmall::BM;
+  const int BNt = big ? CombineTileBig::BN : CombineTileSmall::BN;
+  p.G = s->ffn / (BNt / 2);
+  p.D = s->hidden / BNt;
   p.L = (o.grid + p.G - 1) / p.G;
-  p.u_max = (int32_t)((grouped_cap + S::BM - 1) / S::BM) + p.E_loc;
+  p.u_max = (int32_t)((grouped_cap + BMt - 1) / BMt) + p.E_loc;
   if ((size_t)2 * p.u_max > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
   p.spin_limit = o.spin_limit;
   p.ws = static_cast<WsHeader*>(ws);
@@ -447,7 +463,19 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   auto launch = [&](const CombineParams& q, const char* what) {
-    hipLaunchKernelGGL((moe_combine_kernel<S>), dim3(o.grid), dim3(S::NT), 0, strm, q);
+    const bool coh = q.wait_flags != 0;
+    if (big && coh)
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, true>), dim3(o.grid), dim3(CombineTileBig::NT), 0, strm,
+                         q);
+    else if (big)
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, false>), dim3(o.grid), dim3(CombineTileBig::NT), 0,
+                         strm, q);
+    else if (coh)
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, true>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+                         strm, q);
+    else
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, false>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+                         strm, q);
     return launch_status(what);
   };
   if (o.mode == KOS_MODE_UNFUSED) {

@@ -78,7 +78,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ void route_block(const DispatchParams& p, int b, DispatchLds& L) {
+__device__ __forceinline__ void route_block(const DispatchParams& p, int b, DispatchLds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.m[e] = 0ull;
   __syncthreads();
@@ -145,7 +145,7 @@ __device__ void route_block(const DispatchParams& p, int b, DispatchLds& L) {
 // Run once, by the workgroup that routed the last block.  Returns false
 // (for every thread) when a capacity would overflow; the error is recorded
 // and the movers are never released.
-__device__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
+__device__ __forceinline__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
     int run = 0;
     for (int b = 0; b < p.nblk; ++b) {
@@ -178,7 +178,7 @@ __device__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
       const int ge = p.rank * p.E_loc + el;
       go += L.off[ge + 1] - L.off[ge];
       for (int q = 0; q < p.world; ++q)
-        if (q != p.rank) go += p.peer_counts[q * p.E_loc + el];
+        if (q != p.rank) go += L.pc[q][el];
     }
     p.grouped_offsets[p.E_loc] = (int32_t)go;
     if (go > p.grouped_cap) over = true;
@@ -190,7 +190,7 @@ __device__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
 }
 
 // Loads the scan's results into LDS (after counter[1]).
-__device__ void load_meta(const DispatchParams& p, DispatchLds& L) {
+__device__ __forceinline__ void load_meta(const DispatchParams& p, DispatchLds& L) {
   for (int e = threadIdx.x; e <= p.E; e += blockDim.x) L.off[e] = p.off[e];
   for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) L.go[el] = p.grouped_offsets[el];
   __syncthreads();
@@ -305,7 +305,21 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
             }
           }
           const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * H);
-          for (int c = lane; c < row_bytes / 16; c += 64) {
+          const int nc = row_bytes / 16;
+          int c = lane;
+          for (; c + 3 * 64 < nc; c += 4 * 64) {   // four loads in flight per lane
+            const u32x4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
+#pragma unroll
+            for (int j = 0; j < kMoeMaxTopk; ++j) {
+              if (j >= p.k) break;
+              u32x4* d = reinterpret_cast<u32x4*>(dst[j]);
+              d[c] = v0;
+              d[c + 64] = v1;
+              d[c + 128] = v2;
+              d[c + 192] = v3;
+            }
+          }
+          for (; c < nc; c += 64) {
             const u32x4 v = src[c];
 #pragma unroll
             for (int j = 0; j < kMoeMaxTopk; ++j) {

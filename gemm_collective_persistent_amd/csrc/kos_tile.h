@@ -15,7 +15,7 @@
 //      at position c ^ ((m >> 2) & 3).  The A operand of lane l (row l%32,
 //      8 k values from 8*(l/32)) is one ds_read_b128.
 //   B: BK rows (k) x BN/8 chunks, K x N as in HBM, chunk c of row k stored at
-//      position c ^ (4 * (k & 3)) (XOR kept inside the row).  The B operand
+//      position b_pos(c, k) (XOR or rotation by 4*(k%4) inside the row).  The B operand
 //      (8 consecutive k of one column) is two ds_read_b64_tr_b16: in each
 //      16-lane group, lane j receives element j%4 of source lanes j/4 + 4v,
 //      v = 0..3, so source lane i = 4v + q points at row k0+v, columns
@@ -51,6 +51,7 @@ struct TileShape {
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int BROW_CHUNKS = BN / 8;            // 16-byte chunks per B row
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
+  static_assert(B_BYTES % 4096 == 0 && A_BYTES % 4096 == 0, "whole 1 KiB loads per wave");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "each wave loads at least 1 KiB of A and of B");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(3 * LOADS <= 63, "vmcnt range");
@@ -74,29 +75,51 @@ struct BSrc {
 };
 
 __device__ __forceinline__ int a_swz(int m) { return (m >> 2) & 3; }
+
+// B rows: chunk c of row k sits at position b_pos(c, k).  Rows of a power
+// of two chunks XOR the chunk index with 4*(k%4); other widths rotate it by
+// 4*(k%4).  Both keep aligned 4-chunk groups together and send the four
+// rows read by one transpose read to different banks.
 template <class S>
-__device__ __forceinline__ int b_swz(int k) { return (4 * (k & 3)) & (S::BROW_CHUNKS - 1); }
+__device__ __forceinline__ int b_pos(int c, int k) {
+  constexpr int W = S::BROW_CHUNKS;
+  if constexpr ((W & (W - 1)) == 0) {
+    return c ^ ((4 * (k & 3)) & (W - 1));
+  } else {
+    const int p = c + 4 * (k & 3);
+    return p >= W ? p - W : p;
+  }
+}
+template <class S>
+__device__ __forceinline__ int b_chunk(int p, int k) {
+  constexpr int W = S::BROW_CHUNKS;
+  if constexpr ((W & (W - 1)) == 0) {
+    return p ^ ((4 * (k & 3)) & (W - 1));
+  } else {
+    const int c = p - 4 * (k & 3);
+    return c < 0 ? c + W : c;
+  }
+}
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Per-lane source offsets of this wave's direct loads, fixed for a tile:
 // every stage reads base + k0 (A) or base + k0*ld (B) plus these.
-template <class S>
+template <class S, bool DUAL, bool COH_A = false>
 struct LoadPlan {
-  const char* a_base;              // uniform
-  const char* b_base;              // uniform (plain B)
-  uint32_t a_off[S::A_LOADS];      // bytes from a_base
-  uint32_t b_off[S::B_LOADS];      // bytes from b_base (plain B)
-  const char* b_ptr[S::B_LOADS];   // per-lane pointers (dual B)
-  int64_t b_stride;                // bytes per k row of B
-  bool dual;
+  const char* a_base;                          // uniform
+  const char* b_base;                          // uniform (plain B)
+  uint32_t a_off[S::A_LOADS];                  // bytes from a_base
+  uint32_t b_off[DUAL ? 1 : S::B_LOADS];       // bytes from b_base (plain B)
+  const char* b_ptr[DUAL ? S::B_LOADS : 1];    // per-lane pointers (dual B)
+  int64_t b_stride;                            // bytes per k row of B
 };
 
 // A rows are clamped to m_valid-1: rows past the valid ones only feed
 // accumulator rows that are never stored.
-template <class S>
-__device__ __forceinline__ void plan_loads(LoadPlan<S>& P, const uint16_t* __restrict__ A, int64_t lda, int m_valid,
-                                           const BSrc& b) {
+template <class S, bool DUAL, bool COH_A>
+__device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const uint16_t* __restrict__ A, int64_t lda,
+                                           int m_valid, const BSrc& b) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   P.a_base = reinterpret_cast<const char*>(A);
 #pragma unroll
@@ -107,32 +130,37 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S>& P, const uint16_t* __res
     const int mr = m < m_valid ? m : m_valid - 1;
     P.a_off[i] = (uint32_t)(mr * lda * 2 + c * 16);
   }
-  P.dual = b.seg != 0;
   P.b_stride = b.ld * 2;
   P.b_base = reinterpret_cast<const char*>(b.p0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
     const int slot = (wave * S::B_LOADS + i) * 64 + lane;
     const int k = slot / S::BROW_CHUNKS, p = slot % S::BROW_CHUNKS;
-    const int c = p ^ b_swz<S>(k);
+    const int c = b_chunk<S>(p, k);
     const char* g = reinterpret_cast<const char*>(b.col8(c)) + (int64_t)k * P.b_stride;
-    P.b_ptr[i] = g;
-    P.b_off[i] = (uint32_t)(g - P.b_base);
+    if constexpr (DUAL)
+      P.b_ptr[i] = g;
+    else
+      P.b_off[i] = (uint32_t)(g - P.b_base);
   }
 }
 
 // Issues this wave's direct loads of the stage starting at k0.
-template <class S>
-__device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S>& P, int k0) {
+// Cache policy of the A loads: device-coherent (sc1) when A is written by
+// other workgroups of the same launch.
+constexpr int kCpolDevice = 16;
+
+template <class S, bool DUAL, bool COH_A>
+__device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A>& P, int k0) {
   const int wave = wave_id();
   const char* a = P.a_base + (int64_t)k0 * 2;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
     __builtin_amdgcn_global_load_lds(a + P.a_off[i], (lds_void*)(lds_stage + (wave * S::A_LOADS + i) * 1024), 16,
-                                     0, 0);
+                                     0, COH_A ? kCpolDevice : 0);
   char* bst = lds_stage + S::A_BYTES;
   const int64_t kb = (int64_t)k0 * P.b_stride;
-  if (!P.dual) {
+  if constexpr (!DUAL) {
     const char* bb = P.b_base + kb;
 #pragma unroll
     for (int i = 0; i < S::B_LOADS; ++i)
@@ -174,7 +202,7 @@ __device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, in
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = s * 16 + 8 * (g >> 1) + 4 * r + v;
-      const int c = (n >> 3) ^ b_swz<S>(k);
+      const int c = b_pos<S>(n >> 3, k);
       h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(bst + k * (S::BN * 2) + (c << 4) + ((n & 7) << 1)));
     }
@@ -240,9 +268,9 @@ __device__ __forceinline__ void sched_interleave() {
 // (kt+1, step 0).  `steady`: the look-ahead load is always issued (past the
 // end it re-reads the last stage: cache hits, never used), so the counts in
 // flight stay uniform and the loop body has no branches.
-template <class S, bool steady>
+template <class S, bool DUAL, bool COH_A, bool steady>
 __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0, Frags<S>& f1, int kt, int nk,
-                                       const LoadPlan<S>& P, char* cur, char* nxt) {
+                                       const LoadPlan<S, DUAL, COH_A>& P, char* cur, char* nxt) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
   constexpr int NM = S::TM * S::TN, ND = S::TM + 2 * S::TN;
@@ -258,12 +286,12 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
   }
   lds_barrier();
   if (steady) {
-    stage_load<S>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
+    stage_load<S, DUAL, COH_A>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
     frag_load<S>(f0, nxt, 0);
     frag_mfma<S>(acc, f1);
     sched_interleave<NM, ND, S::LOADS>();
   } else {
-    if (kt + ST < nk) stage_load<S>(cur, P, (kt + ST) * S::BK);
+    if (kt + ST < nk) stage_load<S, DUAL, COH_A>(cur, P, (kt + ST) * S::BK);
     if (kt + 1 < nk) frag_load<S>(f0, nxt, 0);
     frag_mfma<S>(acc, f1);
   }
@@ -272,7 +300,7 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
 
 // Full K loop: acc = A[0:m_valid rows] . B over k in [0, K) (K a multiple of
 // 32).  Begins and ends with the LDS ring free.
-template <class S>
+template <class S, bool DUAL = false, bool COH_A = false>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const uint16_t* __restrict__ A,
                                               int64_t lda, int m_valid, const BSrc& b, int K) {
   constexpr int ST = S::STAGES;
@@ -284,8 +312,8 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / S::BK;
-  LoadPlan<S> P;
-  plan_loads<S>(P, A, lda, m_valid, b);
+  LoadPlan<S, DUAL, COH_A> P;
+  plan_loads<S, DUAL, COH_A>(P, A, lda, m_valid, b);
   char* r0 = ring<S, 0>();
   char* r1 = ring<S, 1>();
   char* r2 = ring<S, 2>();
@@ -293,28 +321,28 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   KOS_WAITCNT(0, 0);
   lds_barrier();   // the ring is free (previous user done)
   if (nk >= ST && nk % ST == 0) {
-    stage_load<S>(r0, P, 0);
-    stage_load<S>(r1, P, 1 * S::BK);
-    stage_load<S>(r2, P, 2 * S::BK);
-    stage_load<S>(r3, P, 3 * S::BK);
+    stage_load<S, DUAL, COH_A>(r0, P, 0);
+    stage_load<S, DUAL, COH_A>(r1, P, 1 * S::BK);
+    stage_load<S, DUAL, COH_A>(r2, P, 2 * S::BK);
+    stage_load<S, DUAL, COH_A>(r3, P, 3 * S::BK);
     KOS_WAITCNT(3 * S::LOADS, 0);
     lds_barrier();
     Frags<S> f0, f1;
     frag_load<S>(f0, r0, 0);
     for (int kt = 0; kt < nk; kt += ST) {
-      k_iter<S, true>(acc, f0, f1, kt, nk, P, r0, r1);
-      k_iter<S, true>(acc, f0, f1, kt + 1, nk, P, r1, r2);
-      k_iter<S, true>(acc, f0, f1, kt + 2, nk, P, r2, r3);
-      k_iter<S, true>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt, nk, P, r0, r1);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 1, nk, P, r1, r2);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 2, nk, P, r2, r3);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 3, nk, P, r3, r0);
     }
     KOS_WAITCNT(0, 0);
     lds_barrier();
     return;
   }
-  stage_load<S>(r0, P, 0);
-  if (1 < nk) stage_load<S>(r1, P, 1 * S::BK);
-  if (2 < nk) stage_load<S>(r2, P, 2 * S::BK);
-  if (3 < nk) stage_load<S>(r3, P, 3 * S::BK);
+  stage_load<S, DUAL, COH_A>(r0, P, 0);
+  if (1 < nk) stage_load<S, DUAL, COH_A>(r1, P, 1 * S::BK);
+  if (2 < nk) stage_load<S, DUAL, COH_A>(r2, P, 2 * S::BK);
+  if (3 < nk) stage_load<S, DUAL, COH_A>(r3, P, 3 * S::BK);
   // stage 0 landed; up to three later stages may still fly
   if (nk >= 4) {
     KOS_WAITCNT(3 * S::LOADS, 0);
@@ -325,10 +353,10 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   Frags<S> f0, f1;
   frag_load<S>(f0, r0, 0);
   for (int kt = 0; kt < nk; kt += ST) {
-    k_iter<S, false>(acc, f0, f1, kt, nk, P, r0, r1);
-    if (kt + 1 < nk) k_iter<S, false>(acc, f0, f1, kt + 1, nk, P, r1, r2);
-    if (kt + 2 < nk) k_iter<S, false>(acc, f0, f1, kt + 2, nk, P, r2, r3);
-    if (kt + 3 < nk) k_iter<S, false>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+    k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt, nk, P, r0, r1);
+    if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 1, nk, P, r1, r2);
+    if (kt + 2 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 2, nk, P, r2, r3);
+    if (kt + 3 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 3, nk, P, r3, r0);
   }
   KOS_WAITCNT(0, 0);
   lds_barrier();
