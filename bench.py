@@ -110,21 +110,82 @@ def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0):
     return [("ag_gemm", op_ag), ("gemm_rs", op_rs), ("moe_dispatch", op_dispatch), ("moe_combine", op_combine)]
 
 
-def time_ops(torch, ops, reps, ws):
-    """Runs `reps` steps; returns (per-op mean ms from events, wall ms/step)."""
+def source_digest() -> str:
+    """Digest of the kernel sources: ties a stored counter reading to the
+    kernels it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "gemm_collective_persistent_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(op: str, workload: str):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
+    None when there is none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"{op}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#")):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    """Three plain device copies of 1 GiB: the reference that scales the HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) read under rocprofv3."""
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes": 1 << 30, "copies": 3}
+
+
+class CacheFlush:
+    """Writes a buffer twice the size of the 256 MB Infinity Cache, so that the
+    next op reads its inputs from HBM rather than from a cache."""
+
+    def __init__(self, torch, enabled=True):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if enabled else None
+
+    def __call__(self):
+        if self.buf is not None:
+            self.buf.fill_(1)
+
+
+def time_ops(torch, ops, reps, ws, flush):
+    """Runs `reps` steps, each op preceded by a cache flush outside its timed
+    interval; returns (per-op mean ms from events on the launch stream, wall
+    ms/step including the flushes)."""
     n = len(ops)
-    ev = [_events(torch, n + 1) for _ in range(reps)]
+    ev = [_events(torch, 2 * n) for _ in range(reps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(reps):
-        ev[r][0].record()
         for i, (_, fn) in enumerate(ops):
+            flush()
+            ev[r][2 * i].record()
             fn()
-            ev[r][i + 1].record()
+            ev[r][2 * i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / reps
     ws.status()
-    per = [sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps for i in range(n)]
+    per = [sum(ev[r][2 * i].elapsed_time(ev[r][2 * i + 1]) for r in range(reps)) / reps for i in range(n)]
     return per, wall
 
 
@@ -185,6 +246,9 @@ def main():
     ap.add_argument("--moe", choices=["dsv3", "qwen3"], default="dsv3")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between ops")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run three plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share only (emulated peers); --gpus {args.gpus} is not supported: "
@@ -205,7 +269,8 @@ def main():
             fn()
     torch.cuda.synchronize()
     ws.status()
-    per, wall = time_ops(torch, ops, args.steps, ws)
+    flush = CacheFlush(torch, not args.no_flush)
+    per, wall = time_ops(torch, ops, args.steps, ws, flush)
     ms_step = sum(per)
     names = [n for n, _ in ops]
     rows = int(inp["moe"]["goff"][-1].item())
@@ -224,11 +289,15 @@ def main():
     moe_tok_s = moe_shape.tokens / (t_moe * 1e-3)
     dom = max(range(len(per)), key=lambda i: per[i] if fl[names[i]] > 0 else -1)
     ach = fl[names[dom]] / (per[dom] * 1e-3) / 1e12
+    traffic = measured_traffic(names[dom], moe_shape.name if names[dom].startswith("moe") else "")
     roofline = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
     extra = {"per_op": per_op, "moe_tokens_per_s": round(moe_tok_s, 1), "moe_grouped_rows": rows,
-             "wall_ms_per_step": round(wall, 3)}
+             "wall_ms_per_step": round(wall, 3), "caches_flushed": not args.no_flush,
+             "source_digest": source_digest()}
+    if args.copy_calibration:
+        extra["copy_calibration"] = copy_calibration(torch)
     if not args.no_baselines:
         base = {}
         reps = max(3, args.steps // 4)
@@ -236,7 +305,7 @@ def main():
             ops_b = make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew)
             for _, fn in ops_b:
                 fn()
-            pb, _ = time_ops(torch, ops_b, reps, ws)
+            pb, _ = time_ops(torch, ops_b, reps, ws, flush)
             base[label] = {n: round(t, 4) for n, t in zip(names, pb)}
         fixed = {n: min(base[k][n] for k in base if k.startswith("fixed")) for n in names}
         extra["baselines_ms"] = base
@@ -252,7 +321,7 @@ def main():
             o = kos.opts(mode=2, grid=grid)
             fn = lambda: kos.ag_gemm(a_all, [None], ag["w"], a_all, cfull, 0, ws, o)  # noqa: E731
             fn()
-            t, _ = time_ops(torch, [("gemm", fn)], reps, ws)
+            t, _ = time_ops(torch, [("gemm", fn)], reps, ws, flush)
             res[grid] = t[0]
         extra["gemm_224_vs_256_cu_throughput"] = round(res[256] / res[224], 3)
         extra["gemm_256cu_ms"] = round(res[256], 4)

@@ -113,10 +113,10 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       const int64_t col0 = (int64_t)nt * BN;
       if (p.c_f32) {
         float* C = reinterpret_cast<float*>(p.c) + row0 * N + col0;
-        tile_foreach<S>(acc, [&](int r, int c, float v) { C[r * N + c] = v; });
+        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<f32x4*>(&C[r * N + c]) = v; });
       } else {
         uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + row0 * N + col0;
-        tile_foreach<S>(acc, [&](int r, int c, float v) { C[r * N + c] = f32_to_bf16_bits(v); });
+        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<u32x2*>(&C[r * N + c]) = pack4_bf16(v); });
       }
     }
   }
@@ -188,7 +188,10 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
   kos_opts o;
-  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+  // Movers over device memory: half the grid saturates HBM copy bandwidth
+  // and the other half builds the local shard meanwhile; over PCIe a few
+  // workgroups saturate the link.
+  if ((st = resolve_opts(opts, dev, CrewDefaults{kCrewHalfGrid, 8, 16, 8}, &o)) != KOS_OK) return st;
 
   int bm = 64, bn = 64;
   pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);

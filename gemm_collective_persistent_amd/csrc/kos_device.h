@@ -32,6 +32,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // atomics and fences (agent scope = the whole GPU)
@@ -138,33 +139,44 @@ __device__ inline bool wg_observe(const uint32_t* counter, uint32_t target, WsHe
   return s->ok != 0;
 }
 
-// Device-scope (sc1) stores and loads for the coherent exchange.
-__device__ __forceinline__ void st_dev_b16(uint16_t* p, uint16_t v) {
-  asm volatile("global_store_short %0, %1, off sc1" : : "v"(p), "v"((uint32_t)v) : "memory");
-}
+// Device-scope (sc1) stores and loads for the coherent exchange.  All are
+// compiler-visible (atomics or buffer builtins), so the compiler accounts
+// for their waits and for the register hazards of wide stores.
 __device__ __forceinline__ void st_dev_b32(void* p, uint32_t v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev_b128(void* p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+__device__ __forceinline__ void st_dev_b64(void* p, u32x2 v) {   // p 8-byte aligned
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
-// Issues a device-scope 16-byte load; the value is valid only after
-// wait_dev_loads() names it.
-__device__ __forceinline__ u32x4 ld_dev_b128_issue(const void* p) {
-  u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
+
+// A pointer that is the same in every lane of the wave, moved to scalar
+// registers (the caller guarantees the uniformity).
+template <class T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void wait_dev_loads(u32x4& a) { asm volatile("s_waitcnt vmcnt(0)" : "+v"(a)); }
-__device__ __forceinline__ void wait_dev_loads(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-__device__ __forceinline__ void wait_dev_loads(u32x4 (&v)[16]) {
-  asm volatile("s_waitcnt vmcnt(0)"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
-                 "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
-                 "+v"(v[15]));
-}
+
+constexpr int kCpolSc1 = 16;                 // cache-policy operand: sc1 (device scope)
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor word 3 (32-bit data format)
+
+// 16-byte device-scope accesses at byte offsets (below 2 GiB) from a
+// wave-uniform base, through a raw buffer descriptor.
+struct DevBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit DevBuf(const void* base)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform(base)), (short)0, 0x7fffffff,
+                                            kRawBufferWord3)) {}
+  __device__ __forceinline__ void st128(uint32_t off, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
+  }
+  __device__ __forceinline__ u32x4 ld128(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+  }
+};
 
 // Non-blocking readiness test by thread 0, broadcast (no fence: callers that
 // act on `true` must still call wg_wait or fence_acquire before reading).
@@ -208,24 +220,25 @@ __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_count
 // movers: coalesced 128-bit copies
 // ---------------------------------------------------------------------------
 
-// Copies `bytes` (a multiple of 16) from src to dst with the whole
-// workgroup, stores device-coherent (see wg_publish); consecutive threads
-// touch consecutive 16-byte chunks and each thread keeps 8 loads in flight.
+// Copies `bytes` (a multiple of 16, below 2 GiB) from src to dst with the
+// whole workgroup, stores device-coherent (see wg_publish); consecutive
+// threads touch consecutive 16-byte chunks and each thread keeps 8 loads in
+// flight.  dst and src are the same in every thread.
 __device__ inline void wg_copy_dev(void* __restrict__ dst, const void* __restrict__ src, size_t bytes) {
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
-  const size_t n = bytes >> 4;
-  const size_t nt = blockDim.x;
-  size_t i = threadIdx.x;
+  const DevBuf d(dst);
+  const uint32_t n = (uint32_t)(bytes >> 4);
+  const uint32_t nt = blockDim.x;
+  uint32_t i = threadIdx.x;
   constexpr int U = 8;
   for (; i + (U - 1) * nt < n; i += U * nt) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + u * nt]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) st_dev_b128(&d[i + u * nt], v[u]);
+    for (int u = 0; u < U; ++u) d.st128((i + u * nt) * 16u, v[u]);
   }
-  for (; i < n; i += nt) st_dev_b128(&d[i], __builtin_nontemporal_load(&s[i]));
+  for (; i < n; i += nt) d.st128(i * 16u, __builtin_nontemporal_load(&s[i]));
 }
 
 // Copies `bytes` (a multiple of 16) from src to dst with the whole
@@ -255,6 +268,13 @@ __device__ inline void wg_copy(void* __restrict__ dst, const void* __restrict__ 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   __bf16 b = static_cast<__bf16>(f);   // round to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(uint16_t, b);
+}
+// Four floats to four packed bf16 (round to nearest even), lowest first.
+__device__ __forceinline__ u32x2 pack4_bf16(f32x4 v) {
+  u32x2 r;
+  r.x = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+  r.y = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+  return r;
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);

@@ -50,14 +50,16 @@ struct RsParams {
 // Rows of one reduce entry: a slab of kSlabRows rows of one output tile.
 constexpr int kSlabRows = 32;
 
-// y[slab rows, tile cols] = sum over ranks, ascending, in fp32; two float4
-// per thread per pass so that 2 x world loads are in flight.
+// y[slab rows, tile cols] = sum over ranks, ascending, in fp32.  Each pass
+// issues every load first (U float4 per source per thread, up to 8 x U in
+// flight), then adds and stores.
 template <int BN>
 __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int col_tile) {
   const int64_t N = p.n;
   const int64_t c0 = (int64_t)col_tile * BN;
   constexpr int V = BN / 4;                              // float4 per row
   constexpr int E = kSlabRows * V;                       // float4 per slab
+  constexpr int U = 4;
   const float* src[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
@@ -65,38 +67,40 @@ __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int 
                           : (q == p.rank ? p.partial + ((int64_t)p.rank * p.mc + r0) * N + c0
                                          : p.peers[q] + r0 * N + c0);
   float* dst = p.y + r0 * N + c0;
-  for (int e = threadIdx.x; e < E; e += 2 * blockDim.x) {
-    const int e2 = e + blockDim.x;
-    const int64_t o1 = (int64_t)(e / V) * N + (e % V) * 4;
-    const int64_t o2 = (int64_t)(e2 / V) * N + (e2 % V) * 4;
-    const bool two = e2 < E;
-    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 x1[8], x2[8];
+  const DevBuf own(src[p.rank]);
+  for (int e0 = threadIdx.x; e0 < E; e0 += U * blockDim.x) {
+    int64_t off[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * (int)blockDim.x;
+      ok[u] = e < E;
+      off[u] = (int64_t)(e / V) * N + (e % V) * 4;
+    }
+    f32x4 x[8][U];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q >= p.world) break;
-      if (q == p.rank) {   // written by builders of this launch: device-coherent loads
-        const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src[q] + o1);
-        const uint32_t* s2 = reinterpret_cast<const uint32_t*>(src[q] + o2);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          x1[q][c] = __builtin_bit_cast(float, __hip_atomic_load(s1 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          if (two)
-            x2[q][c] = __builtin_bit_cast(float, __hip_atomic_load(s2 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-      } else {
-        x1[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + o1));
-        if (two) x2[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + o2));
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        if (q == p.rank)   // written by builders of this launch: device-coherent loads
+          x[q][u] = __builtin_bit_cast(f32x4, own.ld128((uint32_t)off[u] * 4u));
+        else
+          x[q][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + off[u]));
       }
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (q >= p.world) break;
-      a1 += x1[q];
-      if (two) a2 += x2[q];
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q >= p.world) break;
+        a += x[q][u];
+      }
+      *reinterpret_cast<f32x4*>(dst + off[u]) = a;
     }
-    *reinterpret_cast<f32x4*>(dst + o1) = a1;
-    if (two) *reinterpret_cast<f32x4*>(dst + o2) = a2;
   }
 }
 
@@ -134,10 +138,13 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
       tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k);
       float* P = p.partial + row0 * N + (int64_t)col * BN;
       if (chunk == p.rank) {   // read by this launch's reducers: device-coherent stores
-        tile_foreach<S>(acc, [&](int r, int c, float v) { st_dev_b32(&P[r * N + c], __builtin_bit_cast(uint32_t, v)); });
+        const DevBuf pb(P);
+        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) {
+          pb.st128((uint32_t)(r * N + c) * 4u, __builtin_bit_cast(u32x4, v));
+        });
         wg_publish(&p.ready[band * p.tiles_n + col], 1u);
       } else {
-        tile_foreach<S>(acc, [&](int r, int c, float v) { P[r * N + c] = v; });
+        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<f32x4*>(&P[r * N + c]) = v; });
       }
     }
     if (!p.builders_switch || !p.do_reduce) {
@@ -200,7 +207,9 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
   kos_opts o;
-  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+  // FUSED: nobody waits idle for the first band; builders switch to reducing
+  // when the tiles run out.  FIXED: a reserved reduction crew.
+  if ((st = resolve_opts(opts, dev, CrewDefaults{0, 0, 16, 8}, &o)) != KOS_OK) return st;
 
   const int64_t mc = m / world;
   int bm = 64, bn = 64;
@@ -245,9 +254,10 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
     rd.wait_flags = 0;
     return launch_rs_tile(bm, bn, rd, grid, s);
   }
-  // The crew that starts reducing (FUSED) or only reduces (FIXED).
-  if (o.n_movers < 1 || o.n_movers >= grid)
-    return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, grid);
+  // The crew that starts reducing (FUSED, may be empty) or only reduces (FIXED).
+  const int min_crew = o.mode == KOS_MODE_FUSED ? 0 : 1;
+  if (o.n_movers < min_crew || o.n_movers >= grid)
+    return fail(KOS_ERR_ARG, "n_movers %d must be in [%d, grid %d)", o.n_movers, min_crew, grid);
   p.n_reducers = o.n_movers;
   p.builders_switch = o.mode == KOS_MODE_FUSED;
   p.do_build = 1;

@@ -23,9 +23,18 @@ kos_status current_device(DeviceInfo* out);
 // Validates a workspace pointer/size.
 kos_status check_workspace(const void* ws, size_t ws_bytes);
 
+// Initial crew (workgroups that start in the communication role) of one op,
+// per mode and peer link.  A property of the op and the link, set once and
+// never per shape or call: there is no tuned split.
+constexpr int kCrewHalfGrid = -2;   // a CrewDefaults value: half of the launch grid
+struct CrewDefaults {
+  int fused_hbm, fused_host;   // FUSED: the crew that starts communicating, then switches
+  int fixed_hbm, fixed_host;   // FIXED: the crew that only communicates
+};
+
 // Fills `o` from `in` (NULL -> defaults), resolving the default crew size
-// for the peer link and the grid.  Validates enums and ranges.
-kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, kos_opts* o);
+// for the op, mode and peer link, and the grid.  Validates enums and ranges.
+kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, const CrewDefaults& crew, kos_opts* o);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -12,14 +12,6 @@ namespace kos {
 namespace {
 thread_local char g_msg[512] = "";
 
-// Initial crew (workgroups that start as movers / reducers / pushers) per
-// peer link.  A property of the link, set once, never per shape or call:
-// the pages insist on no tuned split.  Values from the copy-bandwidth
-// saturation sweep on MI355X (HBM peers: device memory copy; mapped host
-// memory: PCIe reads).
-constexpr int kCrewHbm = 16;
-constexpr int kCrewHost = 8;
-
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
 }  // namespace
@@ -59,7 +51,7 @@ kos_status check_workspace(const void* ws, size_t ws_bytes) {
   return KOS_OK;
 }
 
-kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, kos_opts* o) {
+kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, const CrewDefaults& crew, kos_opts* o) {
   kos_opts_default(o);
   if (in) *o = *in;
   if (o->mode < KOS_MODE_FUSED || o->mode > KOS_MODE_UNFUSED) return fail(KOS_ERR_ARG, "bad mode %d", o->mode);
@@ -69,7 +61,13 @@ kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, kos_opts* o) 
   if (o->grid == 0) o->grid = dev.cus;
   if (o->grid < 2 || o->grid > dev.cus)
     return fail(KOS_ERR_ARG, "grid %d outside [2, %d] (all workgroups must be co-resident)", o->grid, dev.cus);
-  if (o->n_movers < 0) o->n_movers = o->peer_link ? kCrewHost : kCrewHbm;
+  if (o->n_movers < 0) {
+    const bool host = o->peer_link == 1;
+    int c = o->mode == KOS_MODE_FIXED ? (host ? crew.fixed_host : crew.fixed_hbm)
+                                      : (host ? crew.fused_host : crew.fused_hbm);
+    if (c == kCrewHalfGrid) c = o->grid / 2;
+    o->n_movers = c < o->grid ? c : o->grid - 1;   // a default never takes the whole grid
+  }
   if (o->spin_limit == 0) o->spin_limit = kDefaultSpinLimit;
   return KOS_OK;
 }

@@ -28,27 +28,23 @@ __device__ __forceinline__ void wave_copy_row(void* __restrict__ dst, const void
 }
 
 // Same, reading the source with device-scope loads (rows written by other
-// workgroups of the same launch).
-__device__ __forceinline__ void wave_copy_row_dev_src(void* __restrict__ dst, const void* __restrict__ src, int bytes) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+// workgroups of the same launch): src_off is the row's byte offset in `src`
+// (wave-uniform; offsets below 2 GiB).
+__device__ __forceinline__ void wave_copy_row_dev_src(void* __restrict__ dst, const DevBuf& src, uint32_t src_off,
+                                                      int bytes) {
   u32x4* d = reinterpret_cast<u32x4*>(dst);
   const int lane = threadIdx.x & 63;
   const int n = bytes >> 4;
   int i = lane;
   for (; i + 3 * 64 < n; i += 4 * 64) {
-    u32x4 v0 = ld_dev_b128_issue(&s[i]), v1 = ld_dev_b128_issue(&s[i + 64]);
-    u32x4 v2 = ld_dev_b128_issue(&s[i + 128]), v3 = ld_dev_b128_issue(&s[i + 192]);
-    wait_dev_loads(v0, v1, v2, v3);
+    const u32x4 v0 = src.ld128(src_off + i * 16u), v1 = src.ld128(src_off + (i + 64) * 16u);
+    const u32x4 v2 = src.ld128(src_off + (i + 128) * 16u), v3 = src.ld128(src_off + (i + 192) * 16u);
     d[i] = v0;
     d[i + 64] = v1;
     d[i + 128] = v2;
     d[i + 192] = v3;
   }
-  for (; i < n; i += 64) {
-    u32x4 v = ld_dev_b128_issue(&s[i]);
-    wait_dev_loads(v);
-    d[i] = v;
-  }
+  for (; i < n; i += 64) d[i] = src.ld128(src_off + i * 16u);
 }
 
 }  // namespace kos

@@ -149,54 +149,62 @@ __device__ __forceinline__ void decode_tile(const CombineParams& p, int U, int j
   nt = jj2 % p.D;
 }
 
-template <class S>
+template <class S, int RING>
 __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   constexpr int HN = S::BN / 2;    // h columns per tile
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
          S::BN / 4};
-  tile_mainloop<S, true>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  tile_mainloop<S, true, false, RING>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
+  const WaveCtx w = wave_ctx();
+  const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   uint16_t* hb = p.h + (int64_t)x.row0 * F + (int64_t)nt * HN;
+  // gate column block j pairs with up column block j + TN/2 (same h columns);
+  // accumulator layout as in tile_foreach4
 #pragma unroll
-  for (int i = 0; i < S::TM; ++i)
+  for (int i = 0; i < S::TM; ++i) {
+    const int row = wm * S::WM + i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < S::TN / 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * S::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * (S::BN / 4) + j * 32 + (lane & 31);
-        if (row < x.m_valid) {   // read by this launch's down tiles: device-coherent stores
-          const float g = acc[i][j][r], u = acc[i][j + S::TN / 2][r];
-          const float hv = g / (1.0f + expf(-g)) * u;
-          st_dev_b16(&hb[(int64_t)row * F + col], f32_to_bf16_bits(hv));
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * (S::BN / 4) + j * 32 + g * 8 + (lane >> 5) * 4;
+        f32x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gv = acc[i][j][4 * g + e], uv = acc[i][j + S::TN / 2][4 * g + e];
+          hv[e] = gv / (1.0f + expf(-gv)) * uv;
         }
+        // read by this launch's down tiles: device-coherent stores
+        if (row < x.m_valid) st_dev_b64(&hb[(int64_t)row * F + col], pack4_bf16(hv));
       }
+  }
 }
 
 // COH: h was written by this launch's gate/up tiles (read device-coherent).
-template <class S, bool COH>
+template <class S, bool COH, int RING>
 __device__ __forceinline__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
-  tile_mainloop<S, false, COH>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
+  tile_mainloop<S, false, COH, RING>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
   uint16_t* yb = p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN;
   const int mv = x.m_valid;
-  tile_foreach<S>(acc, [&](int r, int c, float v) {   // read by pushes and folds: device-coherent
-    if (r < mv) st_dev_b16(&yb[(int64_t)r * H + c], f32_to_bf16_bits(v));
+  tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) {   // read by pushes and folds: device-coherent
+    if (r < mv) st_dev_b64(&yb[(int64_t)r * H + c], pack4_bf16(v));
   });
 }
 
 __device__ __forceinline__ void push_unit(const CombineParams& p, const Unit& x) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   (void)lane;
+  const DevBuf yb(p.yg);
   for (int r = wave; r < x.m_valid; r += nw) {
     const int64_t grow = (int64_t)x.row0 + r;
     const int src = p.row_src[grow * 2];
     if (src == p.rank) continue;
     const int64_t i = p.row_src[grow * 2 + 1];
-    wave_copy_row_dev_src(p.out_return[src] + i * p.H, p.yg + grow * p.H, p.H * 2);
+    wave_copy_row_dev_src(p.out_return[src] + i * p.H, yb, (uint32_t)(grow * p.H * 2), p.H * 2);
   }
 }
 
@@ -241,8 +249,12 @@ __device__ __forceinline__ bool fold_block(const CombineParams& p, const Combine
   if (!s->ok) return false;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int E_loc = p.E_loc;
+  const DevBuf yb(p.yg);
   for (int t = t0 + wave; t < t1; t += nw) {
-    const uint16_t* src[kMoeMaxTopk];
+    // result j: local (row of yg, written by this launch: device-coherent
+    // loads at byte offset loc[j]) or returned by a peer (plain loads)
+    const u32x4* src[kMoeMaxTopk];
+    uint32_t loc[kMoeMaxTopk];
     float w[kMoeMaxTopk];
 #pragma unroll
     for (int j = 0; j < kMoeMaxTopk; ++j) {
@@ -253,18 +265,19 @@ __device__ __forceinline__ bool fold_block(const CombineParams& p, const Combine
       w[j] = p.topk_w[(int64_t)t * p.k + j];
       if (d == p.rank) {
         const int el = e - p.rank * E_loc;
-        src[j] = p.yg + ((int64_t)M.go[el] + M.before[el] + (pos - M.off[e])) * p.H;
+        src[j] = nullptr;
+        loc[j] = (uint32_t)(((int64_t)M.go[el] + M.before[el] + (pos - M.off[e])) * p.H * 2);
       } else {
-        src[j] = p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H;
+        src[j] = reinterpret_cast<const u32x4*>(p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H);
+        loc[j] = 0;
       }
     }
     for (int c = lane; c < p.H / 8; c += 64) {
       float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       u32x4 vj[kMoeMaxTopk];
 #pragma unroll
-      for (int j = 0; j < kMoeMaxTopk; ++j)   // local rows come from this launch: device-coherent
-        if (j < p.k) vj[j] = ld_dev_b128_issue(reinterpret_cast<const u32x4*>(src[j]) + c);
-      wait_dev_loads(vj);
+      for (int j = 0; j < kMoeMaxTopk; ++j)
+        if (j < p.k) vj[j] = src[j] ? __builtin_nontemporal_load(src[j] + c) : yb.ld128(loc[j] + c * 16u);
 #pragma unroll
       for (int j = 0; j < kMoeMaxTopk; ++j) {
         if (j >= p.k) break;
@@ -287,10 +300,14 @@ __device__ __forceinline__ bool fold_block(const CombineParams& p, const Combine
   return true;
 }
 
-// COH: one launch produces and consumes h and Y (fused and fixed-crew modes).
-template <class S, bool COH>
+// S: the unit's tile (BM rows of one expert).  ST: a tile of the same width
+// and fewer rows for an expert's last unit when its rows fit (less work
+// spent on rows past the end).  COH: one launch produces and consumes h and
+// Y (fused and fixed-crew modes).
+template <class S, class ST, bool COH>
 __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams args) {
   constexpr int BM = S::BM;
+  static_assert(ST::BN == S::BN && ST::BM < S::BM && ST::NT == S::NT, "tail tile: same width, fewer rows");
   __shared__ CombineMeta M;
   __shared__ WgSlots slots;
   // The parameter block lives in LDS: the role code reads the fields it needs
@@ -311,6 +328,8 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   // ---- builder role (two-way: push any ready result between tiles) -------
   if (!crew && (p.do_gu || p.do_dn)) {
     f32x16 acc[S::TM][S::TN];
+    f32x16 acc_t[ST::TM][ST::TN];
+    constexpr int RB = S::STAGE_BYTES;
     const int n_entries = (p.do_gu && p.do_dn) ? U * (p.G + p.D) : (p.do_gu ? U * p.G : U * p.D);
     for (;;) {
       if (p.two_way && p.do_push) {
@@ -337,15 +356,18 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
       int u, nt;
       decode_tile(p, U, (int)j, down, u, nt);
       const Unit x = unit_of<BM>(M, p.E_loc, u);
+      const bool tail = x.m_valid <= ST::BM;
       if (!down) {
-        gate_up_tile<S>(p, x, nt, acc);
+        if (tail) gate_up_tile<ST, RB>(p, x, nt, acc_t);
+        else gate_up_tile<S, RB>(p, x, nt, acc);
         wg_publish(&gu_done[u], 1u);
       } else {
         if (p.wait_flags && p.do_gu && !wg_observe(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
           failed = true;
           break;
         }
-        down_tile<S, COH>(p, x, nt, acc);
+        if (tail) down_tile<ST, COH, RB>(p, x, nt, acc_t);
+        else down_tile<S, COH, RB>(p, x, nt, acc);
         wg_publish(&dn_done[u], 1u);
       }
     }
@@ -379,7 +401,9 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
 
 // Big tile when the widths allow it (hidden % 256, ffn % 128), else 128 x 128.
 using CombineTileBig = TileShape<256, 256>;
+using CombineTailBig = TileShape<128, 256>;
 using CombineTileSmall = TileShape<128, 128>;
+using CombineTailSmall = TileShape<64, 128>;
 
 }  // namespace kos
 
@@ -416,12 +440,15 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
       !aligned16(y_grouped) || !aligned16(y))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
+  // the grouped results are read back through 32-bit byte offsets
+  if (grouped_cap * s->hidden * 2 >= (int64_t(1) << 31))
+    return fail(KOS_ERR_SHAPE, "grouped_cap x hidden x 2 bytes must stay below 2 GiB");
   kos_status st = check_workspace(ws, ws_bytes);
   if (st != KOS_OK) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
   kos_opts o;
-  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+  if ((st = resolve_opts(opts, dev, CrewDefaults{16, 8, 16, 8}, &o)) != KOS_OK) return st;
 
   CombineParams p{};
   p.world = R;
@@ -465,16 +492,16 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   auto launch = [&](const CombineParams& q, const char* what) {
     const bool coh = q.wait_flags != 0;
     if (big && coh)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, true>), dim3(o.grid), dim3(CombineTileBig::NT), 0, strm,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, true>), dim3(o.grid), dim3(CombineTileBig::NT), 0, strm,
                          q);
     else if (big)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, false>), dim3(o.grid), dim3(CombineTileBig::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, false>), dim3(o.grid), dim3(CombineTileBig::NT), 0,
                          strm, q);
     else if (coh)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, true>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, true>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
                          strm, q);
     else
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, false>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, false>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
                          strm, q);
     return launch_status(what);
   };

@@ -388,7 +388,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
   kos_opts o;
-  if ((st = resolve_opts(opts, dev, &o)) != KOS_OK) return st;
+  if ((st = resolve_opts(opts, dev, CrewDefaults{16, 8, 16, 8}, &o)) != KOS_OK) return st;
   if (o.mode == KOS_MODE_FIXED) return fail(KOS_ERR_UNSUPPORTED, "dispatch has no compute role to split from");
 
   DispatchParams p{};

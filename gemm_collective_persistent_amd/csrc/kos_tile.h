@@ -103,6 +103,22 @@ __device__ __forceinline__ int b_chunk(int p, int k) {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// This thread's lane and its wave's index, computed afresh where a tile
+// starts or ends.  The empty asm makes them opaque to the optimizer, so the
+// addresses derived from them are computed per tile rather than hoisted to
+// the start of the persistent kernel and kept live (register pressure)
+// through every role.
+struct WaveCtx {
+  int lane;   // 0..63
+  int wave;   // 0..3, uniform (scalar register)
+};
+__device__ __forceinline__ WaveCtx wave_ctx() {
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  int wave = wave_id();
+  asm volatile("" : "+v"(lane), "+s"(wave));
+  return {lane, wave};
+}
+
 // Per-lane source offsets of this wave's direct loads, fixed for a tile:
 // every stage reads base + k0 (A) or base + k0*ld (B) plus these.
 template <class S, bool DUAL, bool COH_A = false>
@@ -113,14 +129,17 @@ struct LoadPlan {
   uint32_t b_off[DUAL ? 1 : S::B_LOADS];       // bytes from b_base (plain B)
   const char* b_ptr[DUAL ? S::B_LOADS : 1];    // per-lane pointers (dual B)
   int64_t b_stride;                            // bytes per k row of B
+  int a_lds, b_lds;                            // this wave's bytes into a stage (uniform)
 };
 
 // A rows are clamped to m_valid-1: rows past the valid ones only feed
 // accumulator rows that are never stored.
 template <class S, bool DUAL, bool COH_A>
 __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const uint16_t* __restrict__ A, int64_t lda,
-                                           int m_valid, const BSrc& b) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+                                           int m_valid, const BSrc& b, const WaveCtx& w) {
+  const int lane = w.lane, wave = w.wave;
+  P.a_lds = wave * S::A_LOADS * 1024;
+  P.b_lds = S::A_BYTES + wave * S::B_LOADS * 1024;
   P.a_base = reinterpret_cast<const char*>(A);
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
@@ -152,25 +171,22 @@ constexpr int kCpolDevice = 16;
 
 template <class S, bool DUAL, bool COH_A>
 __device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A>& P, int k0) {
-  const int wave = wave_id();
   const char* a = P.a_base + (int64_t)k0 * 2;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
-    __builtin_amdgcn_global_load_lds(a + P.a_off[i], (lds_void*)(lds_stage + (wave * S::A_LOADS + i) * 1024), 16,
-                                     0, COH_A ? kCpolDevice : 0);
-  char* bst = lds_stage + S::A_BYTES;
+    __builtin_amdgcn_global_load_lds(a + P.a_off[i], (lds_void*)(lds_stage + P.a_lds + i * 1024), 16, 0,
+                                     COH_A ? kCpolDevice : 0);
+  char* bst = lds_stage + P.b_lds;
   const int64_t kb = (int64_t)k0 * P.b_stride;
   if constexpr (!DUAL) {
     const char* bb = P.b_base + kb;
 #pragma unroll
     for (int i = 0; i < S::B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(bb + P.b_off[i], (lds_void*)(bst + (wave * S::B_LOADS + i) * 1024), 16, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds(bb + P.b_off[i], (lds_void*)(bst + i * 1024), 16, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < S::B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(P.b_ptr[i] + kb, (lds_void*)(bst + (wave * S::B_LOADS + i) * 1024), 16, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds(P.b_ptr[i] + kb, (lds_void*)(bst + i * 1024), 16, 0, 0);
   }
 }
 
@@ -183,8 +199,8 @@ struct Frags {
 
 // LDS -> registers for k16 step s (0 or 1) of a stage.
 template <class S>
-__device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, int s) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, int s, const WaveCtx& w) {
+  const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const char* ast = lds_stage;
   const char* bst = lds_stage + S::A_BYTES;
@@ -218,7 +234,10 @@ __device__ __forceinline__ void frag_mfma(f32x16 (&acc)[S::TM][S::TN], const Fra
   for (int i = 0; i < S::TM; ++i)
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      // B fragment as the first operand: the product comes out transposed, so
+      // each lane holds four consecutive output columns of one row (vector
+      // stores in the epilogue)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // s_waitcnt immediate: vmcnt <= v, lgkmcnt <= l (expcnt untouched).
@@ -243,9 +262,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // The LDS ring: one __shared__ array per stage, so the compiler can tell a
 // stage being read from the stages being filled and does not wait for them.
-template <class S, int I>
+// Keyed by the stage size: tile shapes of one kernel share a ring sized for
+// the largest.
+template <int STAGE_BYTES, int I>
 __device__ __forceinline__ char* ring() {
-  __shared__ __attribute__((aligned(1024))) char buf[S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char buf[STAGE_BYTES];
   return buf;
 }
 
@@ -270,11 +291,11 @@ __device__ __forceinline__ void sched_interleave() {
 // flight stay uniform and the loop body has no branches.
 template <class S, bool DUAL, bool COH_A, bool steady>
 __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0, Frags<S>& f1, int kt, int nk,
-                                       const LoadPlan<S, DUAL, COH_A>& P, char* cur, char* nxt) {
+                                       const LoadPlan<S, DUAL, COH_A>& P, char* cur, char* nxt, const WaveCtx& w) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
   constexpr int NM = S::TM * S::TN, ND = S::TM + 2 * S::TN;
-  frag_load<S>(f1, cur, 1);
+  frag_load<S>(f1, cur, 1, w);
   frag_mfma<S>(acc, f0);
   if (steady) sched_interleave<NM, ND, 0>();
   // stage kt+1 must have landed (all waves) and stage kt must be read by all
@@ -287,20 +308,21 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
   lds_barrier();
   if (steady) {
     stage_load<S, DUAL, COH_A>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
-    frag_load<S>(f0, nxt, 0);
+    frag_load<S>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
     sched_interleave<NM, ND, S::LOADS>();
   } else {
     if (kt + ST < nk) stage_load<S, DUAL, COH_A>(cur, P, (kt + ST) * S::BK);
-    if (kt + 1 < nk) frag_load<S>(f0, nxt, 0);
+    if (kt + 1 < nk) frag_load<S>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
   }
 #endif
 }
 
 // Full K loop: acc = A[0:m_valid rows] . B over k in [0, K) (K a multiple of
-// 32).  Begins and ends with the LDS ring free.
-template <class S, bool DUAL = false, bool COH_A = false>
+// 32).  Begins and ends with the LDS ring free.  RING: stage size of the
+// ring (at least the tile's; a kernel with two tile shapes passes the larger).
+template <class S, bool DUAL = false, bool COH_A = false, int RING = S::STAGE_BYTES>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const uint16_t* __restrict__ A,
                                               int64_t lda, int m_valid, const BSrc& b, int K) {
   constexpr int ST = S::STAGES;
@@ -312,12 +334,14 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / S::BK;
+  const WaveCtx w = wave_ctx();
   LoadPlan<S, DUAL, COH_A> P;
-  plan_loads<S, DUAL, COH_A>(P, A, lda, m_valid, b);
-  char* r0 = ring<S, 0>();
-  char* r1 = ring<S, 1>();
-  char* r2 = ring<S, 2>();
-  char* r3 = ring<S, 3>();
+  plan_loads<S, DUAL, COH_A>(P, A, lda, m_valid, b, w);
+  static_assert(S::STAGE_BYTES <= RING, "tile stage larger than the ring");
+  char* r0 = ring<RING, 0>();
+  char* r1 = ring<RING, 1>();
+  char* r2 = ring<RING, 2>();
+  char* r3 = ring<RING, 3>();
   KOS_WAITCNT(0, 0);
   lds_barrier();   // the ring is free (previous user done)
   if (nk >= ST && nk % ST == 0) {
@@ -328,12 +352,12 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
     KOS_WAITCNT(3 * S::LOADS, 0);
     lds_barrier();
     Frags<S> f0, f1;
-    frag_load<S>(f0, r0, 0);
+    frag_load<S>(f0, r0, 0, w);
     for (int kt = 0; kt < nk; kt += ST) {
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt, nk, P, r0, r1);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 1, nk, P, r1, r2);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 2, nk, P, r2, r3);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt, nk, P, r0, r1, w);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
+      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
     }
     KOS_WAITCNT(0, 0);
     lds_barrier();
@@ -351,31 +375,37 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   }
   lds_barrier();
   Frags<S> f0, f1;
-  frag_load<S>(f0, r0, 0);
+  frag_load<S>(f0, r0, 0, w);
   for (int kt = 0; kt < nk; kt += ST) {
-    k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt, nk, P, r0, r1);
-    if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 1, nk, P, r1, r2);
-    if (kt + 2 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 2, nk, P, r2, r3);
-    if (kt + 3 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 3, nk, P, r3, r0);
+    k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt, nk, P, r0, r1, w);
+    if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
+    if (kt + 2 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
+    if (kt + 3 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
   }
   KOS_WAITCNT(0, 0);
   lds_barrier();
 }
 
-// Visits every accumulator element with its tile-relative (row, col).
+// Accumulator layout (operands of the 32x32x16 MFMA swapped): in column
+// block j of row block i, lane l and register r hold tile element
+//   row = wm*WM + i*32 + l%32,  col = wn*WN + j*32 + 8*(r/4) + 4*(l/32) + r%4.
+// Visits the accumulators four consecutive columns at a time:
+// f(tile row, first tile column, the four values).
 template <class S, class F>
-__device__ __forceinline__ void tile_foreach(const f32x16 (&acc)[S::TM][S::TN], F&& f) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void tile_foreach4(const f32x16 (&acc)[S::TM][S::TN], F&& f) {
+  const WaveCtx w = wave_ctx();
+  const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
 #pragma unroll
   for (int i = 0; i < S::TM; ++i)
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * S::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * S::WN + j * 32 + (lane & 31);
-        f(row, col, acc[i][j][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int row = wm * S::WM + i * 32 + (lane & 31);
+        const int col = wn * S::WN + j * 32 + g * 8 + (lane >> 5) * 4;
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        f(row, col, v);
       }
 }
 

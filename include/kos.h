@@ -94,7 +94,11 @@ typedef struct kos_opts {
   int32_t mode;         /* kos_mode                                            */
   int32_t n_movers;     /* workgroups that START in the communication role (and,
                            under FIXED, stay there); < 0 = the library's default
-                           for the peer link.  Never tuned per shape.          */
+                           for the op, mode and peer link (never per shape):
+                           kos_ag_gemm FUSED half the grid over device memory,
+                           8 over PCIe; kos_gemm_rs FUSED 0 (builders switch
+                           to reducing when the tiles run out); FIXED 16, or 8
+                           over PCIe.  Unused by FUSED kos_moe_*.             */
   int32_t rs_order;     /* kos_rs_order (kos_gemm_rs only)                     */
   int32_t grid;         /* workgroups; 0 = one per compute unit.  Must not
                            exceed the compute-unit count (all co-resident).    */
@@ -258,7 +262,8 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
  *              inspection);  y_grouped: out bf16 [grouped_cap, H]
  * out_return   host array[world] of out bf16 [rows p sent us, H]
  * y            out bf16 [T, H]
- * Shapes: H % 128 == 0, F % 64 == 0.
+ * Shapes: H % 128 == 0, F % 64 == 0, grouped_cap * H * 2 < 2^31 bytes
+ * (else KOS_ERR_SHAPE).
  */
 kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
                            const int32_t* grouped_offsets, const int32_t* row_src,
