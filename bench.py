@@ -246,6 +246,9 @@ def main():
     ap.add_argument("--moe", choices=["dsv3", "qwen3"], default="dsv3")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", choices=["fused", "fixed", "unfused"], default="fused",
+                    help="fused: the persistent kernels (the measured product); fixed / unfused: the same-GPU "
+                         "baselines timed as the step (for per-launch profiles)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between ops")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 1 GiB device copies (reference for HBM byte counters)")
@@ -263,7 +266,8 @@ def main():
     torch.cuda.set_device(0)
     ws = kos.Workspace("cuda")
     inp = build_inputs(torch, KI, kos, moe_shape)
-    ops = make_ops(kos, KI, inp, ws, moe_shape)
+    mode = {"fused": 0, "fixed": 1, "unfused": 2}[args.mode]
+    ops = make_ops(kos, KI, inp, ws, moe_shape, mode=mode)
     for _ in range(args.warmup):
         for _, fn in ops:
             fn()
@@ -335,7 +339,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"kosmos layer pass: ag_gemm {KI.AG_QKV.name} + gemm_rs {KI.RS_MLP.name} + "
-                               f"moe {moe_shape.name}", "emulated_ranks": 8, "mode": "fused",
+                               f"moe {moe_shape.name}", "emulated_ranks": 8, "mode": args.mode,
                    "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 1)},
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -160,6 +160,16 @@ __device__ __forceinline__ T* wave_uniform(T* p) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+// Lane j's value of a 64-bit quantity, as a scalar.  The readlane builtin
+// returns a signed int: each half goes through uint32_t before it is
+// widened, or a low word with bit 31 set would be sign-extended into the
+// high word.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int j) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 constexpr int kCpolSc1 = 16;                 // cache-policy operand: sc1 (device scope)
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor word 3 (32-bit data format)
 
@@ -167,6 +177,7 @@ constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor word 
 // wave-uniform base, through a raw buffer descriptor.
 struct DevBuf {
   __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ DevBuf() : r(__builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, kRawBufferWord3)) {}
   __device__ __forceinline__ explicit DevBuf(const void* base)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform(base)), (short)0, 0x7fffffff,
                                             kRawBufferWord3)) {}

@@ -67,7 +67,7 @@ __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int 
                           : (q == p.rank ? p.partial + ((int64_t)p.rank * p.mc + r0) * N + c0
                                          : p.peers[q] + r0 * N + c0);
   float* dst = p.y + r0 * N + c0;
-  const DevBuf own(src[p.rank]);
+  const DevBuf ob(src[p.rank]);
   for (int e0 = threadIdx.x; e0 < E; e0 += U * blockDim.x) {
     int64_t off[U];
     bool ok[U];
@@ -77,19 +77,22 @@ __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int 
       ok[u] = e < E;
       off[u] = (int64_t)(e / V) * N + (e % V) * 4;
     }
+    // peers' slices (plain loads) and our own staged rows (device-coherent:
+    // written by builders of this launch) into separate registers, all
+    // issued before the first add
     f32x4 x[8][U];
+    f32x4 own[U];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (q >= p.world) break;
+      if (q == p.rank) continue;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!ok[u]) continue;
-        if (q == p.rank)   // written by builders of this launch: device-coherent loads
-          x[q][u] = __builtin_bit_cast(f32x4, own.ld128((uint32_t)off[u] * 4u));
-        else
-          x[q][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + off[u]));
-      }
+      for (int u = 0; u < U; ++u)
+        if (ok[u]) x[q][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src[q] + off[u]));
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) own[u] = __builtin_bit_cast(f32x4, ob.ld128((uint32_t)off[u] * 4u));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
@@ -97,7 +100,7 @@ __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int 
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q >= p.world) break;
-        a += x[q][u];
+        a += q == p.rank ? own[u] : x[q][u];
       }
       *reinterpret_cast<f32x4*>(dst + off[u]) = a;
     }

@@ -15,21 +15,23 @@
 //            tiles of units 0..L-1, then for each unit i the gate/up tiles
 //            of unit i+L followed by the down tiles of unit i -- a down tile
 //            is claimed about a wave of tiles after the tiles it needs.
-//   head[2]  push entries, one per unit, in unit order: rows whose source is
-//            another rank are copied to that rank's return buffer once the
-//            unit's D down tiles are done.  Between tiles a workgroup takes
-//            the head entry if it is ready, else builds the next tile.
-//   head[3]  fold entries, 16 tokens each: y[t] = bf16(sum_j w[t,j] *
-//            res(t,j)), fp32, j ascending; local results gated on their
-//            unit's down tiles, remote results read from what the peers
-//            returned.
+//   head[2]  push entries, kPushRows-row slabs of each unit, in unit order:
+//            rows whose source is another rank are copied to that rank's
+//            return buffer once the unit's D down tiles are done.  Between
+//            tiles a workgroup takes the head entry if it is ready, else
+//            builds the next tile.
+//   head[3]  fold entries, kFoldTokens tokens each, one token per wave at a
+//            time: y[t] = bf16(sum_j w[t,j] * res(t,j)), fp32, j ascending;
+//            local results gated on their unit's down tiles, remote results
+//            read from what the peers returned.
 #include "kos_host.h"
 #include "kos_moe.h"
 #include "kos_tile.h"
 
 namespace kos {
 
-constexpr int kFoldTokens = 16;
+constexpr int kFoldTokens = 8;
+constexpr int kPushRows = 64;
 
 struct CombineParams {
   int32_t world, rank, T, H, E, k, F, E_loc;
@@ -156,30 +158,8 @@ __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit&
   BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
          S::BN / 4};
   tile_mainloop<S, true, false, RING>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
-  const WaveCtx w = wave_ctx();
-  const int lane = w.lane, wave = w.wave;
-  const int wm = wave / S::WGN, wn = wave % S::WGN;
-  uint16_t* hb = p.h + (int64_t)x.row0 * F + (int64_t)nt * HN;
-  // gate column block j pairs with up column block j + TN/2 (same h columns);
-  // accumulator layout as in tile_foreach4
-#pragma unroll
-  for (int i = 0; i < S::TM; ++i) {
-    const int row = wm * S::WM + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < S::TN / 2; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = wn * (S::BN / 4) + j * 32 + g * 8 + (lane >> 5) * 4;
-        f32x4 hv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gv = acc[i][j][4 * g + e], uv = acc[i][j + S::TN / 2][4 * g + e];
-          hv[e] = gv / (1.0f + expf(-gv)) * uv;
-        }
-        // read by this launch's down tiles: device-coherent stores
-        if (row < x.m_valid) st_dev_b64(&hb[(int64_t)row * F + col], pack4_bf16(hv));
-      }
-  }
+  // read by this launch's down tiles: device-coherent stores
+  tile_store_rows<S, RING, true, true>(acc, p.h + (int64_t)x.row0 * F + (int64_t)nt * HN, F, x.m_valid);
 }
 
 // COH: h was written by this launch's gate/up tiles (read device-coherent).
@@ -188,38 +168,132 @@ __device__ __forceinline__ void down_tile(const CombineParams& p, const Unit& x,
   const int64_t H = p.H, F = p.F;
   BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
   tile_mainloop<S, false, COH, RING>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
-  uint16_t* yb = p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN;
-  const int mv = x.m_valid;
-  tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) {   // read by pushes and folds: device-coherent
-    if (r < mv) st_dev_b64(&yb[(int64_t)r * H + c], pack4_bf16(v));
-  });
+  // read by pushes and folds of this launch: device-coherent stores
+  tile_store_rows<S, RING, true>(acc, p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN, H, x.m_valid);
 }
 
-__device__ __forceinline__ void push_unit(const CombineParams& p, const Unit& x) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  (void)lane;
+// Push entry: rows [slab * kPushRows, +kPushRows) of unit x, one row per
+// wave at a time.
+__device__ __forceinline__ void push_slab(const CombineParams& p, const Unit& x, int slab) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const DevBuf yb(p.yg);
-  for (int r = wave; r < x.m_valid; r += nw) {
+  const int r1 = min(x.m_valid, (slab + 1) * kPushRows);
+  for (int r = slab * kPushRows + wave; r < r1; r += nw) {
     const int64_t grow = (int64_t)x.row0 + r;
     const int src = p.row_src[grow * 2];
     if (src == p.rank) continue;
     const int64_t i = p.row_src[grow * 2 + 1];
-    wave_copy_row_dev_src(p.out_return[src] + i * p.H, yb, (uint32_t)(grow * p.H * 2), p.H * 2);
+    wave_copy_row_dev_src(wave_uniform(p.out_return[src] + i * p.H), yb, (uint32_t)(grow * p.H * 2), p.H * 2);
   }
 }
 
-// Thread 0 polls a counter (bounded); others idle.  Returns the outcome in
-// thread 0 only.
-__device__ inline bool t0_poll(const uint32_t* c, uint32_t target, WsHeader* h, uint32_t limit, uint32_t info) {
-  uint32_t it = 0;
-  while (ld_relaxed(c) < target) {
-    if (aborted(h)) return false;
-    if (++it >= limit) {
-      raise_error(h, KOS_ERR_TIMEOUT, info);
-      return false;
+// y row of one token = bf16(sum_j w[j] * res_j), fp32, j ascending.  row[j]
+// is a scalar descriptor of result j's row (device-coherent loads: local
+// rows come from this launch).  KN results (KN == k, or KMAX with the
+// weights of j >= k zero and their rows repeating row 0); CB column chunks
+// per lane per pass, all CB x KN loads issued unconditionally (tail lanes
+// re-read the last chunk) before any use.
+template <int KN, int CB>
+__device__ __forceinline__ void fold_token(int H, const DevBuf (&row)[KN], const float (&w)[KN], uint16_t* yrow,
+                                           int lane) {
+  const int nc = H / 8;
+  for (int c0 = lane; c0 < nc; c0 += 64 * CB) {
+    u32x4 v[CB][KN];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = min(c0 + 64 * u, nc - 1);
+#pragma unroll
+      for (int j = 0; j < KN; ++j) v[u][j] = row[j].ld128((uint32_t)c * 16u);
     }
-    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int c = c0 + 64 * u;
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KN; ++j) {
+        const uint32_t q[4] = {v[u][j].x, v[u][j].y, v[u][j].z, v[u][j].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          a[2 * m] += w[j] * __builtin_bit_cast(float, q[m] << 16);
+          a[2 * m + 1] += w[j] * __builtin_bit_cast(float, q[m] & 0xFFFF0000u);
+        }
+      }
+      u32x4 o;
+      o.x = (uint32_t)f32_to_bf16_bits(a[0]) | ((uint32_t)f32_to_bf16_bits(a[1]) << 16);
+      o.y = (uint32_t)f32_to_bf16_bits(a[2]) | ((uint32_t)f32_to_bf16_bits(a[3]) << 16);
+      o.z = (uint32_t)f32_to_bf16_bits(a[4]) | ((uint32_t)f32_to_bf16_bits(a[5]) << 16);
+      o.w = (uint32_t)f32_to_bf16_bits(a[6]) | ((uint32_t)f32_to_bf16_bits(a[7]) << 16);
+      if (c < nc) reinterpret_cast<u32x4*>(yrow)[c] = o;
+    }
   }
+}
+
+// Broadcasts lane j's result row and weight as scalars, then folds.
+template <int KN, int CB>
+__device__ __forceinline__ void fold_token_rows(int H, int k, uint64_t rowp, float wj, uint16_t* yrow, int lane) {
+  const uint64_t row0 = readlane_u64(rowp, 0);
+  DevBuf row[KN] = {};
+  float w[KN];
+#pragma unroll
+  for (int j = 0; j < KN; ++j) {
+    const uint64_t rj = readlane_u64(rowp, j);
+    const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, wj), j));
+    row[j] = DevBuf(reinterpret_cast<const void*>(j < k ? rj : row0));
+    w[j] = j < k ? wv : 0.f;
+  }
+  fold_token<KN, CB>(H, row, w, yrow, lane);
+}
+
+// Folds token t with one wave.  Lane j < k resolves result j (local: a
+// row of yg, gated on its unit's down tiles when flagged; remote: the row
+// its rank returned); the choices are then broadcast as scalars.  Returns
+// false (wave-uniform) on abort or time-out.
+template <int BM>
+__device__ __forceinline__ bool fold_token_wave(const CombineParams& p, const CombineMeta& M, int t, uint32_t info) {
+  const int lane = threadIdx.x & 63;
+  const int E_loc = p.E_loc;
+  bool local = false;
+  int u = 0;
+  uint64_t rowp = 0;   // result row of lane j < k
+  float wj = 0.f;
+  const int k = p.k;
+  if (lane < k) {
+    const int e = p.topk_idx[(int64_t)t * k + lane];
+    const int pos = p.perm[(int64_t)t * k + lane];
+    wj = p.topk_w[(int64_t)t * k + lane];
+    const int d = e / E_loc;
+    if (d == p.rank) {
+      const int el = e - p.rank * E_loc;
+      const int grow = M.go[el] + M.before[el] + (pos - M.off[e]);
+      local = true;
+      u = M.ub[el] + (grow - M.go[el]) / BM;
+      rowp = reinterpret_cast<uint64_t>(p.yg + (int64_t)grow * p.H);
+    } else {
+      rowp = reinterpret_cast<uint64_t>(p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H);
+    }
+  }
+  if (p.wait_flags) {
+    const uint32_t* dn_done = p.ctr + p.u_max;
+    uint32_t it = 0;
+    for (;;) {
+      const bool ready = !local || ld_relaxed(&dn_done[u]) >= (uint32_t)p.D;
+      if (__all(ready)) break;
+      if (aborted(p.ws)) return false;
+      if (++it >= p.spin_limit) {
+        if (lane == 0) raise_error(p.ws, KOS_ERR_TIMEOUT, info);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  uint16_t* yrow = p.y + (int64_t)t * p.H;
+  const int ks = __builtin_amdgcn_readfirstlane(k);
+  if (ks == 8)
+    fold_token_rows<8, 4>(p.H, ks, rowp, wj, yrow, lane);
+  else if (ks < 8)
+    fold_token_rows<8, 2>(p.H, ks, rowp, wj, yrow, lane);
+  else
+    fold_token_rows<kMoeMaxTopk, 1>(p.H, ks, rowp, wj, yrow, lane);
   return true;
 }
 
@@ -227,77 +301,17 @@ template <int BM>
 __device__ __forceinline__ bool fold_block(const CombineParams& p, const CombineMeta& M, int fb, WgSlots* s) {
   const int t0 = fb * kFoldTokens;
   const int t1 = min(p.T, t0 + kFoldTokens);
-  const uint32_t* dn_done = p.ctr + p.u_max;
-  // wait for every local result these tokens read
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    if (p.wait_flags) {
-      for (int t = t0; t < t1 && ok; ++t)
-        for (int j = 0; j < p.k && ok; ++j) {
-          const int e = p.topk_idx[(int64_t)t * p.k + j];
-          if (e / p.E_loc != p.rank) continue;
-          const int el = e - p.rank * p.E_loc;
-          const int grow = M.go[el] + M.before[el] + (p.perm[(int64_t)t * p.k + j] - M.off[e]);
-          const int u = M.ub[el] + (grow - M.go[el]) / BM;
-          if (!t0_poll(&dn_done[u], (uint32_t)p.D, p.ws, p.spin_limit, 0x40000000u | (uint32_t)fb)) ok = 0;
-        }
-    }
-    s->ok = ok;
-  }
+  if (threadIdx.x == 0) s->ok = 1;
   __syncthreads();
-  if (!s->ok) return false;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int E_loc = p.E_loc;
-  const DevBuf yb(p.yg);
-  for (int t = t0 + wave; t < t1; t += nw) {
-    // result j: local (row of yg, written by this launch: device-coherent
-    // loads at byte offset loc[j]) or returned by a peer (plain loads)
-    const u32x4* src[kMoeMaxTopk];
-    uint32_t loc[kMoeMaxTopk];
-    float w[kMoeMaxTopk];
-#pragma unroll
-    for (int j = 0; j < kMoeMaxTopk; ++j) {
-      if (j >= p.k) break;
-      const int e = p.topk_idx[(int64_t)t * p.k + j];
-      const int pos = p.perm[(int64_t)t * p.k + j];
-      const int d = e / E_loc;
-      w[j] = p.topk_w[(int64_t)t * p.k + j];
-      if (d == p.rank) {
-        const int el = e - p.rank * E_loc;
-        src[j] = nullptr;
-        loc[j] = (uint32_t)(((int64_t)M.go[el] + M.before[el] + (pos - M.off[e])) * p.H * 2);
-      } else {
-        src[j] = reinterpret_cast<const u32x4*>(p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H);
-        loc[j] = 0;
-      }
+  for (int t = t0 + wave; t < t1; t += nw)
+    if (!fold_token_wave<BM>(p, M, t, 0x40000000u | (uint32_t)fb)) {
+      if ((threadIdx.x & 63) == 0) s->ok = 0;
+      break;
     }
-    for (int c = lane; c < p.H / 8; c += 64) {
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      u32x4 vj[kMoeMaxTopk];
-#pragma unroll
-      for (int j = 0; j < kMoeMaxTopk; ++j)
-        if (j < p.k) vj[j] = src[j] ? __builtin_nontemporal_load(src[j] + c) : yb.ld128(loc[j] + c * 16u);
-#pragma unroll
-      for (int j = 0; j < kMoeMaxTopk; ++j) {
-        if (j >= p.k) break;
-        const u32x4 v = vj[j];
-        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          a[2 * m] += w[j] * __builtin_bit_cast(float, q[m] << 16);
-          a[2 * m + 1] += w[j] * __builtin_bit_cast(float, q[m] & 0xFFFF0000u);
-        }
-      }
-      uint4 o;
-      o.x = (uint32_t)f32_to_bf16_bits(a[0]) | ((uint32_t)f32_to_bf16_bits(a[1]) << 16);
-      o.y = (uint32_t)f32_to_bf16_bits(a[2]) | ((uint32_t)f32_to_bf16_bits(a[3]) << 16);
-      o.z = (uint32_t)f32_to_bf16_bits(a[4]) | ((uint32_t)f32_to_bf16_bits(a[5]) << 16);
-      o.w = (uint32_t)f32_to_bf16_bits(a[6]) | ((uint32_t)f32_to_bf16_bits(a[7]) << 16);
-      reinterpret_cast<uint4*>(p.y + (int64_t)t * p.H)[c] = o;
-    }
-  }
-  return true;
+  __syncthreads();
+  return s->ok != 0;
 }
 
 // S: the unit's tile (BM rows of one expert).  ST: a tile of the same width
@@ -319,6 +333,8 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   WsHeader* h = p.ws;
   load_combine_meta<BM>(p, M);
   const int U = M.ub[p.E_loc];
+  constexpr int kPushSlabs = (BM + kPushRows - 1) / kPushRows;
+  const int n_push = U * kPushSlabs;
   uint32_t* gu_done = p.ctr;
   uint32_t* dn_done = p.ctr + p.u_max;
   const uint32_t ticket = wg_ticket(h, &slots);
@@ -338,7 +354,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           if (threadIdx.x == 0) {
             uint32_t hd = ld_relaxed(&h->head[2]);
             uint32_t got = kNoEntry;
-            if (hd < (uint32_t)U && ld_relaxed(&dn_done[hd]) >= (uint32_t)p.D &&
+            if (hd < (uint32_t)n_push && ld_relaxed(&dn_done[hd / kPushSlabs]) >= (uint32_t)p.D &&
                 __hip_atomic_compare_exchange_strong(&h->head[2], &hd, hd + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT))
               got = hd;
@@ -347,7 +363,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           __syncthreads();
           const uint32_t got = slots.claim;
           if (got == kNoEntry) break;
-          push_unit(p, unit_of<BM>(M, p.E_loc, (int)got));
+          push_slab(p, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
         }
       }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
@@ -381,9 +397,10 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   if (!failed && p.do_push) {
     for (;;) {
       const uint32_t i = wg_claim(&h->head[2], h, &slots);
-      if (i >= (uint32_t)U) break;
-      if (p.wait_flags && !wg_observe(&dn_done[i], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
-      push_unit(p, unit_of<BM>(M, p.E_loc, (int)i));
+      if (i >= (uint32_t)n_push) break;
+      const int u = (int)i / kPushSlabs;
+      if (p.wait_flags && !wg_observe(&dn_done[u], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
+      push_slab(p, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
     }
   }
 

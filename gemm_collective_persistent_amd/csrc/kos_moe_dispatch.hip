@@ -5,12 +5,13 @@
 // expert].
 //
 // Queues and counters:
-//   head[0]      router entries, one per block of 64 tokens: top-k of each
-//                token's logits (descending, ties to the lowest expert
-//                index), softmax over the k, and a 64-bit mask per expert of
-//                the block's tokens routed to it (order-free, so the result
-//                is deterministic).
-//   counter[0]   routed blocks.  The workgroup that routes the last block
+//   head[0]      router entries, one per quarter (16 tokens) of a block of
+//                64 tokens: top-k of each token's logits (descending, ties
+//                to the lowest expert index), softmax over the k, and, per
+//                expert, the 16-bit quarter of the block's 64-bit mask of
+//                tokens routed to it (order-free, so the result is
+//                deterministic).
+//   counter[0]   routed entries.  The workgroup that routes the last one
 //                runs the scan: per-expert counts, the exclusive scan over
 //                experts (packed offsets), per-(block, expert) bases, the
 //                grouped offsets of our local experts, capacity checks; then
@@ -53,7 +54,9 @@ struct DispatchParams {
 };
 
 struct DispatchLds {
-  unsigned long long m[kMoeMaxExperts];
+  uint32_t m[kMoeMaxExperts];           // router: 16-bit token masks of one entry
+  int32_t cnt[kMoeMaxExperts];          // scan: per-expert counts
+  int32_t wave_tot[4];
   int32_t off[kMoeMaxExperts + 1];
   int32_t pc[8][kMoeMaxLocal];          // peer counts (row `rank` = our own local counts after the scan)
   int32_t cum[8][kMoeMaxLocal + 1];     // per-source prefix over local experts
@@ -78,13 +81,15 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ __forceinline__ void route_block(const DispatchParams& p, int b, DispatchLds& L) {
+// Router entry `b4`: tokens [16*b4, 16*b4 + 16) = quarter b4 % 4 of block b4 / 4.
+__device__ __forceinline__ void route_entry(const DispatchParams& p, int b4, DispatchLds& L) {
+  constexpr int QT = kMoeTokBlock / 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.m[e] = 0ull;
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.m[e] = 0u;
   __syncthreads();
   const int nv = (p.E + 63) / 64;
-  for (int tl = wave; tl < kMoeTokBlock; tl += nw) {
-    const int t = b * kMoeTokBlock + tl;
+  for (int tl = wave; tl < QT; tl += nw) {
+    const int t = b4 * QT + tl;
     if (t >= p.T) break;
     float v[kMoeMaxExperts / 64];
     uint32_t taken = 0;
@@ -131,40 +136,85 @@ __device__ __forceinline__ void route_block(const DispatchParams& p, int b, Disp
       if (j < p.k && lane == j) {
         p.topk_idx[(int64_t)t * p.k + j] = sel_i[j];
         p.topk_w[(int64_t)t * p.k + j] = z[j] * inv;
-        atomicOr(&L.m[sel_i[j]], 1ull << tl);
+        atomicOr(&L.m[sel_i[j]], 1u << tl);
       }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
-    const unsigned long long m = L.m[e];
-    p.masks[(int64_t)b * p.E + e] = m;
-    p.base[(int64_t)b * p.E + e] = __popcll(m);
-  }
+  // quarter q of the block's 64-bit mask: its 16-bit lane q (little endian)
+  const int b = b4 >> 2, q = b4 & 3;
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
+    reinterpret_cast<uint16_t*>(&p.masks[(int64_t)b * p.E + e])[q] = (uint16_t)L.m[e];
 }
 
-// Run once, by the workgroup that routed the last block.  Returns false
+// Exclusive prefix sums of in[0, n) into out[0, n], out[n] = total; n <=
+// 4 * blockDim.x (256 threads).  All threads call it.
+__device__ inline void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int32_t* wave_tot) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+  int v[4];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = 4 * t + i < n ? in[4 * t + i] : 0;
+    sum += v[i];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int ex = inc - sum;
+  for (int w = 0; w < wave; ++w) ex += wave_tot[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * t + i < n) out[4 * t + i] = ex;
+    ex += v[i];
+  }
+  if (t == 0) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += wave_tot[w];
+    out[n] = tot;
+  }
+  __syncthreads();
+}
+
+// Run once, by the workgroup that routed the last entry.  Returns false
 // (for every thread) when a capacity would overflow; the error is recorded
 // and the movers are never released.
 __device__ __forceinline__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
+  constexpr int B = 16;   // masks loaded per batch per thread
+  // per-expert counts: popcounts of the block masks
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
     int run = 0;
-    for (int b = 0; b < p.nblk; ++b) {
-      const int h = p.base[(int64_t)b * p.E + e];
-      p.base[(int64_t)b * p.E + e] = run;
-      run += h;
+    for (int b0 = 0; b0 < p.nblk; b0 += B) {
+      unsigned long long m[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) m[u] = b0 + u < p.nblk ? p.masks[(int64_t)(b0 + u) * p.E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < B; ++u) run += __popcll(m[u]);
     }
     p.counts[e] = run;
-    L.off[e + 1] = run;
+    L.cnt[e] = run;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    L.off[0] = 0;
-    for (int e = 0; e < p.E; ++e) L.off[e + 1] += L.off[e];
-  }
-  __syncthreads();
+  block_exclusive_scan(L.cnt, L.off, p.E, L.wave_tot);
   for (int e = threadIdx.x; e <= p.E; e += blockDim.x) p.off[e] = L.off[e];
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
-    for (int b = 0; b < p.nblk; ++b) p.base[(int64_t)b * p.E + e] += L.off[e];
+  // base of (block, expert): packed offset of the expert + its tokens in earlier blocks
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    int run = L.off[e];
+    for (int b0 = 0; b0 < p.nblk; b0 += B) {
+      unsigned long long m[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) m[u] = b0 + u < p.nblk ? p.masks[(int64_t)(b0 + u) * p.E + e] : 0ull;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (b0 + u < p.nblk) p.base[(int64_t)(b0 + u) * p.E + e] = run;
+        run += __popcll(m[u]);
+      }
+    }
+  }
   if (threadIdx.x == 0) {
     bool over = false;
     for (int d = 0; d < p.world; ++d) {
@@ -245,16 +295,17 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
     if (p.nblk == 0 && slots.claim == 0) {   // no tokens: the first arrival scans
       if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
     }
+    const uint32_t n_route = (uint32_t)p.nblk * 4;
     for (;;) {
-      const uint32_t b = wg_claim(&h->head[0], h, &slots);
-      if (b >= (uint32_t)p.nblk) break;
-      route_block(p, (int)b, L);
+      const uint32_t b4 = wg_claim(&h->head[0], h, &slots);
+      if (b4 >= n_route) break;
+      route_entry(p, (int)b4, L);
       fence_release();
       __syncthreads();
       if (threadIdx.x == 0)
         slots.aux[0] = __hip_atomic_fetch_add(&p.ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
-      if (slots.aux[0] == (uint32_t)p.nblk - 1) {   // the last block: scan
+      if (slots.aux[0] == n_route - 1) {   // the last entry: scan
         fence_acquire();
         if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
       }
@@ -304,27 +355,23 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
               }
             }
           }
+          // the whole row in registers (up to 16 chunks per lane per pass),
+          // then one copy per destination
           const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (int64_t)t * H);
           const int nc = row_bytes / 16;
-          int c = lane;
-          for (; c + 3 * 64 < nc; c += 4 * 64) {   // four loads in flight per lane
-            const u32x4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
+          constexpr int U = 16;
+          for (int c0 = lane; c0 < nc; c0 += U * 64) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (c0 + u * 64 < nc) v[u] = src[c0 + u * 64];
 #pragma unroll
             for (int j = 0; j < kMoeMaxTopk; ++j) {
               if (j >= p.k) break;
-              u32x4* d = reinterpret_cast<u32x4*>(dst[j]);
-              d[c] = v0;
-              d[c + 64] = v1;
-              d[c + 128] = v2;
-              d[c + 192] = v3;
-            }
-          }
-          for (; c < nc; c += 64) {
-            const u32x4 v = src[c];
+              u32x4* d = reinterpret_cast<u32x4*>(wave_uniform(dst[j]));
 #pragma unroll
-            for (int j = 0; j < kMoeMaxTopk; ++j) {
-              if (j >= p.k) break;
-              reinterpret_cast<u32x4*>(dst[j])[c] = v;
+              for (int u = 0; u < U; ++u)
+                if (c0 + u * 64 < nc) d[c0 + u * 64] = v[u];
             }
           }
         }

@@ -409,4 +409,69 @@ __device__ __forceinline__ void tile_foreach4(const f32x16 (&acc)[S::TM][S::TN],
       }
 }
 
+// SwiGLU of a gate and an up value: silu(g) * u = g / (1 + e^-g) * u, fp32.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Stores the tile as bf16 rows [0, m_valid) of dst (row stride ld elements)
+// through the LDS ring: every lane writes its four-column pieces into LDS,
+// then each group of lanes stores whole rows with 16-byte stores, so the
+// global writes are whole cache lines (what device-coherent write-through
+// stores need to be cheap).  SWIGLU: the tile holds gate and up columns
+// (BSrc dual layout) and the BN/2 output columns are swiglu(gate, up).
+// COH: device-scope (sc1) stores.  Call right after tile_mainloop (the ring
+// is free); the next tile_mainloop waits for the ring.  dst is the same in
+// every thread.
+template <class S, int RING, bool COH, bool SWIGLU = false>
+__device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst, int64_t ld,
+                                                int m_valid) {
+  constexpr int OW = SWIGLU ? S::BN / 2 : S::BN;   // output columns
+  constexpr int OJ = SWIGLU ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
+  constexpr int ROW_BYTES = OW * 2;
+  constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
+  constexpr int ROWS_PER_RING = RING / ROW_BYTES;
+  static_assert(RING % ROW_BYTES == 0 && 4 * ROWS_PER_RING >= S::BM, "the tile must fit the ring");
+  static_assert((CPR & (CPR - 1)) == 0 && S::NT % CPR == 0, "power-of-two chunks per row");
+  char* rb[4] = {ring<RING, 0>(), ring<RING, 1>(), ring<RING, 2>(), ring<RING, 3>()};
+  const WaveCtx w = wave_ctx();
+  const int lane = w.lane, wave = w.wave;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  // chunk c of row r sits at chunk position c ^ (r % CPR) (spreads the 32
+  // rows one write instruction touches over the banks)
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i) {
+    const int row = wm * S::WM + i * 32 + (lane & 31);
+    char* base = rb[row / ROWS_PER_RING] + (row % ROWS_PER_RING) * ROW_BYTES;
+#pragma unroll
+    for (int j = 0; j < OJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * (OW / 2) + j * 32 + g * 8 + (lane >> 5) * 4;
+        const int chunk = (col >> 3) ^ (row & (CPR - 1));
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
+        *reinterpret_cast<u32x2*>(base + chunk * 16 + (col & 7) * 2) = pack4_bf16(v);
+      }
+  }
+  KOS_WAITCNT(0, 0);
+  lds_barrier();
+  const DevBuf d(dst);
+  constexpr int ROWS_PER_PASS = S::NT / CPR;
+  const int t = wave * 64 + lane;
+  const int c = t % CPR;
+#pragma unroll 4
+  for (int r0 = 0; r0 < S::BM; r0 += ROWS_PER_PASS) {
+    const int row = r0 + t / CPR;
+    if (row >= m_valid) break;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(rb[row / ROWS_PER_RING] + (row % ROWS_PER_RING) * ROW_BYTES +
+                                                    ((c ^ (row & (CPR - 1))) * 16));
+    const int64_t off = ((int64_t)row * ld + c * 8) * 2;
+    if constexpr (COH)
+      d.st128((uint32_t)off, v);
+    else
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + off) = v;
+  }
+}
+
 }  // namespace kos
