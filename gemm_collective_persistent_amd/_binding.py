@@ -25,7 +25,7 @@ RS_BAND, RS_ROW = 0, 1
 EXPORTS = [
     "kos_opts_default", "kos_workspace_bytes", "kos_workspace_init", "kos_workspace_status",
     "kos_last_error", "kos_device_cu_count", "kos_ag_gemm", "kos_gemm_rs",
-    "kos_moe_dispatch", "kos_moe_combine",
+    "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace",
 ]
 
 
@@ -39,7 +39,17 @@ class KosError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("n_movers", c_int32), ("rs_order", c_int32),
                 ("grid", c_int32), ("spin_limit", c_uint32), ("peer_link", c_int32),
-                ("reserved", c_int32 * 2)]
+                ("trace", c_int32), ("reserved", c_int32)]
+
+
+class TraceRec(ctypes.Structure):
+    _fields_ = [("t0", ctypes.c_uint64), ("dt", c_uint32), ("tag", c_uint32)]
+
+
+TRACE_RECORDS = 512     # KOS_TRACE_RECORDS: records per workgroup
+TRACE_MAX_WG = 256      # KOS_TRACE_MAX_WG
+TRACE_KINDS = {1: "move", 2: "tile", 3: "wait", 4: "reduce", 5: "route", 6: "scan", 7: "push", 8: "fold",
+               9: "tile_down"}
 
 
 class MoeShape(ctypes.Structure):
@@ -62,6 +72,7 @@ def _load():
         "kos_workspace_status": (c_int32, [P, P]),
         "kos_last_error": (c_char_p, []),
         "kos_device_cu_count": (c_int32, []),
+        "kos_workspace_trace": (c_int32, [P, P, c_size_t, P]),
         "kos_ag_gemm": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, PP, P, P, P,
                                   c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, P, P,
@@ -88,11 +99,12 @@ def check(status: int) -> None:
         raise KosError(status, lib.kos_last_error().decode(errors="replace"))
 
 
-def opts(mode=MODE_FUSED, n_movers=-1, rs_order=RS_BAND, grid=0, spin_limit=0, peer_link=0) -> Opts:
+def opts(mode=MODE_FUSED, n_movers=-1, rs_order=RS_BAND, grid=0, spin_limit=0, peer_link=0,
+         trace=False) -> Opts:
     o = Opts()
     lib.kos_opts_default(ctypes.byref(o))
     o.mode, o.n_movers, o.rs_order, o.grid = mode, n_movers, rs_order, grid
-    o.spin_limit, o.peer_link = spin_limit, peer_link
+    o.spin_limit, o.peer_link, o.trace = spin_limit, peer_link, int(bool(trace))
     return o
 
 

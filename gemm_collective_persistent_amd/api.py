@@ -41,6 +41,35 @@ class Workspace:
         """Synchronizes and raises KosError if a device-side error was recorded."""
         check(lib.kos_workspace_status(self.ptr, _stream(stream)))
 
+    def trace(self, grid: int, stream=None):
+        """Timeline of the last call made with ``opts(trace=True)`` on a grid of
+        `grid` workgroups: a list, per workgroup, of (ticket, t_begin, t_end,
+        [(kind, entry, t0, t1), ...]) with times in microseconds from the
+        earliest workgroup start (kos_workspace_trace).  ``self.trace_xcd``
+        then holds each workgroup's XCD."""
+        from ._binding import TRACE_KINDS, TRACE_MAX_WG, TRACE_RECORDS, TraceRec
+        if not 0 < grid <= TRACE_MAX_WG:
+            raise ValueError(f"grid {grid} outside [1, {TRACE_MAX_WG}]")
+        n = grid * TRACE_RECORDS
+        buf = (TraceRec * n)()
+        check(lib.kos_workspace_trace(self.ptr, ctypes.cast(buf, ctypes.c_void_p), n, _stream(stream)))
+        tick_us = 0.01                      # 100 MHz constant-rate counter
+        heads = [buf[g * TRACE_RECORDS] for g in range(grid)]
+        t_ref = min(h.t0 for h in heads)
+        out = []
+        self.trace_xcd = [(h.tag >> 12) & 15 for h in heads]
+        for g, h in enumerate(heads):
+            used = h.tag & 0xFFF
+            recs = []
+            for i in range(1, min(used, TRACE_RECORDS)):
+                r = buf[g * TRACE_RECORDS + i]
+                t0 = (r.t0 - t_ref) * tick_us
+                recs.append((TRACE_KINDS.get(r.tag >> 24, str(r.tag >> 24)), r.tag & 0xFFFFFF, t0,
+                             t0 + r.dt * tick_us))
+            tb = (h.t0 - t_ref) * tick_us
+            out.append((h.tag >> 16, tb, tb + h.dt * tick_us, recs))
+        return out
+
 
 def ag_gemm(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w: torch.Tensor,
             a_gathered: torch.Tensor, c: torch.Tensor, rank: int, ws: Workspace,

@@ -42,6 +42,7 @@ struct AgParams {
   int32_t n_tiles;
   WsHeader* ws;
   uint32_t* ready;
+  kos_trace_rec* trace;   // null: tracing off
 };
 
 template <class S>
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
+  Tracer tr(p.trace);
   const uint32_t ticket = wg_ticket(h, &slots);
 
   // ---- mover role -------------------------------------------------------
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
     for (;;) {
       const uint32_t i = wg_claim(&h->head[0], h, &slots);
       if (i >= (uint32_t)p.n_move) break;
+      const uint64_t t0 = tr.now();
       int shard, rem;
       const uint16_t* src_shard;
       if ((int32_t)i < n_remote) {
@@ -76,8 +79,10 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * K, src_shard + row * K,
                   (size_t)p.rows_per_move * K * 2);
       wg_publish(&p.ready[shard * p.rb_per_shard + rb], 1u);
+      tr.put(KOS_TR_MOVE, i, t0);
     }
     if (!p.movers_switch) {
+      tr.finish(ticket);
       wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
       return;
     }
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
       const int shard = (p.rank + q) % p.world;
       BSrc b{p.w + (int64_t)nt * BN, nullptr, N, 0};
+      uint64_t t0 = tr.now();
       if (q == 0) {
         tile_mainloop<S>(acc, p.a_local + (int64_t)rb * BM * K, K, BM, b, p.k);
       } else {
@@ -104,6 +110,8 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
           if (!wg_observe(&p.ready[shard * p.rb_per_shard + rb], (uint32_t)p.moves_per_rb, h, p.spin_limit, j,
                           &slots))
             break;
+          tr.put(KOS_TR_WAIT, j, t0);
+          t0 = tr.now();
           tile_mainloop<S, false, true>(acc, A, K, BM, b, p.k);
         } else {
           tile_mainloop<S>(acc, A, K, BM, b, p.k);
@@ -118,8 +126,10 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
         uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + row0 * N + col0;
         tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<u32x2*>(&C[r * N + c]) = pack4_bf16(v); });
       }
+      tr.put(KOS_TR_TILE, j, t0);
     }
   }
+  tr.finish(ticket);
   wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
 }
 
@@ -222,6 +232,7 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   p.n_tiles = world * p.rb_per_shard * p.tiles_n;
   p.ws = static_cast<WsHeader*>(ws);
   p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
   if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
 
   // A single rank whose gathered output is its own shard has nothing to move.

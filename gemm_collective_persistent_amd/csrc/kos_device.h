@@ -228,6 +228,48 @@ __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_count
 }
 
 // ---------------------------------------------------------------------------
+// optional timeline (kos_opts.trace): one row of KOS_TRACE_RECORDS records
+// per workgroup, written by thread 0
+// ---------------------------------------------------------------------------
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u; }
+
+struct Tracer {
+  kos_trace_rec* row;   // this workgroup's row; null when tracing is off
+  uint32_t n;           // records used, header included
+  uint64_t t_begin;
+
+  __device__ __forceinline__ explicit Tracer(kos_trace_rec* base)
+      : row(base ? base + (size_t)blockIdx.x * KOS_TRACE_RECORDS : nullptr), n(1), t_begin(now()) {}
+  __device__ __forceinline__ bool on() const { return row != nullptr; }
+  // The constant-rate counter when tracing, else 0.
+  __device__ __forceinline__ uint64_t now() const { return row ? __builtin_amdgcn_s_memrealtime() : 0; }
+  // One piece of work of `kind` on `entry`, begun at t0 (from now()).
+  __device__ __forceinline__ void put(uint32_t kind, uint32_t entry, uint64_t t0) {
+    if (!row) return;
+    if (threadIdx.x == 0 && n < KOS_TRACE_RECORDS) {
+      kos_trace_rec r;
+      r.t0 = t0;
+      r.dt = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t0);
+      r.tag = (kind << 24) | (entry & 0xFFFFFFu);
+      row[n] = r;
+    }
+    ++n;
+  }
+  // The header: start, lifetime, arrival ticket, the accelerator complex
+  // die (XCD) the workgroup runs on, and the record count.
+  __device__ __forceinline__ void finish(uint32_t ticket) {
+    if (!row || threadIdx.x != 0) return;
+    kos_trace_rec r;
+    r.t0 = t_begin;
+    r.dt = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_begin);
+    r.tag = (ticket << 16) | (xcd_id() << 12) | (n < KOS_TRACE_RECORDS ? n : KOS_TRACE_RECORDS);
+    row[0] = r;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // movers: coalesced 128-bit copies
 // ---------------------------------------------------------------------------
 

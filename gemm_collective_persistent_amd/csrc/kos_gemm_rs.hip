@@ -45,6 +45,7 @@ struct RsParams {
   int32_t n_tiles, n_reduce;
   WsHeader* ws;
   uint32_t* ready;
+  kos_trace_rec* trace;     // null: tracing off
 };
 
 // Rows of one reduce entry: a slab of kSlabRows rows of one output tile.
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
+  Tracer tr(p.trace);
   const uint32_t ticket = wg_ticket(h, &slots);
   const bool starts_reducer = p.do_reduce && ticket < (uint32_t)p.n_reducers;
 
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
     for (;;) {
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
       if (j >= (uint32_t)p.n_tiles) break;
+      const uint64_t t0 = tr.now();
       int band, chunk, col;
       if (!p.row_order) {
         band = (int)j / per_band;
@@ -149,8 +152,10 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
       } else {
         tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<f32x4*>(&P[r * N + c]) = v; });
       }
+      tr.put(KOS_TR_TILE, j, t0);
     }
     if (!p.builders_switch || !p.do_reduce) {
+      tr.finish(ticket);
       wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
       return;
     }
@@ -164,10 +169,17 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
       if (i >= (uint32_t)p.n_reduce * SLABS) break;
       const int tile = (int)i / SLABS, slab = (int)i % SLABS;
       const int band = tile / p.tiles_n, col = tile % p.tiles_n;
-      if (p.wait_flags && !wg_observe(&p.ready[tile], 1u, h, p.spin_limit, i, &slots)) break;
+      uint64_t t0 = tr.now();
+      if (p.wait_flags) {
+        if (!wg_observe(&p.ready[tile], 1u, h, p.spin_limit, i, &slots)) break;
+        tr.put(KOS_TR_WAIT, i, t0);
+        t0 = tr.now();
+      }
       reduce_entry<BN>(p, (int64_t)band * BM + slab * kSlabRows, col);
+      tr.put(KOS_TR_REDUCE, i, t0);
     }
   }
+  tr.finish(ticket);
   wg_exit(h, p.ready, p.bands * p.tiles_n, &slots);
 }
 
@@ -240,6 +252,7 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
   p.n_reduce = p.bands * p.tiles_n;
   p.ws = static_cast<WsHeader*>(ws);
   p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
   if ((size_t)p.n_reduce > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many output tiles");
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -57,7 +57,9 @@ kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, const CrewDef
   if (o->mode < KOS_MODE_FUSED || o->mode > KOS_MODE_UNFUSED) return fail(KOS_ERR_ARG, "bad mode %d", o->mode);
   if (o->rs_order != KOS_RS_BAND && o->rs_order != KOS_RS_ROW) return fail(KOS_ERR_ARG, "bad rs_order %d", o->rs_order);
   if (o->peer_link != 0 && o->peer_link != 1) return fail(KOS_ERR_ARG, "bad peer_link %d", o->peer_link);
-  if (o->reserved[0] || o->reserved[1]) return fail(KOS_ERR_ARG, "reserved fields must be 0");
+  if (o->reserved) return fail(KOS_ERR_ARG, "reserved field must be 0");
+  if (o->trace && o->grid > KOS_TRACE_MAX_WG)
+    return fail(KOS_ERR_ARG, "tracing holds at most %d workgroups", KOS_TRACE_MAX_WG);
   if (o->grid == 0) o->grid = dev.cus;
   if (o->grid < 2 || o->grid > dev.cus)
     return fail(KOS_ERR_ARG, "grid %d outside [2, %d] (all workgroups must be co-resident)", o->grid, dev.cus);
@@ -118,6 +120,19 @@ kos_status kos_workspace_status(void* ws, void* stream) {
       hipSuccess)
     return fail(KOS_ERR_HIP, "clearing the workspace status failed");
   return fail(static_cast<kos_status>(h.status), "device error %u (entry %u)", h.status, h.err_info);
+}
+
+kos_status kos_workspace_trace(void* ws, kos_trace_rec* out, size_t n_records, void* stream) {
+  if (!ws || (!out && n_records)) return fail(KOS_ERR_ARG, "null buffer");
+  if (n_records > (size_t)KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS)
+    return fail(KOS_ERR_ARG, "%zu records requested, the trace region holds %d", n_records,
+                KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS);
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(KOS_ERR_HIP, "stream synchronization failed");
+  if (n_records && hipMemcpy(out, static_cast<char*>(ws) + kTraceOffset, n_records * sizeof(kos_trace_rec),
+                             hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(KOS_ERR_HIP, "reading the trace region failed");
+  return KOS_OK;
 }
 
 const char* kos_last_error(void) { return g_msg; }

@@ -60,6 +60,7 @@ struct CombineParams {
   uint32_t spin_limit;
   WsHeader* ws;
   uint32_t* ctr;          // gu_done[u_max], then dn_done[u_max]
+  kos_trace_rec* trace;   // null: tracing off
 };
 
 struct CombineMeta {
@@ -337,6 +338,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   const int n_push = U * kPushSlabs;
   uint32_t* gu_done = p.ctr;
   uint32_t* dn_done = p.ctr + p.u_max;
+  Tracer tr(p.trace);
   const uint32_t ticket = wg_ticket(h, &slots);
   const bool crew = p.n_crew > 0 && ticket < (uint32_t)p.n_crew;
   bool failed = false;
@@ -363,7 +365,9 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           __syncthreads();
           const uint32_t got = slots.claim;
           if (got == kNoEntry) break;
+          const uint64_t t0 = tr.now();
           push_slab(p, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
+          tr.put(KOS_TR_PUSH, got, t0);
         }
       }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
@@ -373,21 +377,29 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
       decode_tile(p, U, (int)j, down, u, nt);
       const Unit x = unit_of<BM>(M, p.E_loc, u);
       const bool tail = x.m_valid <= ST::BM;
+      uint64_t t0 = tr.now();
       if (!down) {
         if (tail) gate_up_tile<ST, RB>(p, x, nt, acc_t);
         else gate_up_tile<S, RB>(p, x, nt, acc);
         wg_publish(&gu_done[u], 1u);
+        tr.put(KOS_TR_TILE, j, t0);
       } else {
-        if (p.wait_flags && p.do_gu && !wg_observe(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
-          failed = true;
-          break;
+        if (p.wait_flags && p.do_gu) {
+          if (!wg_observe(&gu_done[u], (uint32_t)p.G, h, p.spin_limit, j, &slots)) {
+            failed = true;
+            break;
+          }
+          tr.put(KOS_TR_WAIT, j, t0);
+          t0 = tr.now();
         }
         if (tail) down_tile<ST, COH, RB>(p, x, nt, acc_t);
         else down_tile<S, COH, RB>(p, x, nt, acc);
         wg_publish(&dn_done[u], 1u);
+        tr.put(KOS_TR_TILE2, j, t0);
       }
     }
     if (p.n_crew > 0) {   // fixed crew: builders only build
+      tr.finish(ticket);
       wg_exit(h, p.ctr, 2 * p.u_max, &slots);
       return;
     }
@@ -399,8 +411,14 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
       const uint32_t i = wg_claim(&h->head[2], h, &slots);
       if (i >= (uint32_t)n_push) break;
       const int u = (int)i / kPushSlabs;
-      if (p.wait_flags && !wg_observe(&dn_done[u], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
+      uint64_t t0 = tr.now();
+      if (p.wait_flags) {
+        if (!wg_observe(&dn_done[u], (uint32_t)p.D, h, p.spin_limit, 0x20000000u | i, &slots)) break;
+        tr.put(KOS_TR_WAIT, i, t0);
+        t0 = tr.now();
+      }
       push_slab(p, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
+      tr.put(KOS_TR_PUSH, i, t0);
     }
   }
 
@@ -410,9 +428,12 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
     for (;;) {
       const uint32_t i = wg_claim(&h->head[3], h, &slots);
       if (i >= (uint32_t)nfb) break;
+      const uint64_t t0 = tr.now();
       if (!fold_block<BM>(p, M, (int)i, &slots)) break;
+      tr.put(KOS_TR_FOLD, i, t0);
     }
   }
+  tr.finish(ticket);
   wg_exit(h, p.ctr, 2 * p.u_max, &slots);
 }
 
@@ -504,6 +525,7 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   p.spin_limit = o.spin_limit;
   p.ws = static_cast<WsHeader*>(ws);
   p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   auto launch = [&](const CombineParams& q, const char* what) {

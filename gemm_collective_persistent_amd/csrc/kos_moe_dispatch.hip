@@ -47,6 +47,7 @@ struct DispatchParams {
   int32_t do_route, do_copy, wait_scan;
   uint32_t spin_limit;
   WsHeader* ws;
+  kos_trace_rec* trace;          // null: tracing off
   uint32_t* ctr;                 // [0] routed blocks, [1] scan done
   unsigned long long* masks;     // scratch [nblk, E]
   int32_t* base;                 // scratch [nblk, E]: histogram, then bases
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
   __shared__ WgSlots slots;
   WsHeader* h = p.ws;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NT / 64;
-  wg_ticket(h, &slots);
+  Tracer tr(p.trace);
+  const uint32_t ticket = wg_ticket(h, &slots);
 
   // peer counts (inputs) and the per-source prefixes
   for (int i = threadIdx.x; i < p.world * p.E_loc; i += NT) {
@@ -292,22 +294,28 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
 
   // ---- router role ------------------------------------------------------
   if (p.do_route) {
-    if (p.nblk == 0 && slots.claim == 0) {   // no tokens: the first arrival scans
+    if (p.nblk == 0 && ticket == 0) {   // no tokens: the first arrival scans
+      const uint64_t t0 = tr.now();
       if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
+      tr.put(KOS_TR_SCAN, 0, t0);
     }
     const uint32_t n_route = (uint32_t)p.nblk * 4;
     for (;;) {
       const uint32_t b4 = wg_claim(&h->head[0], h, &slots);
       if (b4 >= n_route) break;
+      uint64_t t0 = tr.now();
       route_entry(p, (int)b4, L);
       fence_release();
       __syncthreads();
       if (threadIdx.x == 0)
         slots.aux[0] = __hip_atomic_fetch_add(&p.ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
+      tr.put(KOS_TR_ROUTE, b4, t0);
       if (slots.aux[0] == n_route - 1) {   // the last entry: scan
+        t0 = tr.now();
         fence_acquire();
         if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
+        tr.put(KOS_TR_SCAN, 0, t0);
       }
     }
   }
@@ -320,11 +328,14 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
       const uint32_t i = wg_claim(&h->head[1], h, &slots);
       if (i >= (uint32_t)n_entries) break;
       if (!have_meta) {
+        const uint64_t tw = tr.now();
         if (p.wait_scan && !wg_wait(&p.ctr[1], 1u, h, p.spin_limit, 0xFFFF0000u, &slots)) break;
         fence_acquire();
         load_meta(p, L);
         have_meta = true;
+        tr.put(KOS_TR_WAIT, i, tw);
       }
+      const uint64_t t0 = tr.now();
       const int H = p.H;
       const int row_bytes = H * 2;
       if ((int)i < p.nblk * 4) {
@@ -394,8 +405,10 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
           }
         }
       }
+      tr.put(KOS_TR_MOVE, i, t0);
     }
   }
+  tr.finish(ticket);
   wg_exit(h, p.ctr, 2, &slots);
 }
 
@@ -465,6 +478,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   p.nblk = (s->tokens + kMoeTokBlock - 1) / kMoeTokBlock;
   p.spin_limit = o.spin_limit;
   p.ws = static_cast<WsHeader*>(ws);
+  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
   p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   char* scratch = static_cast<char*>(ws) + kScratchOffset;
   const size_t mask_bytes = (size_t)p.nblk * p.E * 8, base_bytes = (size_t)p.nblk * p.E * 4;

@@ -107,8 +107,41 @@ typedef struct kos_opts {
   int32_t peer_link;    /* 0: peers' buffers in device memory; 1: in pinned,
                            device-mapped host memory (PCIe).  Only picks the
                            default crew size.                                  */
-  int32_t reserved[2];  /* must be 0                                            */
+  int32_t trace;        /* non-zero: every workgroup records a timeline of its
+                           work in the workspace's trace region (read it with
+                           kos_workspace_trace).  Adds a few stores per entry;
+                           leave it off for timed runs.                        */
+  int32_t reserved;     /* must be 0                                            */
 } kos_opts;
+
+/* Timeline of one traced call (kos_opts.trace).  Workgroup g (launch order,
+ * 0..grid-1) owns records [g*KOS_TRACE_RECORDS, (g+1)*KOS_TRACE_RECORDS).
+ * Its record 0 is a header: t0 = when it started, dt = its lifetime, tag =
+ * (arrival ticket << 16) | (XCD it ran on << 12) | records written (header
+ * included, at most KOS_TRACE_RECORDS; later pieces of work are dropped).  Every other record
+ * is one piece of work: t0 = start, dt = duration, tag = (kos_trace_kind
+ * << 24) | entry index (low 24 bits).  Times are ticks of the GPU's
+ * constant-rate 100 MHz counter (s_memrealtime).  Used for the idle-CU
+ * fraction: the share of workgroup-time outside work records, waits
+ * included, over the kernel's span. */
+#define KOS_TRACE_RECORDS 512
+#define KOS_TRACE_MAX_WG 256
+typedef struct kos_trace_rec {
+  uint64_t t0;
+  uint32_t dt;
+  uint32_t tag;
+} kos_trace_rec;
+typedef enum kos_trace_kind {
+  KOS_TR_MOVE = 1,    /* a mover's copy: an all-gather slice; dispatch rows     */
+  KOS_TR_TILE = 2,    /* a builder tile (combine: gate/up)                      */
+  KOS_TR_WAIT = 3,    /* polling a ready counter before a dependent entry       */
+  KOS_TR_REDUCE = 4,  /* a reduce-scatter slab                                  */
+  KOS_TR_ROUTE = 5,   /* a router entry (16 tokens)                             */
+  KOS_TR_SCAN = 6,    /* the dispatch scan                                      */
+  KOS_TR_PUSH = 7,    /* a combine push slab                                    */
+  KOS_TR_FOLD = 8,    /* a combine fold block                                   */
+  KOS_TR_TILE2 = 9    /* a combine down tile                                    */
+} kos_trace_kind;
 
 /* Fills `o` with the defaults (FUSED, default crew, band order, full grid). */
 void kos_opts_default(kos_opts* o);
@@ -123,6 +156,13 @@ kos_status kos_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * in `ws` since the last call of this function (KOS_OK if none) and clears
  * it.  KOS_ERR_HIP if the synchronization itself fails. */
 kos_status kos_workspace_status(void* ws, void* stream);
+
+/* Synchronizes `stream`, then copies the first `n_records` records of the
+ * trace region of `ws` (see kos_trace_rec) to host memory `out`.  n_records
+ * is at most KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS (else KOS_ERR_ARG).  The
+ * region holds the timeline of the last call made with kos_opts.trace set;
+ * rows of workgroups beyond that call's grid are stale. */
+kos_status kos_workspace_trace(void* ws, kos_trace_rec* out, size_t n_records, void* stream);
 
 /* Thread-local description of the last non-OK status returned on this
  * thread ("" if none).  Valid until the next library call on the thread. */

@@ -54,3 +54,15 @@ def test_ag_gemm_argument_validation():
     assert _ag(kos, a=ctypes.c_void_p(0x10008)) == KOS_ERR_ALIGN
     assert _ag(kos, wsb=1024) == KOS_ERR_WORKSPACE
     assert b"workspace" in kos.lib.kos_last_error()
+
+
+def test_trace_reader_validation():
+    import gemm_collective_persistent_amd as kos
+    from gemm_collective_persistent_amd._binding import KOS_ERR_ARG, TRACE_MAX_WG, TRACE_RECORDS
+    lib = kos.lib
+    fake = ctypes.c_void_p(0x10000)            # never dereferenced: validation fails first
+    assert lib.kos_workspace_trace(None, fake, 1, None) == KOS_ERR_ARG
+    assert lib.kos_workspace_trace(fake, None, 1, None) == KOS_ERR_ARG
+    assert lib.kos_workspace_trace(fake, fake, TRACE_MAX_WG * TRACE_RECORDS + 1, None) == KOS_ERR_ARG
+    assert ctypes.sizeof(kos._binding.TraceRec) == 16
+    assert ctypes.sizeof(kos.Opts) == 32
