@@ -99,7 +99,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
       const int rem = (int)j % per_q;
       const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
       const int shard = (p.rank + q) % p.world;
-      BSrc b{p.w + (int64_t)nt * BN, nullptr, N, 0};
+      BSrc b{p.w + (int64_t)nt * BN, nullptr, N};
       uint64_t t0 = tr.now();
       if (q == 0) {
         tile_mainloop<S>(acc, p.a_local + (int64_t)rb * BM * K, K, BM, b, p.k);
@@ -189,6 +189,8 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
                 (long long)k, (long long)n);
   if (m_local * world > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20))
     return fail(KOS_ERR_SHAPE, "sizes too large");
+  // the tiles address W through 32-bit buffer offsets
+  if (k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
   if (!aligned16(a_local) || !aligned16(w) || !aligned16(a_gathered) || !aligned16(c))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   for (int p = 0; p < world; ++p)

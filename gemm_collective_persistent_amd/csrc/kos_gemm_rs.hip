@@ -140,7 +140,7 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
         col = rem % p.tiles_n;
       }
       const int64_t row0 = (int64_t)chunk * p.mc + (int64_t)band * BM;
-      BSrc b{p.w + (int64_t)col * BN, nullptr, N, 0};
+      BSrc b{p.w + (int64_t)col * BN, nullptr, N};
       tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k);
       float* P = p.partial + row0 * N + (int64_t)col * BN;
       if (chunk == p.rank) {   // read by this launch's reducers: device-coherent stores
@@ -213,6 +213,8 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
     return fail(KOS_ERR_SHAPE, "m %lld (m/world a multiple of 64), k %lld, n %lld (multiples of 64) unsupported",
                 (long long)m, (long long)k, (long long)n);
   if (m > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20)) return fail(KOS_ERR_SHAPE, "sizes too large");
+  // the tiles address W through 32-bit buffer offsets
+  if (k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
   if (!aligned16(a) || !aligned16(w) || !aligned16(partial) || !aligned16(y))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   for (int p = 0; p < world; ++p)

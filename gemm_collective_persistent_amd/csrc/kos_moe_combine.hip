@@ -156,8 +156,7 @@ template <class S, int RING>
 __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   constexpr int HN = S::BN / 2;    // h columns per tile
   const int64_t H = p.H, F = p.F;
-  BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F,
-         S::BN / 4};
+  BSrc b{p.wg + (int64_t)x.el * H * F + (int64_t)nt * HN, p.wu + (int64_t)x.el * H * F + (int64_t)nt * HN, F};
   tile_mainloop<S, true, false, RING>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
   // read by this launch's down tiles: device-coherent stores
   tile_store_rows<S, RING, true, true>(acc, p.h + (int64_t)x.row0 * F + (int64_t)nt * HN, F, x.m_valid);
@@ -167,7 +166,7 @@ __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit&
 template <class S, bool COH, int RING>
 __device__ __forceinline__ void down_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   const int64_t H = p.H, F = p.F;
-  BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H, 0};
+  BSrc b{p.wd + (int64_t)x.el * F * H + (int64_t)nt * S::BN, nullptr, H};
   tile_mainloop<S, false, COH, RING>(acc, p.h + (int64_t)x.row0 * F, F, x.m_valid, b, p.F);
   // read by pushes and folds of this launch: device-coherent stores
   tile_store_rows<S, RING, true>(acc, p.yg + (int64_t)x.row0 * H + (int64_t)nt * S::BN, H, x.m_valid);
@@ -478,6 +477,9 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
       !aligned16(y_grouped) || !aligned16(y))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
+  // the tiles address one expert's weights through 32-bit buffer offsets
+  if ((int64_t)s->hidden * s->ffn * 2 >= (int64_t(1) << 31))
+    return fail(KOS_ERR_SHAPE, "one expert's weight (hidden x ffn bf16) must be smaller than 2 GiB");
   // the grouped results are read back through 32-bit byte offsets
   if (grouped_cap * s->hidden * 2 >= (int64_t(1) << 31))
     return fail(KOS_ERR_SHAPE, "grouped_cap x hidden x 2 bytes must stay below 2 GiB");

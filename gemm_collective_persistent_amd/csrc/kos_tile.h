@@ -5,17 +5,20 @@
 // sub-tile of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16, the
 // accumulators held in registers for the whole K loop.
 //
-// Operands go straight from HBM/L2 into LDS (global_load_lds_dwordx4: each
-// lane's 16 bytes land at lds_base + 16*lane, so the lanes' global addresses
-// are chosen to realise the swizzled layouts below), through a ring of
-// STAGES buffers of BK = 32 k-columns, loads issued STAGES-1 stages ahead.
+// Operands go straight from HBM/L2 into LDS (buffer_load_dwordx4 ... lds
+// through raw buffer descriptors: each lane's 16 bytes land at lds_base +
+// 16*lane, so the lanes' source offsets are chosen to realise the swizzled
+// layouts below; a stage adds one scalar offset), through a ring of STAGES
+// buffers of BK = 32 k-columns, loads issued STAGES-1 stages ahead.
 //
 // LDS layouts per stage:
 //   A: BM rows x 4 chunks of 16 bytes (8 k values), chunk c of row m stored
 //      at position c ^ ((m >> 2) & 3).  The A operand of lane l (row l%32,
 //      8 k values from 8*(l/32)) is one ds_read_b128.
 //   B: BK rows (k) x BN/8 chunks, K x N as in HBM, chunk c of row k stored at
-//      position b_pos(c, k) (XOR or rotation by 4*(k%4) inside the row).  The B operand
+//      position b_pos(c, k) (XOR or rotation by 4*(k%4) inside the row); the
+//      SwiGLU tile stores a gate half and an up half, each BK rows of BN/16
+//      chunks laid out the same way.  The B operand
 //      (8 consecutive k of one column) is two ds_read_b64_tr_b16: in each
 //      16-lane group, lane j receives element j%4 of source lanes j/4 + 4v,
 //      v = 0..3, so source lane i = 4v + q points at row k0+v, columns
@@ -57,32 +60,26 @@ struct TileShape {
   static_assert(3 * LOADS <= 63, "vmcnt range");
 };
 
-// Where the B tile's columns come from.  Plain: BN consecutive columns of
-// one K x N matrix.  Dual (SwiGLU): tile columns in four segments of BN/4,
-// [gate s0 | up s0 | gate s1 | up s1], so each wave's 32x32 blocks j and
-// j + TN/2 hold the gate and up values of the same output column.
+// Where the B tile's columns come from: BN consecutive columns of one
+// K x N matrix (plain), or, for the SwiGLU tile (dual), BN/2 columns of the
+// gate matrix and the same BN/2 columns of the up matrix.  In the dual
+// tile each wave's 32x32 blocks j < TN/2 hold gate values and blocks
+// j + TN/2 the up values of the same output columns.
 struct BSrc {
   const uint16_t* p0;   // B[0][n0] of the (gate) matrix
   const uint16_t* p1;   // B[0][n0] of the up matrix (dual only)
   int64_t ld;           // row stride of B, in elements
-  int seg;              // BN/4 when dual, 0 when plain
-  __device__ __forceinline__ const uint16_t* col8(int nb) const {
-    const int c = nb * 8;
-    if (seg == 0) return p0 + c;
-    const int s = c / seg, w = c - s * seg;
-    return ((s & 1) ? p1 : p0) + (s >> 1) * seg + w;
-  }
 };
 
 __device__ __forceinline__ int a_swz(int m) { return (m >> 2) & 3; }
 
-// B rows: chunk c of row k sits at position b_pos(c, k).  Rows of a power
-// of two chunks XOR the chunk index with 4*(k%4); other widths rotate it by
-// 4*(k%4).  Both keep aligned 4-chunk groups together and send the four
-// rows read by one transpose read to different banks.
-template <class S>
+// B rows of W chunks (16 bytes each): chunk c of row k sits at position
+// b_pos<W>(c, k).  Power-of-two widths XOR the chunk index with 4*(k%4);
+// other widths rotate it by 4*(k%4).  Both keep aligned 4-chunk groups
+// together and send the four rows read by one transpose read to different
+// banks.
+template <int W>
 __device__ __forceinline__ int b_pos(int c, int k) {
-  constexpr int W = S::BROW_CHUNKS;
   if constexpr ((W & (W - 1)) == 0) {
     return c ^ ((4 * (k & 3)) & (W - 1));
   } else {
@@ -90,9 +87,8 @@ __device__ __forceinline__ int b_pos(int c, int k) {
     return p >= W ? p - W : p;
   }
 }
-template <class S>
+template <int W>
 __device__ __forceinline__ int b_chunk(int p, int k) {
-  constexpr int W = S::BROW_CHUNKS;
   if constexpr ((W & (W - 1)) == 0) {
     return p ^ ((4 * (k & 3)) & (W - 1));
   } else {
@@ -119,28 +115,44 @@ __device__ __forceinline__ WaveCtx wave_ctx() {
   return {lane, wave};
 }
 
-// Per-lane source offsets of this wave's direct loads, fixed for a tile:
-// every stage reads base + k0 (A) or base + k0*ld (B) plus these.
+// LDS layout of a stage's B part: plain, BK rows of BN/8 chunks; dual, the
+// gate half (BK rows of BN/16 chunks) then the up half, same layout.
+template <class S, bool DUAL>
+struct BLayout {
+  static constexpr int W = DUAL ? S::BROW_CHUNKS / 2 : S::BROW_CHUNKS;   // chunks per LDS row
+  static constexpr int ROW_BYTES = W * 16;
+  static constexpr int HALF_BYTES = S::B_BYTES / 2;
+  static_assert(!DUAL || (S::B_LOADS * 2 * 1024 == HALF_BYTES), "dual: waves 0-1 load the gate half, 2-3 the up half");
+};
+
+// This wave's direct loads, fixed for a tile: raw buffer descriptors of the
+// A rows and of its B matrix, and per-lane byte offsets; every stage adds
+// k0*2 (A) or k0*ldb*2 (B) as a scalar offset.  Offsets stay below 2^31
+// (the entry points check the operand extents).
 template <class S, bool DUAL, bool COH_A = false>
 struct LoadPlan {
-  const char* a_base;                          // uniform
-  const char* b_base;                          // uniform (plain B)
-  uint32_t a_off[S::A_LOADS];                  // bytes from a_base
-  uint32_t b_off[DUAL ? 1 : S::B_LOADS];       // bytes from b_base (plain B)
-  const char* b_ptr[DUAL ? S::B_LOADS : 1];    // per-lane pointers (dual B)
-  int64_t b_stride;                            // bytes per k row of B
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t a_off[S::A_LOADS];
+  uint32_t b_off[S::B_LOADS];
+  int b_stride;                                // bytes per k row of B
   int a_lds, b_lds;                            // this wave's bytes into a stage (uniform)
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform(base)), (short)0, 0x7fffffff,
+                                           kRawBufferWord3);
+}
 
 // A rows are clamped to m_valid-1: rows past the valid ones only feed
 // accumulator rows that are never stored.
 template <class S, bool DUAL, bool COH_A>
 __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const uint16_t* __restrict__ A, int64_t lda,
                                            int m_valid, const BSrc& b, const WaveCtx& w) {
+  using L = BLayout<S, DUAL>;
   const int lane = w.lane, wave = w.wave;
   P.a_lds = wave * S::A_LOADS * 1024;
   P.b_lds = S::A_BYTES + wave * S::B_LOADS * 1024;
-  P.a_base = reinterpret_cast<const char*>(A);
+  P.ra = raw_rsrc(A);
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
     const int slot = (wave * S::A_LOADS + i) * 64 + lane;   // 16-byte slot in the A stage
@@ -149,45 +161,37 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
     const int mr = m < m_valid ? m : m_valid - 1;
     P.a_off[i] = (uint32_t)(mr * lda * 2 + c * 16);
   }
-  P.b_stride = b.ld * 2;
-  P.b_base = reinterpret_cast<const char*>(b.p0);
+  P.b_stride = (int)(b.ld * 2);
+  // dual: waves 0-1 fill the gate half, 2-3 the up half
+  const bool up = DUAL && wave >= 2;
+  P.rb = raw_rsrc(up ? b.p1 : b.p0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
-    const int slot = (wave * S::B_LOADS + i) * 64 + lane;
-    const int k = slot / S::BROW_CHUNKS, p = slot % S::BROW_CHUNKS;
-    const int c = b_chunk<S>(p, k);
-    const char* g = reinterpret_cast<const char*>(b.col8(c)) + (int64_t)k * P.b_stride;
-    if constexpr (DUAL)
-      P.b_ptr[i] = g;
-    else
-      P.b_off[i] = (uint32_t)(g - P.b_base);
+    int slot = (wave * S::B_LOADS + i) * 64 + lane;
+    if (up) slot -= L::HALF_BYTES / 16;
+    const int k = slot / L::W, p = slot % L::W;
+    const int c = b_chunk<L::W>(p, k);
+    P.b_off[i] = (uint32_t)(k * P.b_stride + c * 16);
   }
 }
 
-// Issues this wave's direct loads of the stage starting at k0.
-// Cache policy of the A loads: device-coherent (sc1) when A is written by
-// other workgroups of the same launch.
+// Cache policy of loads: device-coherent (sc1) for A rows written by other
+// workgroups of the same launch.
 constexpr int kCpolDevice = 16;
 
+// Issues this wave's direct loads (buffer -> LDS) of the stage at k0.
 template <class S, bool DUAL, bool COH_A>
 __device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A>& P, int k0) {
-  const char* a = P.a_base + (int64_t)k0 * 2;
+  const int soa = k0 * 2;
+  const int sob = k0 * P.b_stride;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
-    __builtin_amdgcn_global_load_lds(a + P.a_off[i], (lds_void*)(lds_stage + P.a_lds + i * 1024), 16, 0,
-                                     COH_A ? kCpolDevice : 0);
-  char* bst = lds_stage + P.b_lds;
-  const int64_t kb = (int64_t)k0 * P.b_stride;
-  if constexpr (!DUAL) {
-    const char* bb = P.b_base + kb;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(P.ra, (lds_void*)(lds_stage + P.a_lds + i * 1024), 16, P.a_off[i], soa,
+                                             0, COH_A ? kCpolDevice : 0);
 #pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(bb + P.b_off[i], (lds_void*)(bst + i * 1024), 16, 0, 0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i)
-      __builtin_amdgcn_global_load_lds(P.b_ptr[i] + kb, (lds_void*)(bst + i * 1024), 16, 0, 0);
-  }
+  for (int i = 0; i < S::B_LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(P.rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i], sob,
+                                             0, 0);
 }
 
 // Operand fragments of one k16 step.
@@ -198,7 +202,7 @@ struct Frags {
 };
 
 // LDS -> registers for k16 step s (0 or 1) of a stage.
-template <class S>
+template <class S, bool DUAL>
 __device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, int s, const WaveCtx& w) {
   const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
@@ -213,14 +217,19 @@ __device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, in
   }
 #pragma unroll
   for (int j = 0; j < S::TN; ++j) {
-    const int n = wn * S::WN + j * 32 + 16 * (g & 1) + 4 * q;
+    using L = BLayout<S, DUAL>;
+    // plain: tile column n; dual: column n of the gate (j < TN/2) or up half
+    const bool up = DUAL && j >= S::TN / 2;
+    const int jb = up ? j - S::TN / 2 : j;
+    const int n = wn * (DUAL ? S::WN / 2 : S::WN) + jb * 32 + 16 * (g & 1) + 4 * q;
+    const char* bh = bst + (up ? L::HALF_BYTES : 0);
     s16x4 h[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = s * 16 + 8 * (g >> 1) + 4 * r + v;
-      const int c = b_pos<S>(n >> 3, k);
+      const int c = b_pos<L::W>(n >> 3, k);
       h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(bst + k * (S::BN * 2) + (c << 4) + ((n & 7) << 1)));
+          (lds_s16x4*)(bh + k * L::ROW_BYTES + (c << 4) + ((n & 7) << 1)));
     }
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 both = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -295,7 +304,7 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
   constexpr int NM = S::TM * S::TN, ND = S::TM + 2 * S::TN;
-  frag_load<S>(f1, cur, 1, w);
+  frag_load<S, DUAL>(f1, cur, 1, w);
   frag_mfma<S>(acc, f0);
   if (steady) sched_interleave<NM, ND, 0>();
   // stage kt+1 must have landed (all waves) and stage kt must be read by all
@@ -308,12 +317,12 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
   lds_barrier();
   if (steady) {
     stage_load<S, DUAL, COH_A>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
-    frag_load<S>(f0, nxt, 0, w);
+    frag_load<S, DUAL>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
     sched_interleave<NM, ND, S::LOADS>();
   } else {
     if (kt + ST < nk) stage_load<S, DUAL, COH_A>(cur, P, (kt + ST) * S::BK);
-    if (kt + 1 < nk) frag_load<S>(f0, nxt, 0, w);
+    if (kt + 1 < nk) frag_load<S, DUAL>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
   }
 #endif
@@ -352,7 +361,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
     KOS_WAITCNT(3 * S::LOADS, 0);
     lds_barrier();
     Frags<S> f0, f1;
-    frag_load<S>(f0, r0, 0, w);
+    frag_load<S, DUAL>(f0, r0, 0, w);
     for (int kt = 0; kt < nk; kt += ST) {
       k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt, nk, P, r0, r1, w);
       k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
@@ -375,7 +384,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   }
   lds_barrier();
   Frags<S> f0, f1;
-  frag_load<S>(f0, r0, 0, w);
+  frag_load<S, DUAL>(f0, r0, 0, w);
   for (int kt = 0; kt < nk; kt += ST) {
     k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt, nk, P, r0, r1, w);
     if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
