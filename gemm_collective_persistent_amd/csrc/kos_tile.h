@@ -418,8 +418,24 @@ __device__ __forceinline__ void tile_foreach4(const f32x16 (&acc)[S::TM][S::TN],
       }
 }
 
-// SwiGLU of a gate and an up value: silu(g) * u = g / (1 + e^-g) * u, fp32.
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SwiGLU of a gate and an up value: silu(g) * u = g / (1 + e^-g) * u, fp32,
+// with the hardware exponential and reciprocal (about 1 ulp each; the result
+// is rounded to bf16 next).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Ring buffer i (0..3) as an LDS pointer; i is uniform (scalar selects).
+template <int RING>
+__device__ __forceinline__ lds_char* ring_lds(int i) {
+  lds_char* b0 = (lds_char*)ring<RING, 0>();
+  lds_char* b1 = (lds_char*)ring<RING, 1>();
+  lds_char* b2 = (lds_char*)ring<RING, 2>();
+  lds_char* b3 = (lds_char*)ring<RING, 3>();
+  return i == 0 ? b0 : i == 1 ? b1 : i == 2 ? b2 : b3;
+}
 
 // Stores the tile as bf16 rows [0, m_valid) of dst (row stride ld elements)
 // through the LDS ring: every lane writes its four-column pieces into LDS,
@@ -438,9 +454,11 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
   constexpr int ROW_BYTES = OW * 2;
   constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
   constexpr int ROWS_PER_RING = RING / ROW_BYTES;
+  constexpr int ROWS_PER_PASS = S::NT / CPR;
   static_assert(RING % ROW_BYTES == 0 && 4 * ROWS_PER_RING >= S::BM, "the tile must fit the ring");
   static_assert((CPR & (CPR - 1)) == 0 && S::NT % CPR == 0, "power-of-two chunks per row");
-  char* rb[4] = {ring<RING, 0>(), ring<RING, 1>(), ring<RING, 2>(), ring<RING, 3>()};
+  static_assert(ROWS_PER_RING % 32 == 0 && ROWS_PER_RING % ROWS_PER_PASS == 0,
+                "32-row groups and store passes stay inside one ring buffer");
   const WaveCtx w = wave_ctx();
   const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
@@ -448,8 +466,9 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
   // rows one write instruction touches over the banks)
 #pragma unroll
   for (int i = 0; i < S::TM; ++i) {
-    const int row = wm * S::WM + i * 32 + (lane & 31);
-    char* base = rb[row / ROWS_PER_RING] + (row % ROWS_PER_RING) * ROW_BYTES;
+    const int row0 = wm * S::WM + i * 32;          // uniform: the 32 rows share a ring buffer
+    const int row = row0 + (lane & 31);
+    lds_char* base = ring_lds<RING>(row0 / ROWS_PER_RING) + (row % ROWS_PER_RING) * ROW_BYTES;
 #pragma unroll
     for (int j = 0; j < OJ; ++j)
 #pragma unroll
@@ -460,26 +479,45 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
-        *reinterpret_cast<u32x2*>(base + chunk * 16 + (col & 7) * 2) = pack4_bf16(v);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col & 7) * 2) =
+            pack4_bf16(v);
+        // one 32x32 block at a time: keeps the accumulator reads from being
+        // hoisted together (they would need a VGPR each)
+        if (g == 3) __builtin_amdgcn_sched_barrier(0);
       }
   }
   KOS_WAITCNT(0, 0);
   lds_barrier();
   const DevBuf d(dst);
-  constexpr int ROWS_PER_PASS = S::NT / CPR;
   const int t = wave * 64 + lane;
   const int c = t % CPR;
-#pragma unroll 4
-  for (int r0 = 0; r0 < S::BM; r0 += ROWS_PER_PASS) {
-    const int row = r0 + t / CPR;
-    if (row >= m_valid) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(rb[row / ROWS_PER_RING] + (row % ROWS_PER_RING) * ROW_BYTES +
-                                                    ((c ^ (row & (CPR - 1))) * 16));
-    const int64_t off = ((int64_t)row * ld + c * 8) * 2;
-    if constexpr (COH)
-      d.st128((uint32_t)off, v);
-    else
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + off) = v;
+  // passes in batches of 8: the batch's LDS reads, then its stores (rows
+  // past m_valid predicated off); the scheduling barrier keeps a batch's
+  // registers from being hoisted into the previous one
+  constexpr int PASSES = S::BM / ROWS_PER_PASS, BATCH = PASSES < 8 ? PASSES : 8;
+  static_assert(PASSES % BATCH == 0, "whole batches");
+#pragma unroll
+  for (int b0 = 0; b0 < PASSES; b0 += BATCH) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int r0 = (b0 + q) * ROWS_PER_PASS;
+      const int row = r0 + t / CPR;
+      v[q] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          ring_lds<RING>(r0 / ROWS_PER_RING) + (row % ROWS_PER_RING) * ROW_BYTES + ((c ^ (row & (CPR - 1))) * 16));
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int row = (b0 + q) * ROWS_PER_PASS + t / CPR;
+      const int64_t off = ((int64_t)row * ld + c * 8) * 2;
+      if (row < m_valid) {
+        if constexpr (COH)
+          d.st128((uint32_t)off, v[q]);
+        else
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + off) = v[q];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
