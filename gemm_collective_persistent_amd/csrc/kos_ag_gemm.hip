@@ -46,9 +46,15 @@ struct AgParams {
 };
 
 template <class S>
-__global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams p) {
+__global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
   constexpr int BM = S::BM, BN = S::BN;
   __shared__ WgSlots slots;
+  // The parameter block lives in LDS: each role reads the fields it needs
+  // when it needs them instead of pinning them all in scalar registers.
+  __shared__ AgParams ps;
+  if (threadIdx.x == 0) ps = args;
+  __syncthreads();
+  const AgParams& p = ps;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
   Tracer tr(p.trace);

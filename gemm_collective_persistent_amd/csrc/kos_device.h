@@ -187,6 +187,9 @@ struct DevBuf {
   __device__ __forceinline__ u32x4 ld128(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
   }
+  __device__ __forceinline__ void st16(uint32_t off, uint16_t v) const {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kCpolSc1);
+  }
 };
 
 // Non-blocking readiness test by thread 0, broadcast (no fence: callers that

@@ -109,9 +109,15 @@ __device__ __forceinline__ void reduce_entry(const RsParams& p, int64_t r0, int 
 }
 
 template <class S>
-__global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams p) {
+__global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
   constexpr int BM = S::BM, BN = S::BN;
   __shared__ WgSlots slots;
+  // The parameter block lives in LDS: each role reads the fields it needs
+  // when it needs them instead of pinning them all in scalar registers.
+  __shared__ RsParams ps;
+  if (threadIdx.x == 0) ps = args;
+  __syncthreads();
+  const RsParams& p = ps;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
   Tracer tr(p.trace);

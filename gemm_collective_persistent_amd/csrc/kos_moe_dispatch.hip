@@ -67,84 +67,118 @@ struct DispatchLds {
   int32_t meta_loaded;
 };
 
-// Wave-wide argmax of (value, index) pairs: larger value wins, equal values
-// go to the lower index; idx == INT_MAX marks "no candidate".
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+// Order-preserving key of a (logit, expert) candidate: larger logit first,
+// equal logits (+0 and -0 included) to the lower expert index.  Key 0 means
+// "no candidate" (every real key is larger).
+__device__ __forceinline__ uint64_t cand_key(float v, int e) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);   // -0 -> +0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __builtin_bit_cast(float, (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+// One step of a wave-wide maximum over 64-bit keys through DPP lane moves;
+// lanes outside ROW_MASK keep their own key.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t key_max_dpp(uint64_t k) {
+  const int lo = (int)(uint32_t)k, hi = (int)(uint32_t)(k >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > k ? o : k;
+}
+
+// Largest key of the wave, in every lane: within quads (swap 1, swap 2),
+// within rows of 16 (half-row mirror, row mirror), then across rows
+// (broadcast of lane 15 into rows 1 and 3, of lane 31 into rows 2 and 3),
+// leaving the maximum in lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = key_max_dpp<0xB1, 0xF>(k);    // quad_perm [1,0,3,2]
+  k = key_max_dpp<0x4E, 0xF>(k);    // quad_perm [2,3,0,1]
+  k = key_max_dpp<0x141, 0xF>(k);   // row_half_mirror
+  k = key_max_dpp<0x140, 0xF>(k);   // row_mirror
+  k = key_max_dpp<0x142, 0xA>(k);   // row_bcast:15
+  k = key_max_dpp<0x143, 0xC>(k);   // row_bcast:31
+  return readlane_u64(k, 63);
+}
+
+// Sum over the wave (every lane gets it).
+__device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(i, off);
-    const bool take = oi != INT_MAX && (i == INT_MAX || ov > v || (ov == v && oi < i));
-    if (take) {
-      v = ov;
-      i = oi;
-    }
-  }
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
 // Router entry `b4`: tokens [16*b4, 16*b4 + 16) = quarter b4 % 4 of block b4 / 4.
+// Each wave takes every 4th token; all its tokens' logits are loaded
+// before the first selection.  NV: 64-logit slots per lane (E <= 64*NV).
+// Lane j keeps the j-th selection of the token being routed.
+template <int NV>
 __device__ __forceinline__ void route_entry(const DispatchParams& p, int b4, DispatchLds& L) {
   constexpr int QT = kMoeTokBlock / 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  constexpr int TPW = QT / 4;                 // tokens per wave (4 waves)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.m[e] = 0u;
   __syncthreads();
-  const int nv = (p.E + 63) / 64;
-  for (int tl = wave; tl < QT; tl += nw) {
+  float v[TPW][NV];
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int t = b4 * QT + wave + 4 * x;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      v[x][i] = (t < p.T && e < p.E) ? p.logits[(int64_t)t * p.E + e] : 0.f;
+    }
+  }
+  const int k = p.k;
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int tl = wave + 4 * x;
     const int t = b4 * QT + tl;
     if (t >= p.T) break;
-    float v[kMoeMaxExperts / 64];
     uint32_t taken = 0;
 #pragma unroll
-    for (int i = 0; i < kMoeMaxExperts / 64; ++i) {
-      if (i < nv) {
-        const int e = lane + 64 * i;
-        if (e < p.E) v[i] = p.logits[(int64_t)t * p.E + e];
-        else taken |= 1u << i;
-      }
-    }
-    float sel_v[kMoeMaxTopk];
-    int sel_i[kMoeMaxTopk];
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i >= p.E) taken |= 1u << i;
+    float my_v = 0.f;   // selection `lane` (lanes < k)
+    int my_i = 0;
+    for (int j = 0; j < k; ++j) {
+      // this lane's best remaining candidate, then the wave's
+      uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kMoeMaxTopk; ++j) {
-      if (j < p.k) {
-        float bv = 0.f;
-        int bi = INT_MAX;
-#pragma unroll
-        for (int i = 0; i < kMoeMaxExperts / 64; ++i) {
-          if (i < nv && !((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
-            bv = v[i];
-            bi = lane + 64 * i;
-          }
-        }
-        wave_argmax(bv, bi);
-        sel_v[j] = bv;
-        sel_i[j] = bi;
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      for (int i = 0; i < NV; ++i) {
+        const uint64_t kk = ((taken >> i) & 1u) ? 0 : cand_key(v[x][i], lane + 64 * i);
+        best = kk > best ? kk : best;
       }
+      const uint64_t win = wave_max_key(best);
+      const int wi = key_index(win);
+      if (lane == j) {
+        my_v = key_value(win);
+        my_i = wi;
+      }
+      if ((wi & 63) == lane) taken |= 1u << (wi >> 6);
     }
     // softmax over the k selected logits (largest first)
-    float z[kMoeMaxTopk];
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMoeMaxTopk; ++j)
-      if (j < p.k) {
-        z[j] = expf(sel_v[j] - sel_v[0]);
-        s += z[j];
-      }
-    const float inv = 1.0f / s;
-#pragma unroll
-    for (int j = 0; j < kMoeMaxTopk; ++j)
-      if (j < p.k && lane == j) {
-        p.topk_idx[(int64_t)t * p.k + j] = sel_i[j];
-        p.topk_w[(int64_t)t * p.k + j] = z[j] * inv;
-        atomicOr(&L.m[sel_i[j]], 1u << tl);
-      }
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
+    const float z = lane < k ? expf(my_v - v0) : 0.f;
+    const float w = z / wave_sum(z);
+    if (lane < k) {
+      // read by other workgroups of this launch: device-coherent stores
+      st_dev_b32(&p.topk_idx[(int64_t)t * k + lane], (uint32_t)my_i);
+      st_dev_b32(&p.topk_w[(int64_t)t * k + lane], __builtin_bit_cast(uint32_t, w));
+      atomicOr(&L.m[my_i], 1u << tl);
+    }
   }
   __syncthreads();
-  // quarter q of the block's 64-bit mask: its 16-bit lane q (little endian)
+  // quarter q of the block's 64-bit mask: its 16-bit lane q (little endian),
+  // stored device-coherent (the scan runs in another workgroup)
   const int b = b4 >> 2, q = b4 & 3;
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
-    reinterpret_cast<uint16_t*>(&p.masks[(int64_t)b * p.E + e])[q] = (uint16_t)L.m[e];
+  const DevBuf mb(p.masks + (int64_t)b * p.E);
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) mb.st16((uint32_t)(e * 8 + q * 2), (uint16_t)L.m[e]);
 }
 
 // Exclusive prefix sums of in[0, n) into out[0, n], out[n] = total; n <=
@@ -258,9 +292,15 @@ __device__ __forceinline__ void load_meta(const DispatchParams& p, DispatchLds& 
 }
 
 template <int NT>
-__global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
+__global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args) {
   __shared__ DispatchLds L;
   __shared__ WgSlots slots;
+  // The parameter block lives in LDS: each role reads the fields it needs
+  // when it needs them instead of pinning them all in scalar registers.
+  __shared__ DispatchParams ps;
+  if (threadIdx.x == 0) ps = args;
+  __syncthreads();
+  const DispatchParams& p = ps;
   WsHeader* h = p.ws;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NT / 64;
   Tracer tr(p.trace);
@@ -304,11 +344,15 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams p) {
       const uint32_t b4 = wg_claim(&h->head[0], h, &slots);
       if (b4 >= n_route) break;
       uint64_t t0 = tr.now();
-      route_entry(p, (int)b4, L);
-      fence_release();
+      if (p.E <= 64) route_entry<1>(p, (int)b4, L);
+      else if (p.E <= 128) route_entry<2>(p, (int)b4, L);
+      else if (p.E <= 256) route_entry<4>(p, (int)b4, L);
+      else if (p.E <= 512) route_entry<8>(p, (int)b4, L);
+      else route_entry<16>(p, (int)b4, L);
+      // this entry's device-coherent stores have completed: count it
+      __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
       __syncthreads();
-      if (threadIdx.x == 0)
-        slots.aux[0] = __hip_atomic_fetch_add(&p.ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) slots.aux[0] = add_relaxed(&p.ctr[0], 1u);
       __syncthreads();
       tr.put(KOS_TR_ROUTE, b4, t0);
       if (slots.aux[0] == n_route - 1) {   // the last entry: scan
