@@ -146,14 +146,16 @@ def measured_traffic(op: str, workload: str):
 
 
 def copy_calibration(torch):
-    """Three plain device copies of 1 GiB: the reference that scales the HBM
-    byte counters (FETCH_SIZE, WRITE_SIZE) read under rocprofv3."""
-    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    """Three plain elementwise passes over 1 GiB of bf16 (dst = -src: 1 GiB
+    read, 1 GiB written, 16-byte vector accesses like the kernels'): the
+    reference that scales the HBM byte counters (FETCH_SIZE, WRITE_SIZE) read
+    under rocprofv3."""
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    return {"copy_bytes": 1 << 30, "copies": 3}
+    return {"copy_bytes": 1 << 30, "copies": 3, "kernel": "neg"}
 
 
 class CacheFlush:
