@@ -84,9 +84,9 @@ def build_inputs(torch, KI, kos, moe_shape):
     return inp
 
 
-def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0):
+def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=False):
     from gemm_collective_persistent_amd.api import moe_shape as mk_shape
-    o = kos.opts(mode=mode, n_movers=n_movers, grid=grid)
+    o = kos.opts(mode=mode, n_movers=n_movers, grid=grid, trace=trace)
     ag, rs, m = inp["ag"], inp["rs"], inp["moe"]
     s = moe_shape
     shp = mk_shape(s.world, 0, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
@@ -98,7 +98,7 @@ def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0):
         kos.gemm_rs(rs["a"], rs["w"], rs["peer_slices"], rs["partial"], rs["y"], 7, ws, o)
 
     def op_dispatch():
-        od = o if mode != 1 else kos.opts(mode=0, grid=grid)
+        od = o if mode != 1 else kos.opts(mode=0, grid=grid, trace=trace)
         kos.moe_dispatch(shp, m["x"], m["logits"], m["peer_send"], m["peer_counts"], m["idx"], m["w"],
                          m["counts"], m["perm"], m["send"], m["grouped"], m["goff"], m["row_src"], ws, od)
 
@@ -189,6 +189,78 @@ def time_ops(torch, ops, reps, ws, flush):
     ws.status()
     per = [sum(ev[r][2 * i].elapsed_time(ev[r][2 * i + 1]) for r in range(reps)) / reps for i in range(n)]
     return per, wall
+
+
+def idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush, modes, base):
+    """Idle-CU fraction (share of workgroup-time outside pieces of work, over
+    the kernel's span; kos_opts.trace) of each op, per mode.  The fixed-split
+    baseline is traced at its best crew from `base`."""
+    from gemm_collective_persistent_amd.timeline import summarize
+    grid = int(kos.lib.kos_device_cu_count())
+    names = ["ag_gemm", "gemm_rs", "moe_dispatch", "moe_combine"]
+    out = {}
+    for label, mc in modes.items():
+        if mc is None:   # best fixed crew per op
+            best = {n: min((k for k in base if k.startswith("fixed")), key=lambda k: base[k][n]) for n in names}
+        out[label] = {}
+        for n in names:
+            if mc is None:
+                mode, crew = 1, int(best[n].replace("fixed_crew", ""))
+            else:
+                mode, crew = mc
+            ops = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew, trace=True))
+            flush()
+            ops[n]()
+            ws.status()
+            out[label][n] = summarize(ws.trace(grid))["idle_frac"]
+    return out
+
+
+def cu_subset_gemm(torch, kos, inp, ws, reps, flush):
+    """Plain GEMM throughput on 224 of the 256 compute units relative to all
+    256, on the QKV GEMM (4096 x 8192 x 3072: exactly 256 tiles, so 224
+    workgroups need a second round) and on a large square GEMM (8192^3:
+    1024 tiles) -- the explainer's worked example reports about 93%."""
+    res = {}
+    ag = inp["ag"]
+    big = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    cases = {"qkv_4096x8192x3072": (ag["g"], ag["w"]), "square_8192": (big, big)}
+    for name, (a, w) in cases.items():
+        c = torch.empty((a.shape[0], w.shape[1]), dtype=torch.bfloat16, device="cuda")
+        t = {}
+        for grid in (256, 224):
+            o = kos.opts(mode=2, grid=grid)
+            fn = lambda: kos.ag_gemm(a, [None], w, a, c, 0, ws, o)  # noqa: E731
+            fn()
+            t[grid] = time_ops(torch, [("gemm", fn)], reps, ws, flush)[0][0]
+        res[name] = {"ms_256": round(t[256], 4), "ms_224": round(t[224], 4),
+                     "throughput_224_vs_256": round(t[256] / t[224], 3)}
+    del big
+    return res
+
+
+def ag_pinned(torch, kos, KI, inp, ws, reps, flush):
+    """The QKV all-gather+GEMM with the 7 peer shards in pinned,
+    device-mapped host memory (a PCIe link instead of HBM): fused, unfused
+    and fixed-crew times, the link rate implied by the unfused copy, and the
+    overlap (t_unfused - t_fused) / min(t_copy, t_gemm)."""
+    ag = inp["ag"]
+    peers = [None if t is None else t.cpu().pin_memory() for t in ag["a_peers"]]
+    gemm_only = lambda: kos.ag_gemm(ag["g"], [None], ag["w"], ag["g"], ag["c"], 0, ws,  # noqa: E731
+                                    kos.opts(mode=2))
+    gemm_only()
+    t_gemm = time_ops(torch, [("gemm", gemm_only)], reps, ws, flush)[0][0]
+    t = {}
+    for label, mode, crew in (("fused", 0, -1), ("unfused", 2, -1), ("fixed_crew8", 1, 8), ("fixed_crew16", 1, 16)):
+        o = kos.opts(mode=mode, n_movers=crew, peer_link=1)
+        fn = lambda: kos.ag_gemm(ag["a_local"], peers, ag["w"], ag["g"], ag["c"], 0, ws, o)  # noqa: E731
+        fn()
+        t[label] = time_ops(torch, [("ag", fn)], max(2, reps // 2), ws, flush)[0][0]
+    t_copy = max(t["unfused"] - t_gemm, 1e-6)
+    moved = sum(p.numel() * 2 for p in peers if p is not None)
+    return {"ms": {k: round(v, 4) for k, v in t.items()}, "gemm_alone_ms": round(t_gemm, 4),
+            "link_gb_s": round(moved / (t_copy * 1e-3) / 1e9, 1),
+            "overlap": round((t["unfused"] - t["fused"]) / min(t_copy, t_gemm), 3)}
 
 
 def cpu_baseline(inp, moe_shape, budget_s=12.0):
@@ -318,19 +390,15 @@ def main():
         extra["speedup_vs_unfused"] = {n: round(base["unfused"][n] / t, 3) for n, t in zip(names, per)}
         extra["speedup_vs_best_fixed"] = {n: round(fixed[n] / t, 3) for n, t in zip(names, per)
                                           if n != "moe_dispatch"}
-        # GEMM throughput on 224 of 256 CUs (plain GEMM: the unfused GEMM launch at world 1)
-        ag = inp["ag"]
-        a_all = ag["g"]
-        cfull = torch.empty((a_all.shape[0], ag["w"].shape[1]), dtype=torch.bfloat16, device="cuda")
-        res = {}
-        for grid in (256, 224):
-            o = kos.opts(mode=2, grid=grid)
-            fn = lambda: kos.ag_gemm(a_all, [None], ag["w"], a_all, cfull, 0, ws, o)  # noqa: E731
-            fn()
-            t, _ = time_ops(torch, [("gemm", fn)], reps, ws, flush)
-            res[grid] = t[0]
-        extra["gemm_224_vs_256_cu_throughput"] = round(res[256] / res[224], 3)
-        extra["gemm_256cu_ms"] = round(res[256], 4)
+        # idle-CU fraction of each op in each mode (one traced, untimed call)
+        extra["idle_cu_fraction"] = idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush,
+                                                   {"fused": (0, -1), "unfused": (2, -1),
+                                                    "fixed_best": None}, base)
+        # GEMM throughput on 224 of 256 CUs: the explainer's worked example
+        # (plain GEMM = the unfused GEMM launch at world 1)
+        extra["gemm_224_of_256_cus"] = cu_subset_gemm(torch, kos, inp, ws, reps, flush)
+        # all-gather+GEMM with the peers' shards in pinned host memory (PCIe)
+        extra["ag_gemm_pinned_host_peers"] = ag_pinned(torch, kos, KI, inp, ws, reps, flush)
     if not args.no_cpu:
         cpu = cpu_baseline(inp, moe_shape)
     else:
