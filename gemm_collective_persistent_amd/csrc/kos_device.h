@@ -150,6 +150,15 @@ __device__ __forceinline__ void st_dev_b64(void* p, u32x2 v) {   // p 8-byte ali
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Device-scope (sc1) loads of data written by other workgroups of the same
+// launch (compiler-visible atomics; no cache invalidation needed).
+__device__ __forceinline__ uint32_t ld_dev_b32(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_b64(const void* p) {   // p 8-byte aligned
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // A pointer that is the same in every lane of the wave, moved to scalar
 // registers (the caller guarantees the uniformity).
 template <class T>

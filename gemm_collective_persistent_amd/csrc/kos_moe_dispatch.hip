@@ -11,14 +11,15 @@
 //                expert, the 16-bit quarter of the block's 64-bit mask of
 //                tokens routed to it (order-free, so the result is
 //                deterministic).
-//   counter[0]   routed entries.  The workgroup that routes the last one
-//                runs the scan: per-expert counts, the exclusive scan over
-//                experts (packed offsets), per-(block, expert) bases, the
-//                grouped offsets of our local experts, capacity checks; then
-//                sets counter[1].
+//   counter[0]   routed entries.
+//   head[2]      scan entries, one per expert (once counter[0] is
+//                complete): the expert's count and, per block, the pairs of
+//                that expert in earlier blocks; counter[1] counts them.
+//                Every mover then scans the counts itself (packed offsets,
+//                grouped offsets of our local experts, capacity checks).
 //   head[1]      mover entries (after counter[1]): a quarter block of our
-//                tokens -- pair (t, j) of expert e lands at base[block][e] +
-//                popcount(mask & tokens before t); the row goes to the send
+//                tokens -- pair (t, j) of expert e lands at off[e] +
+//                base[block][e] + popcount(mask & tokens before t); the row goes to the send
 //                buffer of e's rank, or straight into the grouped input when
 //                e is local -- then 64-row chunks of each peer's rows, pulled
 //                into the grouped input.
@@ -50,8 +51,7 @@ struct DispatchParams {
   kos_trace_rec* trace;          // null: tracing off
   uint32_t* ctr;                 // [0] routed blocks, [1] scan done
   unsigned long long* masks;     // scratch [nblk, E]
-  int32_t* base;                 // scratch [nblk, E]: histogram, then bases
-  int32_t* off;                  // scratch [E + 1]
+  int32_t* base;                 // scratch [nblk, E]: pairs of expert e in blocks before b
 };
 
 struct DispatchLds {
@@ -64,7 +64,6 @@ struct DispatchLds {
   int32_t before[8][kMoeMaxLocal];      // rows of sources < p, per local expert
   int32_t go[kMoeMaxLocal + 1];         // grouped offsets
   int32_t chunk_base[9];                // first peer entry of each source
-  int32_t meta_loaded;
 };
 
 // Order-preserving key of a (logit, expert) candidate: larger logit first,
@@ -215,39 +214,40 @@ __device__ inline void block_exclusive_scan(const int32_t* in, int32_t* out, int
   __syncthreads();
 }
 
-// Run once, by the workgroup that routed the last entry.  Returns false
-// (for every thread) when a capacity would overflow; the error is recorded
-// and the movers are never released.
-__device__ __forceinline__ bool scan(const DispatchParams& p, DispatchLds& L, WgSlots* slots) {
-  constexpr int B = 16;   // masks loaded per batch per thread
-  // per-expert counts: popcounts of the block masks
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
-    int run = 0;
-    for (int b0 = 0; b0 < p.nblk; b0 += B) {
-      unsigned long long m[B];
-#pragma unroll
-      for (int u = 0; u < B; ++u) m[u] = b0 + u < p.nblk ? p.masks[(int64_t)(b0 + u) * p.E + e] : 0ull;
-#pragma unroll
-      for (int u = 0; u < B; ++u) run += __popcll(m[u]);
-    }
-    p.counts[e] = run;
-    L.cnt[e] = run;
-  }
+// Scan entry: expert e, once every router entry is counted.  Its block
+// masks -> per-block counts -> exclusive prefix over the blocks:
+// base[b][e] = pairs of e in blocks before b (relative to e's packed
+// offset), counts[e] = total.  Stored device-coherent (movers of this launch
+// read them after counter[1]).  nblk <= 1024.
+__device__ __forceinline__ void scan_expert(const DispatchParams& p, DispatchLds& L, int e) {
+  for (int b = threadIdx.x; b < p.nblk; b += blockDim.x)
+    L.cnt[b] = __popcll(ld_dev_b64(&p.masks[(int64_t)b * p.E + e]));
+  __syncthreads();
+  block_exclusive_scan(L.cnt, L.off, p.nblk, L.wave_tot);
+  for (int b = threadIdx.x; b < p.nblk; b += blockDim.x) st_dev_b32(&p.base[(int64_t)b * p.E + e], (uint32_t)L.off[b]);
+  if (threadIdx.x == 0) st_dev_b32(&p.counts[e], (uint32_t)L.off[p.nblk]);
+  __syncthreads();
+}
+
+// After counter[1] (every expert scanned): the packed offsets (exclusive
+// scan of the counts), our local experts' grouped offsets and the
+// per-source prefixes, in LDS; every mover computes the same values.
+// Capacity checks: an overflow records KOS_ERR_CAPACITY and returns false
+// (every thread).  `writer` stores the grouped offsets (an output).
+__device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& L, WgSlots* slots, bool writer) {
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) L.cnt[e] = (int32_t)ld_dev_b32(&p.counts[e]);
   __syncthreads();
   block_exclusive_scan(L.cnt, L.off, p.E, L.wave_tot);
-  for (int e = threadIdx.x; e <= p.E; e += blockDim.x) p.off[e] = L.off[e];
-  // base of (block, expert): packed offset of the expert + its tokens in earlier blocks
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
-    int run = L.off[e];
-    for (int b0 = 0; b0 < p.nblk; b0 += B) {
-      unsigned long long m[B];
-#pragma unroll
-      for (int u = 0; u < B; ++u) m[u] = b0 + u < p.nblk ? p.masks[(int64_t)(b0 + u) * p.E + e] : 0ull;
-#pragma unroll
-      for (int u = 0; u < B; ++u) {
-        if (b0 + u < p.nblk) p.base[(int64_t)(b0 + u) * p.E + e] = run;
-        run += __popcll(m[u]);
-      }
+  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
+    const int ge = p.rank * p.E_loc + el;
+    L.pc[p.rank][el] = L.off[ge + 1] - L.off[ge];
+  }
+  __syncthreads();
+  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
+    int run = 0;
+    for (int q = 0; q < p.world; ++q) {
+      L.before[q][el] = run;
+      run += L.pc[q][el];
     }
   }
   if (threadIdx.x == 0) {
@@ -259,36 +259,18 @@ __device__ __forceinline__ bool scan(const DispatchParams& p, DispatchLds& L, Wg
     }
     int64_t go = 0;
     for (int el = 0; el < p.E_loc; ++el) {
-      p.grouped_offsets[el] = (int32_t)go;
-      const int ge = p.rank * p.E_loc + el;
-      go += L.off[ge + 1] - L.off[ge];
-      for (int q = 0; q < p.world; ++q)
-        if (q != p.rank) go += L.pc[q][el];
+      L.go[el] = (int32_t)go;
+      for (int q = 0; q < p.world; ++q) go += L.pc[q][el];
     }
-    p.grouped_offsets[p.E_loc] = (int32_t)go;
+    L.go[p.E_loc] = (int32_t)go;
     if (go > p.grouped_cap) over = true;
     if (over) raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)go);
     slots->ok = over ? 0 : 1;
   }
   __syncthreads();
+  if (writer && slots->ok)
+    for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) p.grouped_offsets[el] = L.go[el];
   return slots->ok != 0;
-}
-
-// Loads the scan's results into LDS (after counter[1]).
-__device__ __forceinline__ void load_meta(const DispatchParams& p, DispatchLds& L) {
-  for (int e = threadIdx.x; e <= p.E; e += blockDim.x) L.off[e] = p.off[e];
-  for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) L.go[el] = p.grouped_offsets[el];
-  __syncthreads();
-  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
-    const int ge = p.rank * p.E_loc + el;
-    L.pc[p.rank][el] = L.off[ge + 1] - L.off[ge];
-    int run = 0;
-    for (int q = 0; q < p.world; ++q) {
-      L.before[q][el] = run;
-      run += L.pc[q][el];
-    }
-  }
-  __syncthreads();
 }
 
 template <int NT>
@@ -332,53 +314,46 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
   }
   __syncthreads();
 
-  // ---- router role ------------------------------------------------------
+  // ---- router role, then one scan entry per expert ---------------------
   if (p.do_route) {
-    if (p.nblk == 0 && ticket == 0) {   // no tokens: the first arrival scans
-      const uint64_t t0 = tr.now();
-      if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
-      tr.put(KOS_TR_SCAN, 0, t0);
-    }
     const uint32_t n_route = (uint32_t)p.nblk * 4;
     for (;;) {
       const uint32_t b4 = wg_claim(&h->head[0], h, &slots);
       if (b4 >= n_route) break;
-      uint64_t t0 = tr.now();
+      const uint64_t t0 = tr.now();
       if (p.E <= 64) route_entry<1>(p, (int)b4, L);
       else if (p.E <= 128) route_entry<2>(p, (int)b4, L);
       else if (p.E <= 256) route_entry<4>(p, (int)b4, L);
       else if (p.E <= 512) route_entry<8>(p, (int)b4, L);
       else route_entry<16>(p, (int)b4, L);
       // this entry's device-coherent stores have completed: count it
-      __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0)
-      __syncthreads();
-      if (threadIdx.x == 0) slots.aux[0] = add_relaxed(&p.ctr[0], 1u);
-      __syncthreads();
+      wg_publish(&p.ctr[0], 1u);
       tr.put(KOS_TR_ROUTE, b4, t0);
-      if (slots.aux[0] == n_route - 1) {   // the last entry: scan
-        t0 = tr.now();
-        fence_acquire();
-        if (scan(p, L, &slots)) wg_signal(&p.ctr[1], 1u);
-        tr.put(KOS_TR_SCAN, 0, t0);
-      }
+    }
+    for (;;) {
+      const uint32_t e = wg_claim(&h->head[2], h, &slots);
+      if (e >= (uint32_t)p.E) break;
+      uint64_t t0 = tr.now();
+      if (!wg_observe(&p.ctr[0], n_route, h, p.spin_limit, 0xFFFE0000u | e, &slots)) break;
+      tr.put(KOS_TR_WAIT, e, t0);
+      t0 = tr.now();
+      scan_expert(p, L, (int)e);
+      wg_publish(&p.ctr[1], 1u);
+      tr.put(KOS_TR_SCAN, e, t0);
     }
   }
 
   // ---- mover role -------------------------------------------------------
   if (p.do_copy) {
     const int n_entries = L.chunk_base[p.world];
-    bool have_meta = false;
+    const uint64_t tw = tr.now();
+    bool go_on = !p.wait_scan || wg_observe(&p.ctr[1], (uint32_t)p.E, h, p.spin_limit, 0xFFFF0000u, &slots);
+    if (go_on) go_on = load_meta(p, L, &slots, ticket == 0);
+    tr.put(KOS_TR_WAIT, 0xFFFFFF, tw);
     for (;;) {
+      if (!go_on) break;
       const uint32_t i = wg_claim(&h->head[1], h, &slots);
       if (i >= (uint32_t)n_entries) break;
-      if (!have_meta) {
-        const uint64_t tw = tr.now();
-        if (p.wait_scan && !wg_wait(&p.ctr[1], 1u, h, p.spin_limit, 0xFFFF0000u, &slots)) break;
-        fence_acquire();
-        load_meta(p, L);
-        have_meta = true;
-        tr.put(KOS_TR_WAIT, i, tw);
-      }
       const uint64_t t0 = tr.now();
       const int H = p.H;
       const int row_bytes = H * 2;
@@ -393,9 +368,9 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
 #pragma unroll
           for (int j = 0; j < kMoeMaxTopk; ++j) {
             if (j >= p.k) break;
-            const int e = p.topk_idx[(int64_t)t * p.k + j];
-            const unsigned long long m = p.masks[(int64_t)b * p.E + e];
-            const int pos = p.base[(int64_t)b * p.E + e] + __popcll(m & ((1ull << tl) - 1ull));
+            const int e = (int)ld_dev_b32(&p.topk_idx[(int64_t)t * p.k + j]);
+            const unsigned long long m = ld_dev_b64(&p.masks[(int64_t)b * p.E + e]);
+            const int pos = L.off[e] + (int)ld_dev_b32(&p.base[(int64_t)b * p.E + e]) + __popcll(m & ((1ull << tl) - 1ull));
             const int d = e / p.E_loc;
             if (lane == j) p.perm[(int64_t)t * p.k + j] = pos;
             if (d != p.rank) {
@@ -526,11 +501,10 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   char* scratch = static_cast<char*>(ws) + kScratchOffset;
   const size_t mask_bytes = (size_t)p.nblk * p.E * 8, base_bytes = (size_t)p.nblk * p.E * 4;
-  if (mask_bytes + base_bytes + (size_t)(p.E + 1) * 4 > kScratchBytes)
-    return fail(KOS_ERR_SHAPE, "too many tokens x experts for the workspace");
+  if (p.nblk > 1024 || mask_bytes + base_bytes > kScratchBytes)
+    return fail(KOS_ERR_SHAPE, "too many tokens (at most 65536) or tokens x experts for the workspace");
   p.masks = reinterpret_cast<unsigned long long*>(scratch);
   p.base = reinterpret_cast<int32_t*>(scratch + mask_bytes);
-  p.off = reinterpret_cast<int32_t*>(scratch + mask_bytes + base_bytes);
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   constexpr int NT = 256;

@@ -137,7 +137,7 @@ typedef enum kos_trace_kind {
   KOS_TR_WAIT = 3,    /* polling a ready counter before a dependent entry       */
   KOS_TR_REDUCE = 4,  /* a reduce-scatter slab                                  */
   KOS_TR_ROUTE = 5,   /* a router entry (16 tokens)                             */
-  KOS_TR_SCAN = 6,    /* the dispatch scan                                      */
+  KOS_TR_SCAN = 6,    /* a dispatch scan entry (one expert)                     */
   KOS_TR_PUSH = 7,    /* a combine push slab                                    */
   KOS_TR_FOLD = 8,    /* a combine fold block                                   */
   KOS_TR_TILE2 = 9    /* a combine down tile                                    */
@@ -268,6 +268,8 @@ typedef struct kos_moe_shape {
  * grouped_offsets out int32 [E_loc + 1]: expert e's rows start here
  * row_src      out int32 [grouped_cap, 2]: (source rank, row index in what
  *              that source sends us) of every grouped row
+ * T <= 65536 and T * E * 12 bytes within the workspace's 15 MiB scratch
+ * (KOS_ERR_SHAPE otherwise).
  * Capacities overflow -> KOS_ERR_CAPACITY (device, see kos_workspace_status);
  * send_cap >= T*min(k, E_loc) and grouped_cap >= sum(peer_counts) +
  * T*min(k, E_loc) never overflow.  Shapes: H % 64 == 0.
