@@ -70,8 +70,10 @@ struct CombineMeta {
   int32_t off[kMoeMaxExperts + 1];  // our packed offsets
 };
 
+// Also checks that every peer buffer that would be read or written is
+// non-NULL: returns false (every thread) and records KOS_ERR_ARG otherwise.
 template <int BM>
-__device__ __forceinline__ void load_combine_meta(const CombineParams& p, CombineMeta& M) {
+__device__ __forceinline__ bool load_combine_meta(const CombineParams& p, CombineMeta& M, WgSlots* s) {
   for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) M.go[el] = p.go_in[el];
   for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
     int run = 0;
@@ -87,8 +89,19 @@ __device__ __forceinline__ void load_combine_meta(const CombineParams& p, Combin
       const int n = M.go[el + 1] - M.go[el];
       M.ub[el + 1] = M.ub[el] + (n + BM - 1) / BM;
     }
+    bool bad = false;
+    for (int q = 0; q < p.world; ++q) {
+      if (q == p.rank) continue;
+      const int sent = M.off[(q + 1) * p.E_loc] - M.off[q * p.E_loc];   // results q returns
+      int recv = 0;                                                      // rows q sent us
+      for (int el = 0; el < p.E_loc; ++el) recv += p.peer_counts[q * p.E_loc + el];
+      if ((sent > 0 && p.peer_return[q] == nullptr) || (recv > 0 && p.out_return[q] == nullptr)) bad = true;
+    }
+    if (bad) raise_error(p.ws, KOS_ERR_ARG, 0x00C00000u);
+    s->ok = bad ? 0 : 1;
   }
   __syncthreads();
+  return s->ok != 0;
 }
 
 struct Unit {
@@ -331,7 +344,10 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   __syncthreads();
   const CombineParams& p = ps;
   WsHeader* h = p.ws;
-  load_combine_meta<BM>(p, M);
+  if (!load_combine_meta<BM>(p, M, &slots)) {   // a peer buffer it needs is NULL (every workgroup agrees)
+    wg_exit(h, p.ctr, 2 * p.u_max, &slots);
+    return;
+  }
   const int U = M.ub[p.E_loc];
   constexpr int kPushSlabs = (BM + kPushRows - 1) / kPushRows;
   const int n_push = U * kPushSlabs;
@@ -464,13 +480,15 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
       s->experts <= 0 || s->experts > kMoeMaxExperts || s->experts % R || s->experts / R > kMoeMaxLocal ||
       s->topk < 1 || s->topk > kMoeMaxTopk || s->topk > s->experts)
     return fail(KOS_ERR_SHAPE, "unsupported expert-layer shape (hidden %% %d, ffn %% %d)", S::BN, S::BN / 2);
-  if (!x_grouped || !grouped_offsets || !row_src || !w_gate || !w_up || !w_down || !topk_idx || !topk_w ||
-      !counts || !perm || !peer_counts || !h || !y_grouped || !y)
+  // per-token buffers may be NULL for an empty batch (nothing reads them)
+  const bool no_tokens = s->tokens == 0;
+  if (!x_grouped || !grouped_offsets || !row_src || !w_gate || !w_up || !w_down ||
+      (!no_tokens && (!topk_idx || !topk_w || !perm || !y)) || !counts || !peer_counts || !h || !y_grouped)
     return fail(KOS_ERR_ARG, "null buffer");
   if (R > 1 && (!peer_return || !out_return)) return fail(KOS_ERR_ARG, "peer_return / out_return is NULL");
   for (int q = 0; q < R; ++q) {
     if (q == r) continue;
-    if (!peer_return[q] || !out_return[q]) return fail(KOS_ERR_ARG, "peer buffers of rank %d are NULL", q);
+    // NULL is allowed where nothing travels (checked on the device)
     if (!aligned16(peer_return[q]) || !aligned16(out_return[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(x_grouped) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(h) ||

@@ -252,10 +252,12 @@ __device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& 
   }
   if (threadIdx.x == 0) {
     bool over = false;
+    bool null_send = false;
     for (int d = 0; d < p.world; ++d) {
       if (d == p.rank) continue;
       const int sent = L.off[(d + 1) * p.E_loc] - L.off[d * p.E_loc];
       if (sent > p.send_cap) over = true;
+      if (sent > 0 && p.out_send[d] == nullptr) null_send = true;   // rows for a NULL buffer
     }
     int64_t go = 0;
     for (int el = 0; el < p.E_loc; ++el) {
@@ -265,7 +267,8 @@ __device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& 
     L.go[p.E_loc] = (int32_t)go;
     if (go > p.grouped_cap) over = true;
     if (over) raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)go);
-    slots->ok = over ? 0 : 1;
+    if (null_send) raise_error(p.ws, KOS_ERR_ARG, 0x00B00000u);
+    slots->ok = over || null_send ? 0 : 1;
   }
   __syncthreads();
   if (writer && slots->ok)
@@ -292,6 +295,18 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
   for (int i = threadIdx.x; i < p.world * p.E_loc; i += NT) {
     const int q = i / p.E_loc, el = i % p.E_loc;
     L.pc[q][el] = q == p.rank ? 0 : p.peer_counts[i];
+  }
+  __syncthreads();
+  // a peer whose send buffer is NULL must send nothing: else this
+  // workgroup takes its rows as absent (never reads the NULL buffer) and
+  // the call reports KOS_ERR_ARG
+  if (threadIdx.x < p.world && threadIdx.x != p.rank && p.peer_send[threadIdx.x] == nullptr) {
+    bool any = false;
+    for (int el = 0; el < p.E_loc; ++el) any |= L.pc[threadIdx.x][el] != 0;
+    if (any) {
+      raise_error(p.ws, KOS_ERR_ARG, 0x00A00000u | threadIdx.x);
+      for (int el = 0; el < p.E_loc; ++el) L.pc[threadIdx.x][el] = 0;
+    }
   }
   __syncthreads();
   if (threadIdx.x < p.world) {
@@ -450,13 +465,15 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
       s->experts % R || s->experts / R > kMoeMaxLocal || s->topk < 1 || s->topk > kMoeMaxTopk ||
       s->topk > s->experts || s->ffn <= 0)
     return fail(KOS_ERR_SHAPE, "unsupported expert-layer shape");
-  if (!x || !logits || !peer_counts || !topk_idx || !topk_w || !counts || !perm || !x_grouped ||
+  // per-token buffers may be NULL for an empty batch (nothing reads them)
+  const bool no_tokens = s->tokens == 0;
+  if ((!no_tokens && (!x || !logits || !topk_idx || !topk_w || !perm)) || !peer_counts || !counts || !x_grouped ||
       !grouped_offsets || !row_src)
     return fail(KOS_ERR_ARG, "null buffer");
   if (R > 1 && (!peer_send || !out_send)) return fail(KOS_ERR_ARG, "peer_send / out_send is NULL");
   for (int q = 0; q < R; ++q) {
     if (q == r) continue;
-    if (!peer_send[q] || !out_send[q]) return fail(KOS_ERR_ARG, "peer buffers of rank %d are NULL", q);
+    // NULL is allowed where nothing travels (checked on the device)
     if (!aligned16(peer_send[q]) || !aligned16(out_send[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(x) || !aligned16(x_grouped)) return fail(KOS_ERR_ALIGN, "row buffers must be 16-byte aligned");

@@ -268,6 +268,11 @@ typedef struct kos_moe_shape {
  * grouped_offsets out int32 [E_loc + 1]: expert e's rows start here
  * row_src      out int32 [grouped_cap, 2]: (source rank, row index in what
  *              that source sends us) of every grouped row
+ * With T == 0, x, logits, topk_idx, topk_w and perm may be NULL.
+ * peer_send[p] may be NULL if peer p sends nothing (its peer_counts row is
+ * zero) and out_send[d] if no pair routes to d's experts; a NULL buffer
+ * that something would travel through is reported as KOS_ERR_ARG by
+ * kos_workspace_status (the rows are skipped, never dereferenced).
  * T <= 65536 and T * E * 12 bytes within the workspace's 15 MiB scratch
  * (KOS_ERR_SHAPE otherwise).
  * Capacities overflow -> KOS_ERR_CAPACITY (device, see kos_workspace_status);
@@ -304,6 +309,10 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
  *              inspection);  y_grouped: out bf16 [grouped_cap, H]
  * out_return   host array[world] of out bf16 [rows p sent us, H]
  * y            out bf16 [T, H]
+ * With T == 0, topk_idx, topk_w, perm and y may be NULL.  peer_return[d]
+ * may be NULL if we sent d nothing and out_return[p] if p sent us nothing;
+ * otherwise a NULL peer buffer is reported as KOS_ERR_ARG by
+ * kos_workspace_status and the kernel does nothing.
  * Shapes: H % 128 == 0, F % 64 == 0, grouped_cap * H * 2 < 2^31 bytes
  * (else KOS_ERR_SHAPE).
  */

@@ -252,7 +252,7 @@ def moe_inputs(s: MoeShape, rank: int, device="cpu", with_weights=True):
     local expert weights wg, wu [E_loc,H,F] N(0,1/H), wd [E_loc,F,H] N(0,1/F);
     peer_counts [R,E_loc] int32 (emulated routing of the peers);
     peer_send[p] [n_p,H] bf16 N(0,1): rows p sends us, expert-major;
-    peer_return[d] [peer_cap,H] bf16 N(0,1): results d returns for the rows we
+    peer_return[d] [max(peer_cap,1),H] bf16 N(0,1): results d returns for the rows we
     send it, in our packed order (only the first send-count rows are read)."""
     out = {}
     out["x"] = normal((s.tokens, s.hidden), 1.0, s.wid, T_X, rank, device)
@@ -268,7 +268,7 @@ def moe_inputs(s: MoeShape, rank: int, device="cpu", with_weights=True):
         n_p = int(pc[p].sum())
         peer_send.append(normal((max(n_p, 1), s.hidden), 1.0, s.wid, T_SEND,
                                 p * 64 + rank, device)[:n_p])
-        peer_ret.append(normal((s.peer_cap, s.hidden), 1.0, s.wid, T_RET,
+        peer_ret.append(normal((max(s.peer_cap, 1), s.hidden), 1.0, s.wid, T_RET,
                                p * 64 + rank, device))
     out["peer_send"] = peer_send
     out["peer_return"] = peer_ret
