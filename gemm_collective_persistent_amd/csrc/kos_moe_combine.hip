@@ -453,8 +453,10 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
 }
 
 // Big tile when the widths allow it (hidden % 256, ffn % 128), else 128 x 128.
-using CombineTileBig = TileShape<256, 256>;
-using CombineTailBig = TileShape<128, 256>;
+// The big tiles run eight waves (two per SIMD), which hides more of the LDS
+// and memory latency on these long (gate/up) and short (down) K loops.
+using CombineTileBig = TileShape<256, 256, 4, 2, 4>;
+using CombineTailBig = TileShape<128, 256, 4, 2, 4>;
 using CombineTileSmall = TileShape<128, 128>;
 using CombineTailSmall = TileShape<64, 128>;
 

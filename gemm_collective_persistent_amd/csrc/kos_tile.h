@@ -1,9 +1,10 @@
 // The builders' bf16 MFMA tile (gfx950): C[BM x BN] = A[BM x K] . B[K x BN],
 // fp32 accumulate.
 //
-// Workgroup of 4 wave64s arranged 2 x 2; each wave owns a (BM/2) x (BN/2)
-// sub-tile of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16, the
-// accumulators held in registers for the whole K loop.
+// Workgroup of WGM x WGN wave64s (2 x 2, or 2 x 4 with two waves per SIMD);
+// each wave owns a (BM/WGM) x (BN/WGN) sub-tile of 32 x 32 blocks computed
+// with v_mfma_f32_32x32x16_bf16, the accumulators held in registers for the
+// whole K loop.
 //
 // Operands go straight from HBM/L2 into LDS (buffer_load_dwordx4 ... lds
 // through raw buffer descriptors: each lane's 16 bytes land at lds_base +
@@ -38,23 +39,28 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int BM_, int BN_, int STAGES_ = 4>
+// WGM x WGN waves: 2 x 2 (one wave per SIMD) or 2 x 4 (two waves per SIMD:
+// while one waits on LDS or memory the other issues MFMAs; each holds half
+// the accumulators).
+template <int BM_, int BN_, int STAGES_ = 4, int WGM_ = 2, int WGN_ = 2>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
-  static constexpr int WGM = 2, WGN = 2;
-  static constexpr int NT = 256;                        // threads (4 waves)
+  static constexpr int WGM = WGM_, WGN = WGN_;
+  static constexpr int NW = WGM * WGN;                  // waves
+  static constexpr int NT = 64 * NW;                    // threads
   static constexpr int WM = BM / WGM, WN = BN / WGN;    // wave sub-tile
   static constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 blocks per wave
   static constexpr int A_BYTES = BM * BK * 2;           // per stage
   static constexpr int B_BYTES = BK * BN * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int A_LOADS = A_BYTES / 1024 / 4;    // 1 KiB wave loads per wave per stage
-  static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+  static constexpr int A_LOADS = A_BYTES / 1024 / NW;   // 1 KiB wave loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / NW;
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int BROW_CHUNKS = BN / 8;            // 16-byte chunks per B row
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
-  static_assert(B_BYTES % 4096 == 0 && A_BYTES % 4096 == 0, "whole 1 KiB loads per wave");
+  static_assert(B_BYTES % (1024 * NW) == 0 && A_BYTES % (1024 * NW) == 0, "whole 1 KiB loads per wave");
+  static_assert(TM >= 1 && TN >= 1, "at least one 32x32 block per wave");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "each wave loads at least 1 KiB of A and of B");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(3 * LOADS <= 63, "vmcnt range");
@@ -122,7 +128,9 @@ struct BLayout {
   static constexpr int W = DUAL ? S::BROW_CHUNKS / 2 : S::BROW_CHUNKS;   // chunks per LDS row
   static constexpr int ROW_BYTES = W * 16;
   static constexpr int HALF_BYTES = S::B_BYTES / 2;
-  static_assert(!DUAL || (S::B_LOADS * 2 * 1024 == HALF_BYTES), "dual: waves 0-1 load the gate half, 2-3 the up half");
+  static_assert(!DUAL || (S::B_LOADS * (S::NW / 2) * 1024 == HALF_BYTES),
+                "dual: the first half of the waves load the gate half, the rest the up half");
+  static_assert(!DUAL || S::TN % 2 == 0, "dual: gate and up blocks pair up in each wave");
 };
 
 // This wave's direct loads, fixed for a tile: raw buffer descriptors of the
@@ -162,8 +170,8 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
     P.a_off[i] = (uint32_t)(mr * lda * 2 + c * 16);
   }
   P.b_stride = (int)(b.ld * 2);
-  // dual: waves 0-1 fill the gate half, 2-3 the up half
-  const bool up = DUAL && wave >= 2;
+  // dual: the first half of the waves fill the gate half, the rest the up half
+  const bool up = DUAL && wave >= S::NW / 2;
   P.rb = raw_rsrc(up ? b.p1 : b.p0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
@@ -473,7 +481,7 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
     for (int j = 0; j < OJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = wn * (OW / 2) + j * 32 + g * 8 + (lane >> 5) * 4;
+        const int col = wn * (OW / S::WGN) + j * 32 + g * 8 + (lane >> 5) * 4;
         const int chunk = (col >> 3) ^ (row & (CPR - 1));
         f32x4 v;
 #pragma unroll
