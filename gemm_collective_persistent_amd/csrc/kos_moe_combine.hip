@@ -68,10 +68,15 @@ struct CombineMeta {
   int32_t ub[kMoeMaxLocal + 1];     // first unit of each local expert
   int32_t before[kMoeMaxLocal];     // grouped rows of sources < rank, per local expert
   int32_t off[kMoeMaxExperts + 1];  // our packed offsets
+  int32_t recv[8];                  // rows each rank sent us
+  int32_t wave_tot[16];             // scan scratch
 };
 
-// Also checks that every peer buffer that would be read or written is
-// non-NULL: returns false (every thread) and records KOS_ERR_ARG otherwise.
+// Every workgroup's copy of the layer's bookkeeping, in LDS: grouped offsets,
+// units per expert, our packed offsets (a block scan of the counts) and the
+// rows of lower ranks per expert.  Also checks that every peer buffer that
+// would be read or written is non-NULL: returns false (every thread) and
+// records KOS_ERR_ARG otherwise.
 template <int BM>
 __device__ __forceinline__ bool load_combine_meta(const CombineParams& p, CombineMeta& M, WgSlots* s) {
   for (int el = threadIdx.x; el <= p.E_loc; el += blockDim.x) M.go[el] = p.go_in[el];
@@ -80,27 +85,26 @@ __device__ __forceinline__ bool load_combine_meta(const CombineParams& p, Combin
     for (int q = 0; q < p.rank; ++q) run += p.peer_counts[q * p.E_loc + el];
     M.before[el] = run;
   }
-  __syncthreads();
+  if (threadIdx.x < 8) M.recv[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s->ok = 1;
+  block_exclusive_scan(p.counts, M.off, p.E, M.wave_tot);
+  for (int i = threadIdx.x; i < p.world * p.E_loc; i += blockDim.x)
+    if (p.peer_counts[i] != 0) atomicAdd(&M.recv[i / p.E_loc], p.peer_counts[i]);   // rows each rank sent us
   if (threadIdx.x == 0) {
-    M.off[0] = 0;
-    for (int e = 0; e < p.E; ++e) M.off[e + 1] = M.off[e] + p.counts[e];
     M.ub[0] = 0;
     for (int el = 0; el < p.E_loc; ++el) {
       const int n = M.go[el + 1] - M.go[el];
       M.ub[el + 1] = M.ub[el] + (n + BM - 1) / BM;
     }
-    bool bad = false;
-    for (int q = 0; q < p.world; ++q) {
-      if (q == p.rank) continue;
-      const int sent = M.off[(q + 1) * p.E_loc] - M.off[q * p.E_loc];   // results q returns
-      int recv = 0;                                                      // rows q sent us
-      for (int el = 0; el < p.E_loc; ++el) recv += p.peer_counts[q * p.E_loc + el];
-      if ((sent > 0 && p.peer_return[q] == nullptr) || (recv > 0 && p.out_return[q] == nullptr)) bad = true;
-    }
-    if (bad) raise_error(p.ws, KOS_ERR_ARG, 0x00C00000u);
-    s->ok = bad ? 0 : 1;
   }
   __syncthreads();
+  const int q = threadIdx.x;
+  if (q < p.world && q != p.rank) {
+    const int sent = M.off[(q + 1) * p.E_loc] - M.off[q * p.E_loc];   // results q returns
+    if ((sent > 0 && p.peer_return[q] == nullptr) || (M.recv[q] > 0 && p.out_return[q] == nullptr)) s->ok = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && !s->ok) raise_error(p.ws, KOS_ERR_ARG, 0x00C00000u);
   return s->ok != 0;
 }
 

@@ -180,40 +180,6 @@ __device__ __forceinline__ void route_entry(const DispatchParams& p, int b4, Dis
   for (int e = threadIdx.x; e < p.E; e += blockDim.x) mb.st16((uint32_t)(e * 8 + q * 2), (uint16_t)L.m[e]);
 }
 
-// Exclusive prefix sums of in[0, n) into out[0, n], out[n] = total; n <=
-// 4 * blockDim.x (256 threads).  All threads call it.
-__device__ inline void block_exclusive_scan(const int32_t* in, int32_t* out, int n, int32_t* wave_tot) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
-  int v[4];
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = 4 * t + i < n ? in[4 * t + i] : 0;
-    sum += v[i];
-  }
-  int inc = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
-  if (lane == 63) wave_tot[wave] = inc;
-  __syncthreads();
-  int ex = inc - sum;
-  for (int w = 0; w < wave; ++w) ex += wave_tot[w];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (4 * t + i < n) out[4 * t + i] = ex;
-    ex += v[i];
-  }
-  if (t == 0) {
-    int tot = 0;
-    for (int w = 0; w < nw; ++w) tot += wave_tot[w];
-    out[n] = tot;
-  }
-  __syncthreads();
-}
-
 // Scan entry: expert e, once every router entry is counted.  Its block
 // masks -> per-block counts -> exclusive prefix over the blocks:
 // base[b][e] = pairs of e in blocks before b (relative to e's packed
