@@ -17,16 +17,22 @@
 //                that expert in earlier blocks; counter[1] counts them.
 //                Every mover then scans the counts itself (packed offsets,
 //                grouped offsets of our local experts, capacity checks).
-//   head[1]      mover entries (after counter[1]): a quarter block of our
+//   head[1]      mover entries (after counter[1]): kMoveTokens of our
 //                tokens -- pair (t, j) of expert e lands at off[e] +
-//                base[block][e] + popcount(mask & tokens before t); the row goes to the send
-//                buffer of e's rank, or straight into the grouped input when
-//                e is local -- then 64-row chunks of each peer's rows, pulled
-//                into the grouped input.
+//                base[block][e] + popcount(mask & tokens before t); the row
+//                goes to the send buffer of e's rank, or straight into the
+//                grouped input when e is local -- then kMoveRows-row chunks of
+//                each peer's rows, pulled into the grouped input.  Entries
+//                are small (about 0.5 MB of traffic) so that the workgroups
+//                run out of them together.
 #include "kos_host.h"
 #include "kos_moe.h"
 
 namespace kos {
+
+constexpr int kMoveTokens = 4;    // our tokens per mover entry
+constexpr int kMoveRows = 16;     // peer rows per mover entry
+constexpr int kMoveSubs = kMoeTokBlock / kMoveTokens;   // own entries per 64-token block
 
 struct DispatchParams {
   int32_t world, rank, T, H, E, k, E_loc;
@@ -286,10 +292,10 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int nb = p.nblk * 4;
+    int nb = p.nblk * kMoveSubs;
     for (int q = 0; q < p.world; ++q) {
       L.chunk_base[q] = nb;
-      if (q != p.rank) nb += (L.cum[q][p.E_loc] + 63) / 64;
+      if (q != p.rank) nb += (L.cum[q][p.E_loc] + kMoveRows - 1) / kMoveRows;
     }
     L.chunk_base[p.world] = nb;
   }
@@ -338,11 +344,11 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
       const uint64_t t0 = tr.now();
       const int H = p.H;
       const int row_bytes = H * 2;
-      if ((int)i < p.nblk * 4) {
-        // our own tokens: a quarter block, one token per wave at a time
-        const int b = (int)i >> 2, q = (int)i & 3;
-        for (int tq = wave; tq < kMoeTokBlock / 4; tq += nw) {
-          const int tl = q * (kMoeTokBlock / 4) + tq;
+      if ((int)i < p.nblk * kMoveSubs) {
+        // kMoveTokens of our tokens, one token per wave at a time
+        const int b = (int)i / kMoveSubs, q = (int)i % kMoveSubs;
+        for (int tq = wave; tq < kMoveTokens; tq += nw) {
+          const int tl = q * kMoveTokens + tq;
           const int t = b * kMoeTokBlock + tl;
           if (t >= p.T) break;
           uint16_t* dst[kMoeMaxTopk];
@@ -387,12 +393,12 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
           }
         }
       } else {
-        // a chunk of 64 rows peer q sent us, pulled into the grouped input
+        // a chunk of kMoveRows rows peer q sent us, pulled into the grouped input
         int q = 0;
         while (q + 1 <= p.world && L.chunk_base[q + 1] <= (int)i) ++q;
-        const int r0 = ((int)i - L.chunk_base[q]) * 64;
+        const int r0 = ((int)i - L.chunk_base[q]) * kMoveRows;
         const int n_q = L.cum[q][p.E_loc];
-        for (int rr = wave; rr < 64; rr += nw) {
+        for (int rr = wave; rr < kMoveRows; rr += nw) {
           const int r = r0 + rr;
           if (r >= n_q) break;
           int el = 0;
