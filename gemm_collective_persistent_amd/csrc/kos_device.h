@@ -220,15 +220,20 @@ __device__ __forceinline__ uint32_t wg_ticket(WsHeader* h, WgSlots* s) {
 
 // Departure: the last workgroup out returns the workspace to all-zero (queue
 // heads, tickets, the first `n_counters` ready counters), keeping only the
-// sticky error word, so the next call needs no clearing launch.
+// sticky error word, so the next call needs no clearing launch.  Those words
+// are only touched by device-scope atomics and device-coherent stores, which
+// complete at the device's coherence point: waiting for this workgroup's own
+// memory operations before it counts itself out orders them before the
+// reset, with no fence.  (An agent-scope fence writes back and invalidates
+// the XCD's whole L2, stalling every workgroup still running there; the
+// launch's outputs become visible to later work when it ends.)
 __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_counters, WgSlots* s) {
-  fence_release();
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt, lgkmcnt = 0
   __syncthreads();
   if (threadIdx.x == 0)
-    s->claim = __hip_atomic_fetch_add(&h->exit_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s->claim = __hip_atomic_fetch_add(&h->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s->claim != gridDim.x - 1) return;
-  fence_acquire();
   for (uint32_t i = threadIdx.x; i < n_counters; i += blockDim.x) st_relaxed(&counters[i], 0u);
   if (threadIdx.x < kNumHeads) st_relaxed(&h->head[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
@@ -236,7 +241,6 @@ __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_count
     st_relaxed(&h->abort, 0u);
     st_relaxed(&h->exit_count, 0u);
   }
-  fence_release();
 }
 
 // ---------------------------------------------------------------------------
