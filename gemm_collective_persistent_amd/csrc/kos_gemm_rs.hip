@@ -196,7 +196,7 @@ static kos_status launch_rs(const RsParams& p, int grid, hipStream_t stream) {
 }
 
 static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_rs<TileShape<256, 256>>(p, grid, s);
+  if (bm == 256 && bn == 256) return launch_rs<TileShape<256, 256, 4, 2, 4>>(p, grid, s);
   if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128>>(p, grid, s);
   if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128>>(p, grid, s);
   return launch_rs<TileShape<64, 64>>(p, grid, s);
