@@ -331,14 +331,17 @@ __device__ __forceinline__ bool fold_block(const CombineParams& p, const Combine
   return s->ok != 0;
 }
 
-// S: the unit's tile (BM rows of one expert).  ST: a tile of the same width
-// and fewer rows for an expert's last unit when its rows fit (less work
-// spent on rows past the end).  COH: one launch produces and consumes h and
-// Y (fused and fixed-crew modes).
-template <class S, class ST, bool COH>
+// S: the unit's tile (BM rows of one expert).  ST, ST2: tiles of the same
+// width and fewer rows for an expert's last unit when its rows fit (less
+// work spent on rows past the end; ST2 == ST when there is one tail size).
+// COH: one launch produces and consumes h and Y (fused and fixed-crew
+// modes).
+template <class S, class ST, class ST2, bool COH>
 __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams args) {
   constexpr int BM = S::BM;
   static_assert(ST::BN == S::BN && ST::BM < S::BM && ST::NT == S::NT, "tail tile: same width, fewer rows");
+  static_assert(ST2::BN == S::BN && ST2::BM <= ST::BM && ST2::NT == S::NT, "second tail: no more rows than the first");
+  constexpr bool kTail2 = ST2::BM < ST::BM;
   __shared__ CombineMeta M;
   __shared__ WgSlots slots;
   // The parameter block lives in LDS: the role code reads the fields it needs
@@ -366,6 +369,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
   if (!crew && (p.do_gu || p.do_dn)) {
     f32x16 acc[S::TM][S::TN];
     f32x16 acc_t[ST::TM][ST::TN];
+    f32x16 acc_t2[ST2::TM][ST2::TN];
     constexpr int RB = S::STAGE_BYTES;
     const int n_entries = (p.do_gu && p.do_dn) ? U * (p.G + p.D) : (p.do_gu ? U * p.G : U * p.D);
     for (;;) {
@@ -396,9 +400,11 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
       decode_tile(p, U, (int)j, down, u, nt);
       const Unit x = unit_of<BM>(M, p.E_loc, u);
       const bool tail = x.m_valid <= ST::BM;
+      const bool tail2 = kTail2 && x.m_valid <= ST2::BM;
       uint64_t t0 = tr.now();
       if (!down) {
-        if (tail) gate_up_tile<ST, RB>(p, x, nt, acc_t);
+        if (tail2) gate_up_tile<ST2, RB>(p, x, nt, acc_t2);
+        else if (tail) gate_up_tile<ST, RB>(p, x, nt, acc_t);
         else gate_up_tile<S, RB>(p, x, nt, acc);
         wg_publish(&gu_done[u], 1u);
         tr.put(KOS_TR_TILE, j, t0);
@@ -411,7 +417,8 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           tr.put(KOS_TR_WAIT, j, t0);
           t0 = tr.now();
         }
-        if (tail) down_tile<ST, COH, RB>(p, x, nt, acc_t);
+        if (tail2) down_tile<ST2, COH, RB>(p, x, nt, acc_t2);
+        else if (tail) down_tile<ST, COH, RB>(p, x, nt, acc_t);
         else down_tile<S, COH, RB>(p, x, nt, acc);
         wg_publish(&dn_done[u], 1u);
         tr.put(KOS_TR_TILE2, j, t0);
@@ -461,6 +468,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
 // and memory latency on these long (gate/up) and short (down) K loops.
 using CombineTileBig = TileShape<256, 256, 4, 2, 4>;
 using CombineTailBig = TileShape<128, 256, 4, 2, 4>;
+using CombineTail2Big = TileShape<64, 256, 4, 2, 4>;
 using CombineTileSmall = TileShape<128, 128>;
 using CombineTailSmall = TileShape<64, 128>;
 
@@ -557,16 +565,16 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   auto launch = [&](const CombineParams& q, const char* what) {
     const bool coh = q.wait_flags != 0;
     if (big && coh)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, true>), dim3(o.grid), dim3(CombineTileBig::NT), 0, strm,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, CombineTail2Big, true>), dim3(o.grid), dim3(CombineTileBig::NT), 0, strm,
                          q);
     else if (big)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, false>), dim3(o.grid), dim3(CombineTileBig::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileBig, CombineTailBig, CombineTail2Big, false>), dim3(o.grid), dim3(CombineTileBig::NT), 0,
                          strm, q);
     else if (coh)
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, true>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, CombineTailSmall, true>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
                          strm, q);
     else
-      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, false>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
+      hipLaunchKernelGGL((moe_combine_kernel<CombineTileSmall, CombineTailSmall, CombineTailSmall, false>), dim3(o.grid), dim3(CombineTileSmall::NT), 0,
                          strm, q);
     return launch_status(what);
   };

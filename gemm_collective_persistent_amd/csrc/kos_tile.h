@@ -54,12 +54,18 @@ struct TileShape {
   static constexpr int B_BYTES = BK * BN * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int A_LOADS = A_BYTES / 1024 / NW;   // 1 KiB wave loads per wave per stage
-  static constexpr int B_LOADS = B_BYTES / 1024 / NW;
+  // An A stage of half a KiB per wave (64 rows on eight waves) is loaded by
+  // the lower 32 lanes of every wave, so every wave still issues the same
+  // number of loads per stage (the waits count instructions).
+  static constexpr bool A_HALF = A_BYTES == 512 * NW;
+  static constexpr int A_WAVE_BYTES = A_HALF ? 512 : 1024;   // bytes per A load instruction
+  static constexpr int A_LOADS = A_HALF ? 1 : A_BYTES / 1024 / NW;   // A loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / NW;                // 1 KiB B loads per wave per stage
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int BROW_CHUNKS = BN / 8;            // 16-byte chunks per B row
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
-  static_assert(B_BYTES % (1024 * NW) == 0 && A_BYTES % (1024 * NW) == 0, "whole 1 KiB loads per wave");
+  static_assert(B_BYTES % (1024 * NW) == 0 && (A_HALF || A_BYTES % (1024 * NW) == 0),
+                "whole loads per wave");
   static_assert(TM >= 1 && TN >= 1, "at least one 32x32 block per wave");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "each wave loads at least 1 KiB of A and of B");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -144,6 +150,7 @@ struct LoadPlan {
   uint32_t b_off[S::B_LOADS];
   int b_stride;                                // bytes per k row of B
   int a_lds, b_lds;                            // this wave's bytes into a stage (uniform)
+  bool a_on;                                   // this lane loads A (A_HALF: lanes 0..31)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
@@ -158,12 +165,14 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
                                            int m_valid, const BSrc& b, const WaveCtx& w) {
   using L = BLayout<S, DUAL>;
   const int lane = w.lane, wave = w.wave;
-  P.a_lds = wave * S::A_LOADS * 1024;
+  P.a_lds = wave * S::A_LOADS * S::A_WAVE_BYTES;
   P.b_lds = S::A_BYTES + wave * S::B_LOADS * 1024;
+  P.a_on = !S::A_HALF || lane < 32;
   P.ra = raw_rsrc(A);
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
-    const int slot = (wave * S::A_LOADS + i) * 64 + lane;   // 16-byte slot in the A stage
+    // 16-byte slot in the A stage
+    const int slot = S::A_HALF ? wave * 32 + (lane & 31) : (wave * S::A_LOADS + i) * 64 + lane;
     const int m = slot >> 2, p = slot & 3;
     const int c = p ^ a_swz(m);
     const int mr = m < m_valid ? m : m_valid - 1;
@@ -194,8 +203,9 @@ __device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DU
   const int sob = k0 * P.b_stride;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(P.ra, (lds_void*)(lds_stage + P.a_lds + i * 1024), 16, P.a_off[i], soa,
-                                             0, COH_A ? kCpolDevice : 0);
+    if (!S::A_HALF || P.a_on)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(P.ra, (lds_void*)(lds_stage + P.a_lds + i * S::A_WAVE_BYTES), 16,
+                                               P.a_off[i], soa, 0, COH_A ? kCpolDevice : 0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(P.rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i], sob,
