@@ -7,17 +7,14 @@
 // works if ..." paragraphs].
 //
 // Memory ordering: the MI355X's eight XCDs each have their own L2, which is
-// not coherent with the others for ordinary accesses.  Two protocols:
-//  * coherent exchange (the hot paths): data that another workgroup of the
-//    same launch reads is stored with device-scope (sc1) stores; the
-//    producer waits for its stores to complete (vmcnt(0)) in every thread,
-//    then one thread bumps the ready counter (wg_publish); the consumer
-//    polls the counter and reads the data with device-scope (sc1) loads
-//    (wg_observe).  No L2 write-back or invalidation is needed, so the L2
-//    keeps serving every other workgroup's operands.
-//  * fenced exchange (small metadata): agent-scope release fence in every
-//    thread before the bump (wg_signal), acquire fence after the poll
-//    (wg_wait).
+// not coherent with the others for ordinary accesses.  Data that another
+// workgroup of the same launch reads is stored with device-scope (sc1)
+// stores; the producer waits for its stores to complete (vmcnt(0)) in every
+// thread, then one thread bumps the ready counter (wg_publish); the consumer
+// polls the counter and reads the data with device-scope (sc1) loads
+// (wg_observe).  No kernel uses agent-scope fences: on this part a release
+// fence writes back the whole L2 of the XCD it runs on and an acquire fence
+// invalidates it, which stalls every workgroup on that XCD.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,7 +32,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
-// atomics and fences (agent scope = the whole GPU)
+// atomics (agent scope = the whole GPU)
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
@@ -47,8 +44,6 @@ __device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Records the first device-side error and tells every workgroup to drain.
 __device__ inline void raise_error(WsHeader* h, uint32_t code, uint32_t info) {
@@ -81,36 +76,6 @@ __device__ __forceinline__ uint32_t wg_claim(uint32_t* head, WsHeader* h, WgSlot
   return s->claim;
 }
 
-// Makes this workgroup's global stores visible GPU-wide, then adds `v` to a
-// ready counter.
-__device__ __forceinline__ void wg_signal(uint32_t* counter, uint32_t v) {
-  fence_release();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Waits until *counter >= target.  Bounded: after `limit` polls it records
-// KOS_ERR_TIMEOUT (with `info`) and returns false; it also returns false as
-// soon as another workgroup has recorded an error.
-__device__ inline bool wg_wait(const uint32_t* counter, uint32_t target, WsHeader* h,
-                               uint32_t limit, uint32_t info, WgSlots* s) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    uint32_t it = 0;
-    while (ld_relaxed(counter) < target) {
-      if (aborted(h)) { ok = 0; break; }
-      if (++it >= limit) { raise_error(h, KOS_ERR_TIMEOUT, info); ok = 0; break; }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    s->ok = ok;
-  }
-  __syncthreads();
-  const bool ok = s->ok != 0;
-  fence_acquire();
-  return ok;
-}
-
 // Coherent exchange, producer side: this workgroup's device-scope stores
 // have completed (every thread waits), then `v` is added to the counter.
 __device__ __forceinline__ void wg_publish(uint32_t* counter, uint32_t v) {
@@ -119,9 +84,10 @@ __device__ __forceinline__ void wg_publish(uint32_t* counter, uint32_t v) {
   if (threadIdx.x == 0) add_relaxed(counter, v);
 }
 
-// Coherent exchange, consumer side: waits until *counter >= target (same
-// bound and error behaviour as wg_wait); the caller then reads the data with
-// device-scope loads.
+// Coherent exchange, consumer side: waits until *counter >= target, then the
+// caller reads the data with device-scope loads.  Bounded: after `limit`
+// polls it records KOS_ERR_TIMEOUT (with `info`) and returns false; it also
+// returns false as soon as another workgroup has recorded an error.
 __device__ inline bool wg_observe(const uint32_t* counter, uint32_t target, WsHeader* h, uint32_t limit,
                                   uint32_t info, WgSlots* s) {
   __syncthreads();
@@ -200,15 +166,6 @@ struct DevBuf {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kCpolSc1);
   }
 };
-
-// Non-blocking readiness test by thread 0, broadcast (no fence: callers that
-// act on `true` must still call wg_wait or fence_acquire before reading).
-__device__ __forceinline__ bool wg_ready(const uint32_t* counter, uint32_t target, WgSlots* s) {
-  __syncthreads();
-  if (threadIdx.x == 0) s->ok = ld_relaxed(counter) >= target ? 1 : 0;
-  __syncthreads();
-  return s->ok != 0;
-}
 
 // Role assignment ticket: arrival order of the workgroups.
 __device__ __forceinline__ uint32_t wg_ticket(WsHeader* h, WgSlots* s) {
