@@ -263,6 +263,29 @@ def ag_pinned(torch, kos, KI, inp, ws, reps, flush):
             "overlap": round((t["unfused"] - t["fused"]) / min(t_copy, t_gemm), 3)}
 
 
+def rs_order_ablation(torch, kos, KI, inp, ws, reps, flush):
+    """GEMM+reduce-scatter in band order (the design) and row order (the
+    slower ablation the explainer compares it with), fused, at rank 7 (whose
+    chunk comes last in row order: the reduction waits for the whole GEMM)
+    and at rank 0."""
+    s = KI.RS_MLP
+    res = {}
+    for rank, rs in ((7, inp["rs"]), (0, None)):
+        if rs is None:
+            rs = KI.rs_inputs(s, rank, "cuda")
+            rs["partial"], rs["y"] = inp["rs"]["partial"], inp["rs"]["y"]
+        t = {}
+        for label, order in (("band", kos.RS_BAND), ("row", kos.RS_ROW)):
+            o = kos.opts(rs_order=order)
+            fn = lambda: kos.gemm_rs(rs["a"], rs["w"], rs["peer_slices"], rs["partial"], rs["y"], rank, ws, o)  # noqa: E731
+            fn()
+            t[label] = time_ops(torch, [("rs", fn)], reps, ws, flush)[0][0]
+        res[f"rank{rank}"] = {"band_ms": round(t["band"], 4), "row_ms": round(t["row"], 4),
+                              "row_over_band": round(t["row"] / t["band"], 3)}
+        del rs
+    return res
+
+
 def cpu_baseline(inp, moe_shape, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same step: the
     all-gather+GEMM of 8 rows of each of the 8 shards, the GEMM+reduce-scatter
@@ -399,6 +422,8 @@ def main():
         extra["gemm_224_of_256_cus"] = cu_subset_gemm(torch, kos, inp, ws, reps, flush)
         # all-gather+GEMM with the peers' shards in pinned host memory (PCIe)
         extra["ag_gemm_pinned_host_peers"] = ag_pinned(torch, kos, KI, inp, ws, reps, flush)
+        # reduce-scatter band order vs row order
+        extra["gemm_rs_band_vs_row"] = rs_order_ablation(torch, kos, KI, inp, ws, reps, flush)
     if not args.no_cpu:
         cpu = cpu_baseline(inp, moe_shape)
     else:
