@@ -50,6 +50,7 @@ TRACE_RECORDS = 512     # KOS_TRACE_RECORDS: records per workgroup
 TRACE_MAX_WG = 256      # KOS_TRACE_MAX_WG
 TRACE_KINDS = {1: "move", 2: "tile", 3: "wait", 4: "reduce", 5: "route", 6: "scan", 7: "push", 8: "fold",
                9: "tile_down"}
+TRACE_CLOCK = 10        # KOS_TR_CLOCK: record 1, shader-clock cycles over the lifetime
 
 
 class MoeShape(ctypes.Structure):

@@ -6,7 +6,7 @@ from typing import Optional, Sequence
 
 import torch
 
-from ._binding import KOS_BF16, KOS_F32, MoeShape, Opts, check, lib, opts as make_opts, ptr_array
+from ._binding import KOS_BF16, KOS_F32, KosError, MoeShape, Opts, check, lib, opts as make_opts, ptr_array
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -46,8 +46,9 @@ class Workspace:
         `grid` workgroups: a list, per workgroup, of (ticket, t_begin, t_end,
         [(kind, entry, t0, t1), ...]) with times in microseconds from the
         earliest workgroup start (kos_workspace_trace).  ``self.trace_xcd``
-        then holds each workgroup's XCD."""
-        from ._binding import TRACE_KINDS, TRACE_MAX_WG, TRACE_RECORDS, TraceRec
+        then holds each workgroup's XCD and ``self.trace_clock_mhz`` the
+        shader clock it ran at (its clock record)."""
+        from ._binding import TRACE_CLOCK, TRACE_KINDS, TRACE_MAX_WG, TRACE_RECORDS, TraceRec
         if not 0 < grid <= TRACE_MAX_WG:
             raise ValueError(f"grid {grid} outside [1, {TRACE_MAX_WG}]")
         n = grid * TRACE_RECORDS
@@ -58,10 +59,15 @@ class Workspace:
         t_ref = min(h.t0 for h in heads)
         out = []
         self.trace_xcd = [(h.tag >> 12) & 15 for h in heads]
+        self.trace_clock_mhz = []
         for g, h in enumerate(heads):
+            clk = buf[g * TRACE_RECORDS + 1]
+            if clk.tag >> 24 != TRACE_CLOCK:
+                raise KosError(f"workgroup {g}: record 1 is not a clock record")
+            self.trace_clock_mhz.append(100.0 * clk.t0 / clk.dt if clk.dt else 0.0)
             used = h.tag & 0xFFF
             recs = []
-            for i in range(1, min(used, TRACE_RECORDS)):
+            for i in range(2, min(used, TRACE_RECORDS)):
                 r = buf[g * TRACE_RECORDS + i]
                 t0 = (r.t0 - t_ref) * tick_us
                 recs.append((TRACE_KINDS.get(r.tag >> 24, str(r.tag >> 24)), r.tag & 0xFFFFFF, t0,

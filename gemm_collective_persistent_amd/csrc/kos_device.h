@@ -210,11 +210,13 @@ __device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg(
 
 struct Tracer {
   kos_trace_rec* row;   // this workgroup's row; null when tracing is off
-  uint32_t n;           // records used, header included
-  uint64_t t_begin;
+  uint32_t n;           // records used, header and clock record included
+  uint64_t t_begin;     // constant-rate counter at the start
+  uint64_t c_begin;     // shader-clock counter at the start
 
   __device__ __forceinline__ explicit Tracer(kos_trace_rec* base)
-      : row(base ? base + (size_t)blockIdx.x * KOS_TRACE_RECORDS : nullptr), n(1), t_begin(now()) {}
+      : row(base ? base + (size_t)blockIdx.x * KOS_TRACE_RECORDS : nullptr), n(2), t_begin(now()),
+        c_begin(row ? __builtin_amdgcn_s_memtime() : 0) {}
   __device__ __forceinline__ bool on() const { return row != nullptr; }
   // The constant-rate counter when tracing, else 0.
   __device__ __forceinline__ uint64_t now() const { return row ? __builtin_amdgcn_s_memrealtime() : 0; }
@@ -230,15 +232,22 @@ struct Tracer {
     }
     ++n;
   }
-  // The header: start, lifetime, arrival ticket, the accelerator complex
-  // die (XCD) the workgroup runs on, and the record count.
+  // The header (start, lifetime, arrival ticket, the accelerator complex die
+  // (XCD) the workgroup runs on, the record count) and the clock record
+  // (shader-clock cycles over the same lifetime).
   __device__ __forceinline__ void finish(uint32_t ticket) {
     if (!row || threadIdx.x != 0) return;
+    const uint64_t cycles = __builtin_amdgcn_s_memtime() - c_begin;
     kos_trace_rec r;
     r.t0 = t_begin;
     r.dt = (uint32_t)(__builtin_amdgcn_s_memrealtime() - t_begin);
     r.tag = (ticket << 16) | (xcd_id() << 12) | (n < KOS_TRACE_RECORDS ? n : KOS_TRACE_RECORDS);
     row[0] = r;
+    kos_trace_rec c;
+    c.t0 = cycles;
+    c.dt = r.dt;
+    c.tag = (uint32_t)KOS_TR_CLOCK << 24;
+    row[1] = c;
   }
 };
 

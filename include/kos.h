@@ -118,12 +118,15 @@ typedef struct kos_opts {
  * 0..grid-1) owns records [g*KOS_TRACE_RECORDS, (g+1)*KOS_TRACE_RECORDS).
  * Its record 0 is a header: t0 = when it started, dt = its lifetime, tag =
  * (arrival ticket << 16) | (XCD it ran on << 12) | records written (header
- * included, at most KOS_TRACE_RECORDS; later pieces of work are dropped).  Every other record
- * is one piece of work: t0 = start, dt = duration, tag = (kos_trace_kind
- * << 24) | entry index (low 24 bits).  Times are ticks of the GPU's
- * constant-rate 100 MHz counter (s_memrealtime).  Used for the idle-CU
- * fraction: the share of workgroup-time outside work records, waits
- * included, over the kernel's span. */
+ * and clock record included, at most KOS_TRACE_RECORDS; later pieces of work
+ * are dropped).  Record 1 is the clock record: t0 = shader-clock cycles
+ * (s_memtime) over the workgroup's lifetime, dt = the lifetime again, tag =
+ * KOS_TR_CLOCK << 24, so t0 / dt is the clock the workgroup ran at, in units
+ * of 100 MHz.  Every other record is one piece of work: t0 = start, dt =
+ * duration, tag = (kos_trace_kind << 24) | entry index (low 24 bits).  Times
+ * are ticks of the GPU's constant-rate 100 MHz counter (s_memrealtime).  Used
+ * for the idle-CU fraction (the share of workgroup-time outside work records,
+ * waits included, over the kernel's span) and the clock under load. */
 #define KOS_TRACE_RECORDS 512
 #define KOS_TRACE_MAX_WG 256
 typedef struct kos_trace_rec {
@@ -140,7 +143,8 @@ typedef enum kos_trace_kind {
   KOS_TR_SCAN = 6,    /* a dispatch scan entry (one expert)                     */
   KOS_TR_PUSH = 7,    /* a combine push slab                                    */
   KOS_TR_FOLD = 8,    /* a combine fold block                                   */
-  KOS_TR_TILE2 = 9    /* a combine down tile                                    */
+  KOS_TR_TILE2 = 9,   /* a combine down tile                                    */
+  KOS_TR_CLOCK = 10   /* record 1: shader-clock cycles over the lifetime        */
 } kos_trace_kind;
 
 /* Fills `o` with the defaults (FUSED, default crew, band order, full grid). */

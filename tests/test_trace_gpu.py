@@ -46,6 +46,9 @@ def test_ag_trace_covers_every_entry(kos):
     sm = summarize(tl)
     assert 0.0 <= sm["wait_frac"] <= sm["idle_frac"] <= 1.0
     assert sm["kinds"]["tile"]["n"] == 16
+    # clock record: every workgroup ran between 100 MHz and the 2.4 GHz peak
+    assert len(ws.trace_clock_mhz) == grid
+    assert all(100.0 <= f <= 2500.0 for f in ws.trace_clock_mhz), ws.trace_clock_mhz[:8]
 
 
 def test_trace_off_leaves_header_untouched(kos):
