@@ -173,6 +173,54 @@ def test_combine_tiny(kos, ws, shape, rank, mode, crew):
     assert_close(O.bf16_to_f64(KI.bf16_bits(out["y"])), O.bf16_to_f64(yref), "y")
 
 
+# Rows per local expert straddling the combine's tile heights (64-, 128- and
+# 256-row tiles): one row, one short of / exactly / one past each height, and
+# a second 256-row unit holding a single row.
+TAIL_COUNTS = [1, 63, 64, 65, 127, 128, 129, 257]
+MOE_TAILS = KI.MoeShape("moe_tails_1r_t417_h256_e8_k2_f128", 44, 1, sum(TAIL_COUNTS) // 2, 256,
+                        len(TAIL_COUNTS), 2, 128)
+
+
+def _tail_logits(s, counts):
+    """Logits whose top-2 routing gives expert e exactly counts[e] pairs:
+    the pair list sorted by expert, token t taking entries t and t + T (two
+    different experts, as no count exceeds T), the first one ranked higher."""
+    T = s.tokens
+    ids = np.repeat(np.arange(len(counts)), counts)
+    assert ids.size == 2 * T and max(counts) <= T
+    g = torch.Generator().manual_seed(44)
+    lg = 0.1 * torch.randn((T, s.experts), generator=g)
+    for t in range(T):
+        lg[t, int(ids[t])] = 10.0
+        lg[t, int(ids[t + T])] = 9.0
+    return lg
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_combine_tile_boundaries(kos, ws, mode):
+    """Expert row counts at and around every tile height: h, the expert
+    outputs and the folded tokens against the oracle."""
+    s, rank = MOE_TAILS, 0
+    say(f"[moe combine tails] mode={mode}")
+    inp = KI.moe_inputs(s, rank, "cuda")
+    inp["logits"] = _tail_logits(s, TAIL_COUNTS).to("cuda")
+    dref = _oracle_dispatch(s, rank, inp)
+    assert dref["counts"].tolist() == TAIL_COUNTS
+    out = _run_combine(kos, ws, s, rank, inp, dref, mode)
+    wg, wu, wd = (KI.bf16_bits(inp[k]) for k in ("wg", "wu", "wd"))
+    go = dref["grouped_offsets"]
+    href = np.zeros((int(go[-1]), s.ffn), np.uint16)
+    for e in range(s.e_local):
+        lo, hi = int(go[e]), int(go[e + 1])
+        href[lo:hi] = O.expert_hidden(dref["grouped"][lo:hi], wg[e], wu[e])
+    assert_close(O.bf16_to_f64(KI.bf16_bits(out["h"])), O.bf16_to_f64(href), "h")
+    yg_ref = O.grouped_ffn(dref["grouped"], go, wg, wu, wd)
+    assert_close(O.bf16_to_f64(KI.bf16_bits(out["yg"])), O.bf16_to_f64(yg_ref), "y_grouped")
+    pc = inp["peer_counts"].cpu().numpy()
+    yref = O.fold(dref["idx"], dref["w"], dref["perm"], dref["offsets"], yg_ref, go, pc, [None], s.world, rank)
+    assert_close(O.bf16_to_f64(KI.bf16_bits(out["y"])), O.bf16_to_f64(yref), "y")
+
+
 @pytest.mark.parametrize("shape", [KI.MOE_DSV3, KI.MOE_QWEN3])
 def test_moe_full_size_sampled(kos, ws, shape):
     """Full expert-layer shapes, rank 0: routing, counts, permutation, offsets
