@@ -60,15 +60,11 @@ struct TileShape {
   static constexpr bool A_HALF = A_BYTES == 512 * NW;
   static constexpr int A_WAVE_BYTES = A_HALF ? 512 : 1024;   // bytes per A load instruction
   static constexpr int A_LOADS = A_HALF ? 1 : A_BYTES / 1024 / NW;   // A loads per wave per stage
-  // B bytes per wave per stage: whole KiB loads, the last one possibly half a
-  // KiB (lanes 0..31; a 256 x 192 tile on eight waves)
-  static constexpr int B_WAVE_BYTES = B_BYTES / NW;
-  static constexpr bool B_HALF_LAST = B_WAVE_BYTES % 1024 == 512;
-  static constexpr int B_LOADS = (B_WAVE_BYTES + 1023) / 1024;       // B loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / NW;                // 1 KiB B loads per wave per stage
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int BROW_CHUNKS = BN / 8;            // 16-byte chunks per B row
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
-  static_assert(B_BYTES % (512 * NW) == 0 && (A_HALF || A_BYTES % (1024 * NW) == 0),
+  static_assert(B_BYTES % (1024 * NW) == 0 && (A_HALF || A_BYTES % (1024 * NW) == 0),
                 "whole loads per wave");
   static_assert(TM >= 1 && TN >= 1, "at least one 32x32 block per wave");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "each wave loads at least 1 KiB of A and of B");
@@ -138,7 +134,7 @@ struct BLayout {
   static constexpr int W = DUAL ? S::BROW_CHUNKS / 2 : S::BROW_CHUNKS;   // chunks per LDS row
   static constexpr int ROW_BYTES = W * 16;
   static constexpr int HALF_BYTES = S::B_BYTES / 2;
-  static_assert(!DUAL || (S::B_WAVE_BYTES * (S::NW / 2) == HALF_BYTES),
+  static_assert(!DUAL || (S::B_LOADS * (S::NW / 2) * 1024 == HALF_BYTES),
                 "dual: the first half of the waves load the gate half, the rest the up half");
   static_assert(!DUAL || S::TN % 2 == 0, "dual: gate and up blocks pair up in each wave");
 };
@@ -155,7 +151,6 @@ struct LoadPlan {
   int b_stride;                                // bytes per k row of B
   int a_lds, b_lds;                            // this wave's bytes into a stage (uniform)
   bool a_on;                                   // this lane loads A (A_HALF: lanes 0..31)
-  bool b_last_on;                              // this lane issues the last B load (B_HALF_LAST: lanes 0..31)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
@@ -171,9 +166,8 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
   using L = BLayout<S, DUAL>;
   const int lane = w.lane, wave = w.wave;
   P.a_lds = wave * S::A_LOADS * S::A_WAVE_BYTES;
-  P.b_lds = S::A_BYTES + wave * S::B_WAVE_BYTES;
+  P.b_lds = S::A_BYTES + wave * S::B_LOADS * 1024;
   P.a_on = !S::A_HALF || lane < 32;
-  P.b_last_on = !S::B_HALF_LAST || lane < 32;
   P.ra = raw_rsrc(A);
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
@@ -190,7 +184,7 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
   P.rb = raw_rsrc(up ? b.p1 : b.p0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
-    int slot = (wave * S::B_WAVE_BYTES + i * 1024) / 16 + lane;   // 16-byte slot in the B stage
+    int slot = (wave * S::B_LOADS + i) * 64 + lane;
     if (up) slot -= L::HALF_BYTES / 16;
     const int k = slot / L::W, p = slot % L::W;
     const int c = b_chunk<L::W>(p, k);
@@ -214,9 +208,8 @@ __device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DU
                                                P.a_off[i], soa, 0, COH_A ? kCpolDevice : 0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i)
-    if (!S::B_HALF_LAST || i < S::B_LOADS - 1 || P.b_last_on)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(P.rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i],
-                                               sob, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(P.rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i], sob,
+                                             0, 0);
 }
 
 // Operand fragments of one k16 step.
