@@ -281,6 +281,29 @@ def ag_pinned(torch, kos, KI, inp, ws, reps, flush):
             "overlap": round((t["unfused"] - t["fused"]) / min(t_copy, t_gemm), 3)}
 
 
+def planned_crews(KI, moe_shape, rows, grid):
+    """The split a per-call cost model would plan (the explainer's kitchen
+    paragraph: a split predicted before each call, which the paper measured
+    slower than a plain fixed one): the crew that finishes its bytes at the
+    published HBM rate when the builders finish their FLOPs at the published
+    MFMA rate, M = grid * t_bytes / (t_bytes + t_flops).  Bytes per op: AG
+    the gather (peer shards read + written, local shard copied); RS the
+    reduction (7 peer slices + own staging read, reduced chunk written);
+    combine the pushes (rows returned to peers, read + written) and the fold
+    (k results read per token, the token written)."""
+    ag, rs, m = KI.AG_QKV, KI.RS_MLP, moe_shape
+    b = {"ag_gemm": 2.0 * ag.world * ag.m_local * ag.k * 2,
+         "gemm_rs": (rs.world + 1) * rs.m_chunk * rs.n * 4.0,
+         "moe_combine": 2.0 * rows * m.hidden * 2 * (m.world - 1) / m.world
+                        + m.tokens * (m.topk + 1) * m.hidden * 2.0}
+    f = {"ag_gemm": ag.flops, "gemm_rs": rs.flops, "moe_combine": rows * m.flops_per_row}
+    out = {}
+    for n in b:
+        tb, tf = b[n] / (PEAK_HBM_GBS * 1e9), f[n] / (PEAK_BF16_TFLOPS * 1e12)
+        out[n] = max(1, min(grid - 1, round(grid * tb / (tb + tf))))
+    return out
+
+
 def rs_order_ablation(torch, kos, KI, inp, ws, reps, flush):
     """GEMM+reduce-scatter in band order (the design) and row order (the
     slower ablation the explainer compares it with), fused, at rank 7 (whose
@@ -434,6 +457,18 @@ def main():
                 fn()
             pb, _ = time_ops(torch, ops_b, reps, ws, flush)
             base[label] = {n: round(t, 4) for n, t in zip(names, pb)}
+        # the planned split: a FIXED crew sized per op by the cost model
+        grid = int(kos.lib.kos_device_cu_count())
+        crews = planned_crews(KI, moe_shape, rows, grid)
+        planned = {}
+        for n, crew in crews.items():
+            ops_p = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=1, n_movers=crew))
+            if n == "moe_combine":
+                ops_p["moe_dispatch"]()   # the combine reads the dispatch's outputs
+            ops_p[n]()
+            planned[n] = {"crew": crew, "ms": round(time_ops(torch, [(n, ops_p[n])], reps, ws, flush)[0][0], 4)}
+        extra["planned_split"] = planned
+        extra["speedup_vs_planned_split"] = {n: round(planned[n]["ms"] / per[names.index(n)], 3) for n in planned}
         fixed = {n: min(base[k][n] for k in base if k.startswith("fixed")) for n in names}
         extra["baselines_ms"] = base
         extra["speedup_vs_unfused"] = {n: round(base["unfused"][n] / t, 3) for n, t in zip(names, per)}
