@@ -112,16 +112,21 @@ def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=Fal
 
 
 def source_digest() -> str:
-    """Digest of the kernel sources: ties a stored counter reading to the
-    kernels it was taken on."""
+    """Digest of the kernel sources with comments and whitespace removed:
+    ties a stored counter reading to the kernels it was taken on (an edit to
+    a comment does not change the kernels)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for d in (os.path.join(ROOT, "gemm_collective_persistent_amd", "csrc"), os.path.join(ROOT, "include")):
         for name in sorted(os.listdir(d)):
             if name.endswith((".hip", ".h")):
+                with open(os.path.join(d, name)) as f:
+                    text = f.read()
+                text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+                text = re.sub(r"//[^\n]*", "", text)
                 h.update(name.encode())
-                with open(os.path.join(d, name), "rb") as f:
-                    h.update(f.read())
+                h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -111,10 +111,6 @@ __device__ inline bool wg_observe(const uint32_t* counter, uint32_t target, WsHe
 __device__ __forceinline__ void st_dev_b32(void* p, uint32_t v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev_b64(void* p, u32x2 v) {   // p 8-byte aligned
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Device-scope (sc1) loads of data written by other workgroups of the same
 // launch (compiler-visible atomics; no cache invalidation needed).
@@ -274,26 +270,6 @@ __device__ inline void wg_copy_dev(void* __restrict__ dst, const void* __restric
     for (int u = 0; u < U; ++u) d.st128((i + u * nt) * 16u, v[u]);
   }
   for (; i < n; i += nt) d.st128(i * 16u, __builtin_nontemporal_load(&s[i]));
-}
-
-// Copies `bytes` (a multiple of 16) from src to dst with the whole
-// workgroup; consecutive threads touch consecutive 16-byte chunks and each
-// thread keeps 8 loads in flight.
-__device__ inline void wg_copy(void* __restrict__ dst, const void* __restrict__ src, size_t bytes) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
-  const size_t n = bytes >> 4;
-  const size_t nt = blockDim.x;
-  size_t i = threadIdx.x;
-  constexpr int U = 8;
-  for (; i + (U - 1) * nt < n; i += U * nt) {
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + u * nt]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) d[i + u * nt] = v[u];
-  }
-  for (; i < n; i += nt) d[i] = __builtin_nontemporal_load(&s[i]);
 }
 
 // ---------------------------------------------------------------------------
