@@ -309,6 +309,36 @@ def planned_crews(KI, moe_shape, rows, grid):
     return out
 
 
+def rest_of_layer(torch, kos, KI, inp, ws, reps, flush):
+    """The other two fused GEMM+collectives of a TP+SP transformer layer at
+    the QKV shape's width -- MLP-up all-gather+GEMM (rank 0) and the
+    attention output projection GEMM+reduce-scatter (rank 7) -- fused and
+    unfused, and the four fused collectives of the layer together (QKV and
+    MLP-down taken from the timed step)."""
+    res = {}
+    ag, rs = KI.AG_MLPUP, KI.RS_OUTPROJ
+    a = KI.ag_inputs(ag, 0, "cuda")
+    g = torch.empty((ag.m, ag.k), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((ag.m, ag.n), dtype=torch.bfloat16, device="cuda")
+    r = KI.rs_inputs(rs, 7, "cuda")
+    part = torch.empty((rs.m, rs.n), dtype=torch.float32, device="cuda")
+    y = torch.empty((rs.m_chunk, rs.n), dtype=torch.float32, device="cuda")
+    for name, shape, call in (
+            ("ag_mlpup", ag, lambda o: kos.ag_gemm(a["a_local"], a["a_peers"], a["w"], g, c, 0, ws, o)),
+            ("rs_outproj", rs, lambda o: kos.gemm_rs(r["a"], r["w"], r["peer_slices"], part, y, 7, ws, o))):
+        t = {}
+        for label, mode in (("fused", 0), ("unfused", 2)):
+            o = kos.opts(mode=mode)
+            fn = lambda o=o, call=call: call(o)  # noqa: E731
+            fn()
+            t[label] = time_ops(torch, [(name, fn)], reps, ws, flush)[0][0]
+        res[name] = {"workload": shape.name, "ms": round(t["fused"], 4),
+                     "tflops": round(shape.flops / (t["fused"] * 1e-3) / 1e12, 1),
+                     "unfused_ms": round(t["unfused"], 4), "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3)}
+    del a, g, c, r, part, y
+    return res
+
+
 def rs_order_ablation(torch, kos, KI, inp, ws, reps, flush):
     """GEMM+reduce-scatter in band order (the design) and row order (the
     slower ablation the explainer compares it with), fused, at rank 7 (whose
@@ -490,6 +520,13 @@ def main():
         extra["ag_gemm_pinned_host_peers"] = ag_pinned(torch, kos, KI, inp, ws, reps, flush)
         # reduce-scatter band order vs row order
         extra["gemm_rs_band_vs_row"] = rs_order_ablation(torch, kos, KI, inp, ws, reps, flush)
+        # the rest of the TP+SP layer, and the layer's four fused collectives
+        rest = rest_of_layer(torch, kos, KI, inp, ws, reps, flush)
+        t4 = per[names.index("ag_gemm")] + per[names.index("gemm_rs")] + rest["ag_mlpup"]["ms"] + \
+            rest["rs_outproj"]["ms"]
+        f4 = KI.AG_QKV.flops + KI.RS_MLP.flops + KI.AG_MLPUP.flops + KI.RS_OUTPROJ.flops
+        rest["tp_sp_layer"] = {"ms": round(t4, 4), "tflops": round(f4 / (t4 * 1e-3) / 1e12, 1)}
+        extra["tp_sp_layer"] = rest
     if not args.no_cpu:
         cpu = cpu_baseline(inp, moe_shape)
     else:

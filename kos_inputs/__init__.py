@@ -116,6 +116,12 @@ MOE_DSV3 = MoeShape("moe_dsv3_8r_t4096_h7168_e256_k8_f2048", 4, 8, 4096, 7168,
 MOE_QWEN3 = MoeShape("moe_qwen3_8r_t8192_h4096_e128_k8_f1536_zipf1.1", 5, 8,
                      8192, 4096, 128, 8, 1536, zipf_s=1.1)
 
+# the rest of a TP+SP transformer layer at the QKV shape's model width
+# (hidden 8192, 8 ranks): MLP-up (gate and up, 2 x 3584 columns per rank)
+# and the attention output projection (1024 columns of attention per rank)
+AG_MLPUP = AgShape("ag_mlpup_8r_4096x8192x7168", 10, 8, 512, 8192, 7168)
+RS_OUTPROJ = RsShape("rs_outproj_8r_4096x1024x8192", 11, 8, 4096, 1024, 8192)
+
 RS_TINY = RsShape("rs_tiny_4r_256x256x256", 8, 4, 256, 256, 256)
 RS_MID = RsShape("rs_mid_4r_2048x192x384", 9, 4, 2048, 192, 384)
 

@@ -122,3 +122,19 @@ def test_ag_qkv_full_size_sampled(kos, ws, mode):
     rows = np.sort(rng.choice(s.m, 96, replace=False))
     cref = O.round_bf16(O.gemm(gref[rows], KI.bf16_bits(inp["w"])))
     assert_close(O.bf16_to_f64(KI.bf16_bits(c)[rows]), O.bf16_to_f64(cref), "C rows")
+
+
+def test_ag_mlpup_full_size_sampled(kos, ws):
+    """MLP-up shape (8 ranks, 4096 x 8192 . 8192 x 7168, 256 x 256 tiles):
+    gathered matrix bit-exact, sampled rows of C within tolerance."""
+    s = KI.AG_MLPUP
+    say("[ag mlp-up full]")
+    inp, g, c = _run(kos, ws, s, 3, False, torch.bfloat16, kos.opts())
+    peers = [None if t is None else KI.bf16_bits(t) for t in inp["a_peers"]]
+    shards = [KI.bf16_bits(inp["a_local"]) if p == 3 else peers[p] for p in range(s.world)]
+    gref = O.gather(shards)
+    assert np.array_equal(KI.bf16_bits(g), gref)
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(s.m, 64, replace=False))
+    cref = O.round_bf16(O.gemm(gref[rows], KI.bf16_bits(inp["w"])))
+    assert_close(O.bf16_to_f64(KI.bf16_bits(c)[rows]), O.bf16_to_f64(cref), "C rows")

@@ -100,3 +100,24 @@ def test_rs_mlp_full_size(kos, ws, rank):
     assert_close(y_band[rows].cpu().numpy(), yref, "y rows")
     other = np.sort(rng.choice(s.m, 32, replace=False))
     assert_close(part_b[other].cpu().numpy(), O.gemm(a[other], w), "outbound partial rows")
+
+
+def test_rs_outproj_full_size(kos, ws):
+    """Attention output-projection shape (8 ranks, 4096 x 1024 . 1024 x 8192,
+    rank 7): band and row order bit-identical; sampled rows within
+    tolerance."""
+    s, rank = KI.RS_OUTPROJ, 7
+    say("[rs out-proj full]")
+    inp, part_b, y_band = _run(kos, ws, s, rank, False, kos.opts(rs_order=0))
+    _, part_r, y_row = _run(kos, ws, s, rank, False, kos.opts(rs_order=1), inp=inp)
+    assert torch.equal(y_band, y_row) and torch.equal(part_b, part_r)
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(s.m_chunk, 48, replace=False))
+    a = KI.bf16_bits(inp["a"])
+    w = KI.bf16_bits(inp["w"])
+    own_rows = rank * s.m_chunk + rows
+    yref = O.gemm(a[own_rows], w)
+    for p in range(s.world):
+        if p != rank:
+            yref += inp["peer_slices"][p][rows].cpu().numpy().astype(np.float64)
+    assert_close(y_band[rows].cpu().numpy(), yref, "y rows")
