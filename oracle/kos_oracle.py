@@ -15,7 +15,9 @@ order the pages describe them:
   add of the partial results after a row-parallel GEMM [KOSMOS explainer,
   "Start with the problem" paragraph];
 * the expert layer "from router to fold": tokens travel to the rank that holds
-  their expert, results travel back [same paragraph; KOSMOS arXiv abstract].
+  their expert, results travel back [same paragraph; KOSMOS arXiv abstract];
+* the same two TP+SP collectives with MXFP8 operands [KOSMOS arXiv abstract],
+  the format taken from the OCP Microscaling specification v1.0.
 
 Arithmetic is float64 (NumPy/BLAS), which is exact for every integer-valued
 case and more accurate than the kernels' fp32 accumulation otherwise.  bf16
@@ -115,9 +117,16 @@ def gemm_rs(a_bits, w_bits, peer_slices, rank: int):
 
     Returns (partial fp32 [M,N], y fp32 [M/R,N]) with
     y = sum over p = 0..R-1, ascending, of X_p, X_rank = P[chunk rank]."""
+    partial = gemm(a_bits, w_bits).astype(np.float32)   # what the builders store
+    return partial, reduce_chunk(partial, peer_slices, rank)
+
+
+def reduce_chunk(partial, peer_slices, rank: int) -> np.ndarray:
+    """This rank's chunk of the reduce-scatter: y = sum over p = 0..R-1,
+    ascending, of X_p, with X_rank = rows [rank*M/R, (rank+1)*M/R) of the fp32
+    ``partial`` and X_p = ``peer_slices[p]``; summed in float64, returned as
+    float32."""
     R = len(peer_slices)
-    p_full = gemm(a_bits, w_bits)
-    partial = p_full.astype(np.float32)          # what the builders store
     M = partial.shape[0]
     mc = M // R
     acc = np.zeros((mc, partial.shape[1]), dtype=np.float64)
@@ -126,7 +135,85 @@ def gemm_rs(a_bits, w_bits, peer_slices, rank: int):
             acc += partial[rank * mc:(rank + 1) * mc].astype(np.float64)
         else:
             acc += np.asarray(peer_slices[p], dtype=np.float32).astype(np.float64)
-    return partial, acc.astype(np.float32)
+    return acc.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 operands (the same two collectives with microscaled fp8 inputs)
+# ---------------------------------------------------------------------------
+#
+# The pages report MXFP8 speed-ups for the same fused collectives [KOSMOS
+# arXiv abstract] and do not restate the format.  Its definition is the OCP
+# Microscaling (MX) specification v1.0: a block of 32 consecutive elements
+# shares one E8M0 scale (the power of two 2^(s-127), s = 255 is NaN); each
+# element is FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+# infinities; S.1111.111 is NaN; exponent field 0 holds the subnormals
+# m/8 * 2^-6).  The value of element k of a row is its E4M3 value times
+# 2^(s_block(k) - 127).  Reading for the products: blocks run along K (the
+# reduction dimension) for both operands, so the row of A and the column of
+# the weight are both scaled per 32-element piece of K; the weight is stored
+# N x K (each output column's K values contiguous, with its scales), the
+# layout MX products consume.
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of FP8 E4M3 codes (uint8): (-1)^s * 2^(e-7) * (1 + m/8)
+    for exponent field e >= 1, (-1)^s * 2^-6 * m/8 for e = 0; the codes
+    0x7F and 0xFF are NaN [OCP MX v1.0, FP8 E4M3]."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scale codes (uint8): 2^(s - 127), s = 255 is NaN [OCP MX
+    v1.0, E8M0]."""
+    s = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    v = np.ldexp(np.ones(s.shape), (s - 127).astype(np.int32))
+    return np.where(s == 255, np.nan, v)
+
+
+MX_BLOCK = 32
+
+
+def mx_to_f64(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Rows of MX elements as float64: data uint8 [R, K] (E4M3 codes), scales
+    uint8 [R, K/32] (E8M0, block b covers columns [32b, 32b+32))."""
+    d = np.asarray(data, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8)
+    R, K = d.shape
+    assert K % MX_BLOCK == 0 and s.shape == (R, K // MX_BLOCK)
+    return e4m3_to_f64(d) * np.repeat(e8m0_to_f64(s), MX_BLOCK, axis=1)
+
+
+def gemm_mx(a, a_scales, w, w_scales) -> np.ndarray:
+    """C = A . W^T in float64: A [M,K] and W [N,K] MX operands (E4M3 codes
+    with per-32 E8M0 scales along K)."""
+    return mx_to_f64(a, a_scales) @ mx_to_f64(w, w_scales).T
+
+
+def ag_gemm_mx(a_local, s_local, a_peers, s_peers, w, w_scales, rank: int, out_dtype: str = "bf16"):
+    """All-gather of MX shards (codes and their scales, rank order; a bit
+    copy), then the MX product.  Returns (gathered codes [R*m,K], gathered
+    scales [R*m,K/32], C) with C as in ``ag_gemm``."""
+    R = len(a_peers)
+    g = np.concatenate([np.asarray(a_local if p == rank else a_peers[p], dtype=np.uint8) for p in range(R)], axis=0)
+    gs = np.concatenate([np.asarray(s_local if p == rank else s_peers[p], dtype=np.uint8) for p in range(R)], axis=0)
+    c = gemm_mx(g, gs, w, w_scales)
+    if out_dtype == "bf16":
+        return g, gs, round_bf16(c)
+    return g, gs, c.astype(np.float32)
+
+
+def gemm_rs_mx(a, a_scales, w, w_scales, peer_slices, rank: int):
+    """MX product then reduce-scatter, as ``gemm_rs``: returns (partial fp32
+    [M,N], y fp32 [M/R,N])."""
+    partial = gemm_mx(a, a_scales, w, w_scales).astype(np.float32)
+    return partial, reduce_chunk(partial, peer_slices, rank)
 
 
 # ---------------------------------------------------------------------------
