@@ -120,6 +120,68 @@ def gemm_rs(a: torch.Tensor, w: torch.Tensor, peer_slices: Sequence[Optional[tor
                           ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
 
 
+def _need_scales(t: torch.Tensor, rows: int, k: int, what: str) -> None:
+    """MX scales in the slab layout: uint8 [k/64, rows, 2]."""
+    _need(t, torch.uint8, what, 3)
+    if tuple(t.shape) != (k // 64, rows, 2):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {(k // 64, rows, 2)}")
+
+
+def ag_gemm_mx(a_local: torch.Tensor, a_local_scales: torch.Tensor,
+               a_peers: Sequence[Optional[torch.Tensor]], a_peer_scales: Sequence[Optional[torch.Tensor]],
+               w: torch.Tensor, w_scales: torch.Tensor, a_gathered: torch.Tensor,
+               a_gathered_scales: torch.Tensor, c: torch.Tensor, rank: int, ws: Workspace,
+               o: Optional[Opts] = None, stream=None) -> None:
+    """kos_ag_gemm_mx: gathers E4M3 shards and their scales (uint8 codes;
+    scales uint8 [k/64, rows, 2]); c = gathered . w^T with w E4M3 [n, k]."""
+    world = len(a_peers)
+    _need(a_local, torch.uint8, "a_local", 2)
+    m_local, k = a_local.shape
+    _need_scales(a_local_scales, m_local, k, "a_local_scales")
+    _need(w, torch.uint8, "w", 2)
+    n = w.shape[0]
+    _need_scales(w_scales, n, k, "w_scales")
+    _need(a_gathered, torch.uint8, "a_gathered", 2)
+    _need_scales(a_gathered_scales, world * m_local, k, "a_gathered_scales")
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("c must be bf16 or fp32")
+    _need(c, c.dtype, "c", 2)
+    for p in range(world):
+        if p != rank:
+            _need(a_peers[p], torch.uint8, f"a_peers[{p}]", 2)
+            _need_scales(a_peer_scales[p], m_local, k, f"a_peer_scales[{p}]")
+    peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(a_peers)])
+    speers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(a_peer_scales)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_ag_gemm_mx(world, rank, m_local, k, n, _p(a_local), _p(a_local_scales), peers, speers,
+                             _p(w), _p(w_scales), _p(a_gathered), _p(a_gathered_scales), _p(c),
+                             KOS_BF16 if c.dtype == torch.bfloat16 else KOS_F32,
+                             ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def gemm_rs_mx(a: torch.Tensor, a_scales: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor,
+               peer_slices: Sequence[Optional[torch.Tensor]], partial: torch.Tensor, y: torch.Tensor,
+               rank: int, ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+    """kos_gemm_rs_mx: partial = a . w^T (E4M3 codes, slab-layout scales,
+    fp32 result); y = reduce of chunk `rank`."""
+    world = len(peer_slices)
+    _need(a, torch.uint8, "a", 2)
+    m, k = a.shape
+    _need_scales(a_scales, m, k, "a_scales")
+    _need(w, torch.uint8, "w", 2)
+    n = w.shape[0]
+    _need_scales(w_scales, n, k, "w_scales")
+    _need(partial, torch.float32, "partial", 2)
+    _need(y, torch.float32, "y", 2)
+    for p, t in enumerate(peer_slices):
+        if p != rank:
+            _need(t, torch.float32, f"peer_slices[{p}]", 2)
+    peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(peer_slices)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_gemm_rs_mx(world, rank, m, k, n, _p(a), _p(a_scales), _p(w), _p(w_scales), peers,
+                             _p(partial), _p(y), ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
 def moe_shape(world, rank, tokens, hidden, experts, topk, ffn) -> MoeShape:
     return MoeShape(world, rank, tokens, hidden, experts, topk, ffn, 0)
 

@@ -15,18 +15,32 @@
 //   head[1]  tiles: local shard first, then the remote shards in the same
 //            order; within a shard row block ascending, then column tile.
 // Ready counter per (shard, row block): the number of its slices landed.
+//
+// MXFP8 variant (same kernel, MX tile shape): the shards are E4M3 rows with
+// slab-packed E8M0 scales (kos_tile_mx.h); a move copies a slice's rows and
+// then its scales in every slab before it is counted.
+#include <algorithm>
+
 #include "kos_host.h"
 #include "kos_tile.h"
+#include "kos_tile_mx.h"
 
 namespace kos {
 
 struct AgParams {
   int32_t world, rank;
   int32_t m_local, k, n;
-  const uint16_t* a_local;
-  const uint16_t* peers[8];
-  const uint16_t* w;
-  uint16_t* gathered;
+  // operands as bytes: bf16 rows of 2k bytes (W k x n), or E4M3 rows of k
+  // bytes (W n x k)
+  const char* a_local;
+  const char* peers[8];
+  const char* w;
+  char* gathered;
+  // MX only: slab-packed scales of the same rows (slab stride 2 x rows)
+  const uint8_t* sc_local;
+  const uint8_t* sc_peers[8];
+  const uint8_t* w_sc;
+  uint8_t* sc_gathered;
   void* c;
   int32_t c_f32;
   int32_t n_movers;       // tickets below this start as movers
@@ -45,6 +59,40 @@ struct AgParams {
   kos_trace_rec* trace;   // null: tracing off
 };
 
+// One output tile's K loop over the BM rows of A at `a_rows` (bytes) and
+// column tile nt of W.  MX: `a_sc` is the rows' slab-0 scales, `a_slab` the
+// slab stride of that scale array.  COH: the rows were written by this
+// launch.
+template <class S, bool COH>
+__device__ __forceinline__ void build_tile(f32x16 (&acc)[S::TM][S::TN], const AgParams& p, const char* a_rows,
+                                           const uint8_t* a_sc, int64_t a_slab, int nt) {
+  const int64_t K = p.k, N = p.n;
+  if constexpr (S::MX) {
+    const MxSrc a{reinterpret_cast<const uint8_t*>(a_rows), a_sc, K, a_slab};
+    const MxSrc b{reinterpret_cast<const uint8_t*>(p.w) + (int64_t)nt * S::BN * K, p.w_sc + (int64_t)nt * S::BN * 2,
+                  K, 2 * N};
+    tile_mainloop_mx<S, COH>(acc, a, S::BM, b, S::BN, p.k);
+  } else {
+    const BSrc b{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)nt * S::BN, nullptr, N};
+    tile_mainloop<S, false, COH>(acc, reinterpret_cast<const uint16_t*>(a_rows), K, S::BM, b, p.k);
+  }
+}
+
+// The scales of `rows` rows (a multiple of 8) in each of `slabs` slabs:
+// 2*rows bytes at dst + s*dst_slab from src + s*src_slab, 16-byte pieces,
+// device-coherent stores (the entry point keeps slabs*dst_slab below 2^31).
+__device__ inline void copy_scale_rows(uint8_t* dst, const uint8_t* src, int rows, int slabs, int64_t dst_slab,
+                                       int64_t src_slab) {
+  const int per = rows * 2 / 16;
+  const int n = slabs * per;
+  const DevBuf d(dst);
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const int sl = t / per, c = t % per;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + sl * src_slab) + c);
+    d.st128((uint32_t)(sl * dst_slab) + c * 16u, v);
+  }
+}
+
 template <class S>
 __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
   constexpr int BM = S::BM, BN = S::BN;
@@ -57,6 +105,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
   const AgParams& p = ps;
   WsHeader* h = p.ws;
   const int64_t K = p.k, N = p.n;
+  const int64_t RB = S::MX ? K : 2 * K;   // bytes per A row
   Tracer tr(p.trace);
   const uint32_t ticket = wg_ticket(h, &slots);
 
@@ -69,7 +118,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
       if (i >= (uint32_t)p.n_move) break;
       const uint64_t t0 = tr.now();
       int shard, rem;
-      const uint16_t* src_shard;
+      const char* src_shard;
       if ((int32_t)i < n_remote) {
         const int q = 1 + (int)i / per_shard;
         rem = (int)i % per_shard;
@@ -82,8 +131,12 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
       }
       const int rb = rem / p.moves_per_rb;
       const int64_t row = (int64_t)rb * BM + (int64_t)(rem % p.moves_per_rb) * p.rows_per_move;
-      wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * K, src_shard + row * K,
-                  (size_t)p.rows_per_move * K * 2);
+      wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * RB, src_shard + row * RB,
+                  (size_t)p.rows_per_move * RB);
+      if constexpr (S::MX)
+        copy_scale_rows(p.sc_gathered + ((int64_t)shard * p.m_local + row) * 2,
+                        (shard == p.rank ? p.sc_local : p.sc_peers[shard]) + row * 2, p.rows_per_move, K / 64,
+                        (int64_t)p.world * p.m_local * 2, (int64_t)p.m_local * 2);
       wg_publish(&p.ready[shard * p.rb_per_shard + rb], 1u);
       tr.put(KOS_TR_MOVE, i, t0);
     }
@@ -105,12 +158,15 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
       const int rem = (int)j % per_q;
       const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
       const int shard = (p.rank + q) % p.world;
-      BSrc b{p.w + (int64_t)nt * BN, nullptr, N};
       uint64_t t0 = tr.now();
       if (q == 0) {
-        tile_mainloop<S>(acc, p.a_local + (int64_t)rb * BM * K, K, BM, b, p.k);
+        build_tile<S, false>(acc, p, p.a_local + (int64_t)rb * BM * RB, p.sc_local + (int64_t)rb * BM * 2,
+                             (int64_t)p.m_local * 2, nt);
       } else {
-        const uint16_t* A = p.gathered + ((int64_t)shard * p.m_local + (int64_t)rb * BM) * K;
+        const int64_t r0 = (int64_t)shard * p.m_local + (int64_t)rb * BM;
+        const char* A = p.gathered + r0 * RB;
+        const uint8_t* As = p.sc_gathered + r0 * 2;
+        const int64_t slab = (int64_t)p.world * p.m_local * 2;
         if (p.wait_flags) {
           // rows written by movers of this launch: wait for them, read device-coherent
           if (!wg_observe(&p.ready[shard * p.rb_per_shard + rb], (uint32_t)p.moves_per_rb, h, p.spin_limit, j,
@@ -118,9 +174,9 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
             break;
           tr.put(KOS_TR_WAIT, j, t0);
           t0 = tr.now();
-          tile_mainloop<S, false, true>(acc, A, K, BM, b, p.k);
+          build_tile<S, true>(acc, p, A, As, slab, nt);
         } else {
-          tile_mainloop<S>(acc, A, K, BM, b, p.k);
+          build_tile<S, false>(acc, p, A, As, slab, nt);
         }
       }
       const int64_t row0 = (int64_t)shard * p.m_local + (int64_t)rb * BM;
@@ -146,7 +202,7 @@ static kos_status launch_ag(const AgParams& p, int grid, hipStream_t stream) {
 }
 
 static kos_status launch_ag_tile(int bm, int bn, const AgParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256>>(p, grid, s);
+  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256, 4, 2, 4>>(p, grid, s);
   if (bm == 256 && bn == 192) return launch_ag<TileShape<256, 192>>(p, grid, s);
   if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128>>(p, grid, s);
   if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128>>(p, grid, s);
@@ -179,29 +235,67 @@ static void pick_ag_tile(int64_t world, int64_t m_local, int64_t n, int grid, in
 
 using namespace kos;
 
-extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
-                                  const void* a_local, const void* const* a_peers, const void* w,
-                                  void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
-                                  size_t ws_bytes, void* stream) {
+namespace kos {
+
+// Arguments of one call, bf16 or MX.
+struct AgCall {
+  bool mx;
+  int32_t world, rank;
+  int64_t m_local, k, n;
+  const void* a_local;
+  const void* const* a_peers;
+  const void* w;
+  void* a_gathered;
+  const void* sc_local;
+  const void* const* sc_peers;
+  const void* w_sc;
+  void* sc_gathered;
+  void* c;
+  int32_t c_dtype;
+  const kos_opts* opts;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+};
+
+static kos_status ag_gemm_run(const AgCall& a) {
+  const int32_t world = a.world, rank = a.rank;
+  const int64_t m_local = a.m_local, k = a.k, n = a.n;
   if (world < 1 || world > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", world);
   if (rank < 0 || rank >= world) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", rank, world);
-  if (c_dtype != KOS_BF16 && c_dtype != KOS_F32) return fail(KOS_ERR_ARG, "bad c_dtype %d", c_dtype);
-  if (!a_local || !w || !a_gathered || !c) return fail(KOS_ERR_ARG, "null buffer");
-  if (world > 1 && !a_peers) return fail(KOS_ERR_ARG, "a_peers is NULL");
-  for (int p = 0; p < world; ++p)
-    if (p != rank && !a_peers[p]) return fail(KOS_ERR_ARG, "a_peers[%d] is NULL", p);
-  if (m_local <= 0 || k <= 0 || n <= 0 || m_local % 64 || k % 64 || n % 64)
+  if (a.c_dtype != KOS_BF16 && a.c_dtype != KOS_F32) return fail(KOS_ERR_ARG, "bad c_dtype %d", a.c_dtype);
+  if (!a.a_local || !a.w || !a.a_gathered || !a.c) return fail(KOS_ERR_ARG, "null buffer");
+  if (a.mx && (!a.sc_local || !a.w_sc || !a.sc_gathered)) return fail(KOS_ERR_ARG, "null scale buffer");
+  if (world > 1 && (!a.a_peers || (a.mx && !a.sc_peers))) return fail(KOS_ERR_ARG, "peer array is NULL");
+  for (int p = 0; p < world; ++p) {
+    if (p == rank) continue;
+    if (!a.a_peers[p]) return fail(KOS_ERR_ARG, "a_peers[%d] is NULL", p);
+    if (a.mx && !a.sc_peers[p]) return fail(KOS_ERR_ARG, "a_peer_scales[%d] is NULL", p);
+  }
+  if (a.mx) {
+    if (m_local <= 0 || k <= 0 || n <= 0 || m_local % 256 || k % 256 || n % 256)
+      return fail(KOS_ERR_SHAPE, "MX: m_local %lld, k %lld, n %lld must be positive multiples of 256",
+                  (long long)m_local, (long long)k, (long long)n);
+  } else if (m_local <= 0 || k <= 0 || n <= 0 || m_local % 64 || k % 64 || n % 64) {
     return fail(KOS_ERR_SHAPE, "m_local %lld, k %lld, n %lld must be positive multiples of 64", (long long)m_local,
                 (long long)k, (long long)n);
+  }
   if (m_local * world > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20))
     return fail(KOS_ERR_SHAPE, "sizes too large");
-  // the tiles address W through 32-bit buffer offsets
-  if (k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
-  if (!aligned16(a_local) || !aligned16(w) || !aligned16(a_gathered) || !aligned16(c))
+  // the tiles address W (bf16) and the scale slabs through 32-bit offsets
+  if (!a.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
+  if (a.mx && (k / 64) * 2 * std::max<int64_t>(m_local * world, n) >= (int64_t(1) << 31))
+    return fail(KOS_ERR_SHAPE, "MX scale arrays must be smaller than 2 GiB");
+  if (!aligned16(a.a_local) || !aligned16(a.w) || !aligned16(a.a_gathered) || !aligned16(a.c))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
-  for (int p = 0; p < world; ++p)
-    if (p != rank && !aligned16(a_peers[p])) return fail(KOS_ERR_ALIGN, "a_peers[%d] not 16-byte aligned", p);
-  kos_status st = check_workspace(ws, ws_bytes);
+  if (a.mx && (!aligned16(a.sc_local) || !aligned16(a.w_sc) || !aligned16(a.sc_gathered)))
+    return fail(KOS_ERR_ALIGN, "scale buffers must be 16-byte aligned");
+  for (int p = 0; p < world; ++p) {
+    if (p == rank) continue;
+    if (!aligned16(a.a_peers[p])) return fail(KOS_ERR_ALIGN, "a_peers[%d] not 16-byte aligned", p);
+    if (a.mx && !aligned16(a.sc_peers[p])) return fail(KOS_ERR_ALIGN, "a_peer_scales[%d] not 16-byte aligned", p);
+  }
+  kos_status st = check_workspace(a.ws, a.ws_bytes);
   if (st != KOS_OK) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
@@ -209,10 +303,11 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   // Movers over device memory: half the grid saturates HBM copy bandwidth
   // and the other half builds the local shard meanwhile; over PCIe a few
   // workgroups saturate the link.
-  if ((st = resolve_opts(opts, dev, CrewDefaults{kCrewHalfGrid, 8, 16, 8}, &o)) != KOS_OK) return st;
+  if ((st = resolve_opts(a.opts, dev, CrewDefaults{kCrewHalfGrid, 8, 16, 8}, &o)) != KOS_OK) return st;
 
-  int bm = 64, bn = 64;
-  pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
+  int bm = 256, bn = 256;   // the MX tile
+  if (!a.mx) pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
+  const int64_t row_bytes = a.mx ? k : 2 * k;
 
   AgParams p{};
   p.world = world;
@@ -220,54 +315,70 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   p.m_local = (int32_t)m_local;
   p.k = (int32_t)k;
   p.n = (int32_t)n;
-  p.a_local = static_cast<const uint16_t*>(a_local);
-  for (int q = 0; q < world; ++q) p.peers[q] = q == rank ? nullptr : static_cast<const uint16_t*>(a_peers[q]);
-  p.w = static_cast<const uint16_t*>(w);
-  p.gathered = static_cast<uint16_t*>(a_gathered);
-  p.c = c;
-  p.c_f32 = c_dtype == KOS_F32;
+  p.a_local = static_cast<const char*>(a.a_local);
+  for (int q = 0; q < world; ++q) p.peers[q] = q == rank ? nullptr : static_cast<const char*>(a.a_peers[q]);
+  p.w = static_cast<const char*>(a.w);
+  p.gathered = static_cast<char*>(a.a_gathered);
+  if (a.mx) {
+    p.sc_local = static_cast<const uint8_t*>(a.sc_local);
+    for (int q = 0; q < world; ++q) p.sc_peers[q] = q == rank ? nullptr : static_cast<const uint8_t*>(a.sc_peers[q]);
+    p.w_sc = static_cast<const uint8_t*>(a.w_sc);
+    p.sc_gathered = static_cast<uint8_t*>(a.sc_gathered);
+  }
+  p.c = a.c;
+  p.c_f32 = a.c_dtype == KOS_F32;
   p.spin_limit = o.spin_limit;
   p.rb_per_shard = (int32_t)(m_local / bm);
   p.tiles_n = (int32_t)(n / bn);
-  // Move entries of about 128 KiB: whole rows, dividing the row block.
-  int rows = (int)((128 * 1024) / (k * 2));
+  // Move entries of about 128 KiB: whole rows, dividing the row block (MX:
+  // a power of two of at least 8 rows, whole 16-byte pieces of scales).
+  int rows = (int)((128 * 1024) / row_bytes);
   if (rows < 1) rows = 1;
   if (rows > bm) rows = bm;
+  if (a.mx) {
+    int r = 8;
+    while (r * 2 <= rows) r *= 2;
+    rows = r;
+  }
   while (bm % rows) --rows;
   p.rows_per_move = rows;
   p.moves_per_rb = bm / rows;
   p.n_move = world * p.rb_per_shard * p.moves_per_rb;
   p.n_tiles = world * p.rb_per_shard * p.tiles_n;
-  p.ws = static_cast<WsHeader*>(ws);
-  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
-  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
+  p.ws = static_cast<WsHeader*>(a.ws);
+  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(a.ws) + kCountersOffset);
+  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(a.ws) + kTraceOffset) : nullptr;
   if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
 
   // A single rank whose gathered output is its own shard has nothing to move.
-  const bool nothing_to_move = world == 1 && a_gathered == a_local;
+  const bool nothing_to_move =
+      world == 1 && a.a_gathered == a.a_local && (!a.mx || a.sc_gathered == a.sc_local);
   if (nothing_to_move) p.n_move = 0;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
   const int grid = o.grid;
+  auto launch = [&](const AgParams& q) {
+    return a.mx ? launch_ag<TileShapeMX<256, 256>>(q, grid, s) : launch_ag_tile(bm, bn, q, grid, s);
+  };
   if (o.mode == KOS_MODE_UNFUSED && nothing_to_move) {
     AgParams gm = p;           // the GEMM alone
     gm.n_movers = 0;
     gm.do_build = 1;
     gm.wait_flags = 0;
-    return launch_ag_tile(bm, bn, gm, grid, s);
+    return launch(gm);
   }
   if (o.mode == KOS_MODE_UNFUSED) {
     AgParams mv = p;           // launch 1: the whole all-gather
     mv.n_movers = grid;
     mv.movers_switch = 0;
     mv.do_build = 0;
-    if ((st = launch_ag_tile(bm, bn, mv, grid, s)) != KOS_OK) return st;
+    if ((st = launch(mv)) != KOS_OK) return st;
     AgParams gm = p;           // launch 2: the whole GEMM
     gm.n_movers = 0;
     gm.n_move = 0;
     gm.do_build = 1;
     gm.wait_flags = 0;
-    return launch_ag_tile(bm, bn, gm, grid, s);
+    return launch(gm);
   }
   if (o.n_movers < 1 || o.n_movers >= grid)
     return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, grid);
@@ -275,5 +386,26 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
   p.movers_switch = o.mode == KOS_MODE_FUSED;
   p.do_build = 1;
   p.wait_flags = 1;
-  return launch_ag_tile(bm, bn, p, grid, s);
+  return launch(p);
+}
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                                  const void* a_local, const void* const* a_peers, const void* w,
+                                  void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return ag_gemm_run(AgCall{false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, nullptr, nullptr,
+                            nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
+}
+
+extern "C" kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                                     const void* a_local, const void* a_local_scales, const void* const* a_peers,
+                                     const void* const* a_peer_scales, const void* w, const void* w_scales,
+                                     void* a_gathered, void* a_gathered_scales, void* c, int32_t c_dtype,
+                                     const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+  return ag_gemm_run(AgCall{true, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, a_local_scales,
+                            a_peer_scales, w_scales, a_gathered_scales, c, c_dtype, opts, ws, ws_bytes, stream});
 }

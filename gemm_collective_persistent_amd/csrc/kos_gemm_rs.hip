@@ -22,16 +22,26 @@
 //            the ready counter of our own tile at (b, column).  The peers'
 //            slices of a band are taken as ready together with ours: every
 //            rank runs the same order at the same pace.
+//
+// MXFP8 variant (same kernel, MX tile shape): A and W are E4M3 rows with
+// slab-packed E8M0 scales (kos_tile_mx.h); partials and the reduction stay
+// fp32.
+#include <algorithm>
+
 #include "kos_host.h"
 #include "kos_tile.h"
+#include "kos_tile_mx.h"
 
 namespace kos {
 
 struct RsParams {
   int32_t world, rank;
   int32_t m, k, n, mc;
-  const uint16_t* a;
-  const uint16_t* w;
+  // operands as bytes: bf16 A m x k and W k x n, or E4M3 A m x k and W n x k
+  const char* a;
+  const char* w;
+  const uint8_t* a_sc;   // MX only: slab-packed scales
+  const uint8_t* w_sc;
   const float* peers[8];
   float* partial;
   float* y;
@@ -146,8 +156,15 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
         col = rem % p.tiles_n;
       }
       const int64_t row0 = (int64_t)chunk * p.mc + (int64_t)band * BM;
-      BSrc b{p.w + (int64_t)col * BN, nullptr, N};
-      tile_mainloop<S>(acc, p.a + row0 * K, K, BM, b, p.k);
+      if constexpr (S::MX) {
+        const MxSrc a{reinterpret_cast<const uint8_t*>(p.a) + row0 * K, p.a_sc + row0 * 2, K, 2 * (int64_t)p.m};
+        const MxSrc b{reinterpret_cast<const uint8_t*>(p.w) + (int64_t)col * BN * K, p.w_sc + (int64_t)col * BN * 2, K,
+                      2 * N};
+        tile_mainloop_mx<S>(acc, a, BM, b, BN, p.k);
+      } else {
+        const BSrc b{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)col * BN, nullptr, N};
+        tile_mainloop<S>(acc, reinterpret_cast<const uint16_t*>(p.a) + row0 * K, K, BM, b, p.k);
+      }
       float* P = p.partial + row0 * N + (int64_t)col * BN;
       if (chunk == p.rank) {   // read by this launch's reducers: device-coherent stores
         const DevBuf pb(P);
@@ -206,23 +223,59 @@ static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hi
 
 using namespace kos;
 
-extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
-                                  const void* w, const float* const* peer_slices, float* partial, float* y,
-                                  const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+namespace kos {
+
+// Arguments of one call, bf16 or MX.
+struct RsCall {
+  bool mx;
+  int32_t world, rank;
+  int64_t m, k, n;
+  const void* a;
+  const void* a_sc;
+  const void* w;
+  const void* w_sc;
+  const float* const* peer_slices;
+  float* partial;
+  float* y;
+  const kos_opts* opts;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+};
+
+static kos_status gemm_rs_run(const RsCall& c) {
+  const int32_t world = c.world, rank = c.rank;
+  const int64_t m = c.m, k = c.k, n = c.n;
+  const void *a = c.a, *w = c.w;
+  const float* const* peer_slices = c.peer_slices;
+  float *partial = c.partial, *y = c.y;
+  const kos_opts* opts = c.opts;
+  void* ws = c.ws;
+  const size_t ws_bytes = c.ws_bytes;
+  void* stream = c.stream;
   if (world < 1 || world > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", world);
   if (rank < 0 || rank >= world) return fail(KOS_ERR_ARG, "rank %d outside [0, %d)", rank, world);
   if (!a || !w || !partial || !y) return fail(KOS_ERR_ARG, "null buffer");
+  if (c.mx && (!c.a_sc || !c.w_sc)) return fail(KOS_ERR_ARG, "null scale buffer");
   if (world > 1 && !peer_slices) return fail(KOS_ERR_ARG, "peer_slices is NULL");
   for (int p = 0; p < world; ++p)
     if (p != rank && !peer_slices[p]) return fail(KOS_ERR_ARG, "peer_slices[%d] is NULL", p);
-  if (m <= 0 || k <= 0 || n <= 0 || m % world || (m / world) % 64 || k % 64 || n % 64)
+  if (c.mx) {
+    if (m <= 0 || k <= 0 || n <= 0 || m % world || (m / world) % 256 || k % 256 || n % 256)
+      return fail(KOS_ERR_SHAPE, "MX: m %lld (m/world), k %lld, n %lld must be positive multiples of 256",
+                  (long long)m, (long long)k, (long long)n);
+  } else if (m <= 0 || k <= 0 || n <= 0 || m % world || (m / world) % 64 || k % 64 || n % 64) {
     return fail(KOS_ERR_SHAPE, "m %lld (m/world a multiple of 64), k %lld, n %lld (multiples of 64) unsupported",
                 (long long)m, (long long)k, (long long)n);
+  }
   if (m > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20)) return fail(KOS_ERR_SHAPE, "sizes too large");
-  // the tiles address W through 32-bit buffer offsets
-  if (k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
+  // the tiles address W (bf16) and the scale slabs through 32-bit offsets
+  if (!c.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
+  if (c.mx && (k / 64) * 2 * std::max(m, n) >= (int64_t(1) << 31))
+    return fail(KOS_ERR_SHAPE, "MX scale arrays must be smaller than 2 GiB");
   if (!aligned16(a) || !aligned16(w) || !aligned16(partial) || !aligned16(y))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  if (c.mx && (!aligned16(c.a_sc) || !aligned16(c.w_sc))) return fail(KOS_ERR_ALIGN, "scale buffers must be 16-byte aligned");
   for (int p = 0; p < world; ++p)
     if (p != rank && !aligned16(peer_slices[p])) return fail(KOS_ERR_ALIGN, "peer_slices[%d] not aligned", p);
   kos_status st = check_workspace(ws, ws_bytes);
@@ -236,7 +289,7 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
 
   const int64_t mc = m / world;
   int bm = 64, bn = 64;
-  if (mc % 256 == 0 && n % 256 == 0) bm = 256, bn = 256;
+  if (c.mx || (mc % 256 == 0 && n % 256 == 0)) bm = 256, bn = 256;
   else if (mc % 256 == 0 && n % 128 == 0) bm = 256, bn = 128;
   else if (mc % 128 == 0 && n % 128 == 0) bm = 128, bn = 128;
 
@@ -247,8 +300,10 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
   p.k = (int32_t)k;
   p.n = (int32_t)n;
   p.mc = (int32_t)mc;
-  p.a = static_cast<const uint16_t*>(a);
-  p.w = static_cast<const uint16_t*>(w);
+  p.a = static_cast<const char*>(a);
+  p.w = static_cast<const char*>(w);
+  p.a_sc = static_cast<const uint8_t*>(c.a_sc);
+  p.w_sc = static_cast<const uint8_t*>(c.w_sc);
   for (int q = 0; q < world; ++q) p.peers[q] = q == rank ? nullptr : peer_slices[q];
   p.partial = partial;
   p.y = y;
@@ -265,18 +320,21 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = o.grid;
+  auto launch = [&](const RsParams& q) {
+    return c.mx ? launch_rs<TileShapeMX<256, 256>>(q, grid, s) : launch_rs_tile(bm, bn, q, grid, s);
+  };
   if (o.mode == KOS_MODE_UNFUSED) {
     RsParams gm = p;            // launch 1: the whole GEMM
     gm.do_build = 1;
     gm.do_reduce = 0;
     gm.n_reducers = 0;
-    if ((st = launch_rs_tile(bm, bn, gm, grid, s)) != KOS_OK) return st;
+    if ((st = launch(gm)) != KOS_OK) return st;
     RsParams rd = p;            // launch 2: the whole reduction
     rd.do_build = 0;
     rd.do_reduce = 1;
     rd.n_reducers = grid;
     rd.wait_flags = 0;
-    return launch_rs_tile(bm, bn, rd, grid, s);
+    return launch(rd);
   }
   // The crew that starts reducing (FUSED, may be empty) or only reduces (FIXED).
   const int min_crew = o.mode == KOS_MODE_FUSED ? 0 : 1;
@@ -287,5 +345,24 @@ extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_
   p.do_build = 1;
   p.do_reduce = 1;
   p.wait_flags = 1;
-  return launch_rs_tile(bm, bn, p, grid, s);
+  return launch(p);
+}
+
+}  // namespace kos
+
+using namespace kos;
+
+extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
+                                  const void* w, const float* const* peer_slices, float* partial, float* y,
+                                  const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_rs_run(RsCall{false, world, rank, m, k, n, a, nullptr, w, nullptr, peer_slices, partial, y, opts, ws,
+                            ws_bytes, stream});
+}
+
+extern "C" kos_status kos_gemm_rs_mx(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
+                                     const void* a_scales, const void* w, const void* w_scales,
+                                     const float* const* peer_slices, float* partial, float* y,
+                                     const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_rs_run(RsCall{true, world, rank, m, k, n, a, a_scales, w, w_scales, peer_slices, partial, y, opts, ws,
+                            ws_bytes, stream});
 }

@@ -44,6 +44,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // the accumulators).
 template <int BM_, int BN_, int STAGES_ = 4, int WGM_ = 2, int WGN_ = 2>
 struct TileShape {
+  static constexpr bool MX = false;                     // bf16 operands
   static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_;
   static constexpr int NW = WGM * WGN;                  // waves

@@ -233,6 +233,60 @@ kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_
                        float* partial, float* y,
                        const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * MXFP8 operands for the two TP+SP collectives [abstract: the same fused
+ * kernels speed up training in MXFP8 as well as in BF16].  The pages do not
+ * restate the format; it is the OCP Microscaling (MX) specification v1.0:
+ * elements are FP8 E4M3 codes (uint8), and every 32 consecutive elements
+ * along K share one E8M0 scale (uint8 s, value 2^(s-127)); element value =
+ * E4M3 value x its block's scale.  Products accumulate in fp32.
+ *
+ * Scale layout (both operands): K/64 slabs; slab s holds, for every row r of
+ * the operand (R rows), the scales of blocks 2s and 2s+1 at bytes
+ * s*2R + 2r and s*2R + 2r + 1 -- i.e. scale[r][b] sits at
+ * (b/2)*2R + 2r + (b%2).  A tile's scales for one 64-k step are then one
+ * contiguous run.  The weight is stored N x K (each output column's K codes
+ * contiguous), with its scales in the same slab layout over its N rows.
+ */
+
+/*
+ * All-gather + GEMM with MX operands: as kos_ag_gemm, with
+ *
+ *   G = [S_0; ...; S_{world-1}] (codes and scales gathered, rank order)
+ *   C = G . W^T    (W stored [n, k])
+ *
+ * a_local, a_peers[p]        E4M3 [m_local, k]
+ * a_local_scales,            E8M0 scales of those rows, slab layout over
+ * a_peer_scales[p]           R = m_local rows (k/64 slabs of 2*m_local bytes)
+ * w, w_scales                E4M3 [n, k]; scales in slab layout over R = n
+ * a_gathered                 out E4M3 [world*m_local, k]: G's codes
+ * a_gathered_scales          out: G's scales, slab layout over
+ *                            R = world*m_local rows (each slab holds the
+ *                            shards' rows in rank order)
+ * c                          out [world*m_local, n] of c_dtype
+ * Shapes: m_local, k, n positive multiples of 256 (KOS_ERR_SHAPE); all
+ * pointers 16-byte aligned (KOS_ERR_ALIGN).  The other arguments, the
+ * modes and the errors are those of kos_ag_gemm.
+ */
+kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                          const void* a_local, const void* a_local_scales,
+                          const void* const* a_peers, const void* const* a_peer_scales,
+                          const void* w, const void* w_scales,
+                          void* a_gathered, void* a_gathered_scales, void* c, int32_t c_dtype,
+                          const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * GEMM + reduce-scatter with MX operands: as kos_gemm_rs with
+ * P = A . W^T, A E4M3 [m, k] with scales in slab layout over R = m rows,
+ * W E4M3 [n, k] with scales over R = n rows.  Partials, peer slices and y
+ * are fp32 as in kos_gemm_rs.  Shapes: m % world == 0, m/world, k and n
+ * positive multiples of 256 (KOS_ERR_SHAPE); pointers 16-byte aligned.
+ */
+kos_status kos_gemm_rs_mx(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n,
+                          const void* a, const void* a_scales, const void* w, const void* w_scales,
+                          const float* const* peer_slices, float* partial, float* y,
+                          const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
 /* Shape of an expert layer seen from one rank.  Experts are spread over the
  * ranks contiguously: rank d holds experts [d*E_loc, (d+1)*E_loc),
  * E_loc = experts / world. */

@@ -20,6 +20,8 @@ an expert layer whose tokens travel to their expert's rank and back):
 * ``MOE_QWEN3`` -- Qwen3-235B-shaped: 8192 tokens, hidden 4096, 128 experts,
   top-8, 16 local experts, SwiGLU 4096->1536->4096, router logits N(0,1) plus a
   per-expert Zipf(s=1.1) bias (skewed routing).
+* ``AG_QKV_MX``, ``RS_MLP_MX`` -- the QKV and MLP-down shapes with MXFP8
+  operands (E4M3 codes with E8M0 scales per 32 along K).
 
 Distributions: N(0, v) means variance v (a fan-in initialiser keeps unit
 output variance).  bf16 tensors are drawn in fp32 and rounded to nearest even
@@ -122,6 +124,13 @@ MOE_QWEN3 = MoeShape("moe_qwen3_8r_t8192_h4096_e128_k8_f1536_zipf1.1", 5, 8,
 AG_MLPUP = AgShape("ag_mlpup_8r_4096x8192x7168", 10, 8, 512, 8192, 7168)
 RS_OUTPROJ = RsShape("rs_outproj_8r_4096x1024x8192", 11, 8, 4096, 1024, 8192)
 
+# MXFP8 operands (E4M3 codes, E8M0 scales) at the QKV and MLP-down shapes,
+# and small shapes of whole 256 x 256 tiles with several tiles each way
+AG_QKV_MX = AgShape("ag_qkv_mx_8r_4096x8192x3072", 12, 8, 512, 8192, 3072)
+RS_MLP_MX = RsShape("rs_mlpdown_mx_8r_4096x3584x8192", 13, 8, 4096, 3584, 8192)
+AG_TINY_MX = AgShape("ag_tiny_mx_4r_1024x512x512", 14, 4, 256, 512, 512)
+RS_TINY_MX = RsShape("rs_tiny_mx_4r_1024x512x512", 15, 4, 1024, 512, 512)
+
 RS_TINY = RsShape("rs_tiny_4r_256x256x256", 8, 4, 256, 256, 256)
 RS_MID = RsShape("rs_mid_4r_2048x192x384", 9, 4, 2048, 192, 384)
 
@@ -138,7 +147,7 @@ MOE_TINY_SKEW = MoeShape("moe_tiny_skew_4r_t160_h256_e16_k4_f192", 7, 4, 160,
 # ---------------------------------------------------------------------------
 
 # tensor ids (stable: part of the seed)
-T_A, T_W, T_PEER, T_X, T_LOGITS, T_WG, T_WU, T_WD, T_SEND, T_RET, T_PLOG = range(11)
+T_A, T_W, T_PEER, T_X, T_LOGITS, T_WG, T_WU, T_WD, T_SEND, T_RET, T_PLOG, T_SA, T_SW = range(13)
 
 
 def _gen(wid: int, tid: int, rank: int, device) -> torch.Generator:
@@ -212,6 +221,65 @@ def rs_inputs(s: RsShape, rank: int, device="cpu", integer=False):
             peers.append(normal((s.m_chunk, s.n), 1.0, s.wid, T_PEER,
                                 p * 64 + rank, device, dtype=torch.float32))
     return dict(a=a, w=w, peer_slices=peers)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 operands
+# ---------------------------------------------------------------------------
+#
+# Codes are drawn directly (no quantisation step): sign uniform, exponent
+# field uniform in [3, 9], mantissa uniform -- E4M3 magnitudes 2^-4 .. 7.5,
+# never NaN -- and scales uniform in [124, 130], so element values span about
+# 2^-7 .. 2^5 around unit size.  Integer-valued variants draw the codes of
+# the integers -4..4 (listed below, OCP MX v1.0 E4M3) and scales in
+# [126, 128], which keeps every fp32 sum of the small cases exact.  Scales
+# are drawn straight into the kernels' slab layout, uint8 [k/64, rows, 2]
+# (i.i.d. draws: the layout only fixes where each lands).
+
+MX_INT_CODES = (0xC8, 0xC4, 0xC0, 0xB8, 0x00, 0x38, 0x40, 0x44, 0x48)   # -4 .. 4
+
+
+def mx_codes(shape, wid, tid, rank, device, integer=False):
+    g = _gen(wid, tid, rank, device)
+    if integer:
+        idx = torch.randint(0, len(MX_INT_CODES), shape, generator=g, device=device)
+        return torch.tensor(MX_INT_CODES, dtype=torch.uint8, device=device)[idx]
+    sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
+    e = torch.randint(3, 10, shape, generator=g, device=device, dtype=torch.int32)
+    m = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
+    return ((sign << 7) | (e << 3) | m).to(torch.uint8)
+
+
+def mx_scales(rows, k, wid, tid, rank, device, integer=False):
+    g = _gen(wid, tid, rank, device)
+    lo, hi = (126, 128) if integer else (124, 130)
+    return torch.randint(lo, hi + 1, (k // 64, rows, 2), generator=g, device=device,
+                         dtype=torch.int32).to(torch.uint8)
+
+
+def ag_mx_inputs(s: AgShape, rank: int, device="cpu", integer=False):
+    """MX shards of every rank with their scales, and the weight shard stored
+    n x k with its scales.  Returns dict(a_local, s_local, a_peers, s_peers,
+    w, w_scales); peer entries ``rank`` are None."""
+    shards = [mx_codes((s.m_local, s.k), s.wid, T_A, p, device, integer) for p in range(s.world)]
+    scales = [mx_scales(s.m_local, s.k, s.wid, T_SA, p, device, integer) for p in range(s.world)]
+    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer)
+    ws = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer)
+    return dict(a_local=shards[rank], s_local=scales[rank],
+                a_peers=[None if p == rank else shards[p] for p in range(s.world)],
+                s_peers=[None if p == rank else scales[p] for p in range(s.world)],
+                w=w, w_scales=ws)
+
+
+def rs_mx_inputs(s: RsShape, rank: int, device="cpu", integer=False):
+    """MX A [m, k] and W [n, k] with scales, and the peers' fp32 slices of
+    chunk ``rank`` (as ``rs_inputs``)."""
+    a = mx_codes((s.m, s.k), s.wid, T_A, rank, device, integer)
+    sa = mx_scales(s.m, s.k, s.wid, T_SA, rank, device, integer)
+    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer)
+    sw = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer)
+    peers = rs_inputs(s, rank, device, integer)["peer_slices"] if s.world > 1 else [None]
+    return dict(a=a, a_scales=sa, w=w, w_scales=sw, peer_slices=peers)
 
 
 # ---------------------------------------------------------------------------

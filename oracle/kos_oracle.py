@@ -190,6 +190,17 @@ def mx_to_f64(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return e4m3_to_f64(d) * np.repeat(e8m0_to_f64(s), MX_BLOCK, axis=1)
 
 
+def scales_from_slabs(slabs: np.ndarray) -> np.ndarray:
+    """Row-major scales [R, K/32] from the kernels' slab layout [K/64, R, 2]:
+    slab s holds, for row r, blocks 2s and 2s+1 (the layout the MX entry
+    points take, chosen so a tile's scales for one 64-wide step of K are one
+    contiguous run)."""
+    sl = np.asarray(slabs, dtype=np.uint8)
+    S, R, two = sl.shape
+    assert two == 2
+    return np.ascontiguousarray(sl.transpose(1, 0, 2)).reshape(R, 2 * S)
+
+
 def gemm_mx(a, a_scales, w, w_scales) -> np.ndarray:
     """C = A . W^T in float64: A [M,K] and W [N,K] MX operands (E4M3 codes
     with per-32 E8M0 scales along K)."""

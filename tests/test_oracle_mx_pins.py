@@ -130,3 +130,21 @@ def test_gemm_rs_mx_vs_brute_force(rank):
     mc = M // R
     want = sum(peers[p].astype(np.float64) if p != rank else full[rank * mc:(rank + 1) * mc] for p in range(R))
     assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_scales_from_slabs_index_formula():
+    # scale[r][b] sits at byte (b/2)*2R + 2r + (b%2) of the slab array
+    rng = np.random.default_rng(3)
+    K, R = 256, 5
+    flat = rng.integers(0, 256, size=(K // 64) * R * 2).astype(np.uint8)
+    nat = O.scales_from_slabs(flat.reshape(K // 64, R, 2))
+    assert nat.shape == (R, K // 32)
+    for r in range(R):
+        for b in range(K // 32):
+            assert nat[r, b] == flat[(b // 2) * 2 * R + 2 * r + (b % 2)]
+
+
+def test_input_integer_codes_decode_to_integers():
+    import kos_inputs as KI
+    v = O.e4m3_to_f64(np.array(KI.MX_INT_CODES, dtype=np.uint8))
+    assert np.array_equal(v, np.arange(-4, 5, dtype=np.float64))
