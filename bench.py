@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused GEMM+collective TFLOP/s (% bf16 MFMA peak); MoE layer tokens/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 / MXFP8 MFMA, published
 PEAK_CLOCK_MHZ = 2400.0        # MI355X peak engine clock (the published peaks assume it)
 
 
@@ -339,6 +340,45 @@ def rest_of_layer(torch, kos, KI, inp, ws, reps, flush):
     return res
 
 
+def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms):
+    """The QKV all-gather+GEMM (rank 0) and MLP-down GEMM+reduce-scatter
+    (rank 7) with MXFP8 operands: fused, unfused and FIXED crews of 16 and 32,
+    TFLOP/s against the dense fp8 peak, and the speed-up over the bf16 op of
+    the timed step."""
+    res = {}
+    ag, rs = KI.AG_QKV_MX, KI.RS_MLP_MX
+    a = KI.ag_mx_inputs(ag, 0, "cuda")
+    g = torch.empty((ag.m, ag.k), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((ag.k // 64, ag.m, 2), dtype=torch.uint8, device="cuda")
+    c = torch.empty((ag.m, ag.n), dtype=torch.bfloat16, device="cuda")
+    r = KI.rs_mx_inputs(rs, 7, "cuda")
+    part = torch.empty((rs.m, rs.n), dtype=torch.float32, device="cuda")
+    y = torch.empty((rs.m_chunk, rs.n), dtype=torch.float32, device="cuda")
+    for name, bf16_name, shape, call in (
+            ("ag_gemm_mx", "ag_gemm", ag,
+             lambda o: kos.ag_gemm_mx(a["a_local"], a["s_local"], a["a_peers"], a["s_peers"], a["w"], a["w_scales"],
+                                      g, gs, c, 0, ws, o)),
+            ("gemm_rs_mx", "gemm_rs", rs,
+             lambda o: kos.gemm_rs_mx(r["a"], r["a_scales"], r["w"], r["w_scales"], r["peer_slices"], part, y, 7,
+                                      ws, o))):
+        t = {}
+        for label, mode, crew in (("fused", 0, -1), ("unfused", 2, -1), ("fixed16", 1, 16), ("fixed32", 1, 32)):
+            o = kos.opts(mode=mode, n_movers=crew)
+            fn = lambda o=o, call=call: call(o)  # noqa: E731
+            fn()
+            t[label] = time_ops(torch, [(name, fn)], reps, ws, flush)[0][0]
+        tf = shape.flops / (t["fused"] * 1e-3) / 1e12
+        fixed = min(t["fixed16"], t["fixed32"])
+        res[name] = {"workload": shape.name, "ms": round(t["fused"], 4), "tflops": round(tf, 1),
+                     "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
+                     "unfused_ms": round(t["unfused"], 4), "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3),
+                     "best_fixed_ms": round(fixed, 4), "speedup_vs_best_fixed": round(fixed / t["fused"], 3),
+                     "speedup_vs_bf16": round(bf16_ms[bf16_name] / t["fused"], 3)}
+    ws.status()
+    del a, g, gs, c, r, part, y
+    return res
+
+
 def rs_order_ablation(torch, kos, KI, inp, ws, reps, flush):
     """GEMM+reduce-scatter in band order (the design) and row order (the
     slower ablation the explainer compares it with), fused, at rank 7 (whose
@@ -527,6 +567,9 @@ def main():
         f4 = KI.AG_QKV.flops + KI.RS_MLP.flops + KI.AG_MLPUP.flops + KI.RS_OUTPROJ.flops
         rest["tp_sp_layer"] = {"ms": round(t4, 4), "tflops": round(f4 / (t4 * 1e-3) / 1e12, 1)}
         extra["tp_sp_layer"] = rest
+        # the same two collectives with MXFP8 operands
+        extra["mxfp8"] = mxfp8(torch, kos, KI, ws, reps, flush,
+                               {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")})
     if not args.no_cpu:
         cpu = cpu_baseline(inp, moe_shape)
     else:
