@@ -340,11 +340,12 @@ def rest_of_layer(torch, kos, KI, inp, ws, reps, flush):
     return res
 
 
-def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms):
+def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms, baselines=True):
     """The QKV all-gather+GEMM (rank 0) and MLP-down GEMM+reduce-scatter
-    (rank 7) with MXFP8 operands: fused, unfused and FIXED crews of 16 and 32,
-    TFLOP/s against the dense fp8 peak, and the speed-up over the bf16 op of
-    the timed step."""
+    (rank 7) with MXFP8 operands: fused (and, with `baselines`, unfused and
+    FIXED crews of 16 and 32), TFLOP/s against the dense fp8 peak, HBM bytes
+    per launch from the committed counter summary, and the speed-up over the
+    bf16 op of the timed step."""
     res = {}
     ag, rs = KI.AG_QKV_MX, KI.RS_MLP_MX
     a = KI.ag_mx_inputs(ag, 0, "cuda")
@@ -362,18 +363,22 @@ def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms):
              lambda o: kos.gemm_rs_mx(r["a"], r["a_scales"], r["w"], r["w_scales"], r["peer_slices"], part, y, 7,
                                       ws, o))):
         t = {}
-        for label, mode, crew in (("fused", 0, -1), ("unfused", 2, -1), ("fixed16", 1, 16), ("fixed32", 1, 32)):
+        runs = (("fused", 0, -1), ("unfused", 2, -1), ("fixed16", 1, 16), ("fixed32", 1, 32))
+        for label, mode, crew in runs if baselines else runs[:1]:
             o = kos.opts(mode=mode, n_movers=crew)
             fn = lambda o=o, call=call: call(o)  # noqa: E731
             fn()
             t[label] = time_ops(torch, [(name, fn)], reps, ws, flush)[0][0]
         tf = shape.flops / (t["fused"] * 1e-3) / 1e12
-        fixed = min(t["fixed16"], t["fixed32"])
-        res[name] = {"workload": shape.name, "ms": round(t["fused"], 4), "tflops": round(tf, 1),
-                     "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
-                     "unfused_ms": round(t["unfused"], 4), "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3),
-                     "best_fixed_ms": round(fixed, 4), "speedup_vs_best_fixed": round(fixed / t["fused"], 3),
-                     "speedup_vs_bf16": round(bf16_ms[bf16_name] / t["fused"], 3)}
+        d = {"workload": shape.name, "ms": round(t["fused"], 4), "tflops": round(tf, 1),
+             "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
+             "traffic": measured_traffic(name, shape.name),
+             "speedup_vs_bf16": round(bf16_ms[bf16_name] / t["fused"], 3)}
+        if baselines:
+            fixed = min(t["fixed16"], t["fixed32"])
+            d.update(unfused_ms=round(t["unfused"], 4), speedup_vs_unfused=round(t["unfused"] / t["fused"], 3),
+                     best_fixed_ms=round(fixed, 4), speedup_vs_best_fixed=round(fixed / t["fused"], 3))
+        res[name] = d
     ws.status()
     del a, g, gs, c, r, part, y
     return res
@@ -463,6 +468,8 @@ def main():
                     help="fused: the persistent kernels (the measured product); fixed / unfused: the same-GPU "
                          "baselines timed as the step (for per-launch profiles)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between ops")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="with --no-baselines: still time the MXFP8 ops (fused only; for their profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -570,6 +577,9 @@ def main():
         # the same two collectives with MXFP8 operands
         extra["mxfp8"] = mxfp8(torch, kos, KI, ws, reps, flush,
                                {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")})
+    elif args.mxfp8:
+        extra["mxfp8"] = mxfp8(torch, kos, KI, ws, max(3, args.steps // 4), flush,
+                               {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")}, baselines=False)
     if not args.no_cpu:
         cpu = cpu_baseline(inp, moe_shape)
     else:
