@@ -34,6 +34,11 @@
 //
 // Accumulator layout: the B fragment is the first MFMA operand, as in the
 // bf16 tile, so tile_foreach4 visits the results unchanged.
+//
+// Pipeline: one workgroup barrier per stage; each A fragment of the next
+// step is read right after its row block's last MFMA of this step (in
+// place), the B fragments into a second set, so LDS reads overlap the
+// matrix cores instead of waiting in front of them.
 #pragma once
 
 #include "kos_tile.h"
@@ -151,86 +156,118 @@ __device__ __forceinline__ void mx_stage_load(char* lds_stage, const MxPlan<S, C
                                              (k0 >> 6) * P.sc_slab, 0, COH_A ? kCpolDevice : 0);
 }
 
+// Operand fragments: the A row blocks (reloaded in place, each right after
+// its last MFMA of the step) and the B column blocks (two sets, current and
+// next step).  Scale words are kept as read (two bytes per row word) and
+// shifted to this lane's byte at the MFMA: a shift right after the read would
+// wait for it there.
 template <class S>
-struct MxFrags {
+struct MxA {
   i32x8 a[S::TM];
-  i32x8 b[S::TN];
   int32_t sa[S::TM];
+};
+template <class S>
+struct MxB {
+  i32x8 b[S::TN];
   int32_t sb[S::TN];
 };
 
-// LDS -> registers for the stage in `lds_stage`: A row blocks [I0, I1) and,
-// with WITH_B, the B column blocks.
-template <class S, int I0, int I1, bool WITH_B>
-__device__ __forceinline__ void mx_frag_load(MxFrags<S>& f, const char* lds_stage, const WaveCtx& w) {
+// This lane's LDS offsets within a stage.  Row m = (32-row block base) + r
+// has swizzle (m >> 2) & 3 = that of r (block bases are multiples of 32), so
+// every block's chunks sit at one lane offset plus a constant.
+struct MxAddr {
+  int lo, hi;        // chunk h and chunk 2+h of row r: (2+h) ^ s = (h ^ s) ^ 2
+  int sh;            // this lane's byte (block h) of a scale word
+  int a, b, sa, sb;  // A, B and scale rows of this wave's sub-tile (+ lane row)
+};
+
+template <class S>
+__device__ __forceinline__ MxAddr mx_addr(const WaveCtx& w) {
   const int lane = w.lane, wave = w.wave;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int h = lane >> 5, r = lane & 31;
-  // Row m = (32-row block base) + r: its swizzle (m >> 2) & 3 depends on r
-  // alone (block bases are multiples of 32), so every block's chunks sit at
-  // one lane offset plus a constant -- one address register per chunk.
-  const int lo = r * 64 + ((h ^ a_swz(r)) << 4);
-  const int hi = lo ^ 32;   // chunk 2+h: (2+h) ^ s = (h ^ s) ^ 2
-  const char* ast = lds_stage + wm * S::WM * 64;
-  const char* bst = lds_stage + S::A_BYTES + wn * S::WN * 64;
-  // scale words: this lane's byte is byte h (a shift; the MFMA's byte
-  // select is one immediate for all lanes)
-  const char* sas = lds_stage + S::SA_OFF + wm * S::WM * 4 + r * 4;
-  const char* sbs = lds_stage + S::SB_OFF + wn * S::WN * 4 + r * 4;
-  const int sh = 8 * h;
+  MxAddr d;
+  d.lo = r * 64 + ((h ^ a_swz(r)) << 4);
+  d.hi = d.lo ^ 32;
+  d.sh = 8 * h;
+  d.a = wm * S::WM * 64;
+  d.b = S::A_BYTES + wn * S::WN * 64;
+  d.sa = S::SA_OFF + wm * S::WM * 4 + r * 4;
+  d.sb = S::SB_OFF + wn * S::WN * 4 + r * 4;
+  return d;
+}
+
+template <class S, int I>
+__device__ __forceinline__ void mx_load_a(MxA<S>& f, const char* stage, const MxAddr& d) {
+  const char* p = stage + d.a + I * 2048;
+  const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + d.lo);
+  const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + d.hi);
+  f.a[I] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  f.sa[I] = (int32_t)*reinterpret_cast<const uint32_t*>(stage + d.sa + I * 128);
+}
+
+template <class S>
+__device__ __forceinline__ void mx_load_b(MxB<S>& f, const char* stage, const MxAddr& d) {
 #pragma unroll
-  for (int i = I0; i < I1; ++i) {
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(ast + i * 2048 + lo);
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(ast + i * 2048 + hi);
-    f.a[i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    f.sa[i] = (int32_t)(*reinterpret_cast<const uint32_t*>(sas + i * 128) >> sh);
-  }
-  if constexpr (WITH_B) {
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(bst + j * 2048 + lo);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(bst + j * 2048 + hi);
-      f.b[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      f.sb[j] = (int32_t)(*reinterpret_cast<const uint32_t*>(sbs + j * 128) >> sh);
-    }
+  for (int j = 0; j < S::TN; ++j) {
+    const char* p = stage + d.b + j * 2048;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + d.lo);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + d.hi);
+    f.b[j] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    f.sb[j] = (int32_t)*reinterpret_cast<const uint32_t*>(stage + d.sb + j * 128);
   }
 }
 
-// MFMAs of row blocks [I0, I1) of the wave's sub-tile.
-template <class S, int I0, int I1>
-__device__ __forceinline__ void mx_frag_mfma(f32x16 (&acc)[S::TM][S::TN], const MxFrags<S>& f) {
+// The MFMAs of row block I (formats 0, 0: E4M3 x E4M3; byte 0 of each
+// scale operand after the shift).
+template <class S, int I>
+__device__ __forceinline__ void mx_mfma_row(f32x16 (&acc)[S::TM][S::TN], const MxA<S>& fa, const MxB<S>& fb,
+                                            const MxAddr& d) {
+  const int32_t sa = (int32_t)((uint32_t)fa.sa[I] >> d.sh);
 #pragma unroll
-  for (int i = I0; i < I1; ++i)
-#pragma unroll
-    for (int j = 0; j < S::TN; ++j)
-      // formats 0, 0: E4M3 x E4M3; byte 0 of each scale operand
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, f.sb[j], 0,
-                                                                   f.sa[i]);
+  for (int j = 0; j < S::TN; ++j)
+    acc[I][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[j], fa.a[I], acc[I][j], 0, 0, 0,
+                                                                (int32_t)((uint32_t)fb.sb[j] >> d.sh), 0, sa);
+}
+
+// Row blocks I.. of the step: each block's MFMAs, then its A fragment of the
+// next step (scheduling barriers keep that order).
+template <class S, int I>
+__device__ __forceinline__ void mx_rows_from(f32x16 (&acc)[S::TM][S::TN], MxA<S>& fa, const MxB<S>& fb,
+                                             const char* nxt, const MxAddr& d) {
+  if constexpr (I < S::TM) {
+    mx_mfma_row<S, I>(acc, fa, fb, d);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_load_a<S, I>(fa, nxt, d);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_rows_from<S, I + 1>(acc, fa, fb, nxt, d);
+  }
 }
 
 // One K-loop iteration on stage kt (ring buffer `cur`, stage kt+1 in `nxt`).
-// On entry f holds stage kt's fragments; on exit stage kt+1's.  The MFMAs
-// of the first half of the row blocks run before the wait for stage kt+1
-// and the workgroup barrier (which also frees `cur` for stage kt+4); then
-// those row blocks' fragments are reloaded in place from stage kt+1 while
-// the second half's MFMAs run, and the rest follow.  One fragment set
-// instead of two keeps the accumulators and operands of two waves per SIMD
-// in registers.  The look-ahead load is always issued (past the end it
-// re-reads the last stage, never used) so the counts in flight stay uniform
-// and the loop has no branches.
+// On entry fa + fb hold stage kt's fragments; on exit fa + fn hold stage
+// kt+1's.  Row block 0's MFMAs run first; then the wait for stage kt+1 and
+// the workgroup barrier (every wave has read stage kt: `cur` takes stage
+// kt+4), the look-ahead load, stage kt+1's block-0 A and B fragments, and
+// the remaining row blocks, each followed by its next A fragment.  The
+// look-ahead load is always issued (past the end it re-reads the last
+// stage, never used) so the counts in flight stay uniform and the loop has
+// no branches.
 template <class S, bool COH_A>
-__device__ __forceinline__ void mx_k_iter(f32x16 (&acc)[S::TM][S::TN], MxFrags<S>& f, int kt, int nk,
-                                          const MxPlan<S, COH_A>& P, char* cur, char* nxt, const WaveCtx& w) {
+__device__ __forceinline__ void mx_k_iter(f32x16 (&acc)[S::TM][S::TN], MxA<S>& fa, const MxB<S>& fb, MxB<S>& fn,
+                                          int kt, int nk, const MxPlan<S, COH_A>& P, char* cur, char* nxt,
+                                          const MxAddr& d) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int ST = S::STAGES;
-  constexpr int H = (S::TM + 1) / 2;
-  mx_frag_mfma<S, 0, H>(acc, f);
+  mx_mfma_row<S, 0>(acc, fa, fb, d);
+  __builtin_amdgcn_sched_barrier(0);
   KOS_WAITCNT(2 * S::LOADS, 0);   // stage kt+1 landed (kt+2, kt+3 may fly); reads of stage kt done
   lds_barrier();
   mx_stage_load<S, COH_A>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
-  mx_frag_load<S, 0, H, false>(f, nxt, w);
-  mx_frag_mfma<S, H, S::TM>(acc, f);
-  mx_frag_load<S, H, S::TM, true>(f, nxt, w);
+  mx_load_a<S, 0>(fa, nxt, d);
+  mx_load_b<S>(fn, nxt, d);
+  __builtin_amdgcn_sched_barrier(0);
+  mx_rows_from<S, 1>(acc, fa, fb, nxt, d);
 #endif
 }
 
@@ -242,6 +279,7 @@ template <class S, bool COH_A = false, int RING = S::STAGE_BYTES>
 __device__ __forceinline__ void tile_mainloop_mx(f32x16 (&acc)[S::TM][S::TN], const MxSrc& a, int m_valid,
                                                  const MxSrc& b, int n_valid, int K) {
   constexpr int ST = S::STAGES;
+  static_assert(S::TM <= 4, "row blocks unrolled below");
 #pragma unroll
   for (int i = 0; i < S::TM; ++i)
 #pragma unroll
@@ -252,6 +290,7 @@ __device__ __forceinline__ void tile_mainloop_mx(f32x16 (&acc)[S::TM][S::TN], co
   const WaveCtx w = wave_ctx();
   MxPlan<S, COH_A> P;
   mx_plan<S, COH_A>(P, a, m_valid, b, n_valid, w);
+  const MxAddr d = mx_addr<S>(w);
   static_assert(S::STAGE_BYTES <= RING, "tile stage larger than the ring");
   char* r0 = ring<RING, 0>();
   char* r1 = ring<RING, 1>();
@@ -265,14 +304,20 @@ __device__ __forceinline__ void tile_mainloop_mx(f32x16 (&acc)[S::TM][S::TN], co
   mx_stage_load<S, COH_A>(r3, P, 3 * S::BK);
   KOS_WAITCNT(3 * S::LOADS, 0);
   lds_barrier();
-  MxFrags<S> f;
-  mx_frag_load<S, 0, S::TM, true>(f, r0, w);
-  // four stages per trip (the ring buffers come back to where they started)
+  MxA<S> fa;
+  MxB<S> f0, f1;
+  mx_load_a<S, 0>(fa, r0, d);
+  if constexpr (S::TM > 1) mx_load_a<S, 1>(fa, r0, d);
+  if constexpr (S::TM > 2) mx_load_a<S, 2>(fa, r0, d);
+  if constexpr (S::TM > 3) mx_load_a<S, 3>(fa, r0, d);
+  mx_load_b<S>(f0, r0, d);
+  // four stages per trip: the ring buffers come back to where they started,
+  // and the two B sets alternate
   for (int kt = 0; kt < nk; kt += ST) {
-    mx_k_iter<S, COH_A>(acc, f, kt + 0, nk, P, r0, r1, w);
-    mx_k_iter<S, COH_A>(acc, f, kt + 1, nk, P, r1, r2, w);
-    mx_k_iter<S, COH_A>(acc, f, kt + 2, nk, P, r2, r3, w);
-    mx_k_iter<S, COH_A>(acc, f, kt + 3, nk, P, r3, r0, w);
+    mx_k_iter<S, COH_A>(acc, fa, f0, f1, kt + 0, nk, P, r0, r1, d);
+    mx_k_iter<S, COH_A>(acc, fa, f1, f0, kt + 1, nk, P, r1, r2, d);
+    mx_k_iter<S, COH_A>(acc, fa, f0, f1, kt + 2, nk, P, r2, r3, d);
+    mx_k_iter<S, COH_A>(acc, fa, f1, f0, kt + 3, nk, P, r3, r0, d);
   }
   KOS_WAITCNT(0, 0);
   lds_barrier();
