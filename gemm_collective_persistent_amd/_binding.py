@@ -25,7 +25,7 @@ RS_BAND, RS_ROW = 0, 1
 EXPORTS = [
     "kos_opts_default", "kos_workspace_bytes", "kos_workspace_init", "kos_workspace_status",
     "kos_last_error", "kos_device_cu_count", "kos_ag_gemm", "kos_gemm_rs",
-    "kos_ag_gemm_mx", "kos_gemm_rs_mx",
+    "kos_ag_gemm_mx", "kos_gemm_rs_mx", "kos_ag_gemm_wt", "kos_gemm_rs_wt",
     "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace",
 ]
 
@@ -79,6 +79,10 @@ def _load():
                                   c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, P, P,
                                   POINTER(Opts), P, c_size_t, P]),
+        "kos_ag_gemm_wt": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, PP, P, P, P,
+                                     c_int32, POINTER(Opts), P, c_size_t, P]),
+        "kos_gemm_rs_wt": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, P, P,
+                                     POINTER(Opts), P, c_size_t, P]),
         "kos_ag_gemm_mx": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, PP, P, P,
                                      P, P, P, c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs_mx": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, P, P, PP, P, P,

@@ -79,8 +79,9 @@ class Workspace:
 
 def ag_gemm(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w: torch.Tensor,
             a_gathered: torch.Tensor, c: torch.Tensor, rank: int, ws: Workspace,
-            o: Optional[Opts] = None, stream=None) -> None:
-    """kos_ag_gemm: a_gathered = concat(shards); c = a_gathered @ w."""
+            o: Optional[Opts] = None, stream=None, w_transposed: bool = False) -> None:
+    """kos_ag_gemm: a_gathered = concat(shards); c = a_gathered @ w (w [k, n]).
+    w_transposed (kos_ag_gemm_wt): w is W^T [n, k] and c = a_gathered @ w.T."""
     world = len(a_peers)
     _need(a_local, torch.bfloat16, "a_local", 2)
     _need(w, torch.bfloat16, "w", 2)
@@ -92,18 +93,20 @@ def ag_gemm(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w:
         if p != rank:
             _need(t, torch.bfloat16, f"a_peers[{p}]", 2)
     m_local, k = a_local.shape
-    n = w.shape[1]
+    n = w.shape[0] if w_transposed else w.shape[1]
     peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(a_peers)])
     o = o if o is not None else make_opts()
-    check(lib.kos_ag_gemm(world, rank, m_local, k, n, _p(a_local), peers, _p(w), _p(a_gathered),
-                          _p(c), KOS_BF16 if c.dtype == torch.bfloat16 else KOS_F32,
-                          ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+    fn = lib.kos_ag_gemm_wt if w_transposed else lib.kos_ag_gemm
+    check(fn(world, rank, m_local, k, n, _p(a_local), peers, _p(w), _p(a_gathered),
+             _p(c), KOS_BF16 if c.dtype == torch.bfloat16 else KOS_F32,
+             ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
 
 
 def gemm_rs(a: torch.Tensor, w: torch.Tensor, peer_slices: Sequence[Optional[torch.Tensor]],
             partial: torch.Tensor, y: torch.Tensor, rank: int, ws: Workspace,
-            o: Optional[Opts] = None, stream=None) -> None:
-    """kos_gemm_rs: partial = a @ w (fp32); y = reduce of chunk `rank`."""
+            o: Optional[Opts] = None, stream=None, w_transposed: bool = False) -> None:
+    """kos_gemm_rs: partial = a @ w (fp32, w [k, n]); y = reduce of chunk
+    `rank`.  w_transposed (kos_gemm_rs_wt): w is W^T [n, k], partial = a @ w.T."""
     world = len(peer_slices)
     _need(a, torch.bfloat16, "a", 2)
     _need(w, torch.bfloat16, "w", 2)
@@ -113,11 +116,12 @@ def gemm_rs(a: torch.Tensor, w: torch.Tensor, peer_slices: Sequence[Optional[tor
         if p != rank:
             _need(t, torch.float32, f"peer_slices[{p}]", 2)
     m, k = a.shape
-    n = w.shape[1]
+    n = w.shape[0] if w_transposed else w.shape[1]
     peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(peer_slices)])
     o = o if o is not None else make_opts()
-    check(lib.kos_gemm_rs(world, rank, m, k, n, _p(a), _p(w), peers, _p(partial), _p(y),
-                          ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+    fn = lib.kos_gemm_rs_wt if w_transposed else lib.kos_gemm_rs
+    check(fn(world, rank, m, k, n, _p(a), _p(w), peers, _p(partial), _p(y),
+             ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
 
 
 def _need_scales(t: torch.Tensor, rows: int, k: int, what: str) -> None:

@@ -73,7 +73,9 @@ __device__ __forceinline__ void build_tile(f32x16 (&acc)[S::TM][S::TN], const Ag
                   K, 2 * N};
     tile_mainloop_mx<S, COH>(acc, a, S::BM, b, S::BN, p.k);
   } else {
-    const BSrc b{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)nt * S::BN, nullptr, N};
+    // W k x n, or (BNT) n x k
+    const BSrc b = S::BNT ? BSrc{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)nt * S::BN * K, nullptr, K}
+                          : BSrc{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)nt * S::BN, nullptr, N};
     tile_mainloop<S, false, COH>(acc, reinterpret_cast<const uint16_t*>(a_rows), K, S::BM, b, p.k);
   }
 }
@@ -201,12 +203,13 @@ static kos_status launch_ag(const AgParams& p, int grid, hipStream_t stream) {
   return launch_status("ag_gemm launch");
 }
 
+template <bool BNT>
 static kos_status launch_ag_tile(int bm, int bn, const AgParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256, 4, 2, 4>>(p, grid, s);
-  if (bm == 256 && bn == 192) return launch_ag<TileShape<256, 192>>(p, grid, s);
-  if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128>>(p, grid, s);
-  if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128>>(p, grid, s);
-  return launch_ag<TileShape<64, 64>>(p, grid, s);
+  if (bm == 256 && bn == 256) return launch_ag<TileShape<256, 256, 4, 2, 4, BNT>>(p, grid, s);
+  if (bm == 256 && bn == 192) return launch_ag<TileShape<256, 192, 4, 2, 2, BNT>>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_ag<TileShape<256, 128, 4, 2, 2, BNT>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_ag<TileShape<128, 128, 4, 2, 2, BNT>>(p, grid, s);
+  return launch_ag<TileShape<64, 64, 4, 2, 2, BNT>>(p, grid, s);
 }
 
 // The largest tile (fewest operand re-reads) that divides the shard rows and
@@ -237,9 +240,9 @@ using namespace kos;
 
 namespace kos {
 
-// Arguments of one call, bf16 or MX.
+// Arguments of one call: bf16 (W k x n, or wt: n x k) or MX.
 struct AgCall {
-  bool mx;
+  bool mx, wt;
   int32_t world, rank;
   int64_t m_local, k, n;
   const void* a_local;
@@ -283,7 +286,7 @@ static kos_status ag_gemm_run(const AgCall& a) {
   if (m_local * world > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20))
     return fail(KOS_ERR_SHAPE, "sizes too large");
   // the tiles address W (bf16) and the scale slabs through 32-bit offsets
-  if (!a.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
+  if (!a.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (bf16) must be smaller than 2 GiB");
   if (a.mx && (k / 64) * 2 * std::max<int64_t>(m_local * world, n) >= (int64_t(1) << 31))
     return fail(KOS_ERR_SHAPE, "MX scale arrays must be smaller than 2 GiB");
   if (!aligned16(a.a_local) || !aligned16(a.w) || !aligned16(a.a_gathered) || !aligned16(a.c))
@@ -358,7 +361,8 @@ static kos_status ag_gemm_run(const AgCall& a) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   const int grid = o.grid;
   auto launch = [&](const AgParams& q) {
-    return a.mx ? launch_ag<TileShapeMX<256, 256>>(q, grid, s) : launch_ag_tile(bm, bn, q, grid, s);
+    return a.mx ? launch_ag<TileShapeMX<256, 256>>(q, grid, s)
+                : a.wt ? launch_ag_tile<true>(bm, bn, q, grid, s) : launch_ag_tile<false>(bm, bn, q, grid, s);
   };
   if (o.mode == KOS_MODE_UNFUSED && nothing_to_move) {
     AgParams gm = p;           // the GEMM alone
@@ -397,8 +401,16 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
                                   const void* a_local, const void* const* a_peers, const void* w,
                                   void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
                                   size_t ws_bytes, void* stream) {
-  return ag_gemm_run(AgCall{false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, nullptr, nullptr,
-                            nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
+  return ag_gemm_run(AgCall{false, false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, nullptr,
+                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
+}
+
+extern "C" kos_status kos_ag_gemm_wt(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                                     const void* a_local, const void* const* a_peers, const void* w_t,
+                                     void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return ag_gemm_run(AgCall{false, true, world, rank, m_local, k, n, a_local, a_peers, w_t, a_gathered, nullptr,
+                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
 }
 
 extern "C" kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
@@ -406,6 +418,6 @@ extern "C" kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_loca
                                      const void* const* a_peer_scales, const void* w, const void* w_scales,
                                      void* a_gathered, void* a_gathered_scales, void* c, int32_t c_dtype,
                                      const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
-  return ag_gemm_run(AgCall{true, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, a_local_scales,
+  return ag_gemm_run(AgCall{true, false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, a_local_scales,
                             a_peer_scales, w_scales, a_gathered_scales, c, c_dtype, opts, ws, ws_bytes, stream});
 }

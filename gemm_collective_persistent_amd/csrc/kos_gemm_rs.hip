@@ -162,7 +162,9 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
                       2 * N};
         tile_mainloop_mx<S>(acc, a, BM, b, BN, p.k);
       } else {
-        const BSrc b{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)col * BN, nullptr, N};
+        // W k x n, or (BNT) n x k
+        const BSrc b = S::BNT ? BSrc{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)col * BN * K, nullptr, K}
+                              : BSrc{reinterpret_cast<const uint16_t*>(p.w) + (int64_t)col * BN, nullptr, N};
         tile_mainloop<S>(acc, reinterpret_cast<const uint16_t*>(p.a) + row0 * K, K, BM, b, p.k);
       }
       float* P = p.partial + row0 * N + (int64_t)col * BN;
@@ -212,11 +214,12 @@ static kos_status launch_rs(const RsParams& p, int grid, hipStream_t stream) {
   return launch_status("gemm_rs launch");
 }
 
+template <bool BNT>
 static kos_status launch_rs_tile(int bm, int bn, const RsParams& p, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_rs<TileShape<256, 256, 4, 2, 4>>(p, grid, s);
-  if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128>>(p, grid, s);
-  if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128>>(p, grid, s);
-  return launch_rs<TileShape<64, 64>>(p, grid, s);
+  if (bm == 256 && bn == 256) return launch_rs<TileShape<256, 256, 4, 2, 4, BNT>>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_rs<TileShape<256, 128, 4, 2, 2, BNT>>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_rs<TileShape<128, 128, 4, 2, 2, BNT>>(p, grid, s);
+  return launch_rs<TileShape<64, 64, 4, 2, 2, BNT>>(p, grid, s);
 }
 
 }  // namespace kos
@@ -225,9 +228,9 @@ using namespace kos;
 
 namespace kos {
 
-// Arguments of one call, bf16 or MX.
+// Arguments of one call: bf16 (W k x n, or wt: n x k) or MX.
 struct RsCall {
-  bool mx;
+  bool mx, wt;
   int32_t world, rank;
   int64_t m, k, n;
   const void* a;
@@ -270,7 +273,7 @@ static kos_status gemm_rs_run(const RsCall& c) {
   }
   if (m > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20)) return fail(KOS_ERR_SHAPE, "sizes too large");
   // the tiles address W (bf16) and the scale slabs through 32-bit offsets
-  if (!c.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (k x n bf16) must be smaller than 2 GiB");
+  if (!c.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (bf16) must be smaller than 2 GiB");
   if (c.mx && (k / 64) * 2 * std::max(m, n) >= (int64_t(1) << 31))
     return fail(KOS_ERR_SHAPE, "MX scale arrays must be smaller than 2 GiB");
   if (!aligned16(a) || !aligned16(w) || !aligned16(partial) || !aligned16(y))
@@ -321,7 +324,8 @@ static kos_status gemm_rs_run(const RsCall& c) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = o.grid;
   auto launch = [&](const RsParams& q) {
-    return c.mx ? launch_rs<TileShapeMX<256, 256>>(q, grid, s) : launch_rs_tile(bm, bn, q, grid, s);
+    return c.mx ? launch_rs<TileShapeMX<256, 256>>(q, grid, s)
+                : c.wt ? launch_rs_tile<true>(bm, bn, q, grid, s) : launch_rs_tile<false>(bm, bn, q, grid, s);
   };
   if (o.mode == KOS_MODE_UNFUSED) {
     RsParams gm = p;            // launch 1: the whole GEMM
@@ -355,14 +359,21 @@ using namespace kos;
 extern "C" kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
                                   const void* w, const float* const* peer_slices, float* partial, float* y,
                                   const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
-  return gemm_rs_run(RsCall{false, world, rank, m, k, n, a, nullptr, w, nullptr, peer_slices, partial, y, opts, ws,
-                            ws_bytes, stream});
+  return gemm_rs_run(RsCall{false, false, world, rank, m, k, n, a, nullptr, w, nullptr, peer_slices, partial, y, opts,
+                            ws, ws_bytes, stream});
+}
+
+extern "C" kos_status kos_gemm_rs_wt(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
+                                     const void* w_t, const float* const* peer_slices, float* partial, float* y,
+                                     const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_rs_run(RsCall{false, true, world, rank, m, k, n, a, nullptr, w_t, nullptr, peer_slices, partial, y, opts,
+                            ws, ws_bytes, stream});
 }
 
 extern "C" kos_status kos_gemm_rs_mx(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n, const void* a,
                                      const void* a_scales, const void* w, const void* w_scales,
                                      const float* const* peer_slices, float* partial, float* y,
                                      const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
-  return gemm_rs_run(RsCall{true, world, rank, m, k, n, a, a_scales, w, w_scales, peer_slices, partial, y, opts, ws,
+  return gemm_rs_run(RsCall{true, false, world, rank, m, k, n, a, a_scales, w, w_scales, peer_slices, partial, y, opts, ws,
                             ws_bytes, stream});
 }

@@ -41,10 +41,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // WGM x WGN waves: 2 x 2 (one wave per SIMD) or 2 x 4 (two waves per SIMD:
 // while one waits on LDS or memory the other issues MFMAs; each holds half
-// the accumulators).
-template <int BM_, int BN_, int STAGES_ = 4, int WGM_ = 2, int WGN_ = 2>
+// the accumulators).  BNT: B stored N x K (row n holds output column n's K
+// values, the transposed weight of a backward pass); its stage is then BN
+// rows of 64 bytes laid out and read like A's.
+template <int BM_, int BN_, int STAGES_ = 4, int WGM_ = 2, int WGN_ = 2, bool BNT_ = false>
 struct TileShape {
   static constexpr bool MX = false;                     // bf16 operands
+  static constexpr bool BNT = BNT_;
   static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_;
   static constexpr int NW = WGM * WGN;                  // waves
@@ -75,7 +78,8 @@ struct TileShape {
 
 // Where the B tile's columns come from: BN consecutive columns of one
 // K x N matrix (plain), or, for the SwiGLU tile (dual), BN/2 columns of the
-// gate matrix and the same BN/2 columns of the up matrix.  In the dual
+// gate matrix and the same BN/2 columns of the up matrix.  BNT tiles: p0 is
+// row n0 of the N x K matrix and ld its row stride.  In the dual
 // tile each wave's 32x32 blocks j < TN/2 hold gate values and blocks
 // j + TN/2 the up values of the same output columns.
 struct BSrc {
@@ -180,6 +184,18 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
     P.a_off[i] = (uint32_t)(mr * lda * 2 + c * 16);
   }
   P.b_stride = (int)(b.ld * 2);
+  if constexpr (S::BNT) {
+    static_assert(!DUAL, "the SwiGLU tile reads K x N weights");
+    // rows n of 64 bytes, A's layout
+    P.rb = raw_rsrc(b.p0);
+#pragma unroll
+    for (int i = 0; i < S::B_LOADS; ++i) {
+      const int slot = (wave * S::B_LOADS + i) * 64 + lane;
+      const int n = slot >> 2, c = (slot & 3) ^ a_swz(slot >> 2);
+      P.b_off[i] = (uint32_t)(n * P.b_stride + c * 16);
+    }
+    return;
+  }
   // dual: the first half of the waves fill the gate half, the rest the up half
   const bool up = DUAL && wave >= S::NW / 2;
   P.rb = raw_rsrc(up ? b.p1 : b.p0);
@@ -201,7 +217,7 @@ constexpr int kCpolDevice = 16;
 template <class S, bool DUAL, bool COH_A>
 __device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A>& P, int k0) {
   const int soa = k0 * 2;
-  const int sob = k0 * P.b_stride;
+  const int sob = S::BNT ? k0 * 2 : k0 * P.b_stride;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
     if (!S::A_HALF || P.a_on)
@@ -233,6 +249,14 @@ __device__ __forceinline__ void frag_load(Frags<S>& f, const char* lds_stage, in
   for (int i = 0; i < S::TM; ++i) {
     const int m = wm * S::WM + i * 32 + (lane & 31);
     f.a[i] = *reinterpret_cast<const bf16x8*>(ast + m * 64 + ((kc ^ a_swz(m)) << 4));
+  }
+  if constexpr (S::BNT) {
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) {
+      const int n = wn * S::WN + j * 32 + (lane & 31);
+      f.b[j] = *reinterpret_cast<const bf16x8*>(bst + n * 64 + ((kc ^ a_swz(n)) << 4));
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < S::TN; ++j) {
@@ -322,7 +346,7 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
                                        const LoadPlan<S, DUAL, COH_A>& P, char* cur, char* nxt, const WaveCtx& w) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
-  constexpr int NM = S::TM * S::TN, ND = S::TM + 2 * S::TN;
+  constexpr int NM = S::TM * S::TN, ND = S::TM + (S::BNT ? 1 : 2) * S::TN;
   frag_load<S, DUAL>(f1, cur, 1, w);
   frag_mfma<S>(acc, f0);
   if (steady) sched_interleave<NM, ND, 0>();

@@ -234,6 +234,30 @@ kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_
                        const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same two collectives with the weight stored transposed, W^T [n, k]
+ * (row j holds output column j's k values): the data-gradient GEMMs of the
+ * backward pass [abstract: KOSMOS fuses every TP+SP collective of a
+ * transformer layer; explainer, "Start with the problem"].  The backward of
+ * an all-gather+GEMM (Y = AG(X) . W) is a GEMM+reduce-scatter of dY . W^T;
+ * the backward of a GEMM+reduce-scatter (Y = RS(X . W)) is an
+ * all-gather+GEMM of dY with W^T -- both with the forward weight as it is
+ * stored, k x n, read as the n x k operand of the transposed product.
+ *
+ * kos_ag_gemm_wt:  as kos_ag_gemm with C = G . W^T, w_t bf16 [n, k].
+ * kos_gemm_rs_wt:  as kos_gemm_rs with P = A . W^T, w_t bf16 [n, k].
+ * Shapes, modes, other arguments and errors as the plain entry points.
+ */
+kos_status kos_ag_gemm_wt(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                          const void* a_local, const void* const* a_peers, const void* w_t,
+                          void* a_gathered, void* c, int32_t c_dtype,
+                          const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+kos_status kos_gemm_rs_wt(int32_t world, int32_t rank, int64_t m, int64_t k, int64_t n,
+                          const void* a, const void* w_t, const float* const* peer_slices,
+                          float* partial, float* y,
+                          const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * MXFP8 operands for the two TP+SP collectives [abstract: the same fused
  * kernels speed up training in MXFP8 as well as in BF16].  The pages do not
  * restate the format; it is the OCP Microscaling (MX) specification v1.0:

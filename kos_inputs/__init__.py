@@ -126,6 +126,14 @@ RS_OUTPROJ = RsShape("rs_outproj_8r_4096x1024x8192", 11, 8, 4096, 1024, 8192)
 
 # MXFP8 operands (E4M3 codes, E8M0 scales) at the QKV and MLP-down shapes,
 # and small shapes of whole 256 x 256 tiles with several tiles each way
+# the backward pass's data-gradient collectives of the same layer, weights
+# stored transposed (n x k): the QKV all-gather+GEMM's backward is a
+# GEMM+reduce-scatter of dY [4096, 3072] with W_qkv^T (8192 output columns),
+# the MLP-down reduce-scatter's backward an all-gather of dY shards
+# [512, 8192] with W_down^T (3584 output columns)
+RS_QKV_BWD = RsShape("rs_qkv_bwd_8r_4096x3072x8192", 18, 8, 4096, 3072, 8192)
+AG_MLP_BWD = AgShape("ag_mlpdown_bwd_8r_4096x8192x3584", 19, 8, 512, 8192, 3584)
+
 AG_QKV_MX = AgShape("ag_qkv_mx_8r_4096x8192x3072", 12, 8, 512, 8192, 3072)
 RS_MLP_MX = RsShape("rs_mlpdown_mx_8r_4096x3584x8192", 13, 8, 4096, 3584, 8192)
 AG_TINY_MX = AgShape("ag_tiny_mx_4r_1024x512x512", 14, 4, 256, 512, 512)
@@ -177,20 +185,21 @@ def integers(shape, lo, hi, wid, tid, rank, device, dtype=torch.bfloat16):
 # all-gather + GEMM
 # ---------------------------------------------------------------------------
 
-def ag_inputs(s: AgShape, rank: int, device="cpu", integer=False):
+def ag_inputs(s: AgShape, rank: int, device="cpu", integer=False, wt=False):
     """Shards of every rank (shard p is the same whichever rank asks) and the
-    column-parallel weight shard.  Returns dict(a_local, a_peers, w) with
-    ``a_peers[rank] is None``."""
+    column-parallel weight shard (``wt``: stored transposed, n x k).  Returns
+    dict(a_local, a_peers, w) with ``a_peers[rank] is None``."""
     shards = []
     for p in range(s.world):
         if integer:
             shards.append(integers((s.m_local, s.k), -4, 4, s.wid, T_A, p, device))
         else:
             shards.append(normal((s.m_local, s.k), 1.0, s.wid, T_A, p, device))
+    wshape = (s.n, s.k) if wt else (s.k, s.n)
     if integer:
-        w = integers((s.k, s.n), -4, 4, s.wid, T_W, 0, device)
+        w = integers(wshape, -4, 4, s.wid, T_W, 0, device)
     else:
-        w = normal((s.k, s.n), 1.0 / s.k, s.wid, T_W, 0, device)
+        w = normal(wshape, 1.0 / s.k, s.wid, T_W, 0, device)
     peers = [None if p == rank else shards[p] for p in range(s.world)]
     return dict(a_local=shards[rank], a_peers=peers, w=w)
 
@@ -199,16 +208,17 @@ def ag_inputs(s: AgShape, rank: int, device="cpu", integer=False):
 # GEMM + reduce-scatter
 # ---------------------------------------------------------------------------
 
-def rs_inputs(s: RsShape, rank: int, device="cpu", integer=False):
-    """A, W and the fp32 rows of chunk ``rank`` that every peer p computed
-    (``peer_slices[rank] is None``).  Same law as the local partial's entries:
-    N(0,1) (K * 1 * 1/K)."""
+def rs_inputs(s: RsShape, rank: int, device="cpu", integer=False, wt=False):
+    """A, W (``wt``: stored transposed, n x k) and the fp32 rows of chunk
+    ``rank`` that every peer p computed (``peer_slices[rank] is None``).  Same
+    law as the local partial's entries: N(0,1) (K * 1 * 1/K)."""
+    wshape = (s.n, s.k) if wt else (s.k, s.n)
     if integer:
         a = integers((s.m, s.k), -4, 4, s.wid, T_A, rank, device)
-        w = integers((s.k, s.n), -4, 4, s.wid, T_W, 0, device)
+        w = integers(wshape, -4, 4, s.wid, T_W, 0, device)
     else:
         a = normal((s.m, s.k), 1.0, s.wid, T_A, rank, device)
-        w = normal((s.k, s.n), 1.0 / s.k, s.wid, T_W, 0, device)
+        w = normal(wshape, 1.0 / s.k, s.wid, T_W, 0, device)
     peers = []
     for p in range(s.world):
         if p == rank:

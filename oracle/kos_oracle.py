@@ -139,6 +139,27 @@ def reduce_chunk(partial, peer_slices, rank: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# the same collectives with the weight stored transposed (backward pass)
+# ---------------------------------------------------------------------------
+#
+# The data-gradient products of the backward pass multiply by the transposed
+# forward weight: the backward of Y = AG(X) . W is a reduce-scatter of
+# dY . W^T, the backward of Y = RS(X . W) an all-gather of dY followed by
+# . W^T [KOSMOS arXiv abstract: every TP+SP collective of the layer is
+# fused].  W^T is given as stored, [n, k].
+
+
+def ag_gemm_wt(a_local, a_peers, w_t_bits, rank: int, out_dtype: str = "bf16"):
+    """``ag_gemm`` with C = G . W^T, W^T bf16 [n, k]."""
+    return ag_gemm(a_local, a_peers, np.asarray(w_t_bits, dtype=np.uint16).T, rank, out_dtype)
+
+
+def gemm_rs_wt(a_bits, w_t_bits, peer_slices, rank: int):
+    """``gemm_rs`` with P = A . W^T, W^T bf16 [n, k]."""
+    return gemm_rs(a_bits, np.asarray(w_t_bits, dtype=np.uint16).T, peer_slices, rank)
+
+
+# ---------------------------------------------------------------------------
 # MXFP8 operands (the same two collectives with microscaled fp8 inputs)
 # ---------------------------------------------------------------------------
 #

@@ -441,3 +441,34 @@ def test_moe_layer_vs_independent_loop():
                 res = O.bf16_to_f64(m["pr"][d][before])
             acc += bw[t, j] * res
         assert np.array_equal(out["y"][t], O.round_bf16(acc)), t
+
+
+# ---------------------------------------------------------------------------
+# transposed weights (backward data-gradient products)
+# ---------------------------------------------------------------------------
+
+def test_ag_gemm_wt_vs_triple_loop():
+    rng = np.random.default_rng(21)
+    R, m, K, N = 3, 2, 5, 4
+    shards = [_ints(rng, (m, K)) for _ in range(R)]
+    wt = _ints(rng, (N, K))                      # stored n x k
+    g, c = O.ag_gemm_wt(shards[1], [shards[0], None, shards[2]], wt, 1, "f32")
+    G = np.vstack([O.bf16_to_f64(x) for x in shards])
+    W = O.bf16_to_f64(wt)
+    for i in range(R * m):
+        for j in range(N):
+            assert c[i, j] == sum(G[i, k] * W[j, k] for k in range(K))
+
+
+def test_gemm_rs_wt_vs_triple_loop():
+    rng = np.random.default_rng(22)
+    R, M, K, N = 2, 4, 3, 5
+    a = _ints(rng, (M, K))
+    wt = _ints(rng, (N, K))
+    peers = [None, rng.integers(-9, 9, size=(M // R, N)).astype(np.float32)]
+    partial, y = O.gemm_rs_wt(a, wt, peers, 0)
+    A, W = O.bf16_to_f64(a), O.bf16_to_f64(wt)
+    for i in range(M):
+        for j in range(N):
+            assert partial[i, j] == sum(A[i, k] * W[j, k] for k in range(K))
+    assert np.array_equal(y, (partial[:M // R].astype(np.float64) + peers[1]).astype(np.float32))
