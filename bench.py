@@ -384,6 +384,44 @@ def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms, baselines=True):
     return res
 
 
+def backward_collectives(torch, kos, KI, ws, reps, flush):
+    """The data-gradient collectives of the same TP+SP layer's backward pass
+    (weights read transposed): the QKV and MLP-up all-gathers become
+    GEMM+reduce-scatters of dY . W^T (rank 7), the MLP-down and output
+    projection reduce-scatters become all-gather+GEMMs of dY with W^T (rank 0);
+    fused and unfused, and the four together."""
+    res = {}
+    tot_ms = tot_fl = 0.0
+    for name, shape in (("rs_qkv_bwd", KI.RS_QKV_BWD), ("rs_mlpup_bwd", KI.RS_MLPUP_BWD),
+                        ("ag_mlpdown_bwd", KI.AG_MLP_BWD), ("ag_outproj_bwd", KI.AG_OUTPROJ_BWD)):
+        if name.startswith("rs"):
+            r = KI.rs_inputs(shape, 7, "cuda", wt=True)
+            part = torch.empty((shape.m, shape.n), dtype=torch.float32, device="cuda")
+            y = torch.empty((shape.m_chunk, shape.n), dtype=torch.float32, device="cuda")
+            call = lambda o, r=r, part=part, y=y: kos.gemm_rs(r["a"], r["w"], r["peer_slices"], part, y, 7, ws, o,  # noqa: E731
+                                                              w_transposed=True)
+        else:
+            a = KI.ag_inputs(shape, 0, "cuda", wt=True)
+            g = torch.empty((shape.m, shape.k), dtype=torch.bfloat16, device="cuda")
+            c = torch.empty((shape.m, shape.n), dtype=torch.bfloat16, device="cuda")
+            call = lambda o, a=a, g=g, c=c: kos.ag_gemm(a["a_local"], a["a_peers"], a["w"], g, c, 0, ws, o,  # noqa: E731
+                                                        w_transposed=True)
+        t = {}
+        for label, mode in (("fused", 0), ("unfused", 2)):
+            o = kos.opts(mode=mode)
+            fn = lambda o=o, call=call: call(o)  # noqa: E731
+            fn()
+            t[label] = time_ops(torch, [(name, fn)], reps, ws, flush)[0][0]
+        res[name] = {"workload": shape.name, "ms": round(t["fused"], 4),
+                     "tflops": round(shape.flops / (t["fused"] * 1e-3) / 1e12, 1),
+                     "unfused_ms": round(t["unfused"], 4), "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3)}
+        tot_ms += t["fused"]
+        tot_fl += shape.flops
+    ws.status()
+    res["layer_backward_data"] = {"ms": round(tot_ms, 4), "tflops": round(tot_fl / (tot_ms * 1e-3) / 1e12, 1)}
+    return res
+
+
 def rs_order_ablation(torch, kos, KI, inp, ws, reps, flush):
     """GEMM+reduce-scatter in band order (the design) and row order (the
     slower ablation the explainer compares it with), fused, at rank 7 (whose
@@ -574,6 +612,8 @@ def main():
         f4 = KI.AG_QKV.flops + KI.RS_MLP.flops + KI.AG_MLPUP.flops + KI.RS_OUTPROJ.flops
         rest["tp_sp_layer"] = {"ms": round(t4, 4), "tflops": round(f4 / (t4 * 1e-3) / 1e12, 1)}
         extra["tp_sp_layer"] = rest
+        # the backward pass's data-gradient collectives of the layer
+        extra["tp_sp_backward"] = backward_collectives(torch, kos, KI, ws, reps, flush)
         # the same two collectives with MXFP8 operands
         extra["mxfp8"] = mxfp8(torch, kos, KI, ws, reps, flush,
                                {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")})

@@ -133,6 +133,8 @@ RS_OUTPROJ = RsShape("rs_outproj_8r_4096x1024x8192", 11, 8, 4096, 1024, 8192)
 # [512, 8192] with W_down^T (3584 output columns)
 RS_QKV_BWD = RsShape("rs_qkv_bwd_8r_4096x3072x8192", 18, 8, 4096, 3072, 8192)
 AG_MLP_BWD = AgShape("ag_mlpdown_bwd_8r_4096x8192x3584", 19, 8, 512, 8192, 3584)
+RS_MLPUP_BWD = RsShape("rs_mlpup_bwd_8r_4096x7168x8192", 20, 8, 4096, 7168, 8192)
+AG_OUTPROJ_BWD = AgShape("ag_outproj_bwd_8r_4096x8192x1024", 21, 8, 512, 8192, 1024)
 
 AG_QKV_MX = AgShape("ag_qkv_mx_8r_4096x8192x3072", 12, 8, 512, 8192, 3072)
 RS_MLP_MX = RsShape("rs_mlpdown_mx_8r_4096x3584x8192", 13, 8, 4096, 3584, 8192)
