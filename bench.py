@@ -341,27 +341,40 @@ def rest_of_layer(torch, kos, KI, inp, ws, reps, flush):
 
 
 def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms, baselines=True):
-    """The QKV all-gather+GEMM (rank 0) and MLP-down GEMM+reduce-scatter
-    (rank 7) with MXFP8 operands: fused (and, with `baselines`, unfused and
+    """The TP+SP layer's four fused collectives with MXFP8 operands -- QKV and
+    MLP-up all-gather+GEMM (rank 0), MLP-down and output-projection
+    GEMM+reduce-scatter (rank 7): fused (and, with `baselines`, unfused and
     FIXED crews of 16 and 32), TFLOP/s against the dense fp8 peak, HBM bytes
-    per launch from the committed counter summary, and the speed-up over the
-    bf16 op of the timed step."""
+    per launch from the committed counter summary, the speed-up over the bf16
+    op, and the four together.  Without `baselines` only the QKV and MLP-down
+    ops."""
     res = {}
-    ag, rs = KI.AG_QKV_MX, KI.RS_MLP_MX
-    a = KI.ag_mx_inputs(ag, 0, "cuda")
-    g = torch.empty((ag.m, ag.k), dtype=torch.uint8, device="cuda")
-    gs = torch.empty((ag.k // 64, ag.m, 2), dtype=torch.uint8, device="cuda")
-    c = torch.empty((ag.m, ag.n), dtype=torch.bfloat16, device="cuda")
-    r = KI.rs_mx_inputs(rs, 7, "cuda")
-    part = torch.empty((rs.m, rs.n), dtype=torch.float32, device="cuda")
-    y = torch.empty((rs.m_chunk, rs.n), dtype=torch.float32, device="cuda")
-    for name, bf16_name, shape, call in (
-            ("ag_gemm_mx", "ag_gemm", ag,
-             lambda o: kos.ag_gemm_mx(a["a_local"], a["s_local"], a["a_peers"], a["s_peers"], a["w"], a["w_scales"],
-                                      g, gs, c, 0, ws, o)),
-            ("gemm_rs_mx", "gemm_rs", rs,
-             lambda o: kos.gemm_rs_mx(r["a"], r["a_scales"], r["w"], r["w_scales"], r["peer_slices"], part, y, 7,
-                                      ws, o))):
+
+    def ag_call(shape):
+        a = KI.ag_mx_inputs(shape, 0, "cuda")
+        g = torch.empty((shape.m, shape.k), dtype=torch.uint8, device="cuda")
+        gs = torch.empty((shape.k // 64, shape.m, 2), dtype=torch.uint8, device="cuda")
+        c = torch.empty((shape.m, shape.n), dtype=torch.bfloat16, device="cuda")
+        return lambda o: kos.ag_gemm_mx(a["a_local"], a["s_local"], a["a_peers"], a["s_peers"], a["w"],
+                                        a["w_scales"], g, gs, c, 0, ws, o)
+
+    def rs_call(shape):
+        r = KI.rs_mx_inputs(shape, 7, "cuda")
+        part = torch.empty((shape.m, shape.n), dtype=torch.float32, device="cuda")
+        y = torch.empty((shape.m_chunk, shape.n), dtype=torch.float32, device="cuda")
+        return lambda o: kos.gemm_rs_mx(r["a"], r["a_scales"], r["w"], r["w_scales"], r["peer_slices"], part, y, 7,
+                                        ws, o)
+
+    ops = [("ag_gemm_mx", "ag_gemm", KI.AG_QKV_MX, ag_call), ("gemm_rs_mx", "gemm_rs", KI.RS_MLP_MX, rs_call),
+           ("ag_mlpup_mx", "ag_mlpup", KI.AG_MLPUP_MX, ag_call),
+           ("rs_outproj_mx", "rs_outproj", KI.RS_OUTPROJ_MX, rs_call)]
+    # without baselines (the profiling runs): one shape per kernel, so the
+    # counters of a kernel belong to one workload
+    if not baselines:
+        ops = ops[:2]
+    tot_ms = tot_fl = 0.0
+    for name, bf16_name, shape, mk in ops:
+        call = mk(shape)
         t = {}
         runs = (("fused", 0, -1), ("unfused", 2, -1), ("fixed16", 1, 16), ("fixed32", 1, 32))
         for label, mode, crew in runs if baselines else runs[:1]:
@@ -372,15 +385,20 @@ def mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms, baselines=True):
         tf = shape.flops / (t["fused"] * 1e-3) / 1e12
         d = {"workload": shape.name, "ms": round(t["fused"], 4), "tflops": round(tf, 1),
              "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
-             "traffic": measured_traffic(name, shape.name),
-             "speedup_vs_bf16": round(bf16_ms[bf16_name] / t["fused"], 3)}
+             "traffic": measured_traffic(name, shape.name)}
+        if bf16_name in bf16_ms:
+            d["speedup_vs_bf16"] = round(bf16_ms[bf16_name] / t["fused"], 3)
         if baselines:
             fixed = min(t["fixed16"], t["fixed32"])
             d.update(unfused_ms=round(t["unfused"], 4), speedup_vs_unfused=round(t["unfused"] / t["fused"], 3),
                      best_fixed_ms=round(fixed, 4), speedup_vs_best_fixed=round(fixed / t["fused"], 3))
         res[name] = d
+        tot_ms += t["fused"]
+        tot_fl += shape.flops
+        del call
     ws.status()
-    del a, g, gs, c, r, part, y
+    if baselines:
+        res["tp_sp_layer_mx"] = {"ms": round(tot_ms, 4), "tflops": round(tot_fl / (tot_ms * 1e-3) / 1e12, 1)}
     return res
 
 
@@ -615,8 +633,9 @@ def main():
         # the backward pass's data-gradient collectives of the layer
         extra["tp_sp_backward"] = backward_collectives(torch, kos, KI, ws, reps, flush)
         # the same two collectives with MXFP8 operands
-        extra["mxfp8"] = mxfp8(torch, kos, KI, ws, reps, flush,
-                               {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")})
+        bf16_ms = {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")}
+        bf16_ms.update(ag_mlpup=rest["ag_mlpup"]["ms"], rs_outproj=rest["rs_outproj"]["ms"])
+        extra["mxfp8"] = mxfp8(torch, kos, KI, ws, reps, flush, bf16_ms)
     elif args.mxfp8:
         extra["mxfp8"] = mxfp8(torch, kos, KI, ws, max(3, args.steps // 4), flush,
                                {n: per[names.index(n)] for n in ("ag_gemm", "gemm_rs")}, baselines=False)

@@ -138,6 +138,8 @@ AG_OUTPROJ_BWD = AgShape("ag_outproj_bwd_8r_4096x8192x1024", 21, 8, 512, 8192, 1
 
 AG_QKV_MX = AgShape("ag_qkv_mx_8r_4096x8192x3072", 12, 8, 512, 8192, 3072)
 RS_MLP_MX = RsShape("rs_mlpdown_mx_8r_4096x3584x8192", 13, 8, 4096, 3584, 8192)
+AG_MLPUP_MX = AgShape("ag_mlpup_mx_8r_4096x8192x7168", 22, 8, 512, 8192, 7168)
+RS_OUTPROJ_MX = RsShape("rs_outproj_mx_8r_4096x1024x8192", 23, 8, 4096, 1024, 8192)
 AG_TINY_MX = AgShape("ag_tiny_mx_4r_1024x512x512", 14, 4, 256, 512, 512)
 RS_TINY_MX = RsShape("rs_tiny_mx_4r_1024x512x512", 15, 4, 1024, 512, 512)
 
