@@ -140,42 +140,52 @@ __device__ __forceinline__ void route_entry(const DispatchParams& p, int b4, Dis
     }
   }
   const int k = p.k;
+  // the wave's TPW tokens select side by side (independent reduction
+  // chains interleave); tokens past T select garbage and store nothing
+  uint32_t taken[TPW];
+  float my_v[TPW];   // selection `lane` (lanes < k)
+  int my_i[TPW];
 #pragma unroll
   for (int x = 0; x < TPW; ++x) {
-    const int tl = wave + 4 * x;
-    const int t = b4 * QT + tl;
-    if (t >= p.T) break;
-    uint32_t taken = 0;
+    taken[x] = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (lane + 64 * i >= p.E) taken |= 1u << i;
-    float my_v = 0.f;   // selection `lane` (lanes < k)
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
+      if (lane + 64 * i >= p.E) taken[x] |= 1u << i;
+    my_v[x] = 0.f;
+    my_i[x] = 0;
+  }
+  for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
       // this lane's best remaining candidate, then the wave's
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const uint64_t kk = ((taken >> i) & 1u) ? 0 : cand_key(v[x][i], lane + 64 * i);
+        const uint64_t kk = ((taken[x] >> i) & 1u) ? 0 : cand_key(v[x][i], lane + 64 * i);
         best = kk > best ? kk : best;
       }
       const uint64_t win = wave_max_key(best);
       const int wi = key_index(win);
       if (lane == j) {
-        my_v = key_value(win);
-        my_i = wi;
+        my_v[x] = key_value(win);
+        my_i[x] = wi;
       }
-      if ((wi & 63) == lane) taken |= 1u << (wi >> 6);
+      if ((wi & 63) == lane) taken[x] |= 1u << (wi >> 6);
     }
+  }
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int tl = wave + 4 * x;
+    const int t = b4 * QT + tl;
     // softmax over the k selected logits (largest first)
-    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
-    const float z = lane < k ? expf(my_v - v0) : 0.f;
+    const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v[x])));
+    const float z = lane < k ? expf(my_v[x] - v0) : 0.f;
     const float w = z / wave_sum(z);
-    if (lane < k) {
+    if (t < p.T && lane < k) {
       // read by other workgroups of this launch: device-coherent stores
-      st_dev_b32(&p.topk_idx[(int64_t)t * k + lane], (uint32_t)my_i);
+      st_dev_b32(&p.topk_idx[(int64_t)t * k + lane], (uint32_t)my_i[x]);
       st_dev_b32(&p.topk_w[(int64_t)t * k + lane], __builtin_bit_cast(uint32_t, w));
-      atomicOr(&L.m[my_i], 1u << tl);
+      atomicOr(&L.m[my_i[x]], 1u << tl);
     }
   }
   __syncthreads();
