@@ -531,7 +531,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share only (emulated peers); --gpus {args.gpus} is not supported: "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the library runs one GPU's share; there is no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
