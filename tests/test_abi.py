@@ -66,3 +66,49 @@ def test_trace_reader_validation():
     assert lib.kos_workspace_trace(fake, fake, TRACE_MAX_WG * TRACE_RECORDS + 1, None) == KOS_ERR_ARG
     assert ctypes.sizeof(kos._binding.TraceRec) == 16
     assert ctypes.sizeof(kos.Opts) == 32
+
+
+def _ag_mx(kos, **over):
+    lib = kos.lib
+    fake = ctypes.c_void_p(0x10000)           # never dereferenced: validation fails first
+    peers = kos._binding.ptr_array([None, 0x10000])
+    args = dict(world=2, rank=0, m=256, k=256, n=256, a=fake, sa=fake, peers=peers, speers=peers, w=fake,
+                sw=fake, g=fake, sg=fake, c=fake, dt=0, ws=fake, wsb=lib.kos_workspace_bytes())
+    args.update(over)
+    o = kos.opts()
+    return lib.kos_ag_gemm_mx(args["world"], args["rank"], args["m"], args["k"], args["n"], args["a"], args["sa"],
+                              args["peers"], args["speers"], args["w"], args["sw"], args["g"], args["sg"],
+                              args["c"], args["dt"], ctypes.byref(o), args["ws"], args["wsb"], None)
+
+
+def _rs(kos, fn, **over):
+    lib = kos.lib
+    fake = ctypes.c_void_p(0x10000)
+    peers = kos._binding.ptr_array([None, 0x10000])
+    args = dict(world=2, rank=0, m=512, k=256, n=256, a=fake, sa=fake, w=fake, sw=fake, peers=peers, p=fake,
+                y=fake, ws=fake, wsb=lib.kos_workspace_bytes())
+    args.update(over)
+    o = kos.opts()
+    if fn == "mx":
+        return lib.kos_gemm_rs_mx(args["world"], args["rank"], args["m"], args["k"], args["n"], args["a"],
+                                  args["sa"], args["w"], args["sw"], args["peers"], args["p"], args["y"],
+                                  ctypes.byref(o), args["ws"], args["wsb"], None)
+    return lib.kos_gemm_rs_wt(args["world"], args["rank"], args["m"], args["k"], args["n"], args["a"], args["w"],
+                              args["peers"], args["p"], args["y"], ctypes.byref(o), args["ws"], args["wsb"], None)
+
+
+def test_mx_and_wt_argument_validation():
+    import gemm_collective_persistent_amd as kos
+    from gemm_collective_persistent_amd._binding import KOS_ERR_ALIGN, KOS_ERR_ARG, KOS_ERR_SHAPE
+    # MX: whole 256 x 256 tiles and whole 256-wide K trips only
+    assert _ag_mx(kos, m=128) == KOS_ERR_SHAPE
+    assert _ag_mx(kos, k=320) == KOS_ERR_SHAPE
+    assert _ag_mx(kos, n=192) == KOS_ERR_SHAPE
+    assert _ag_mx(kos, sa=None) == KOS_ERR_ARG
+    assert _ag_mx(kos, speers=kos._binding.ptr_array([None, None])) == KOS_ERR_ARG
+    assert _ag_mx(kos, sg=ctypes.c_void_p(0x10004)) == KOS_ERR_ALIGN
+    assert _rs(kos, "mx", m=256) == KOS_ERR_SHAPE       # m/world = 128
+    assert _rs(kos, "mx", sw=None) == KOS_ERR_ARG
+    # transposed weights: the bf16 rules
+    assert _rs(kos, "wt", k=100) == KOS_ERR_SHAPE
+    assert _rs(kos, "wt", w=None) == KOS_ERR_ARG
