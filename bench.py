@@ -33,20 +33,35 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 / MXFP8 MFMA, published
 PEAK_CLOCK_MHZ = 2400.0        # MI355X peak engine clock (the published peaks assume it)
 
 
-def crew_model(t_gemm_full, cus_total, cus_reserved, frac_on_rest, tail_fixed, tail_switch):
-    """The explainer's worked example as a model: a GEMM taking t_gemm_full
-    on the whole GPU runs at `frac_on_rest` of full throughput on the CUs left
-    after reserving a crew, then a reduction tail follows; with switching the
-    tail shrinks.  Returns (t_fixed, t_switch, speedup).  (cus_* are kept for
-    the record; the page states the throughput fraction directly.)"""
-    t_rest = t_gemm_full / frac_on_rest
-    t_fixed = t_rest + tail_fixed
-    t_switch = t_rest + tail_switch
-    return t_fixed, t_switch, t_fixed / t_switch
-
-
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def build_moe_inputs(torch, KI, s, rank=0):
+    """One rank's expert-layer inputs (seeded) and output buffers, resident on
+    the GPU: the send buffers hold every row a rank can send one peer, the
+    grouped buffers every row this rank can receive."""
+    dev = "cuda"
+    m = KI.moe_inputs(s, rank, dev)
+    pc = m["peer_counts"].cpu()
+    cap = int(pc.sum()) + s.tokens * min(s.topk, s.e_local)
+    m.update(
+        idx=torch.empty((s.tokens, s.topk), dtype=torch.int32, device=dev),
+        w=torch.empty((s.tokens, s.topk), dtype=torch.float32, device=dev),
+        counts=torch.empty((s.experts,), dtype=torch.int32, device=dev),
+        perm=torch.empty((s.tokens * s.topk,), dtype=torch.int32, device=dev),
+        send=[None if p == rank else torch.empty((s.peer_cap, s.hidden), dtype=torch.bfloat16, device=dev)
+              for p in range(s.world)],
+        grouped=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
+        goff=torch.empty((s.e_local + 1,), dtype=torch.int32, device=dev),
+        row_src=torch.empty((cap, 2), dtype=torch.int32, device=dev),
+        h=torch.empty((cap, s.ffn), dtype=torch.bfloat16, device=dev),
+        yg=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
+        y=torch.empty((s.tokens, s.hidden), dtype=torch.bfloat16, device=dev),
+        ret=[None if p == rank else torch.empty((max(int(pc[p].sum()), 1), s.hidden), dtype=torch.bfloat16,
+                                                device=dev) for p in range(s.world)],
+    )
+    return m
 
 
 def build_inputs(torch, KI, kos, moe_shape):
@@ -62,36 +77,19 @@ def build_inputs(torch, KI, kos, moe_shape):
     rs["partial"] = torch.empty((s.m, s.n), dtype=torch.float32, device=dev)
     rs["y"] = torch.empty((s.m_chunk, s.n), dtype=torch.float32, device=dev)
     inp["rs"] = rs
-    s = moe_shape
-    m = KI.moe_inputs(s, 0, dev)
-    pc = m["peer_counts"].cpu()
-    cap = int(pc.sum()) + s.tokens * min(s.topk, s.e_local)
-    m.update(
-        idx=torch.empty((s.tokens, s.topk), dtype=torch.int32, device=dev),
-        w=torch.empty((s.tokens, s.topk), dtype=torch.float32, device=dev),
-        counts=torch.empty((s.experts,), dtype=torch.int32, device=dev),
-        perm=torch.empty((s.tokens * s.topk,), dtype=torch.int32, device=dev),
-        send=[None if p == 0 else torch.empty((s.peer_cap, s.hidden), dtype=torch.bfloat16, device=dev)
-              for p in range(s.world)],
-        grouped=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
-        goff=torch.empty((s.e_local + 1,), dtype=torch.int32, device=dev),
-        row_src=torch.empty((cap, 2), dtype=torch.int32, device=dev),
-        h=torch.empty((cap, s.ffn), dtype=torch.bfloat16, device=dev),
-        yg=torch.empty((cap, s.hidden), dtype=torch.bfloat16, device=dev),
-        y=torch.empty((s.tokens, s.hidden), dtype=torch.bfloat16, device=dev),
-        ret=[None if p == 0 else torch.empty((max(int(pc[p].sum()), 1), s.hidden), dtype=torch.bfloat16,
-                                             device=dev) for p in range(s.world)],
-    )
-    inp["moe"] = m
+    inp["moe"] = build_moe_inputs(torch, KI, moe_shape)
     return inp
 
 
-def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=False):
+def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=False, rank_moe=0):
+    """The step's ops as closures over resident inputs (the AG and RS ones
+    only when `inp` holds their inputs).  FIXED mode runs the dispatch fused:
+    it has no compute role to split a crew from."""
     from gemm_collective_persistent_amd.api import moe_shape as mk_shape
     o = kos.opts(mode=mode, n_movers=n_movers, grid=grid, trace=trace)
-    ag, rs, m = inp["ag"], inp["rs"], inp["moe"]
+    ag, rs, m = inp.get("ag"), inp.get("rs"), inp["moe"]
     s = moe_shape
-    shp = mk_shape(s.world, 0, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
+    shp = mk_shape(s.world, rank_moe, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
 
     def op_ag():
         kos.ag_gemm(ag["a_local"], ag["a_peers"], ag["w"], ag["g"], ag["c"], 0, ws, o)
@@ -109,7 +107,89 @@ def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=Fal
                         m["counts"], m["perm"], m["peer_counts"], m["peer_return"], m["h"], m["yg"], m["ret"],
                         m["y"], ws, o)
 
-    return [("ag_gemm", op_ag), ("gemm_rs", op_rs), ("moe_dispatch", op_dispatch), ("moe_combine", op_combine)]
+    ops = [("moe_dispatch", op_dispatch), ("moe_combine", op_combine)]
+    if rs is not None:
+        ops.insert(0, ("gemm_rs", op_rs))
+    if ag is not None:
+        ops.insert(0, ("ag_gemm", op_ag))
+    return ops
+
+
+def moe_block(torch, kos, KI, ws, flush, reps, shape, rank=0):
+    """A whole expert layer (dispatch, then combine) of one rank on its own:
+    fused times, tokens/s and the combine's TFLOP/s, the same-GPU baselines
+    (unfused; the combine's FIXED crew sweep, the planned crew included), and
+    per mode the idle-CU fraction and the communication-phase rates."""
+    m = build_moe_inputs(torch, KI, shape, rank)
+    inp = {"moe": m}
+    names = ["moe_dispatch", "moe_combine"]
+    ops = make_ops(kos, KI, inp, ws, shape, rank_moe=rank)
+    for _ in range(2):
+        for _, fn in ops:
+            fn()
+    ws.status()
+    per, _ = time_ops(torch, ops, reps, ws, flush)
+    rows = int(m["goff"][-1].item())
+    fl = rows * shape.flops_per_row
+    ops_u = make_ops(kos, KI, inp, ws, shape, mode=2, rank_moe=rank)
+    for _, fn in ops_u:
+        fn()
+    pu, _ = time_ops(torch, ops_u, reps, ws, flush)
+    grid = int(kos.lib.kos_device_cu_count())
+    planned = planned_crews(KI, shape, rows, grid)["moe_combine"]
+    make_ops(kos, KI, inp, ws, shape, rank_moe=rank)[0][1]()   # dispatch outputs for the combine runs
+    sweep = crew_sweep_moe(torch, kos, KI, inp, ws, shape, flush, reps, planned, rank)
+    best = min(sweep, key=sweep.get)
+    peer_rows = int(m["peer_counts"].sum().item())
+    pb = phase_bytes(KI, shape, rows, peer_rows)
+    idle, rates = idle_fractions(torch, kos, KI, inp, ws, shape, flush, {"moe_combine": best}, pb, names,
+                                 rank_moe=rank)
+    t_layer = per[0] + per[1]
+    return {
+        "workload": shape.name, "rank": rank, "grouped_rows": rows,
+        "ms": {"moe_dispatch": round(per[0], 4), "moe_combine": round(per[1], 4), "layer": round(t_layer, 4)},
+        "tokens_per_s": round(shape.tokens / (t_layer * 1e-3), 1),
+        "combine_tflops": round(fl / (per[1] * 1e-3) / 1e12, 1),
+        "combine_pct_bf16_peak": round(100 * fl / (per[1] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+        "unfused_ms": {"moe_dispatch": round(pu[0], 4), "moe_combine": round(pu[1], 4)},
+        "speedup_vs_unfused": {"moe_dispatch": round(pu[0] / per[0], 3), "moe_combine": round(pu[1] / per[1], 3),
+                               "layer": round((pu[0] + pu[1]) / t_layer, 3)},
+        "combine_fixed_crew_sweep_ms": {str(c): t for c, t in sweep.items()},
+        "combine_best_fixed": {"crew": best, "ms": sweep[best], "speedup": round(sweep[best] / per[1], 3)},
+        "combine_planned_split": {"crew": planned, "ms": sweep[planned], "speedup": round(sweep[planned] / per[1], 3)},
+        "idle_cu_fraction": idle,
+        "phase_rate_gb_s": {lab: {n: {k: v["gb_s"] for k, v in d.items()} for n, d in r.items()}
+                            for lab, r in rates.items()},
+    }
+
+
+def crew_sweep_moe(torch, kos, KI, inp, ws, shape, flush, reps, planned, rank):
+    """The combine's FIXED crew over CREW_SWEEP and the planned crew."""
+    out = {}
+    for c in sorted(set(CREW_SWEEP) | {planned}):
+        fn = dict(make_ops(kos, KI, inp, ws, shape, mode=1, n_movers=c, rank_moe=rank))["moe_combine"]
+        fn()
+        out[c] = round(time_ops(torch, [("moe_combine", fn)], reps, ws, flush)[0][0], 4)
+    return out
+
+
+def tiny_ag(torch, kos, KI, ws, flush, reps=50):
+    """The tiny all-gather+GEMM (4 emulated ranks, 64x256 shards, 256x256
+    weight; rank 0): latency-bound, reported in microseconds -- fused,
+    unfused and a FIXED crew of 4 (one workgroup per remote shard)."""
+    s = KI.AG_TINY
+    a = KI.ag_inputs(s, 0, "cuda")
+    g = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((s.m, s.n), dtype=torch.bfloat16, device="cuda")
+    t = {}
+    for label, mode, crew in (("fused", 0, -1), ("unfused", 2, -1), ("fixed_crew4", 1, 4)):
+        o = kos.opts(mode=mode, n_movers=crew)
+        fn = lambda o=o: kos.ag_gemm(a["a_local"], a["a_peers"], a["w"], g, c, 0, ws, o)  # noqa: E731
+        fn()
+        t[label] = time_ops(torch, [("ag_tiny", fn)], reps, ws, flush)[0][0] * 1e3
+    return {"workload": s.name, "us": {k: round(v, 2) for k, v in t.items()},
+            "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3),
+            "speedup_vs_fixed": round(t["fixed_crew4"] / t["fused"], 3)}
 
 
 def source_digest() -> str:
@@ -198,28 +278,75 @@ def time_ops(torch, ops, reps, ws, flush):
     return per, wall
 
 
-def idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush, modes, base):
-    """Idle-CU fraction (share of workgroup-time outside pieces of work, over
-    the kernel's span; kos_opts.trace) of each op, per mode.  The fixed-split
-    baseline is traced at its best crew from `base`."""
-    from gemm_collective_persistent_amd.timeline import summarize
+# launches an unfused call makes (its trace fills one slot per launch)
+UNFUSED_LAUNCHES = {"ag_gemm": 2, "gemm_rs": 2, "moe_dispatch": 2, "moe_combine": 4}
+# the fixed-crew sweep: every crew size from 8 to 128 in steps of 8 (plus the
+# planned crew), the best of which is the "best fixed split"
+CREW_SWEEP = tuple(range(8, 129, 8))
+
+
+def phase_bytes(KI, moe_shape, rows, peer_rows):
+    """Algorithmic bytes of each op's communication phase (read + written):
+    AG the gather (every shard read and written into the gathered matrix);
+    RS the reduction (the peers' slices and our staged rows read, the chunk
+    written); dispatch the token movement (our tokens read, one row per
+    (token, expert) pair written, the peers' rows read and written into the
+    grouped input); combine the pushes (rows returned to peers, read and
+    written) and the fold (k results read per token, the token written)."""
+    ag, rs, m = KI.AG_QKV, KI.RS_MLP, moe_shape
+    row = m.hidden * 2
+    return {"ag_gemm": {"move": 2.0 * ag.m * ag.k * 2},
+            "gemm_rs": {"reduce": (rs.world + 1) * rs.m_chunk * rs.n * 4.0},
+            "moe_dispatch": {"move": (m.tokens + m.tokens * m.topk + 2.0 * peer_rows) * row},
+            "moe_combine": {"push": 2.0 * peer_rows * row, "fold": m.tokens * (m.topk + 1.0) * row}}
+
+
+def traced_call(kos, ws, fn, grid, launches, flush):
+    """One traced, untimed call; its timeline (every launch)."""
+    flush()
+    fn()
+    ws.status()
+    return ws.trace(grid, launches=launches)
+
+
+def idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush, best_crew, pbytes, names, rank_moe=0):
+    """Per op and mode: the idle-CU fraction (share of compute-unit time, over
+    the call's span, that no piece of work covers; the unfused baselines'
+    gaps between launches count as idle) and the rate of each communication
+    phase (its algorithmic bytes over the span of its pieces of work), from
+    one traced call each (kos_opts.trace).  FIXED is traced at its best crew."""
+    from gemm_collective_persistent_amd.timeline import phase_rate, summarize
     grid = int(kos.lib.kos_device_cu_count())
-    names = ["ag_gemm", "gemm_rs", "moe_dispatch", "moe_combine"]
-    out = {}
-    for label, mc in modes.items():
-        if mc is None:   # best fixed crew per op
-            best = {n: min((k for k in base if k.startswith("fixed")), key=lambda k: base[k][n]) for n in names}
-        out[label] = {}
+    idle, rates = {}, {}
+    for label in ("fused", "unfused", "fixed_best"):
+        idle[label], rates[label] = {}, {}
         for n in names:
-            if mc is None:
-                mode, crew = 1, int(best[n].replace("fixed_crew", ""))
-            else:
-                mode, crew = mc
-            ops = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew, trace=True))
-            flush()
-            ops[n]()
-            ws.status()
-            out[label][n] = summarize(ws.trace(grid))["idle_frac"]
+            if label == "fixed_best" and n not in best_crew:
+                continue
+            mode = {"fused": 0, "unfused": 2, "fixed_best": 1}[label]
+            crew = best_crew.get(n, -1) if label == "fixed_best" else -1
+            fn = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew, trace=True,
+                               rank_moe=rank_moe))[n]
+            L = UNFUSED_LAUNCHES[n] if mode == 2 else 1
+            tl = traced_call(kos, ws, fn, grid, L, flush)
+            idle[label][n] = summarize(tl, workgroups=grid)["idle_frac"]
+            rates[label][n] = {k: phase_rate(tl, k, b) for k, b in pbytes[n].items()}
+    return idle, rates
+
+
+def crew_sweep(torch, kos, KI, inp, ws, moe_shape, flush, reps, names, extra):
+    """FIXED mode of each op with a compute role at every crew of CREW_SWEEP
+    and the crews in `extra` (op -> crew): {op: {crew: ms}}.  The dispatch
+    has no compute role to split from (no FIXED mode)."""
+    out = {}
+    for n in names:
+        if n == "moe_dispatch":
+            continue
+        out[n] = {}
+        for c in sorted(set(CREW_SWEEP) | ({extra[n]} if n in extra else set())):
+            fn = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=1, n_movers=c))[n]
+            fn()
+            out[n][c] = round(time_ops(torch, [(n, fn)], reps, ws, flush)[0][0], 4)
     return out
 
 
@@ -275,16 +402,20 @@ def ag_pinned(torch, kos, KI, inp, ws, reps, flush):
     gemm_only()
     t_gemm = time_ops(torch, [("gemm", gemm_only)], reps, ws, flush)[0][0]
     t = {}
-    for label, mode, crew in (("fused", 0, -1), ("unfused", 2, -1), ("fixed_crew8", 1, 8), ("fixed_crew16", 1, 16)):
+    runs = [("fused", 0, -1), ("unfused", 2, -1)] + [(f"fixed_crew{c}", 1, c) for c in (8, 16, 24, 32, 48, 64)]
+    for label, mode, crew in runs:
         o = kos.opts(mode=mode, n_movers=crew, peer_link=1)
         fn = lambda: kos.ag_gemm(ag["a_local"], peers, ag["w"], ag["g"], ag["c"], 0, ws, o)  # noqa: E731
         fn()
         t[label] = time_ops(torch, [("ag", fn)], max(2, reps // 2), ws, flush)[0][0]
     t_copy = max(t["unfused"] - t_gemm, 1e-6)
     moved = sum(p.numel() * 2 for p in peers if p is not None)
+    best = min((k for k in t if k.startswith("fixed")), key=t.get)
     return {"ms": {k: round(v, 4) for k, v in t.items()}, "gemm_alone_ms": round(t_gemm, 4),
             "link_gb_s": round(moved / (t_copy * 1e-3) / 1e9, 1),
-            "overlap": round((t["unfused"] - t["fused"]) / min(t_copy, t_gemm), 3)}
+            "overlap": round((t["unfused"] - t["fused"]) / min(t_copy, t_gemm), 3),
+            "best_fixed": best, "speedup_vs_best_fixed": round(t[best] / t["fused"], 3),
+            "speedup_vs_unfused": round(t["unfused"] / t["fused"], 3)}
 
 
 def planned_crews(KI, moe_shape, rows, grid):
@@ -587,35 +718,42 @@ def main():
     if args.copy_calibration:
         extra["copy_calibration"] = copy_calibration(torch)
     if not args.no_baselines:
-        base = {}
         reps = max(3, args.steps // 4)
-        for label, mode, crew in [("unfused", 2, -1)] + [(f"fixed_crew{m}", 1, m) for m in (8, 16, 32, 64)]:
-            ops_b = make_ops(kos, KI, inp, ws, moe_shape, mode=mode, n_movers=crew)
-            for _, fn in ops_b:
-                fn()
-            pb, _ = time_ops(torch, ops_b, reps, ws, flush)
-            base[label] = {n: round(t, 4) for n, t in zip(names, pb)}
-        # the planned split: a FIXED crew sized per op by the cost model
+        ops_u = make_ops(kos, KI, inp, ws, moe_shape, mode=2)
+        for _, fn in ops_u:
+            fn()
+        pu, _ = time_ops(torch, ops_u, reps, ws, flush)
+        unfused = {n: round(t, 4) for n, t in zip(names, pu)}
+        # the planned split: a FIXED crew sized per op by the cost model; the
+        # best fixed split: the fastest crew of the sweep (planned crew included)
         grid = int(kos.lib.kos_device_cu_count())
         crews = planned_crews(KI, moe_shape, rows, grid)
-        planned = {}
-        for n, crew in crews.items():
-            ops_p = dict(make_ops(kos, KI, inp, ws, moe_shape, mode=1, n_movers=crew))
-            if n == "moe_combine":
-                ops_p["moe_dispatch"]()   # the combine reads the dispatch's outputs
-            ops_p[n]()
-            planned[n] = {"crew": crew, "ms": round(time_ops(torch, [(n, ops_p[n])], reps, ws, flush)[0][0], 4)}
-        extra["planned_split"] = planned
-        extra["speedup_vs_planned_split"] = {n: round(planned[n]["ms"] / per[names.index(n)], 3) for n in planned}
-        fixed = {n: min(base[k][n] for k in base if k.startswith("fixed")) for n in names}
-        extra["baselines_ms"] = base
-        extra["speedup_vs_unfused"] = {n: round(base["unfused"][n] / t, 3) for n, t in zip(names, per)}
-        extra["speedup_vs_best_fixed"] = {n: round(fixed[n] / t, 3) for n, t in zip(names, per)
-                                          if n != "moe_dispatch"}
-        # idle-CU fraction of each op in each mode (one traced, untimed call)
-        extra["idle_cu_fraction"] = idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush,
-                                                   {"fused": (0, -1), "unfused": (2, -1),
-                                                    "fixed_best": None}, base)
+        sweep = crew_sweep(torch, kos, KI, inp, ws, moe_shape, flush, reps, names, crews)
+        best = {n: min(v, key=v.get) for n, v in sweep.items()}
+        extra["baselines_ms"] = {"unfused": unfused,
+                                 "fixed_crew_sweep": {n: {str(c): t for c, t in v.items()} for n, v in sweep.items()},
+                                 "moe_dispatch_fixed": "n/a (no compute role to split from)"}
+        extra["best_fixed_split"] = {n: {"crew": best[n], "ms": sweep[n][best[n]]} for n in sweep}
+        extra["planned_split"] = {n: {"crew": c, "ms": sweep[n][c]} for n, c in crews.items()}
+        extra["speedup_vs_unfused"] = {n: round(unfused[n] / t, 3) for n, t in zip(names, per)}
+        extra["speedup_vs_best_fixed"] = {n: round(sweep[n][best[n]] / per[names.index(n)], 3) for n in sweep}
+        extra["speedup_vs_planned_split"] = {n: round(sweep[n][c] / per[names.index(n)], 3) for n, c in crews.items()}
+        # idle-CU fraction and communication-phase rates of each op in each
+        # mode (one traced, untimed call each)
+        peer_rows = int(inp["moe"]["peer_counts"].sum().item())
+        pb = phase_bytes(KI, moe_shape, rows, peer_rows)
+        idle, rates = idle_fractions(torch, kos, KI, inp, ws, moe_shape, flush, best, pb, names)
+        extra["idle_cu_fraction"] = idle
+        extra["phase_rate_gb_s"] = {lab: {n: {k: v["gb_s"] for k, v in d.items()} for n, d in r.items()}
+                                    for lab, r in rates.items()}
+        extra["phase_bytes"] = {n: {k: round(v) for k, v in d.items()} for n, d in pb.items()}
+        # the tiny all-gather+GEMM (latency-bound; microseconds)
+        extra["ag_tiny"] = tiny_ag(torch, kos, KI, ws, flush)
+        # the other expert-layer shape, as a block of its own (the Qwen3-235B
+        # shape's skewed routing exercises the combine's two-way switching)
+        other = KI.MOE_QWEN3 if moe_shape is KI.MOE_DSV3 else KI.MOE_DSV3
+        extra["moe_qwen3" if other is KI.MOE_QWEN3 else "moe_dsv3"] = moe_block(torch, kos, KI, ws, flush, reps,
+                                                                                 other)
         # GEMM throughput on 224 of 256 CUs: the explainer's worked example
         # (plain GEMM = the unfused GEMM launch at world 1)
         extra["gemm_224_of_256_cus"] = cu_subset_gemm(torch, kos, inp, ws, reps, flush)

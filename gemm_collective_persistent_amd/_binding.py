@@ -49,9 +49,14 @@ class TraceRec(ctypes.Structure):
 
 TRACE_RECORDS = 512     # KOS_TRACE_RECORDS: records per workgroup
 TRACE_MAX_WG = 256      # KOS_TRACE_MAX_WG
+TRACE_LAUNCHES = 4      # KOS_TRACE_LAUNCHES: slots, one per launch of a call
 TRACE_KINDS = {1: "move", 2: "tile", 3: "wait", 4: "reduce", 5: "route", 6: "scan", 7: "push", 8: "fold",
                9: "tile_down"}
 TRACE_CLOCK = 10        # KOS_TR_CLOCK: record 1, shader-clock cycles over the lifetime
+
+
+class DeviceError(ctypes.Structure):
+    _fields_ = [("status", c_int32), ("entry", c_uint32)]
 
 
 class MoeShape(ctypes.Structure):
@@ -71,7 +76,7 @@ def _load():
         "kos_opts_default": (None, [POINTER(Opts)]),
         "kos_workspace_bytes": (c_size_t, []),
         "kos_workspace_init": (c_int32, [P, c_size_t, P]),
-        "kos_workspace_status": (c_int32, [P, P]),
+        "kos_workspace_status": (c_int32, [P, P, POINTER(DeviceError)]),
         "kos_last_error": (c_char_p, []),
         "kos_device_cu_count": (c_int32, []),
         "kos_workspace_trace": (c_int32, [P, P, c_size_t, P]),
@@ -87,10 +92,10 @@ def _load():
                                      P, P, P, c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs_mx": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, P, P, PP, P, P,
                                      POINTER(Opts), P, c_size_t, P]),
-        "kos_moe_dispatch": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, P, PP, c_int64,
+        "kos_moe_dispatch": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, P, PP, POINTER(c_int64),
                                        P, c_int64, P, P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_combine": (c_int32, [POINTER(MoeShape), P, P, P, c_int64, P, P, P, P, P, P, P, P,
-                                      PP, P, P, PP, P, POINTER(Opts), P, c_size_t, P]),
+                                      PP, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name, None)

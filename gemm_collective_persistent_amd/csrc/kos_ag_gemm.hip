@@ -1,11 +1,11 @@
 // All-gather + GEMM as one persistent kernel (one rank's share).
 //
-// [KOSMOS explainer, "Start with the problem"]: every layer gathers pieces
-// of its input from the other GPUs before a matrix multiplication.
-// ["Role switching only works if ..."]: builders compute their own local
-// shard first while movers fetch remote shards in the order the
-// multiplication needs them.  ["KOSMOS removes the manager"]: movers become
-// builders once their transfers finish (one-way switch).
+// [KOSMOS explainer, "Start with the problem"]: under TP+SP the GEMM's
+// input is first collected from every rank.  ["Role switching only works
+// if ..."]: the tiles of the shard held locally go first, while the movers
+// bring the other shards over in the order the tiles will consume them.
+// ["KOSMOS removes the manager"]: a mover with no transfer left turns
+// builder for good (one-way switch).
 //
 // Queues (heads in the workspace):
 //   head[0]  move entries: remote shards in consumption order (rank+1,
@@ -304,9 +304,9 @@ static kos_status ag_gemm_run(const AgCall& a) {
   if ((st = current_device(&dev)) != KOS_OK) return st;
   kos_opts o;
   // Movers over device memory: half the grid saturates HBM copy bandwidth
-  // and the other half builds the local shard meanwhile; over PCIe a few
-  // workgroups saturate the link.
-  if ((st = resolve_opts(a.opts, dev, CrewDefaults{kCrewHalfGrid, 8, 16, 8}, &o)) != KOS_OK) return st;
+  // and the other half builds the local shard meanwhile; over PCIe sixteen
+  // workgroups keep enough requests in flight to fill the link.
+  if ((st = resolve_opts(a.opts, dev, CrewDefaults{kCrewHalfGrid, 16, 16, 8}, &o)) != KOS_OK) return st;
 
   int bm = 256, bn = 256;   // the MX tile
   if (!a.mx) pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
@@ -350,7 +350,7 @@ static kos_status ag_gemm_run(const AgCall& a) {
   p.n_tiles = world * p.rb_per_shard * p.tiles_n;
   p.ws = static_cast<WsHeader*>(a.ws);
   p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(a.ws) + kCountersOffset);
-  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(a.ws) + kTraceOffset) : nullptr;
+  p.trace = trace_slot(a.ws, o.trace, 0);
   if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
 
   // A single rank whose gathered output is its own shard has nothing to move.
@@ -378,6 +378,7 @@ static kos_status ag_gemm_run(const AgCall& a) {
     mv.do_build = 0;
     if ((st = launch(mv)) != KOS_OK) return st;
     AgParams gm = p;           // launch 2: the whole GEMM
+    gm.trace = trace_slot(a.ws, o.trace, 1);
     gm.n_movers = 0;
     gm.n_move = 0;
     gm.do_build = 1;

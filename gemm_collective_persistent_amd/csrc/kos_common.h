@@ -27,8 +27,11 @@ constexpr size_t kMaxCounters = (size_t(1) << 20) / 4;   // 1 MiB of uint32
 constexpr size_t kScratchOffset = kCountersOffset + (size_t(1) << 20);
 constexpr size_t kScratchBytes = size_t(15) << 20;       // per-op scratch
 constexpr size_t kTraceOffset = kScratchOffset + kScratchBytes;      // timelines (kos_opts.trace)
-constexpr size_t kTraceBytes = (size_t)KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS * sizeof(kos_trace_rec);
-constexpr size_t kWorkspaceBytes = kTraceOffset + kTraceBytes;       // 18 MiB + 4 KiB
+// one slot of KOS_TRACE_MAX_WG rows per launch of a call (the unfused
+// baselines launch up to KOS_TRACE_LAUNCHES kernels per call)
+constexpr size_t kTraceSlotRecords = (size_t)KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS;
+constexpr size_t kTraceBytes = KOS_TRACE_LAUNCHES * kTraceSlotRecords * sizeof(kos_trace_rec);
+constexpr size_t kWorkspaceBytes = kTraceOffset + kTraceBytes;       // 24 MiB + 4 KiB
 
 constexpr uint32_t kDefaultSpinLimit = 1u << 24;  // x s_sleep(2) ~ a few seconds
 

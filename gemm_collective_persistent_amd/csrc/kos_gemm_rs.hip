@@ -1,12 +1,12 @@
 // GEMM + reduce-scatter as one persistent kernel (one rank's share).
 //
-// [KOSMOS explainer, "Start with the problem"]: after a row-parallel matrix
-// multiplication the partial results are scattered and added.
-// ["Role switching only works if ..."]: output is produced band by band
-// across every GPU's chunk, so every GPU's reducers can start after the
-// first band is ready; producing it row by row instead is the slower
-// ablation.  ["KOSMOS removes the manager"]: builders join the reduction
-// when the multiplication tiles run out (one-way switch).
+// [KOSMOS explainer, "Start with the problem"]: after a row-parallel GEMM
+// each rank's partial sums are split by rows over the ranks and summed.
+// ["Role switching only works if ..."]: tiles come out one band of rows at a
+// time, covering that band in every rank's chunk, so summing can begin once
+// the first band exists; finishing one chunk before the next is the slower
+// ablation.  ["KOSMOS removes the manager"]: a builder that finds no tile
+// left turns reducer for good (one-way switch).
 //
 // Chunk c = rows [c*mc, (c+1)*mc), mc = m/world; band b of a chunk = its
 // rows [b*BM, (b+1)*BM).
@@ -318,7 +318,7 @@ static kos_status gemm_rs_run(const RsCall& c) {
   p.n_reduce = p.bands * p.tiles_n;
   p.ws = static_cast<WsHeader*>(ws);
   p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
-  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
+  p.trace = trace_slot(ws, o.trace, 0);
   if ((size_t)p.n_reduce > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many output tiles");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -334,6 +334,7 @@ static kos_status gemm_rs_run(const RsCall& c) {
     gm.n_reducers = 0;
     if ((st = launch(gm)) != KOS_OK) return st;
     RsParams rd = p;            // launch 2: the whole reduction
+    rd.trace = trace_slot(ws, o.trace, 1);
     rd.do_build = 0;
     rd.do_reduce = 1;
     rd.n_reducers = grid;

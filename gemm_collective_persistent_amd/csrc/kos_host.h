@@ -38,6 +38,13 @@ kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, const CrewDef
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Launch `l` of a traced call records into its own slot of the trace
+// region (null when tracing is off).
+inline kos_trace_rec* trace_slot(void* ws, int traced, int l) {
+  return traced ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) + (size_t)l * kTraceSlotRecords
+                : nullptr;
+}
+
 // Maps a launch error to a status.
 kos_status launch_status(const char* what);
 

@@ -107,7 +107,11 @@ kos_status kos_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return KOS_OK;
 }
 
-kos_status kos_workspace_status(void* ws, void* stream) {
+kos_status kos_workspace_status(void* ws, void* stream, kos_device_error* out) {
+  if (out) {
+    out->status = KOS_OK;
+    out->entry = 0;
+  }
   if (!ws) return fail(KOS_ERR_WORKSPACE, "workspace is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(s) != hipSuccess) return fail(KOS_ERR_HIP, "stream synchronization failed");
@@ -119,14 +123,18 @@ kos_status kos_workspace_status(void* ws, void* stream) {
   if (hipMemcpy(reinterpret_cast<char*>(ws) + offsetof(WsHeader, status), &zero, 4, hipMemcpyHostToDevice) !=
       hipSuccess)
     return fail(KOS_ERR_HIP, "clearing the workspace status failed");
+  if (out) {
+    out->status = (int32_t)h.status;
+    out->entry = h.err_info;
+  }
   return fail(static_cast<kos_status>(h.status), "device error %u (entry %u)", h.status, h.err_info);
 }
 
 kos_status kos_workspace_trace(void* ws, kos_trace_rec* out, size_t n_records, void* stream) {
   if (!ws || (!out && n_records)) return fail(KOS_ERR_ARG, "null buffer");
-  if (n_records > (size_t)KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS)
-    return fail(KOS_ERR_ARG, "%zu records requested, the trace region holds %d", n_records,
-                KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS);
+  if (n_records > (size_t)KOS_TRACE_LAUNCHES * kTraceSlotRecords)
+    return fail(KOS_ERR_ARG, "%zu records requested, the trace region holds %zu", n_records,
+                (size_t)KOS_TRACE_LAUNCHES * kTraceSlotRecords);
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
     return fail(KOS_ERR_HIP, "stream synchronization failed");
   if (n_records && hipMemcpy(out, static_cast<char*>(ws) + kTraceOffset, n_records * sizeof(kos_trace_rec),

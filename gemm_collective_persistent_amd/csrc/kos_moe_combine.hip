@@ -1,9 +1,10 @@
 // Expert layer, combine direction, as one persistent kernel: grouped SwiGLU
 // expert GEMMs, results pushed back to the ranks that sent the rows, and the
-// weighted fold of our own tokens [KOSMOS arXiv abstract: "from router to
-// fold", one launch per direction; KOSMOS explainer, "KOSMOS removes the
-// manager": in the combine step a workgroup pushes any ready result and
-// otherwise builds a tile (two-way switching)].
+// weighted fold of our own tokens [KOSMOS arXiv abstract: the whole expert
+// layer, routing through the final weighted sum, in one launch per
+// direction; KOSMOS explainer, "KOSMOS removes the manager": roles switch
+// both ways here -- between tiles a workgroup sends back a finished result
+// if one is waiting, else it computes the next tile].
 //
 // Work units: (local expert e, row block of BM grouped rows), expert-major.
 // Per unit: G gate/up tiles (each BN/2 columns of h = bf16(silu(X.Wg) *
@@ -50,9 +51,11 @@ struct CombineParams {
   uint16_t* h;
   uint16_t* yg;
   uint16_t* out_return[8];
+  int64_t return_cap[8];  // rows out_return[p] holds
   uint16_t* y;
   int32_t G, D, L;        // gate/up tiles per unit, down tiles per unit, lag (units)
   int32_t u_max;          // bound on units: size of each counter array
+  int32_t grouped_cap;    // rows x_grouped, h and y_grouped hold
   int32_t do_gu, do_dn, do_push, do_fold;
   int32_t two_way;        // builders take ready pushes between tiles
   int32_t n_crew;         // > 0: tickets below it only push and fold
@@ -91,10 +94,18 @@ __device__ __forceinline__ bool load_combine_meta(const CombineParams& p, Combin
   for (int i = threadIdx.x; i < p.world * p.E_loc; i += blockDim.x)
     if (p.peer_counts[i] != 0) atomicAdd(&M.recv[i / p.E_loc], p.peer_counts[i]);   // rows each rank sent us
   if (threadIdx.x == 0) {
+    // offsets that decrease or run past the caller's capacity would make
+    // units overlap the counters and tiles write past h / y_grouped
+    bool bad = M.go[0] < 0 || M.go[p.E_loc] > p.grouped_cap;
     M.ub[0] = 0;
     for (int el = 0; el < p.E_loc; ++el) {
       const int n = M.go[el + 1] - M.go[el];
-      M.ub[el + 1] = M.ub[el] + (n + BM - 1) / BM;
+      bad |= n < 0;
+      M.ub[el + 1] = M.ub[el] + (n > 0 ? (n + BM - 1) / BM : 0);
+    }
+    if (bad) {
+      raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)M.go[p.E_loc]);
+      s->ok = 0;
     }
   }
   __syncthreads();
@@ -102,9 +113,13 @@ __device__ __forceinline__ bool load_combine_meta(const CombineParams& p, Combin
   if (q < p.world && q != p.rank) {
     const int sent = M.off[(q + 1) * p.E_loc] - M.off[q * p.E_loc];   // results q returns
     if ((sent > 0 && p.peer_return[q] == nullptr) || (M.recv[q] > 0 && p.out_return[q] == nullptr)) s->ok = 0;
+    if (M.recv[q] > p.return_cap[q]) {   // the results p sent us do not fit its return buffer
+      raise_error(p.ws, KOS_ERR_CAPACITY, 0x00F00000u | (uint32_t)q);
+      s->ok = 0;
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0 && !s->ok) raise_error(p.ws, KOS_ERR_ARG, 0x00C00000u);
+  if (threadIdx.x == 0 && !s->ok) raise_error(p.ws, KOS_ERR_ARG, 0x00C00000u);   // no-op after a capacity error
   return s->ok != 0;
 }
 
@@ -191,7 +206,7 @@ __device__ __forceinline__ void down_tile(const CombineParams& p, const Unit& x,
 
 // Push entry: rows [slab * kPushRows, +kPushRows) of unit x, one row per
 // wave at a time.
-__device__ __forceinline__ void push_slab(const CombineParams& p, const Unit& x, int slab) {
+__device__ __forceinline__ void push_slab(const CombineParams& p, const CombineMeta& M, const Unit& x, int slab) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const DevBuf yb(p.yg);
   const int r1 = min(x.m_valid, (slab + 1) * kPushRows);
@@ -200,6 +215,11 @@ __device__ __forceinline__ void push_slab(const CombineParams& p, const Unit& x,
     const int src = p.row_src[grow * 2];
     if (src == p.rank) continue;
     const int64_t i = p.row_src[grow * 2 + 1];
+    // a row must go back to a rank that sent rows, inside what it sent
+    if (src < 0 || src >= p.world || i < 0 || i >= M.recv[src]) {
+      if ((threadIdx.x & 63) == 0) raise_error(p.ws, KOS_ERR_ARG, 0x00D00000u | (uint32_t)(grow & 0xFFFFF));
+      continue;
+    }
     wave_copy_row_dev_src(wave_uniform(p.out_return[src] + i * p.H), yb, (uint32_t)(grow * p.H * 2), p.H * 2);
   }
 }
@@ -274,20 +294,28 @@ __device__ __forceinline__ bool fold_token_wave(const CombineParams& p, const Co
   uint64_t rowp = 0;   // result row of lane j < k
   float wj = 0.f;
   const int k = p.k;
+  bool bad = false;   // routing that points outside the rows it may name
   if (lane < k) {
     const int e = p.topk_idx[(int64_t)t * k + lane];
     const int pos = p.perm[(int64_t)t * k + lane];
     wj = p.topk_w[(int64_t)t * k + lane];
-    const int d = e / E_loc;
-    if (d == p.rank) {
+    bad = e < 0 || e >= p.E || pos < M.off[e] || pos >= M.off[e + 1];
+    const int d = bad ? p.rank : e / E_loc;
+    if (bad) {
+    } else if (d == p.rank) {
       const int el = e - p.rank * E_loc;
       const int grow = M.go[el] + M.before[el] + (pos - M.off[e]);
+      bad = grow >= M.go[el + 1];
       local = true;
       u = M.ub[el] + (grow - M.go[el]) / BM;
       rowp = reinterpret_cast<uint64_t>(p.yg + (int64_t)grow * p.H);
     } else {
       rowp = reinterpret_cast<uint64_t>(p.peer_return[d] + (int64_t)(pos - M.off[d * E_loc]) * p.H);
     }
+  }
+  if (__any(bad)) {
+    if (lane == 0) raise_error(p.ws, KOS_ERR_ARG, 0x00E00000u | (uint32_t)(t & 0xFFFFF));
+    return false;
   }
   if (p.wait_flags) {
     const uint32_t* dn_done = p.ctr + p.u_max;
@@ -389,7 +417,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           const uint32_t got = slots.claim;
           if (got == kNoEntry) break;
           const uint64_t t0 = tr.now();
-          push_slab(p, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
+          push_slab(p, M, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
           tr.put(KOS_TR_PUSH, got, t0);
         }
       }
@@ -443,7 +471,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
         tr.put(KOS_TR_WAIT, i, t0);
         t0 = tr.now();
       }
-      push_slab(p, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
+      push_slab(p, M, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
       tr.put(KOS_TR_PUSH, i, t0);
     }
   }
@@ -481,7 +509,8 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
                                       const void* w_up, const void* w_down, const int32_t* topk_idx,
                                       const float* topk_w, const int32_t* counts, const int32_t* perm,
                                       const int32_t* peer_counts, const void* const* peer_return, void* h,
-                                      void* y_grouped, void* const* out_return, void* y, const kos_opts* opts,
+                                      void* y_grouped, void* const* out_return, const int64_t* return_caps,
+                                      void* y, const kos_opts* opts,
                                       void* ws, size_t ws_bytes, void* stream) {
   if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
   const bool big = s->hidden % CombineTileBig::BN == 0 && s->ffn % (CombineTileBig::BN / 2) == 0;
@@ -499,7 +528,8 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   if (!x_grouped || !grouped_offsets || !row_src || !w_gate || !w_up || !w_down ||
       (!no_tokens && (!topk_idx || !topk_w || !perm || !y)) || !counts || !peer_counts || !h || !y_grouped)
     return fail(KOS_ERR_ARG, "null buffer");
-  if (R > 1 && (!peer_return || !out_return)) return fail(KOS_ERR_ARG, "peer_return / out_return is NULL");
+  if (R > 1 && (!peer_return || !out_return || !return_caps))
+    return fail(KOS_ERR_ARG, "peer_return / out_return / return_caps is NULL");
   for (int q = 0; q < R; ++q) {
     if (q == r) continue;
     // NULL is allowed where nothing travels (checked on the device)
@@ -545,6 +575,7 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   for (int q = 0; q < R; ++q) {
     p.peer_return[q] = q == r ? nullptr : static_cast<const uint16_t*>(peer_return[q]);
     p.out_return[q] = q == r ? nullptr : static_cast<uint16_t*>(out_return[q]);
+    p.return_cap[q] = q == r ? 0 : return_caps[q];
   }
   p.h = static_cast<uint16_t*>(h);
   p.yg = static_cast<uint16_t*>(y_grouped);
@@ -555,11 +586,12 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
   p.D = s->hidden / BNt;
   p.L = (o.grid + p.G - 1) / p.G;
   p.u_max = (int32_t)((grouped_cap + BMt - 1) / BMt) + p.E_loc;
+  p.grouped_cap = (int32_t)grouped_cap;
   if ((size_t)2 * p.u_max > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
   p.spin_limit = o.spin_limit;
   p.ws = static_cast<WsHeader*>(ws);
   p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
-  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
+  p.trace = trace_slot(ws, o.trace, 0);
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   auto launch = [&](const CombineParams& q, const char* what) {
@@ -584,12 +616,15 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
     a.do_gu = 1;
     if ((st = launch(a, "moe_combine gate/up launch")) != KOS_OK) return st;
     CombineParams b = p;
+    b.trace = trace_slot(ws, o.trace, 1);
     b.do_dn = 1;
     if ((st = launch(b, "moe_combine down launch")) != KOS_OK) return st;
     CombineParams c = p;
+    c.trace = trace_slot(ws, o.trace, 2);
     c.do_push = 1;
     if ((st = launch(c, "moe_combine push launch")) != KOS_OK) return st;
     CombineParams d = p;
+    d.trace = trace_slot(ws, o.trace, 3);
     d.do_fold = 1;
     return launch(d, "moe_combine fold launch");
   }

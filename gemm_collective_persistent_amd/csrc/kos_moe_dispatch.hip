@@ -1,8 +1,8 @@
 // Expert layer, dispatch direction, as one persistent kernel: router ->
-// permutation -> token movement [KOSMOS arXiv abstract: an entire expert
-// layer "from router to fold", one launch per direction; KOSMOS explainer,
-// "Start with the problem": tokens travel to the GPU that holds their
-// expert].
+// permutation -> token movement [KOSMOS arXiv abstract: the whole expert
+// layer, routing through the final weighted sum, runs in one launch per
+// direction; KOSMOS explainer, "Start with the problem": each token's row is
+// sent to the rank that owns its expert].
 //
 // Queues and counters:
 //   head[0]      router entries, one per quarter (16 tokens) of a block of
@@ -45,7 +45,7 @@ struct DispatchParams {
   int32_t* counts;
   int32_t* perm;
   uint16_t* out_send[8];
-  int64_t send_cap;
+  int64_t send_cap[8];          // rows out_send[d] holds
   uint16_t* x_grouped;
   int64_t grouped_cap;
   int32_t* grouped_offsets;
@@ -238,7 +238,7 @@ __device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& 
     for (int d = 0; d < p.world; ++d) {
       if (d == p.rank) continue;
       const int sent = L.off[(d + 1) * p.E_loc] - L.off[d * p.E_loc];
-      if (sent > p.send_cap) over = true;
+      if (sent > p.send_cap[d]) over = true;
       if (sent > 0 && p.out_send[d] == nullptr) null_send = true;   // rows for a NULL buffer
     }
     int64_t go = 0;
@@ -435,7 +435,7 @@ using namespace kos;
 extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* logits,
                                        const void* const* peer_send, const int32_t* peer_counts, int32_t* topk_idx,
                                        float* topk_w, int32_t* counts, int32_t* perm, void* const* out_send,
-                                       int64_t send_cap, void* x_grouped, int64_t grouped_cap,
+                                       const int64_t* send_caps, void* x_grouped, int64_t grouped_cap,
                                        int32_t* grouped_offsets, int32_t* row_src, const kos_opts* opts, void* ws,
                                        size_t ws_bytes, void* stream) {
   if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
@@ -452,14 +452,17 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   if ((!no_tokens && (!x || !logits || !topk_idx || !topk_w || !perm)) || !peer_counts || !counts || !x_grouped ||
       !grouped_offsets || !row_src)
     return fail(KOS_ERR_ARG, "null buffer");
-  if (R > 1 && (!peer_send || !out_send)) return fail(KOS_ERR_ARG, "peer_send / out_send is NULL");
+  if (R > 1 && (!peer_send || !out_send || !send_caps))
+    return fail(KOS_ERR_ARG, "peer_send / out_send / send_caps is NULL");
+  for (int q = 0; q < R; ++q)
+    if (q != r && send_caps[q] < 0) return fail(KOS_ERR_ARG, "send_caps[%d] is negative", q);
   for (int q = 0; q < R; ++q) {
     if (q == r) continue;
     // NULL is allowed where nothing travels (checked on the device)
     if (!aligned16(peer_send[q]) || !aligned16(out_send[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(x) || !aligned16(x_grouped)) return fail(KOS_ERR_ALIGN, "row buffers must be 16-byte aligned");
-  if (send_cap < 0 || grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1)
+  if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1)
     return fail(KOS_ERR_ARG, "bad capacity");
   kos_status st = check_workspace(ws, ws_bytes);
   if (st != KOS_OK) return st;
@@ -488,7 +491,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   p.topk_w = topk_w;
   p.counts = counts;
   p.perm = perm;
-  p.send_cap = send_cap;
+  for (int q = 0; q < R; ++q) p.send_cap[q] = q == r ? 0 : send_caps[q];
   p.x_grouped = static_cast<uint16_t*>(x_grouped);
   p.grouped_cap = grouped_cap;
   p.grouped_offsets = grouped_offsets;
@@ -496,7 +499,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   p.nblk = (s->tokens + kMoeTokBlock - 1) / kMoeTokBlock;
   p.spin_limit = o.spin_limit;
   p.ws = static_cast<WsHeader*>(ws);
-  p.trace = o.trace ? reinterpret_cast<kos_trace_rec*>(static_cast<char*>(ws) + kTraceOffset) : nullptr;
+  p.trace = trace_slot(ws, o.trace, 0);
   p.ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   char* scratch = static_cast<char*>(ws) + kScratchOffset;
   const size_t mask_bytes = (size_t)p.nblk * p.E * 8, base_bytes = (size_t)p.nblk * p.E * 4;
@@ -514,6 +517,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
     hipLaunchKernelGGL(moe_dispatch_kernel<NT>, dim3(o.grid), dim3(NT), 0, strm, a);
     if ((st = launch_status("moe_dispatch route launch")) != KOS_OK) return st;
     DispatchParams b = p;   // launch 2: token movement
+    b.trace = trace_slot(ws, o.trace, 1);
     b.do_route = 0;
     b.do_copy = 1;
     b.wait_scan = 0;

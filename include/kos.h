@@ -10,8 +10,8 @@
  *   [abstract]   "KOSMOS: Self-scheduling Persistent Kernels for
  *                Communication-Compute Overlap", arXiv 2611.07477, abstract.
  *
- * Every entry point launches ONE persistent kernel (two for the unfused
- * baseline) with one workgroup per compute unit.  Workgroups take entries
+ * Every entry point launches ONE persistent kernel (up to four for the
+ * unfused baseline) with one workgroup per compute unit.  Workgroups take entries
  * from atomic queues laid out in the order consumers need them and switch
  * roles as ready flags show which data has landed [explainer, "KOSMOS
  * removes the manager"; "Role switching only works if ..."].
@@ -86,8 +86,8 @@ typedef enum kos_dtype { KOS_BF16 = 0, KOS_F32 = 1 } kos_dtype;
 typedef enum kos_mode { KOS_MODE_FUSED = 0, KOS_MODE_FIXED = 1, KOS_MODE_UNFUSED = 2 } kos_mode;
 
 /* GEMM+reduce-scatter output order: band by band across every rank's chunk
- * (the consumer order), or chunk after chunk, row by row (the ablation the
- * explainer reports as 1.41-1.45x slower) ["Role switching only works if"]. */
+ * (the consumer order), or one chunk after the other (the ablation the
+ * explainer reports 1.41-1.45x slower) ["Role switching only works if"]. */
 typedef enum kos_rs_order { KOS_RS_BAND = 0, KOS_RS_ROW = 1 } kos_rs_order;
 
 typedef struct kos_opts {
@@ -96,7 +96,7 @@ typedef struct kos_opts {
                            under FIXED, stay there); < 0 = the library's default
                            for the op, mode and peer link (never per shape):
                            kos_ag_gemm FUSED half the grid over device memory,
-                           8 over PCIe; kos_gemm_rs FUSED 0 (builders switch
+                           16 over PCIe; kos_gemm_rs FUSED 0 (builders switch
                            to reducing when the tiles run out); FIXED 16, or 8
                            over PCIe.  Unused by FUSED kos_moe_*.             */
   int32_t rs_order;     /* kos_rs_order (kos_gemm_rs only)                     */
@@ -114,8 +114,12 @@ typedef struct kos_opts {
   int32_t reserved;     /* must be 0                                            */
 } kos_opts;
 
-/* Timeline of one traced call (kos_opts.trace).  Workgroup g (launch order,
- * 0..grid-1) owns records [g*KOS_TRACE_RECORDS, (g+1)*KOS_TRACE_RECORDS).
+/* Timeline of one traced call (kos_opts.trace).  The trace region holds
+ * KOS_TRACE_LAUNCHES slots, one per kernel launch of the call (a fused call
+ * launches once and writes slot 0; the unfused baselines launch up to four
+ * kernels and write slots 0, 1, ... in launch order).  In slot l, workgroup
+ * g (launch order, 0..grid-1) owns records
+ * [(l*KOS_TRACE_MAX_WG + g)*KOS_TRACE_RECORDS, ... + KOS_TRACE_RECORDS).
  * Its record 0 is a header: t0 = when it started, dt = its lifetime, tag =
  * (arrival ticket << 16) | (XCD it ran on << 12) | records written (header
  * and clock record included, at most KOS_TRACE_RECORDS; later pieces of work
@@ -124,11 +128,14 @@ typedef struct kos_opts {
  * KOS_TR_CLOCK << 24, so t0 / dt is the clock the workgroup ran at, in units
  * of 100 MHz.  Every other record is one piece of work: t0 = start, dt =
  * duration, tag = (kos_trace_kind << 24) | entry index (low 24 bits).  Times
- * are ticks of the GPU's constant-rate 100 MHz counter (s_memrealtime).  Used
- * for the idle-CU fraction (the share of workgroup-time outside work records,
- * waits included, over the kernel's span) and the clock under load. */
+ * are ticks of the GPU's constant-rate 100 MHz counter (s_memrealtime), one
+ * clock for every launch, so the gaps between the launches of an unfused
+ * call show in the timeline.  Used for the idle-CU fraction (the share of
+ * workgroup-time outside work records, waits and gaps between launches
+ * included, over the call's span) and the clock under load. */
 #define KOS_TRACE_RECORDS 512
 #define KOS_TRACE_MAX_WG 256
+#define KOS_TRACE_LAUNCHES 4
 typedef struct kos_trace_rec {
   uint64_t t0;
   uint32_t dt;
@@ -156,16 +163,26 @@ size_t kos_workspace_bytes(void);
 /* Zeroes a workspace on `stream` (asynchronous).  Call once after allocating. */
 kos_status kos_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
+/* A device-side error as the kernels record it: the status and the entry
+ * that raised it (a queue entry index, or a code naming the check; 0 if
+ * none).  Only the first error since the last read is kept. */
+typedef struct kos_device_error {
+  int32_t status;   /* kos_status: KOS_OK, KOS_ERR_TIMEOUT, KOS_ERR_CAPACITY, KOS_ERR_ARG */
+  uint32_t entry;   /* what raised it                                          */
+} kos_device_error;
+
 /* Synchronizes `stream`, then returns the first device-side error recorded
  * in `ws` since the last call of this function (KOS_OK if none) and clears
- * it.  KOS_ERR_HIP if the synchronization itself fails. */
-kos_status kos_workspace_status(void* ws, void* stream);
+ * it; `out` (may be NULL) receives the status and the entry that raised it.
+ * KOS_ERR_HIP if the synchronization itself fails. */
+kos_status kos_workspace_status(void* ws, void* stream, kos_device_error* out);
 
 /* Synchronizes `stream`, then copies the first `n_records` records of the
  * trace region of `ws` (see kos_trace_rec) to host memory `out`.  n_records
- * is at most KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS (else KOS_ERR_ARG).  The
- * region holds the timeline of the last call made with kos_opts.trace set;
- * rows of workgroups beyond that call's grid are stale. */
+ * is at most KOS_TRACE_LAUNCHES * KOS_TRACE_MAX_WG * KOS_TRACE_RECORDS (else
+ * KOS_ERR_ARG).  The region holds the timeline of the last call made with
+ * kos_opts.trace set; slots beyond that call's launches and rows of
+ * workgroups beyond its grid are stale. */
 kos_status kos_workspace_trace(void* ws, kos_trace_rec* out, size_t n_records, void* stream);
 
 /* Thread-local description of the last non-OK status returned on this
@@ -177,11 +194,11 @@ int32_t kos_device_cu_count(void);
 
 /*
  * All-gather + GEMM, one rank's share [explainer, "Start with the problem":
- * every layer gathers pieces of its input from the other GPUs before a
- * matrix multiplication; "Role switching only works if": the local shard is
- * computed first while movers fetch remote shards in the order the
- * multiplication needs them; "KOSMOS removes the manager": movers become
- * builders once their transfers finish].
+ * under TP+SP a layer's GEMM input is first collected from every rank;
+ * "Role switching only works if": tiles of the shard already held locally
+ * are built first, while the movers bring the other shards over in the
+ * order the tiles will consume them; "KOSMOS removes the manager": a mover
+ * turns builder for good when no transfer is left].
  *
  *   G = [S_0; S_1; ...; S_{world-1}]   (rank-order concatenation of shards)
  *   C = G . W
@@ -207,10 +224,11 @@ kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, 
 
 /*
  * GEMM + reduce-scatter, one rank's share [explainer, "Start with the
- * problem": scatter and add the partial results after the multiplication;
- * "Role switching only works if": output produced band by band across every
- * GPU's chunk so every GPU's reducers start after the first band; "KOSMOS
- * removes the manager": builders join the reduction when the tiles run out].
+ * problem": the GEMM's partial sums are split by rows over the ranks and
+ * summed; "Role switching only works if": tiles come out one band of rows
+ * at a time, covering that band in every rank's chunk, so each rank can
+ * start summing after the first band; "KOSMOS removes the manager": a
+ * builder that finds no tile left turns reducer for good].
  *
  *   P = A . W                     (this rank's fp32 partial of the output)
  *   chunk c = rows [c*m/world, (c+1)*m/world)
@@ -326,8 +344,10 @@ typedef struct kos_moe_shape {
 
 /*
  * Expert layer, dispatch direction: router -> permutation -> token movement
- * [abstract: an entire expert layer "from router to fold"; explainer, "Start
- * with the problem": tokens travel to the GPU that holds their expert].
+ * [abstract: the whole expert layer, routing through the final weighted
+ * sum, in one launch per direction; explainer, "Start with the problem": a
+ * token's row is sent to the rank owning its expert, and the result comes
+ * back].
  *
  * Router: per token, the k experts of largest logit in descending order,
  * ties to the lowest expert index; weights = softmax over the k selected
@@ -343,8 +363,10 @@ typedef struct kos_moe_shape {
  * topk_idx     out int32 [T, k];  topk_w: out fp32 [T, k]
  * counts       out int32 [E]: pairs routed to each expert (global)
  * perm         out int32 [T*k]: packed position of pair (t, j)
- * out_send     host array[world] of out bf16 [send_cap, H]: rows for peer
- *              d != rank, i.e. our packed rows of d's experts, in order
+ * out_send     host array[world] of out bf16 [send_caps[d], H]: rows for
+ *              peer d != rank, i.e. our packed rows of d's experts, in order
+ * send_caps    host array[world]: rows out_send[d] holds (entry `rank`
+ *              ignored); may be NULL when world == 1
  * x_grouped    out bf16 [grouped_cap, H]: rows of our local experts,
  *              expert-major, then by source rank, then in source order
  * grouped_offsets out int32 [E_loc + 1]: expert e's rows start here
@@ -357,14 +379,15 @@ typedef struct kos_moe_shape {
  * kos_workspace_status (the rows are skipped, never dereferenced).
  * T <= 65536 and T * E * 12 bytes within the workspace's 15 MiB scratch
  * (KOS_ERR_SHAPE otherwise).
- * Capacities overflow -> KOS_ERR_CAPACITY (device, see kos_workspace_status);
- * send_cap >= T*min(k, E_loc) and grouped_cap >= sum(peer_counts) +
- * T*min(k, E_loc) never overflow.  Shapes: H % 64 == 0.
+ * Capacities overflow -> KOS_ERR_CAPACITY (device, see kos_workspace_status;
+ * nothing is written past a buffer's capacity); send_caps[d] >=
+ * T*min(k, E_loc) and grouped_cap >= sum(peer_counts) + T*min(k, E_loc)
+ * never overflow.  Shapes: H % 64 == 0.
  */
 kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* logits,
                             const void* const* peer_send, const int32_t* peer_counts,
                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* perm,
-                            void* const* out_send, int64_t send_cap,
+                            void* const* out_send, const int64_t* send_caps,
                             void* x_grouped, int64_t grouped_cap, int32_t* grouped_offsets,
                             int32_t* row_src,
                             const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
@@ -372,8 +395,9 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
 /*
  * Expert layer, combine direction: grouped SwiGLU expert GEMMs, results
  * pushed back to their source ranks, and the weighted fold of this rank's
- * tokens [abstract; explainer, "KOSMOS removes the manager": in the combine
- * step a workgroup pushes any ready result and otherwise builds a tile].
+ * tokens [abstract; explainer, "KOSMOS removes the manager": here roles
+ * switch both ways -- between tiles a workgroup sends back a finished
+ * result if one is waiting, else it computes the next tile].
  *
  *   h  = bf16( silu(X_e . Wg_e) * (X_e . Wu_e) )      fp32 silu and product
  *   Yg = bf16( h . Wd_e )                              per local expert e
@@ -389,12 +413,21 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
  *              `rank` ignored): results d returns, in our packed order
  * h            out bf16 [grouped_cap, F] (the SwiGLU hidden, kept for
  *              inspection);  y_grouped: out bf16 [grouped_cap, H]
- * out_return   host array[world] of out bf16 [rows p sent us, H]
+ * out_return   host array[world] of out bf16 [return_caps[p], H]: the
+ *              results of the rows p sent us, in p's packed order
+ * return_caps  host array[world]: rows out_return[p] holds (entry `rank`
+ *              ignored; at least the rows p sent us, else KOS_ERR_CAPACITY
+ *              from kos_workspace_status and the kernel does nothing); may
+ *              be NULL when world == 1
  * y            out bf16 [T, H]
  * With T == 0, topk_idx, topk_w, perm and y may be NULL.  peer_return[d]
  * may be NULL if we sent d nothing and out_return[p] if p sent us nothing;
  * otherwise a NULL peer buffer is reported as KOS_ERR_ARG by
- * kos_workspace_status and the kernel does nothing.
+ * kos_workspace_status and the kernel does nothing.  So are grouped
+ * offsets that decrease or describe more than grouped_cap rows
+ * (KOS_ERR_CAPACITY).  A grouped row whose row_src names a rank outside
+ * [0, world) or a row past what that rank sent (peer_counts) is not pushed
+ * and is reported as KOS_ERR_ARG.
  * Shapes: H % 128 == 0, F % 64 == 0, grouped_cap * H * 2 < 2^31 bytes
  * (else KOS_ERR_SHAPE).
  */
@@ -406,7 +439,8 @@ kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
                            const int32_t* counts, const int32_t* perm,
                            const int32_t* peer_counts,
                            const void* const* peer_return,
-                           void* h, void* y_grouped, void* const* out_return, void* y,
+                           void* h, void* y_grouped, void* const* out_return,
+                           const int64_t* return_caps, void* y,
                            const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

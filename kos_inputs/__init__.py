@@ -253,8 +253,22 @@ def rs_inputs(s: RsShape, rank: int, device="cpu", integer=False, wt=False):
 MX_INT_CODES = (0xC8, 0xC4, 0xC0, 0xB8, 0x00, 0x38, 0x40, 0x44, 0x48)   # -4 .. 4
 
 
-def mx_codes(shape, wid, tid, rank, device, integer=False):
+def mx_codes(shape, wid, tid, rank, device, integer=False, edge=False):
     g = _gen(wid, tid, rank, device)
+    if edge:
+        # the format's edges: a quarter subnormals (exponent field 0,
+        # mantissa 1..7), a twentieth zeros, a fifth of the largest binade
+        # (exponent field 15, mantissa 0..6: 256 .. 448; mantissa 7 is NaN),
+        # the rest normal (exponent field 1..14); sign uniform
+        cat = torch.rand(shape, generator=g, device=device)
+        sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
+        e_norm = torch.randint(1, 15, shape, generator=g, device=device, dtype=torch.int32)
+        m_any = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
+        m_sub = torch.randint(1, 8, shape, generator=g, device=device, dtype=torch.int32)
+        m_top = torch.randint(0, 7, shape, generator=g, device=device, dtype=torch.int32)
+        e = torch.where(cat < 0.30, 0, torch.where(cat < 0.50, 15, e_norm))
+        m = torch.where(cat < 0.25, m_sub, torch.where(cat < 0.30, 0, torch.where(cat < 0.50, m_top, m_any)))
+        return ((sign << 7) | (e << 3) | m).to(torch.uint8)
     if integer:
         idx = torch.randint(0, len(MX_INT_CODES), shape, generator=g, device=device)
         return torch.tensor(MX_INT_CODES, dtype=torch.uint8, device=device)[idx]
@@ -264,34 +278,37 @@ def mx_codes(shape, wid, tid, rank, device, integer=False):
     return ((sign << 7) | (e << 3) | m).to(torch.uint8)
 
 
-def mx_scales(rows, k, wid, tid, rank, device, integer=False):
+def mx_scales(rows, k, wid, tid, rank, device, integer=False, edge=False):
     g = _gen(wid, tid, rank, device)
-    lo, hi = (126, 128) if integer else (124, 130)
+    # edge: scales 2^-27 .. 2^27 (products of the largest codes at the
+    # largest scales stay far below the fp32 range, the smallest above it)
+    lo, hi = (126, 128) if integer else (100, 154) if edge else (124, 130)
     return torch.randint(lo, hi + 1, (k // 64, rows, 2), generator=g, device=device,
                          dtype=torch.int32).to(torch.uint8)
 
 
-def ag_mx_inputs(s: AgShape, rank: int, device="cpu", integer=False):
+def ag_mx_inputs(s: AgShape, rank: int, device="cpu", integer=False, edge=False):
     """MX shards of every rank with their scales, and the weight shard stored
     n x k with its scales.  Returns dict(a_local, s_local, a_peers, s_peers,
-    w, w_scales); peer entries ``rank`` are None."""
-    shards = [mx_codes((s.m_local, s.k), s.wid, T_A, p, device, integer) for p in range(s.world)]
-    scales = [mx_scales(s.m_local, s.k, s.wid, T_SA, p, device, integer) for p in range(s.world)]
-    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer)
-    ws = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer)
+    w, w_scales); peer entries ``rank`` are None.  ``edge``: codes and scales
+    at the format's edges (subnormals, the largest binade, far scales)."""
+    shards = [mx_codes((s.m_local, s.k), s.wid, T_A, p, device, integer, edge) for p in range(s.world)]
+    scales = [mx_scales(s.m_local, s.k, s.wid, T_SA, p, device, integer, edge) for p in range(s.world)]
+    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer, edge)
+    ws = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer, edge)
     return dict(a_local=shards[rank], s_local=scales[rank],
                 a_peers=[None if p == rank else shards[p] for p in range(s.world)],
                 s_peers=[None if p == rank else scales[p] for p in range(s.world)],
                 w=w, w_scales=ws)
 
 
-def rs_mx_inputs(s: RsShape, rank: int, device="cpu", integer=False):
+def rs_mx_inputs(s: RsShape, rank: int, device="cpu", integer=False, edge=False):
     """MX A [m, k] and W [n, k] with scales, and the peers' fp32 slices of
     chunk ``rank`` (as ``rs_inputs``)."""
-    a = mx_codes((s.m, s.k), s.wid, T_A, rank, device, integer)
-    sa = mx_scales(s.m, s.k, s.wid, T_SA, rank, device, integer)
-    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer)
-    sw = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer)
+    a = mx_codes((s.m, s.k), s.wid, T_A, rank, device, integer, edge)
+    sa = mx_scales(s.m, s.k, s.wid, T_SA, rank, device, integer, edge)
+    w = mx_codes((s.n, s.k), s.wid, T_W, 0, device, integer, edge)
+    sw = mx_scales(s.n, s.k, s.wid, T_SW, 0, device, integer, edge)
     peers = rs_inputs(s, rank, device, integer)["peer_slices"] if s.world > 1 else [None]
     return dict(a=a, a_scales=sa, w=w, w_scales=sw, peer_slices=peers)
 

@@ -14,8 +14,9 @@ order the pages describe them:
 * all-gather of sequence shards before a column-parallel GEMM, and scatter and
   add of the partial results after a row-parallel GEMM [KOSMOS explainer,
   "Start with the problem" paragraph];
-* the expert layer "from router to fold": tokens travel to the rank that holds
-  their expert, results travel back [same paragraph; KOSMOS arXiv abstract];
+* the whole expert layer, routing through the final weighted sum: each
+  token's row goes to the rank owning its expert and the result comes back
+  [same paragraph; KOSMOS arXiv abstract];
 * the same two TP+SP collectives with MXFP8 operands [KOSMOS arXiv abstract],
   the format taken from the OCP Microscaling specification v1.0.
 

@@ -58,12 +58,12 @@ def test_ag_gemm_argument_validation():
 
 def test_trace_reader_validation():
     import gemm_collective_persistent_amd as kos
-    from gemm_collective_persistent_amd._binding import KOS_ERR_ARG, TRACE_MAX_WG, TRACE_RECORDS
+    from gemm_collective_persistent_amd._binding import KOS_ERR_ARG, TRACE_LAUNCHES, TRACE_MAX_WG, TRACE_RECORDS
     lib = kos.lib
     fake = ctypes.c_void_p(0x10000)            # never dereferenced: validation fails first
     assert lib.kos_workspace_trace(None, fake, 1, None) == KOS_ERR_ARG
     assert lib.kos_workspace_trace(fake, None, 1, None) == KOS_ERR_ARG
-    assert lib.kos_workspace_trace(fake, fake, TRACE_MAX_WG * TRACE_RECORDS + 1, None) == KOS_ERR_ARG
+    assert lib.kos_workspace_trace(fake, fake, TRACE_LAUNCHES * TRACE_MAX_WG * TRACE_RECORDS + 1, None) == KOS_ERR_ARG
     assert ctypes.sizeof(kos._binding.TraceRec) == 16
     assert ctypes.sizeof(kos.Opts) == 32
 

@@ -77,7 +77,8 @@ def test_rs_single_rank_is_gemm(kos, ws):
 @pytest.mark.parametrize("rank", [7, 0])
 def test_rs_mlp_full_size(kos, ws, rank):
     """Full 8-rank MLP-down shape: band and row order give bit-identical
-    chunks; sampled rows of the partial and of y within tolerance."""
+    chunks; the whole reduced chunk y and our own partial rows against the
+    oracle, sampled outbound partial rows, within tolerance."""
     s = KI.RS_MLP
     say(f"[rs mlp full] rank={rank}")
     inp, part_b, y_band = _run(kos, ws, s, rank, False, kos.opts(rs_order=0))
@@ -87,37 +88,35 @@ def test_rs_mlp_full_size(kos, ws, rank):
     _, _, y_unf = _run(kos, ws, s, rank, False, kos.opts(mode=2), inp=inp)
     assert torch.equal(y_band, y_unf)
     rng = np.random.default_rng(rank)
-    rows = np.sort(rng.choice(s.m_chunk, 48, replace=False))
     a = KI.bf16_bits(inp["a"])
     w = KI.bf16_bits(inp["w"])
-    own_rows = rank * s.m_chunk + rows
+    # the whole reduced chunk: our own partial of chunk `rank` (every row)
+    # plus every peer's slice, against the oracle
+    own_rows = np.arange(rank * s.m_chunk, (rank + 1) * s.m_chunk)
     p_own = O.gemm(a[own_rows], w)
     assert_close(part_b[own_rows].cpu().numpy(), p_own, "own partial rows")
-    yref = p_own.copy()
-    for p in range(s.world):
-        if p != rank:
-            yref += inp["peer_slices"][p][rows].cpu().numpy().astype(np.float64)
-    assert_close(y_band[rows].cpu().numpy(), yref, "y rows")
-    other = np.sort(rng.choice(s.m, 32, replace=False))
+    peers = [None if t is None else t.cpu().numpy() for t in inp["peer_slices"]]
+    full = np.zeros((s.m, s.n), np.float32)
+    full[own_rows] = p_own.astype(np.float32)
+    yref = O.reduce_chunk(full, peers, rank)
+    assert_close(y_band.cpu().numpy(), yref, "y (whole chunk)")
+    other = np.sort(rng.choice(s.m, 64, replace=False))
     assert_close(part_b[other].cpu().numpy(), O.gemm(a[other], w), "outbound partial rows")
 
 
 def test_rs_outproj_full_size(kos, ws):
     """Attention output-projection shape (8 ranks, 4096 x 1024 . 1024 x 8192,
-    rank 7): band and row order bit-identical; sampled rows within
+    rank 7): band and row order bit-identical; the whole reduced chunk within
     tolerance."""
     s, rank = KI.RS_OUTPROJ, 7
     say("[rs out-proj full]")
     inp, part_b, y_band = _run(kos, ws, s, rank, False, kos.opts(rs_order=0))
     _, part_r, y_row = _run(kos, ws, s, rank, False, kos.opts(rs_order=1), inp=inp)
     assert torch.equal(y_band, y_row) and torch.equal(part_b, part_r)
-    rng = np.random.default_rng(11)
-    rows = np.sort(rng.choice(s.m_chunk, 48, replace=False))
     a = KI.bf16_bits(inp["a"])
     w = KI.bf16_bits(inp["w"])
-    own_rows = rank * s.m_chunk + rows
-    yref = O.gemm(a[own_rows], w)
-    for p in range(s.world):
-        if p != rank:
-            yref += inp["peer_slices"][p][rows].cpu().numpy().astype(np.float64)
-    assert_close(y_band[rows].cpu().numpy(), yref, "y rows")
+    own_rows = np.arange(rank * s.m_chunk, (rank + 1) * s.m_chunk)
+    full = np.zeros((s.m, s.n), np.float32)
+    full[own_rows] = O.gemm(a[own_rows], w).astype(np.float32)
+    peers = [None if t is None else t.cpu().numpy() for t in inp["peer_slices"]]
+    assert_close(y_band.cpu().numpy(), O.reduce_chunk(full, peers, rank), "y (whole chunk)")

@@ -125,3 +125,110 @@ def test_null_peer_buffer_with_rows_is_reported(kos, ws):
     d = O.dispatch(KI.bf16_bits(inp["x"]), inp["logits"].cpu().numpy(), peer_send,
                    inp["peer_counts"].cpu().numpy(), s.world, rank, s.topk)
     assert np.array_equal(out["perm"].cpu().numpy(), d["perm"])
+
+
+def test_capacity_overflows_are_reported_not_written(kos, ws):
+    """Buffers too small for what the routing needs: an out_send buffer
+    shorter than the rows routed to its rank (dispatch), grouped offsets
+    describing more rows than the grouped capacity, and a return buffer
+    shorter than the rows its rank sent (combine).  Each call reports
+    KOS_ERR_CAPACITY through the workspace status and writes nothing past
+    the buffers it was given (guard rows keep their fill); the workspace
+    works again afterwards."""
+    from gemm_collective_persistent_amd._binding import KOS_ERR_CAPACITY, KosError
+    from test_moe_gpu import _oracle_dispatch, _run_combine, _shape
+    s, rank = KI.MOE_TINY, 0
+    say("[moe capacity overflows]")
+    inp = KI.moe_inputs(s, rank, "cuda")
+    dref = _oracle_dispatch(s, rank, inp)
+    dev, T, k, E, H, F = "cuda", s.tokens, s.topk, s.experts, s.hidden, s.ffn
+    pc = inp["peer_counts"].cpu().numpy()
+    cap = int(pc.sum()) + T * min(k, s.e_local)
+    sent = [0 if d == rank else dref["send"][d].shape[0] for d in range(s.world)]
+    assert sent[2] > 1
+    guard = 0x4242
+    full = [None if p == rank else torch.full((max(sent[p], 1) + 8, H), 0, dtype=torch.int16, device=dev)
+            for p in range(s.world)]
+    for p in range(s.world):
+        if p != rank:
+            full[p].fill_(guard)
+    views = [None if t is None else t.view(torch.bfloat16)[:(sent[p] - 1 if p == 2 else sent[p] + 8)]
+             for p, t in enumerate(full)]
+    grouped = torch.zeros((cap, H), dtype=torch.bfloat16, device=dev)
+    out = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               counts=torch.empty((E,), dtype=torch.int32, device=dev),
+               perm=torch.empty((T * k,), dtype=torch.int32, device=dev),
+               goff=torch.full((s.e_local + 1,), -7, dtype=torch.int32, device=dev),
+               row_src=torch.empty((cap, 2), dtype=torch.int32, device=dev))
+    kos.moe_dispatch(_shape(kos, s, rank), inp["x"], inp["logits"], inp["peer_send"], inp["peer_counts"],
+                     out["idx"], out["w"], out["counts"], out["perm"], views, grouped, out["goff"],
+                     out["row_src"], ws)
+    with pytest.raises(KosError) as ei:
+        ws.status()
+    assert ei.value.status == KOS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert int((full[2][sent[2] - 1:] != guard).sum()) == 0, "rows past out_send[2]'s capacity were written"
+    assert out["goff"].tolist() == [-7] * (s.e_local + 1), "grouped offsets written after an overflow"
+
+    # combine: offsets describing more rows than the capacity
+    n = int(dref["grouped_offsets"][-1])
+    small = n - 3
+    with pytest.raises(KosError) as ei:
+        grouped_s = torch.zeros((small, H), dtype=torch.bfloat16, device=dev)
+        grouped_s[:] = KI.from_bf16_bits(dref["grouped"][:small], dev)
+        row_src = torch.as_tensor(dref["row_src"][:small], device=dev)
+        goff = torch.as_tensor(dref["grouped_offsets"], device=dev)
+        hh = torch.full((small + 8, F), float("nan"), dtype=torch.bfloat16, device=dev)
+        yg = torch.full((small + 8, H), float("nan"), dtype=torch.bfloat16, device=dev)
+        y = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)
+        ret = [None if p == rank else torch.full((max(int(pc[p].sum()), 1), H), float("nan"), dtype=torch.bfloat16,
+                                                 device=dev) for p in range(s.world)]
+        kos.moe_combine(_shape(kos, s, rank), grouped_s, goff, row_src, inp["wg"], inp["wu"], inp["wd"],
+                        torch.as_tensor(dref["idx"], device=dev), torch.as_tensor(dref["w"], device=dev),
+                        torch.as_tensor(dref["counts"], device=dev), torch.as_tensor(dref["perm"], device=dev),
+                        inp["peer_counts"], inp["peer_return"], hh, yg, ret, y, ws)
+        ws.status()
+    assert ei.value.status == KOS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(hh.float()).all()) and bool(torch.isnan(yg.float()).all()) and bool(
+        torch.isnan(y.float()).all()), "the combine wrote after a capacity error"
+
+    # combine: a return buffer shorter than the rows its rank sent us
+    q = int(np.argmax(pc.sum(axis=1)))
+    assert pc[q].sum() > 1
+    with pytest.raises(KosError) as ei:
+        _run_combine_short(kos, ws, s, rank, inp, dref, q)
+    assert ei.value.status == KOS_ERR_CAPACITY
+    # the workspace is clean again: a correct call passes
+    c = _run_combine(kos, ws, s, rank, inp, dref)
+    assert bool(torch.isfinite(c["y"].float()).all())
+
+
+def _run_combine_short(kos, ws, s, rank, inp, dref, q):
+    """The combine with out_return[q] one row shorter than the rows q sent."""
+    dev, T, H, F = "cuda", s.tokens, s.hidden, s.ffn
+    pc = inp["peer_counts"].cpu().numpy()
+    cap = int(pc.sum()) + T * min(s.topk, s.e_local)
+    n = int(dref["grouped_offsets"][-1])
+    grouped = torch.zeros((cap, H), dtype=torch.bfloat16, device=dev)
+    grouped[:n] = KI.from_bf16_bits(dref["grouped"], dev)
+    row_src = torch.zeros((cap, 2), dtype=torch.int32, device=dev)
+    row_src[:n] = torch.as_tensor(dref["row_src"], device=dev)
+    ret_full = torch.full((int(pc[q].sum()) + 4, H), 0, dtype=torch.int16, device=dev).fill_(0x4242)
+    ret = [None if p == rank else (ret_full.view(torch.bfloat16)[:int(pc[q].sum()) - 1] if p == q else
+                                   torch.empty((max(int(pc[p].sum()), 1), H), dtype=torch.bfloat16, device=dev))
+           for p in range(s.world)]
+    from test_moe_gpu import _shape
+    try:
+        kos.moe_combine(_shape(kos, s, rank), grouped, torch.as_tensor(dref["grouped_offsets"], device=dev),
+                        row_src, inp["wg"], inp["wu"], inp["wd"], torch.as_tensor(dref["idx"], device=dev),
+                        torch.as_tensor(dref["w"], device=dev), torch.as_tensor(dref["counts"], device=dev),
+                        torch.as_tensor(dref["perm"], device=dev), inp["peer_counts"], inp["peer_return"],
+                        torch.empty((cap, F), dtype=torch.bfloat16, device=dev),
+                        torch.empty((cap, H), dtype=torch.bfloat16, device=dev), ret,
+                        torch.empty((T, H), dtype=torch.bfloat16, device=dev), ws)
+        ws.status()
+    finally:
+        torch.cuda.synchronize()
+        assert int((ret_full != 0x4242).sum()) == 0, "the combine wrote into a return buffer too short for it"

@@ -221,47 +221,75 @@ def test_combine_tile_boundaries(kos, ws, mode):
     assert_close(O.bf16_to_f64(KI.bf16_bits(out["y"])), O.bf16_to_f64(yref), "y")
 
 
+UNIT_ROWS = 256   # the combine's work unit: 256 grouped rows of one expert
+
+
 @pytest.mark.parametrize("shape", [KI.MOE_DSV3, KI.MOE_QWEN3])
-def test_moe_full_size_sampled(kos, ws, shape):
-    """Full expert-layer shapes, rank 0: routing, counts, permutation, offsets
-    and provenance bit-exact; sampled grouped/send rows bit-exact; sampled
-    expert outputs and folded tokens within tolerance."""
+def test_moe_full_size(kos, ws, shape):
+    """Full expert-layer shapes, rank 0, at full concurrency:
+    - dispatch: routing, counts, permutation, offsets, provenance, every
+      grouped row and every send row bit-exact;
+    - combine (fed the oracle's dispatch): every pushed row a bit copy of the
+      expert output at the oracle's provenance; the whole first and last
+      256-row unit of every local expert (tail units included, all columns)
+      against the oracle's expert FFN; every folded token against the
+      oracle's fold of the GPU's expert outputs (the fold and push step
+      alone); and 512 tokens end to end against the oracle (every local
+      result they need recomputed by the oracle)."""
     rank = 0
     say(f"[moe full] {shape.name}")
     inp = KI.moe_inputs(shape, rank, "cuda")
     dref = _oracle_dispatch(shape, rank, inp)
-    rng = np.random.default_rng(5)
     out = _run_dispatch(kos, ws, shape, rank, inp)
-    _check_dispatch(shape, rank, out, dref, rows=np.sort(rng.choice(int(dref["grouped_offsets"][-1]), 256,
-                                                                    replace=False)))
+    _check_dispatch(shape, rank, out, dref)
     del out
+    say(f"[moe full] {shape.name}: dispatch bit-exact; combine")
     c = _run_combine(kos, ws, shape, rank, inp, dref)
     go = dref["grouped_offsets"]
-    wg, wu, wd = inp["wg"], inp["wu"], inp["wd"]
     n = int(go[-1])
-    rows = np.sort(rng.choice(n, 24, replace=False))
-    exp_of = np.searchsorted(go, rows, side="right") - 1
-    ref_rows = np.stack([O.expert_ffn(dref["grouped"][r:r + 1], KI.bf16_bits(wg[e]), KI.bf16_bits(wu[e]),
-                                      KI.bf16_bits(wd[e]))[0] for r, e in zip(rows, exp_of)])
-    got = KI.bf16_bits(c["yg"][torch.as_tensor(rows, device="cuda")])
-    assert_close(O.bf16_to_f64(got), O.bf16_to_f64(ref_rows), "sampled expert rows")
-    # sampled tokens of the fold: the oracle evaluates the local rows they need
-    toks = np.sort(rng.choice(shape.tokens, 6, replace=False))
-    need = {}
+    El, H = shape.e_local, shape.hidden
+    ygpu = KI.bf16_bits(c["yg"])
+    # pushes: out_return[p][i] == y_grouped[r] for row_src[r] == (p, i)
+    rs = dref["row_src"]
     pc = inp["peer_counts"].cpu().numpy()
+    for p in range(shape.world):
+        if p == rank:
+            continue
+        sel = np.where(rs[:, 0] == p)[0]
+        assert sel.size == int(pc[p].sum())
+        got = KI.bf16_bits(c["out_return"][p])[rs[sel, 1]]
+        assert np.array_equal(got, ygpu[sel]), f"pushed rows to rank {p}"
+    # whole first and last unit of every local expert
+    for e in range(El):
+        lo, hi = int(go[e]), int(go[e + 1])
+        if hi == lo:
+            continue
+        last = lo + ((hi - lo - 1) // UNIT_ROWS) * UNIT_ROWS
+        rows = np.unique(np.concatenate([np.arange(lo, min(lo + UNIT_ROWS, hi)), np.arange(last, hi)]))
+        ref = O.expert_ffn(dref["grouped"][rows], KI.bf16_bits(inp["wg"][e]), KI.bf16_bits(inp["wu"][e]),
+                           KI.bf16_bits(inp["wd"][e]))
+        assert_close(O.bf16_to_f64(ygpu[rows]), O.bf16_to_f64(ref), f"expert {e} first/last units")
+    say(f"[moe full] {shape.name}: units checked; fold")
+    pret = [None if t is None else KI.bf16_bits(t) for t in inp["peer_return"]]
+    ygot = KI.bf16_bits(c["y"])
+    # every token: the fold of the GPU's own expert outputs
+    yfold = O.fold(dref["idx"], dref["w"], dref["perm"], dref["offsets"], ygpu, go, pc, pret, shape.world, rank)
+    assert_close(O.bf16_to_f64(ygot), O.bf16_to_f64(yfold), "every folded token (GPU expert outputs)")
+    # 512 tokens end to end
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(shape.tokens, 512, replace=False))
+    need = {}
     for t in toks:
         for j in range(shape.topk):
             e = int(dref["idx"][t, j])
-            if e // shape.e_local == rank:
-                r_ = O.local_row(e, int(dref["perm"][t * shape.topk + j]), rank, shape.e_local, dref["offsets"], go, pc)
-                el = e - rank * shape.e_local
-                need[r_] = O.expert_ffn(dref["grouped"][r_:r_ + 1], KI.bf16_bits(wg[el]), KI.bf16_bits(wu[el]),
-                                        KI.bf16_bits(wd[el]))[0]
-    yg_sparse = np.zeros((n, shape.hidden), np.uint16)
-    for r_, v in need.items():
-        yg_sparse[r_] = v
-    pret = [None if t is None else KI.bf16_bits(t) for t in inp["peer_return"]]
+            if e // El == rank:
+                r_ = O.local_row(e, int(dref["perm"][t * shape.topk + j]), rank, El, dref["offsets"], go, pc)
+                need.setdefault(e - rank * El, []).append(r_)
+    yg_sparse = np.zeros((n, H), np.uint16)
+    for el, rows in need.items():
+        rows = np.unique(rows)
+        yg_sparse[rows] = O.expert_ffn(dref["grouped"][rows], KI.bf16_bits(inp["wg"][el]),
+                                       KI.bf16_bits(inp["wu"][el]), KI.bf16_bits(inp["wd"][el]))
     yref = O.fold(dref["idx"], dref["w"], dref["perm"], dref["offsets"], yg_sparse, go, pc, pret, shape.world,
                   rank, tokens=toks)
-    got = KI.bf16_bits(c["y"][torch.as_tensor(toks, device="cuda")])
-    assert_close(O.bf16_to_f64(got), O.bf16_to_f64(yref), "sampled folded tokens")
+    assert_close(O.bf16_to_f64(ygot[toks]), O.bf16_to_f64(yref), "512 folded tokens end to end")

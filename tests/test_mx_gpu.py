@@ -36,8 +36,8 @@ def _nat(slabs):
     return O.scales_from_slabs(_np(slabs))
 
 
-def _run_ag(kos, ws, s, rank, integer, c_dtype, o):
-    inp = KI.ag_mx_inputs(s, rank, "cuda", integer=integer)
+def _run_ag(kos, ws, s, rank, integer, c_dtype, o, edge=False):
+    inp = KI.ag_mx_inputs(s, rank, "cuda", integer=integer, edge=edge)
     g = torch.full((s.m, s.k), 0xFF, dtype=torch.uint8, device="cuda")
     gs = torch.full((s.k // 64, s.m, 2), 0xFF, dtype=torch.uint8, device="cuda")
     c = torch.full((s.m, s.n), float("nan"), dtype=c_dtype, device="cuda")
@@ -113,8 +113,8 @@ def test_ag_mx_rejects_untiled_shapes(kos, ws):
     assert "SHAPE" in str(e.value)
 
 
-def _run_rs(kos, ws, s, rank, integer, o):
-    inp = KI.rs_mx_inputs(s, rank, "cuda", integer=integer)
+def _run_rs(kos, ws, s, rank, integer, o, edge=False):
+    inp = KI.rs_mx_inputs(s, rank, "cuda", integer=integer, edge=edge)
     partial = torch.full((s.m, s.n), float("nan"), dtype=torch.float32, device="cuda")
     y = torch.full((s.m_chunk, s.n), float("nan"), dtype=torch.float32, device="cuda")
     kos.gemm_rs_mx(inp["a"], inp["a_scales"], inp["w"], inp["w_scales"], inp["peer_slices"], partial, y, rank,
@@ -157,3 +157,25 @@ def test_rs_mx_mlp_full_size(kos, ws, rank):
         yref += own if p == rank else _np(inp["peer_slices"][p]).astype(np.float64)
     assert_close(_np(y), yref, "y")
     assert_close(_np(partial)[rank * mc:(rank + 1) * mc], own, "own chunk of the partial")
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("rank", [0, 3])
+def test_mx_edge_values(kos, ws, rank, mode):
+    """Codes and scales at the format's edges -- subnormal E4M3 codes, zeros,
+    codes up to +-448, scales 2^-27 .. 2^27 -- through both collectives:
+    the gathered codes and scales bit-exact, C, the partial and y within
+    the floating-point bar against the oracle's exact decode."""
+    say(f"[mx edge] rank={rank} mode={mode}")
+    o = kos.opts(mode=mode)
+    inp, g, gs, c = _run_ag(kos, ws, KI.AG_TINY_MX, rank, False, torch.float32, o, edge=True)
+    gref, gsref, cref = _ag_oracle(inp, rank, "f32")
+    codes = _np(g)
+    assert ((codes & 0x78) == 0).mean() > 0.2 and np.abs(O.e4m3_to_f64(codes)).max() == 448.0
+    assert np.array_equal(codes, gref) and np.array_equal(_nat(gs), gsref)
+    assert np.all(np.isfinite(cref)) and np.abs(cref).max() > 1e15
+    assert_close(_np(c), cref, "C (edge values)")
+    inp, partial, y = _run_rs(kos, ws, KI.RS_TINY_MX, rank, False, o, edge=True)
+    pref, yref = _rs_oracle(inp, rank)
+    assert_close(_np(partial), pref, "partial (edge values)")
+    assert_close(_np(y), yref, "y (edge values)")

@@ -370,6 +370,51 @@ def test_push_rows_equal_expert_outputs():
     assert n_peer + n_own == out["grouped"].shape[0]
 
 
+def test_push_returns_each_peer_row_through_its_own_expert():
+    """Independent of the provenance table and of push's own loop: peer p
+    sends its rows expert-major over our local experts (peer_counts[p] rows
+    per expert, in order), so row i it sent belongs to the local expert
+    whose cumulative count range holds i, and the row we return at i must be
+    that expert's FFN of exactly that input row."""
+    rng = np.random.default_rng(19)
+    for rank in (0, 2):
+        m = _tiny_moe(rng, rank=rank, T=20, k=2)
+        out = O.moe_layer(m["x"], m["lg"], m["wg"], m["wu"], m["wd"], m["ps"], m["pc"], m["pr"],
+                          m["R"], m["rank"], m["k"])
+        for p in range(m["R"]):
+            if p == rank:
+                assert out["out_return"][p] is None
+                continue
+            bounds = np.cumsum(m["pc"][p])
+            n_p = int(bounds[-1]) if bounds.size else 0
+            assert out["out_return"][p].shape[0] == n_p == m["ps"][p].shape[0]
+            for i in range(n_p):
+                el = int(np.searchsorted(bounds, i, side="right"))
+                want = O.expert_ffn(m["ps"][p][i:i + 1], m["wg"][el], m["wu"][el], m["wd"][el])[0]
+                assert np.array_equal(out["out_return"][p][i], want), (rank, p, i)
+
+
+def test_push_catches_a_swapped_source():
+    """A planted provenance mistake (two peer rows of different experts
+    swapped in row_src) moves results to the wrong return slots: the
+    independent pin above would fail on it."""
+    rng = np.random.default_rng(20)
+    m = _tiny_moe(rng, rank=1, T=20, k=2)
+    m["pc"][0] = [2, 2]
+    m["ps"][0] = _ints(rng, (4, 8), -3, 3)
+    out = O.moe_layer(m["x"], m["lg"], m["wg"], m["wu"], m["wd"], m["ps"], m["pc"], m["pr"],
+                      m["R"], m["rank"], m["k"])
+    rs = out["row_src"].copy()
+    r0 = int(np.where((rs[:, 0] == 0) & (rs[:, 1] == 0))[0][0])
+    r3 = int(np.where((rs[:, 0] == 0) & (rs[:, 1] == 3))[0][0])
+    rs[[r0, r3]] = rs[[r3, r0]]
+    bad = O.push(out["y_grouped"], rs, m["R"], 1, m["pc"].sum(axis=1))
+    want0 = O.expert_ffn(m["ps"][0][0:1], m["wg"][0], m["wu"][0], m["wd"][0])[0]
+    assert np.array_equal(out["out_return"][0][0], want0)
+    if not np.array_equal(out["y_grouped"][r0], out["y_grouped"][r3]):
+        assert not np.array_equal(bad[0][0], want0)
+
+
 def test_fold_k1_is_the_result_row():
     rng = np.random.default_rng(16)
     m = _tiny_moe(rng, k=1)

@@ -59,7 +59,37 @@ def test_trace_off_leaves_header_untouched(kos):
     inp = KI.ag_inputs(s, rank, "cuda", integer=True)
     g = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
     c = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
-    ws.buf[-(256 * 512 * 16):].fill_(0)
+    region = 4 * 256 * 512 * 16            # KOS_TRACE_LAUNCHES slots at the end of the workspace
+    ws.buf[-region:].fill_(0)
     kos.ag_gemm(inp["a_local"], inp["a_peers"], inp["w"], g, c, rank, ws, kos.opts())
     ws.status()
-    assert int(ws.buf[-(256 * 512 * 16):].count_nonzero()) == 0
+    assert int(ws.buf[-region:].count_nonzero()) == 0
+
+
+def test_unfused_trace_holds_every_launch(kos):
+    """An unfused call's two launches record into two slots of the trace
+    region: the moves in the first, the tiles in the second, the second
+    starting after the first ended; the summary over both counts the gap
+    between them as idle."""
+    from gemm_collective_persistent_amd.timeline import summarize
+    say("[trace ag unfused]")
+    ws = kos.Workspace("cuda")
+    s, rank = KI.AG_TINY, 2
+    grid = kos.lib.kos_device_cu_count()
+    inp = KI.ag_inputs(s, rank, "cuda", integer=True)
+    g = torch.empty((s.m, s.k), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+    kos.ag_gemm(inp["a_local"], inp["a_peers"], inp["w"], g, c, rank, ws, kos.opts(mode=2, trace=True))
+    ws.status()
+    tl = ws.trace(grid, launches=2)
+    assert len(tl) == 2 * grid
+    first, second = tl[:grid], tl[grid:]
+    moves = sorted(e for _, _, _, recs in first for k, e, _, _ in recs if k == "move")
+    tiles = sorted(e for _, _, _, recs in second for k, e, _, _ in recs if k == "tile")
+    assert moves == list(range(4)) and tiles == list(range(16))
+    assert not any(k == "tile" for _, _, _, recs in first for k, _, _, _ in recs)
+    end_first = max(e for _, _, e, _ in first)
+    assert min(b for _, b, _, _ in second) >= end_first - 1e-3
+    sm = summarize(tl, workgroups=grid)
+    work = sum(t1 - t0 for _, _, _, recs in tl for k, _, t0, t1 in recs if k != "wait")
+    assert sm["idle_frac"] == pytest.approx(1.0 - work / (grid * sm["span_us"]), abs=2e-4)
