@@ -26,7 +26,7 @@ EXPORTS = [
     "kos_opts_default", "kos_workspace_bytes", "kos_workspace_init", "kos_workspace_status",
     "kos_last_error", "kos_device_cu_count", "kos_ag_gemm", "kos_gemm_rs",
     "kos_ag_gemm_mx", "kos_gemm_rs_mx", "kos_ag_gemm_wt", "kos_gemm_rs_wt",
-    "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace",
+    "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace", "kos_ag_gemm_noalloc",
 ]
 
 
@@ -84,6 +84,8 @@ def _load():
                                   c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, P, P,
                                   POINTER(Opts), P, c_size_t, P]),
+        "kos_ag_gemm_noalloc": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, PP, P, P, P,
+                                          c_int32, POINTER(Opts), P, P]),
         "kos_ag_gemm_wt": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, PP, P, P, P,
                                      c_int32, POINTER(Opts), P, c_size_t, P]),
         "kos_gemm_rs_wt": (c_int32, [c_int32, c_int32, c_int64, c_int64, c_int64, P, P, PP, P, P,

@@ -134,6 +134,33 @@ def ag_gemm(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w:
              ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
 
 
+def ag_gemm_noalloc(a_local: torch.Tensor, a_peers: Sequence[Optional[torch.Tensor]], w: torch.Tensor,
+                    a_gathered: torch.Tensor, c: torch.Tensor, rank: int, status: Optional[torch.Tensor] = None,
+                    o: Optional[Opts] = None, stream=None) -> None:
+    """kos_ag_gemm_noalloc: as ag_gemm (w [k, n]) with no workspace -- the
+    library's static scratch holds the queues.  `status` (optional int32 [1]
+    on the GPU) receives the call's device-side status when it finishes."""
+    world = len(a_peers)
+    _need(a_local, torch.bfloat16, "a_local", 2)
+    m_local, k = a_local.shape
+    _need(w, torch.bfloat16, "w", 2, (k, None))
+    n = w.shape[1]
+    _need(a_gathered, torch.bfloat16, "a_gathered", 2, (world * m_local, k))
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("c must be bf16 or fp32")
+    _need(c, c.dtype, "c", 2, (world * m_local, n))
+    for p, t in enumerate(a_peers):
+        if p != rank:
+            _need(t, torch.bfloat16, f"a_peers[{p}]", 2, (m_local, k), host_ok=True)
+    if status is not None:
+        _need(status, torch.int32, "status", 1, (1,))
+    peers = ptr_array([None if p == rank else _p(t) for p, t in enumerate(a_peers)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_ag_gemm_noalloc(world, rank, m_local, k, n, _p(a_local), peers, _p(w), _p(a_gathered), _p(c),
+                                  KOS_BF16 if c.dtype == torch.bfloat16 else KOS_F32, ctypes.byref(o),
+                                  _p(status), _stream(stream)))
+
+
 def gemm_rs(a: torch.Tensor, w: torch.Tensor, peer_slices: Sequence[Optional[torch.Tensor]],
             partial: torch.Tensor, y: torch.Tensor, rank: int, ws: Workspace,
             o: Optional[Opts] = None, stream=None, w_transposed: bool = False) -> None:

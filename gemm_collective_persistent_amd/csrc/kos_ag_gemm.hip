@@ -20,6 +20,7 @@
 // slab-packed E8M0 scales (kos_tile_mx.h); a move copies a slice's rows and
 // then its scales in every slab before it is counted.
 #include <algorithm>
+#include <mutex>
 
 #include "kos_host.h"
 #include "kos_tile.h"
@@ -57,6 +58,8 @@ struct AgParams {
   WsHeader* ws;
   uint32_t* ready;
   kos_trace_rec* trace;   // null: tracing off
+  int32_t hand_over;      // the library's static scratch: hand the status over at exit
+  int32_t* status_out;    // where (may be null)
 };
 
 // One output tile's K loop over the BM rows of A at `a_rows` (bytes) and
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
     }
     if (!p.movers_switch) {
       tr.finish(ticket);
-      wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
+      wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots, p.hand_over, p.status_out);
       return;
     }
   }
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
     }
   }
   tr.finish(ticket);
-  wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots);
+  wg_exit(h, p.ready, p.world * p.rb_per_shard, &slots, p.hand_over, p.status_out);
 }
 
 template <class S>
@@ -259,7 +262,57 @@ struct AgCall {
   void* ws;
   size_t ws_bytes;
   void* stream;
+  bool noalloc;           // no caller workspace: the library's static scratch
+  int32_t* status_out;    // noalloc: the call's device-side status goes here
 };
+
+// ---------------------------------------------------------------------------
+// the allocation-free variant's scratch: a file-scope device array (one copy
+// per GPU, held until the process ends) laid out like the head of a
+// workspace -- the 256-byte header, then the ready counters at
+// kCountersOffset -- for callers that cannot allocate.  Host code never
+// passes the array's name to a kernel (on the host it only stands for the
+// symbol); it uses the device address hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kStaticCounters = 16384;   // ready counters: world x row blocks
+constexpr size_t kStaticScratchBytes = kCountersOffset + kStaticCounters * sizeof(uint32_t);   // 68 KiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ void scratch_clear_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];       // per device: the array's device address
+bool g_scratch_clear[64];      // per device: zeroed once (by a fill kernel, never a memset)
+}  // namespace
+
+// The scratch of the current device, zeroed before its first use (on
+// `stream`, ahead of the caller's launch).  Every call leaves it zeroed
+// again (the last workgroup out resets it).
+static kos_status static_scratch(const DeviceInfo& dev, hipStream_t stream, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  const int d = dev.device;
+  if (!g_scratch_ptr[d]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KOS_ERR_HIP, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[d] = ptr;
+  }
+  if (!g_scratch_clear[d]) {
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3(16), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(g_scratch_ptr[d]), (uint32_t)(kStaticScratchBytes / 4));
+    kos_status st = launch_status("static scratch clear");
+    if (st != KOS_OK) return st;
+    g_scratch_clear[d] = true;
+  }
+  *out = g_scratch_ptr[d];
+  return KOS_OK;
+}
 
 static kos_status ag_gemm_run(const AgCall& a) {
   const int32_t world = a.world, rank = a.rank;
@@ -298,10 +351,14 @@ static kos_status ag_gemm_run(const AgCall& a) {
     if (!aligned16(a.a_peers[p])) return fail(KOS_ERR_ALIGN, "a_peers[%d] not 16-byte aligned", p);
     if (a.mx && !aligned16(a.sc_peers[p])) return fail(KOS_ERR_ALIGN, "a_peer_scales[%d] not 16-byte aligned", p);
   }
-  kos_status st = check_workspace(a.ws, a.ws_bytes);
+  kos_status st = a.noalloc ? KOS_OK : check_workspace(a.ws, a.ws_bytes);
   if (st != KOS_OK) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != KOS_OK) return st;
+  if (a.noalloc && a.opts && a.opts->trace)
+    return fail(KOS_ERR_ARG, "the allocation-free entry point has no trace region");
+  if (a.noalloc && (reinterpret_cast<uintptr_t>(a.status_out) & 3u))
+    return fail(KOS_ERR_ALIGN, "status_out must be 4-byte aligned");
   kos_opts o;
   // Movers over device memory: half the grid saturates HBM copy bandwidth
   // and the other half builds the local shard meanwhile; over PCIe sixteen
@@ -348,17 +405,23 @@ static kos_status ag_gemm_run(const AgCall& a) {
   p.moves_per_rb = bm / rows;
   p.n_move = world * p.rb_per_shard * p.moves_per_rb;
   p.n_tiles = world * p.rb_per_shard * p.tiles_n;
-  p.ws = static_cast<WsHeader*>(a.ws);
-  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(a.ws) + kCountersOffset);
-  p.trace = trace_slot(a.ws, o.trace, 0);
-  if ((size_t)world * p.rb_per_shard > kMaxCounters) return fail(KOS_ERR_SHAPE, "too many row blocks");
+  if ((size_t)world * p.rb_per_shard > (a.noalloc ? kStaticCounters : kMaxCounters))
+    return fail(KOS_ERR_SHAPE, "too many row blocks (%lld) for the %s", (long long)world * p.rb_per_shard,
+                a.noalloc ? "static scratch" : "workspace");
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  void* ws = a.ws;
+  if (a.noalloc && (st = static_scratch(dev, s, &ws)) != KOS_OK) return st;
+  p.ws = static_cast<WsHeader*>(ws);
+  p.ready = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
+  p.trace = a.noalloc ? nullptr : trace_slot(ws, o.trace, 0);
+  p.hand_over = a.noalloc;
+  p.status_out = a.status_out;
 
   // A single rank whose gathered output is its own shard has nothing to move.
   const bool nothing_to_move =
       world == 1 && a.a_gathered == a.a_local && (!a.mx || a.sc_gathered == a.sc_local);
   if (nothing_to_move) p.n_move = 0;
 
-  hipStream_t s = static_cast<hipStream_t>(a.stream);
   const int grid = o.grid;
   auto launch = [&](const AgParams& q) {
     return a.mx ? launch_ag<TileShapeMX<256, 256>>(q, grid, s)
@@ -378,7 +441,7 @@ static kos_status ag_gemm_run(const AgCall& a) {
     mv.do_build = 0;
     if ((st = launch(mv)) != KOS_OK) return st;
     AgParams gm = p;           // launch 2: the whole GEMM
-    gm.trace = trace_slot(a.ws, o.trace, 1);
+    gm.trace = a.noalloc ? nullptr : trace_slot(ws, o.trace, 1);
     gm.n_movers = 0;
     gm.n_move = 0;
     gm.do_build = 1;
@@ -403,7 +466,7 @@ extern "C" kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, 
                                   void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
                                   size_t ws_bytes, void* stream) {
   return ag_gemm_run(AgCall{false, false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, nullptr,
-                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
+                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream, false, nullptr});
 }
 
 extern "C" kos_status kos_ag_gemm_wt(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
@@ -411,7 +474,7 @@ extern "C" kos_status kos_ag_gemm_wt(int32_t world, int32_t rank, int64_t m_loca
                                      void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts, void* ws,
                                      size_t ws_bytes, void* stream) {
   return ag_gemm_run(AgCall{false, true, world, rank, m_local, k, n, a_local, a_peers, w_t, a_gathered, nullptr,
-                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream});
+                            nullptr, nullptr, nullptr, c, c_dtype, opts, ws, ws_bytes, stream, false, nullptr});
 }
 
 extern "C" kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
@@ -420,5 +483,13 @@ extern "C" kos_status kos_ag_gemm_mx(int32_t world, int32_t rank, int64_t m_loca
                                      void* a_gathered, void* a_gathered_scales, void* c, int32_t c_dtype,
                                      const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
   return ag_gemm_run(AgCall{true, false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, a_local_scales,
-                            a_peer_scales, w_scales, a_gathered_scales, c, c_dtype, opts, ws, ws_bytes, stream});
+                            a_peer_scales, w_scales, a_gathered_scales, c, c_dtype, opts, ws, ws_bytes, stream, false, nullptr});
+}
+
+extern "C" kos_status kos_ag_gemm_noalloc(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                                          const void* a_local, const void* const* a_peers, const void* w,
+                                          void* a_gathered, void* c, int32_t c_dtype, const kos_opts* opts,
+                                          int32_t* status_out, void* stream) {
+  return ag_gemm_run(AgCall{false, false, world, rank, m_local, k, n, a_local, a_peers, w, a_gathered, nullptr,
+                            nullptr, nullptr, nullptr, c, c_dtype, opts, nullptr, 0, stream, true, status_out});
 }

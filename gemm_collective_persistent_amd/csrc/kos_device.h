@@ -180,7 +180,13 @@ __device__ __forceinline__ uint32_t wg_ticket(WsHeader* h, WgSlots* s) {
 // reset, with no fence.  (An agent-scope fence writes back and invalidates
 // the XCD's whole L2, stalling every workgroup still running there; the
 // launch's outputs become visible to later work when it ends.)
-__device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_counters, WgSlots* s) {
+//
+// hand_over: the call keeps no sticky error word (the library's own scratch,
+// shared by every call on the device); the last one out hands the status to
+// `status_out` (if non-null) and clears it.  Every workgroup's error, if any,
+// was recorded before it counted itself out, so the last one sees them all.
+__device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_counters, WgSlots* s,
+                               bool hand_over = false, int32_t* status_out = nullptr) {
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt, lgkmcnt = 0
   __syncthreads();
   if (threadIdx.x == 0)
@@ -190,6 +196,13 @@ __device__ inline void wg_exit(WsHeader* h, uint32_t* counters, uint32_t n_count
   for (uint32_t i = threadIdx.x; i < n_counters; i += blockDim.x) st_relaxed(&counters[i], 0u);
   if (threadIdx.x < kNumHeads) st_relaxed(&h->head[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
+    if (hand_over) {
+      const uint32_t st = ld_relaxed(&h->status);
+      if (status_out)
+        __hip_atomic_store(status_out, (int32_t)st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_relaxed(&h->status, 0u);
+      st_relaxed(&h->err_info, 0u);
+    }
     st_relaxed(&h->ticket, 0u);
     st_relaxed(&h->abort, 0u);
     st_relaxed(&h->exit_count, 0u);

@@ -223,6 +223,29 @@ kos_status kos_ag_gemm(int32_t world, int32_t rank, int64_t m_local, int64_t k, 
                        const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * All-gather + GEMM that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same operation,
+ * arguments, shapes, modes, kernels and results as kos_ag_gemm; the queue
+ * heads and ready counters live in a static device array of the library
+ * (68 KiB, one per GPU, held until the process ends), zeroed before its
+ * first use and returned to zero by every call.
+ *
+ * status_out  optional device int32 (4-byte aligned): when the call's
+ *             kernels finish it holds KOS_OK or the device-side error
+ *             (KOS_ERR_TIMEOUT); NULL if not wanted.
+ * Limits: world * (m_local / tile rows) <= 16384 ready counters, i.e. at
+ * most 16384 64-row blocks of gathered rows (KOS_ERR_SHAPE beyond);
+ * opts->trace must be 0 (KOS_ERR_ARG).  Every call on one GPU shares its
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.
+ */
+kos_status kos_ag_gemm_noalloc(int32_t world, int32_t rank, int64_t m_local, int64_t k, int64_t n,
+                               const void* a_local, const void* const* a_peers, const void* w,
+                               void* a_gathered, void* c, int32_t c_dtype,
+                               const kos_opts* opts, int32_t* status_out, void* stream);
+
+/*
  * GEMM + reduce-scatter, one rank's share [explainer, "Start with the
  * problem": the GEMM's partial sums are split by rows over the ranks and
  * summed; "Role switching only works if": tiles come out one band of rows
