@@ -81,12 +81,12 @@ def build_inputs(torch, KI, kos, moe_shape):
     return inp
 
 
-def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=False, rank_moe=0):
+def make_ops(kos, KI, inp, ws, moe_shape, mode=0, n_movers=-1, grid=0, trace=False, rank_moe=0, policy=0):
     """The step's ops as closures over resident inputs (the AG and RS ones
     only when `inp` holds their inputs).  FIXED mode runs the dispatch fused:
     it has no compute role to split a crew from."""
     from gemm_collective_persistent_amd.api import moe_shape as mk_shape
-    o = kos.opts(mode=mode, n_movers=n_movers, grid=grid, trace=trace)
+    o = kos.opts(mode=mode, n_movers=n_movers, grid=grid, trace=trace, policy=policy)
     ag, rs, m = inp.get("ag"), inp.get("rs"), inp["moe"]
     s = moe_shape
     shp = mk_shape(s.world, rank_moe, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
@@ -145,7 +145,9 @@ def moe_block(torch, kos, KI, ws, flush, reps, shape, rank=0):
     idle, rates = idle_fractions(torch, kos, KI, inp, ws, shape, flush, {"moe_combine": best}, pb, names,
                                  rank_moe=rank)
     t_layer = per[0] + per[1]
+    one = single_launch(torch, kos, KI, m, ws, flush, reps, shape, t_layer, rank)
     return {
+        "single_launch": one,
         "workload": shape.name, "rank": rank, "grouped_rows": rows,
         "ms": {"moe_dispatch": round(per[0], 4), "moe_combine": round(per[1], 4), "layer": round(t_layer, 4)},
         "tokens_per_s": round(shape.tokens / (t_layer * 1e-3), 1),
@@ -170,6 +172,48 @@ def crew_sweep_moe(torch, kos, KI, inp, ws, shape, flush, reps, planned, rank):
         fn = dict(make_ops(kos, KI, inp, ws, shape, mode=1, n_movers=c, rank_moe=rank))["moe_combine"]
         fn()
         out[c] = round(time_ops(torch, [("moe_combine", fn)], reps, ws, flush)[0][0], 4)
+    return out
+
+
+def layer_op(kos, m, ws, shape, rank=0, trace=False):
+    """The whole expert layer in one launch (kos_moe_layer) on resident inputs."""
+    from gemm_collective_persistent_amd.api import moe_shape as mk_shape
+    shp = mk_shape(shape.world, rank, shape.tokens, shape.hidden, shape.experts, shape.topk, shape.ffn)
+    o = kos.opts(trace=trace)
+    return lambda: kos.moe_layer(shp, m["x"], m["logits"], m["peer_send"], m["peer_counts"], m["wg"], m["wu"],
+                                 m["wd"], m["peer_return"], m["idx"], m["w"], m["counts"], m["perm"], m["send"],
+                                 m["grouped"], m["goff"], m["row_src"], m["h"], m["yg"], m["ret"], m["y"], ws, o)
+
+
+def single_launch(torch, kos, KI, m, ws, flush, reps, shape, two_ms, rank=0):
+    """The expert layer in one launch, router to fold (kos_moe_layer), against
+    the two launches (dispatch, then combine) on the same inputs."""
+    fn = layer_op(kos, m, ws, shape, rank)
+    fn()
+    t = time_ops(torch, [("moe_layer", fn)], reps, ws, flush)[0][0]
+    return {"ms": round(t, 4), "two_launch_ms": round(two_ms, 4), "speedup_vs_two_launch": round(two_ms / t, 3),
+            "tokens_per_s": round(shape.tokens / (t * 1e-3), 1)}
+
+
+def policy_comparison(torch, kos, KI, inp, ws, moe_shape, flush, reps, fused_ms, unfused_ms, sweep, planned):
+    """The role-switching policies side by side, per op with a compute role
+    (the explainer's "How do the policies compare?": each against a fixed
+    communication crew): the pages' policy (one-way all-gather and
+    reduce-scatter, two-way combine), the other one (kos_opts.policy =
+    SWAPPED), the best fixed crew of the sweep, the planned crew and the
+    unfused launches; speed-ups over the best fixed crew."""
+    out = {}
+    for n in ("ag_gemm", "gemm_rs", "moe_combine"):
+        fn = dict(make_ops(kos, KI, inp, ws, moe_shape, policy=1))[n]
+        fn()
+        sw = time_ops(torch, [(n, fn)], reps, ws, flush)[0][0]
+        best = min(sweep[n].values())
+        d = {"default": round(fused_ms[n], 4), "swapped": round(sw, 4), "best_fixed": best,
+             "planned": sweep[n][planned[n]], "unfused": unfused_ms[n]}
+        d["speedup_vs_best_fixed"] = {k: round(best / d[k], 3) for k in ("default", "swapped")}
+        d["policy"] = {"default": "two-way" if n == "moe_combine" else "one-way",
+                       "swapped": "one-way" if n == "moe_combine" else "two-way"}
+        out[n] = d
     return out
 
 
@@ -717,6 +761,10 @@ def main():
              "source_digest": source_digest()}
     if args.copy_calibration:
         extra["copy_calibration"] = copy_calibration(torch)
+    # the expert layer in one launch, router to fold, beside the two launches
+    t_two = per[names.index("moe_dispatch")] + per[names.index("moe_combine")]
+    extra["moe_single_launch"] = single_launch(torch, kos, KI, inp["moe"], ws, flush, max(3, args.steps // 4),
+                                               moe_shape, t_two)
     if not args.no_baselines:
         reps = max(3, args.steps // 4)
         ops_u = make_ops(kos, KI, inp, ws, moe_shape, mode=2)
@@ -747,6 +795,9 @@ def main():
         extra["phase_rate_gb_s"] = {lab: {n: {k: v["gb_s"] for k, v in d.items()} for n, d in r.items()}
                                     for lab, r in rates.items()}
         extra["phase_bytes"] = {n: {k: round(v) for k, v in d.items()} for n, d in pb.items()}
+        # the two switching policies against the fixed crews
+        extra["policy_comparison"] = policy_comparison(torch, kos, KI, inp, ws, moe_shape, flush, reps,
+                                                       {n: t for n, t in zip(names, per)}, unfused, sweep, crews)
         # the tiny all-gather+GEMM (latency-bound; microseconds)
         extra["ag_tiny"] = tiny_ag(torch, kos, KI, ws, flush)
         # the other expert-layer shape, as a block of its own (the Qwen3-235B

@@ -14,4 +14,4 @@ The compute is in ``libkos.so`` (hand-written HIP, C ABI in
 from ._binding import (KOS_BF16, KOS_F32, MODE_FIXED, MODE_FUSED, MODE_UNFUSED, RS_BAND,  # noqa: F401
                        RS_ROW, EXPORTS, KosError, MoeShape, Opts, lib, opts)
 from .api import (Workspace, ag_gemm, ag_gemm_mx, ag_gemm_noalloc, gemm_rs, gemm_rs_mx, moe_combine,  # noqa: F401
-                  moe_dispatch)
+                  moe_dispatch, moe_layer)

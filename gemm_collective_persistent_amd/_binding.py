@@ -20,13 +20,14 @@ STATUS_NAMES = ["OK", "ERR_ARG", "ERR_SHAPE", "ERR_ALIGN", "ERR_WORKSPACE", "ERR
 KOS_BF16, KOS_F32 = 0, 1
 MODE_FUSED, MODE_FIXED, MODE_UNFUSED = 0, 1, 2
 RS_BAND, RS_ROW = 0, 1
+POLICY_DEFAULT, POLICY_SWAPPED = 0, 1
 
 # Every symbol include/kos.h declares.
 EXPORTS = [
     "kos_opts_default", "kos_workspace_bytes", "kos_workspace_init", "kos_workspace_status",
     "kos_last_error", "kos_device_cu_count", "kos_ag_gemm", "kos_gemm_rs",
     "kos_ag_gemm_mx", "kos_gemm_rs_mx", "kos_ag_gemm_wt", "kos_gemm_rs_wt",
-    "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace", "kos_ag_gemm_noalloc",
+    "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace", "kos_ag_gemm_noalloc", "kos_moe_layer",
 ]
 
 
@@ -40,7 +41,7 @@ class KosError(RuntimeError):
 class Opts(ctypes.Structure):
     _fields_ = [("mode", c_int32), ("n_movers", c_int32), ("rs_order", c_int32),
                 ("grid", c_int32), ("spin_limit", c_uint32), ("peer_link", c_int32),
-                ("trace", c_int32), ("reserved", c_int32)]
+                ("trace", c_int32), ("policy", c_int32)]
 
 
 class TraceRec(ctypes.Structure):
@@ -96,6 +97,8 @@ def _load():
                                      POINTER(Opts), P, c_size_t, P]),
         "kos_moe_dispatch": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, P, PP, POINTER(c_int64),
                                        P, c_int64, P, P, POINTER(Opts), P, c_size_t, P]),
+        "kos_moe_layer": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, PP, P, P, P, P, PP, POINTER(c_int64),
+                                    P, c_int64, P, P, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_combine": (c_int32, [POINTER(MoeShape), P, P, P, c_int64, P, P, P, P, P, P, P, P,
                                       PP, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
     }
@@ -117,11 +120,11 @@ def check(status: int) -> None:
 
 
 def opts(mode=MODE_FUSED, n_movers=-1, rs_order=RS_BAND, grid=0, spin_limit=0, peer_link=0,
-         trace=False) -> Opts:
+         trace=False, policy=0) -> Opts:
     o = Opts()
     lib.kos_opts_default(ctypes.byref(o))
     o.mode, o.n_movers, o.rs_order, o.grid = mode, n_movers, rs_order, grid
-    o.spin_limit, o.peer_link, o.trace = spin_limit, peer_link, int(bool(trace))
+    o.spin_limit, o.peer_link, o.trace, o.policy = spin_limit, peer_link, int(bool(trace)), policy
     return o
 
 

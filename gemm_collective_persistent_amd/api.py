@@ -341,3 +341,50 @@ def moe_combine(s: MoeShape, x_grouped, grouped_offsets, row_src, w_gate, w_up, 
                               _p(topk_w), _p(counts), _p(perm), _p(peer_counts), pret, _p(h),
                               _p(y_grouped), oret, rcaps, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes,
                               _stream(stream)))
+
+
+def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_down, peer_return,
+              topk_idx, topk_w, counts, perm, out_send, x_grouped, grouped_offsets, row_src, h, y_grouped,
+              out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+    """kos_moe_layer: the whole expert layer in one launch -- what moe_dispatch
+    followed by moe_combine computes, with the same buffers (see include/kos.h)."""
+    T, H, E, R, F = s.tokens, s.hidden, s.experts, s.world, s.ffn
+    E_loc = E // R
+    for name, lst in (("peer_send", peer_send), ("out_send", out_send), ("peer_return", peer_return),
+                      ("out_return", out_return)):
+        if len(lst) != R:
+            raise ValueError(f"{name} needs one entry per rank")
+    if T > 0:
+        _need(x, torch.bfloat16, "x", 2, (T, H))
+        _need(logits, torch.float32, "logits", 2, (T, E))
+        _need(y, torch.bfloat16, "y", 2, (T, H))
+    _need(peer_counts, torch.int32, "peer_counts", 2, (R, E_loc))
+    _check_tokens(s, topk_idx, topk_w, perm, counts)
+    _need(w_gate, torch.bfloat16, "w_gate", 3, (E_loc, H, F))
+    _need(w_up, torch.bfloat16, "w_up", 3, (E_loc, H, F))
+    _need(w_down, torch.bfloat16, "w_down", 3, (E_loc, F, H))
+    _need(x_grouped, torch.bfloat16, "x_grouped", 2, (None, H))
+    cap = x_grouped.shape[0]
+    _need(grouped_offsets, torch.int32, "grouped_offsets", 1, (E_loc + 1,))
+    _need(row_src, torch.int32, "row_src", 2, (None, 2))
+    _min_rows(row_src, cap, "row_src")
+    _need(h, torch.bfloat16, "h", 2, (None, F))
+    _min_rows(h, cap, "h")
+    _need(y_grouped, torch.bfloat16, "y_grouped", 2, (None, H))
+    _min_rows(y_grouped, cap, "y_grouped")
+    for p in range(R):
+        if p == s.rank:
+            continue
+        for name, lst, host_ok in (("peer_send", peer_send, True), ("out_send", out_send, False),
+                                   ("peer_return", peer_return, True), ("out_return", out_return, False)):
+            if lst[p] is not None:
+                _need(lst[p], torch.bfloat16, f"{name}[{p}]", 2, (None, H), host_ok=host_ok)
+    arr = {n: ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(lst)])
+           for n, lst in (("ps", peer_send), ("os", out_send), ("pr", peer_return), ("or", out_return))}
+    scaps = (ctypes.c_int64 * R)(*[0 if p == s.rank or t is None else t.shape[0] for p, t in enumerate(out_send)])
+    rcaps = (ctypes.c_int64 * R)(*[0 if p == s.rank or t is None else t.shape[0] for p, t in enumerate(out_return)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_moe_layer(ctypes.byref(s), _p(x), _p(logits), arr["ps"], _p(peer_counts), _p(w_gate), _p(w_up),
+                            _p(w_down), arr["pr"], _p(topk_idx), _p(topk_w), _p(counts), _p(perm), arr["os"], scaps,
+                            _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(h), _p(y_grouped), arr["or"],
+                            rcaps, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))

@@ -23,6 +23,7 @@
 #include <mutex>
 
 #include "kos_host.h"
+#include "kos_order.h"
 #include "kos_tile.h"
 #include "kos_tile_mx.h"
 
@@ -48,6 +49,7 @@ struct AgParams {
   int32_t movers_switch;  // movers become builders when moves run out
   int32_t do_build;       // this launch builds tiles
   int32_t wait_flags;     // builders wait for remote row blocks
+  int32_t builders_move;  // two-way: builders take move entries between tiles
   uint32_t spin_limit;
   int32_t rb_per_shard;   // m_local / BM
   int32_t tiles_n;        // n / BN
@@ -114,36 +116,29 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
   Tracer tr(p.trace);
   const uint32_t ticket = wg_ticket(h, &slots);
 
+  // one move entry: a slice of a shard's row block into the gathered rows
+  auto do_move = [&](uint32_t i) {
+    const uint64_t t0 = tr.now();
+    const AgMove mv = ag_move_of((int)i, p.world, p.rank, p.rb_per_shard, p.moves_per_rb);
+    const int shard = mv.shard, rb = mv.rb;
+    const char* src_shard = shard == p.rank ? p.a_local : p.peers[shard];
+    const int64_t row = (int64_t)rb * BM + (int64_t)mv.sub * p.rows_per_move;
+    wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * RB, src_shard + row * RB,
+                (size_t)p.rows_per_move * RB);
+    if constexpr (S::MX)
+      copy_scale_rows(p.sc_gathered + ((int64_t)shard * p.m_local + row) * 2,
+                      (shard == p.rank ? p.sc_local : p.sc_peers[shard]) + row * 2, p.rows_per_move, K / 64,
+                      (int64_t)p.world * p.m_local * 2, (int64_t)p.m_local * 2);
+    wg_publish(&p.ready[shard * p.rb_per_shard + rb], 1u);
+    tr.put(KOS_TR_MOVE, i, t0);
+  };
+
   // ---- mover role -------------------------------------------------------
   if (ticket < (uint32_t)p.n_movers) {
-    const int32_t per_shard = p.rb_per_shard * p.moves_per_rb;
-    const int32_t n_remote = (p.world - 1) * per_shard;
     for (;;) {
       const uint32_t i = wg_claim(&h->head[0], h, &slots);
       if (i >= (uint32_t)p.n_move) break;
-      const uint64_t t0 = tr.now();
-      int shard, rem;
-      const char* src_shard;
-      if ((int32_t)i < n_remote) {
-        const int q = 1 + (int)i / per_shard;
-        rem = (int)i % per_shard;
-        shard = (p.rank + q) % p.world;
-        src_shard = p.peers[shard];
-      } else {
-        rem = (int)i - n_remote;
-        shard = p.rank;
-        src_shard = p.a_local;
-      }
-      const int rb = rem / p.moves_per_rb;
-      const int64_t row = (int64_t)rb * BM + (int64_t)(rem % p.moves_per_rb) * p.rows_per_move;
-      wg_copy_dev(p.gathered + ((int64_t)shard * p.m_local + row) * RB, src_shard + row * RB,
-                  (size_t)p.rows_per_move * RB);
-      if constexpr (S::MX)
-        copy_scale_rows(p.sc_gathered + ((int64_t)shard * p.m_local + row) * 2,
-                        (shard == p.rank ? p.sc_local : p.sc_peers[shard]) + row * 2, p.rows_per_move, K / 64,
-                        (int64_t)p.world * p.m_local * 2, (int64_t)p.m_local * 2);
-      wg_publish(&p.ready[shard * p.rb_per_shard + rb], 1u);
-      tr.put(KOS_TR_MOVE, i, t0);
+      do_move(i);
     }
     if (!p.movers_switch) {
       tr.finish(ticket);
@@ -155,14 +150,23 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
   // ---- builder role -----------------------------------------------------
   if (p.do_build) {
     f32x16 acc[S::TM][S::TN];
-    const int32_t per_q = p.rb_per_shard * p.tiles_n;
     for (;;) {
+      if (p.builders_move) {   // two-way: while move entries are left, take one between tiles
+        __syncthreads();
+        if (threadIdx.x == 0) slots.aux[0] = ld_relaxed(&h->head[0]) < (uint32_t)p.n_move;
+        __syncthreads();
+        if (slots.aux[0]) {
+          const uint32_t i = wg_claim(&h->head[0], h, &slots);
+          if (i < (uint32_t)p.n_move) {
+            do_move(i);
+            continue;
+          }
+        }
+      }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
       if (j >= (uint32_t)p.n_tiles) break;
-      const int q = (int)j / per_q;
-      const int rem = (int)j % per_q;
-      const int rb = rem / p.tiles_n, nt = rem % p.tiles_n;
-      const int shard = (p.rank + q) % p.world;
+      const AgTile tile = ag_tile_of((int)j, p.world, p.rank, p.rb_per_shard, p.tiles_n);
+      const int q = tile.q, rb = tile.rb, nt = tile.nt, shard = tile.shard;
       uint64_t t0 = tr.now();
       if (q == 0) {
         build_tile<S, false>(acc, p, p.a_local + (int64_t)rb * BM * RB, p.sc_local + (int64_t)rb * BM * 2,
@@ -450,8 +454,12 @@ static kos_status ag_gemm_run(const AgCall& a) {
   }
   if (o.n_movers < 1 || o.n_movers >= grid)
     return fail(KOS_ERR_ARG, "n_movers %d must be in [1, grid %d)", o.n_movers, grid);
-  p.n_movers = o.n_movers;
+  // FUSED: a mover without an entry turns builder at once, so a crew larger
+  // than the move entries only makes the first workgroups to arrive (the
+  // movers) reach the tiles last; start no more movers than there are moves
+  p.n_movers = o.mode == KOS_MODE_FUSED ? std::max(1, std::min(o.n_movers, p.n_move)) : o.n_movers;
   p.movers_switch = o.mode == KOS_MODE_FUSED;
+  p.builders_move = o.mode == KOS_MODE_FUSED && o.policy == KOS_POLICY_SWAPPED;
   p.do_build = 1;
   p.wait_flags = 1;
   return launch(p);

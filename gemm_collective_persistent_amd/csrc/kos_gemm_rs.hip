@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "kos_host.h"
+#include "kos_order.h"
 #include "kos_tile.h"
 #include "kos_tile_mx.h"
 
@@ -49,6 +50,7 @@ struct RsParams {
   int32_t n_reducers;       // tickets below this start as reducers
   int32_t builders_switch;  // builders become reducers when tiles run out
   int32_t do_build, do_reduce, wait_flags;
+  int32_t builders_reduce;  // two-way: builders take ready reduce entries between tiles
   uint32_t spin_limit;
   int32_t bands;            // mc / BM
   int32_t tiles_n;          // n / BN
@@ -134,27 +136,45 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
   const uint32_t ticket = wg_ticket(h, &slots);
   const bool starts_reducer = p.do_reduce && ticket < (uint32_t)p.n_reducers;
 
+  constexpr int SLABS = BM / kSlabRows;
+  const uint32_t n_red = (uint32_t)p.n_reduce * SLABS;
+  // one reduce entry (its tile is ready): a slab of our chunk's output
+  auto do_reduce = [&](uint32_t i, uint64_t t0) {
+    const RsReduce re = rs_reduce_of((int)i, p.tiles_n, SLABS);
+    reduce_entry<BN>(p, (int64_t)re.band * BM + re.slab * kSlabRows, re.col);
+    tr.put(KOS_TR_REDUCE, i, t0);
+  };
+
   // ---- builder role -----------------------------------------------------
   if (p.do_build && !starts_reducer) {
     f32x16 acc[S::TM][S::TN];
-    const int32_t per_band = p.world * p.tiles_n;  // band order: tiles of one band
-    const int32_t per_chunk = p.bands * p.tiles_n; // row order: tiles of one chunk
     for (;;) {
+      if (p.builders_reduce) {   // two-way: reduce while the reduce queue's head is ready
+        for (;;) {
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            uint32_t hd = ld_relaxed(&h->head[2]);
+            uint32_t got = kNoEntry;
+            if (hd < n_red) {
+              const RsReduce re = rs_reduce_of((int)hd, p.tiles_n, SLABS);
+              if (ld_relaxed(&p.ready[re.band * p.tiles_n + re.col]) >= 1u &&
+                  __hip_atomic_compare_exchange_strong(&h->head[2], &hd, hd + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT))
+                got = hd;
+            }
+            slots.claim = got;
+          }
+          __syncthreads();
+          const uint32_t got = slots.claim;
+          if (got == kNoEntry) break;
+          do_reduce(got, tr.now());
+        }
+      }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
       if (j >= (uint32_t)p.n_tiles) break;
       const uint64_t t0 = tr.now();
-      int band, chunk, col;
-      if (!p.row_order) {
-        band = (int)j / per_band;
-        const int rem = (int)j % per_band;
-        chunk = rem / p.tiles_n;
-        col = rem % p.tiles_n;
-      } else {
-        chunk = (int)j / per_chunk;
-        const int rem = (int)j % per_chunk;
-        band = rem / p.tiles_n;
-        col = rem % p.tiles_n;
-      }
+      const RsTile tile = rs_tile_of((int)j, p.row_order != 0, p.world, p.bands, p.tiles_n);
+      const int band = tile.band, chunk = tile.chunk, col = tile.col;
       const int64_t row0 = (int64_t)chunk * p.mc + (int64_t)band * BM;
       if constexpr (S::MX) {
         const MxSrc a{reinterpret_cast<const uint8_t*>(p.a) + row0 * K, p.a_sc + row0 * 2, K, 2 * (int64_t)p.m};
@@ -188,20 +208,17 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
 
   // ---- reducer role -----------------------------------------------------
   if (p.do_reduce) {
-    constexpr int SLABS = BM / kSlabRows;
     for (;;) {
       const uint32_t i = wg_claim(&h->head[2], h, &slots);
-      if (i >= (uint32_t)p.n_reduce * SLABS) break;
-      const int tile = (int)i / SLABS, slab = (int)i % SLABS;
-      const int band = tile / p.tiles_n, col = tile % p.tiles_n;
+      if (i >= n_red) break;
+      const RsReduce re = rs_reduce_of((int)i, p.tiles_n, SLABS);
       uint64_t t0 = tr.now();
       if (p.wait_flags) {
-        if (!wg_observe(&p.ready[tile], 1u, h, p.spin_limit, i, &slots)) break;
+        if (!wg_observe(&p.ready[re.band * p.tiles_n + re.col], 1u, h, p.spin_limit, i, &slots)) break;
         tr.put(KOS_TR_WAIT, i, t0);
         t0 = tr.now();
       }
-      reduce_entry<BN>(p, (int64_t)band * BM + slab * kSlabRows, col);
-      tr.put(KOS_TR_REDUCE, i, t0);
+      do_reduce(i, t0);
     }
   }
   tr.finish(ticket);
@@ -347,6 +364,7 @@ static kos_status gemm_rs_run(const RsCall& c) {
     return fail(KOS_ERR_ARG, "n_movers %d must be in [%d, grid %d)", o.n_movers, min_crew, grid);
   p.n_reducers = o.n_movers;
   p.builders_switch = o.mode == KOS_MODE_FUSED;
+  p.builders_reduce = o.mode == KOS_MODE_FUSED && o.policy == KOS_POLICY_SWAPPED;
   p.do_build = 1;
   p.do_reduce = 1;
   p.wait_flags = 1;

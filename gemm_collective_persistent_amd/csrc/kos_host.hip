@@ -57,7 +57,8 @@ kos_status resolve_opts(const kos_opts* in, const DeviceInfo& dev, const CrewDef
   if (o->mode < KOS_MODE_FUSED || o->mode > KOS_MODE_UNFUSED) return fail(KOS_ERR_ARG, "bad mode %d", o->mode);
   if (o->rs_order != KOS_RS_BAND && o->rs_order != KOS_RS_ROW) return fail(KOS_ERR_ARG, "bad rs_order %d", o->rs_order);
   if (o->peer_link != 0 && o->peer_link != 1) return fail(KOS_ERR_ARG, "bad peer_link %d", o->peer_link);
-  if (o->reserved) return fail(KOS_ERR_ARG, "reserved field must be 0");
+  if (o->policy != KOS_POLICY_DEFAULT && o->policy != KOS_POLICY_SWAPPED)
+    return fail(KOS_ERR_ARG, "bad policy %d", o->policy);
   if (o->trace && o->grid > KOS_TRACE_MAX_WG)
     return fail(KOS_ERR_ARG, "tracing holds at most %d workgroups", KOS_TRACE_MAX_WG);
   if (o->grid == 0) o->grid = dev.cus;

@@ -29,6 +29,25 @@ __device__ __forceinline__ void wave_copy_row(void* __restrict__ dst, const void
   }
 }
 
+// Same, storing with device-scope stores (rows read later in the same
+// launch by other workgroups): dst is wave-uniform, below 2 GiB of rows.
+__device__ __forceinline__ void wave_copy_row_dev_dst(void* __restrict__ dst, const void* __restrict__ src, int bytes) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  const DevBuf d(dst);
+  const int lane = threadIdx.x & 63;
+  const int n = bytes >> 4;
+  constexpr int U = 16;
+  for (int b = lane; b < n; b += U * 64) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u * 64 < n) v[u] = __builtin_nontemporal_load(&s[b + u * 64]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u * 64 < n) d.st128((uint32_t)(b + u * 64) * 16u, v[u]);
+  }
+}
+
 // Same, reading the source with device-scope loads (rows written by other
 // workgroups of the same launch): src_off is the row's byte offset in `src`
 // (wave-uniform; offsets below 2 GiB).  Up to 16 loads per lane in flight.

@@ -111,8 +111,23 @@ typedef struct kos_opts {
                            work in the workspace's trace region (read it with
                            kos_workspace_trace).  Adds a few stores per entry;
                            leave it off for timed runs.                        */
-  int32_t reserved;     /* must be 0                                            */
+  int32_t policy;       /* kos_policy: how roles switch under FUSED             */
 } kos_opts;
+
+/* Role-switching policy under KOS_MODE_FUSED [explainer, "KOSMOS removes
+ * the manager": one-way switching in the all-gather and reduce-scatter
+ * kernels, two-way in the expert combine; "How do the policies compare?"].
+ *   DEFAULT  the pages' choice per op: kos_ag_gemm one-way (movers become
+ *            builders), kos_gemm_rs one-way (builders become reducers),
+ *            kos_moe_combine and kos_moe_layer two-way (push a ready result,
+ *            else build a tile).
+ *   SWAPPED  the other choice, for the policy comparison: kos_ag_gemm and
+ *            kos_gemm_rs two-way (between tiles a builder takes a move entry
+ *            while any is left / the reduce queue's head when it is ready),
+ *            kos_moe_combine one-way (builders push only once the tiles run
+ *            out).  kos_moe_dispatch has no compute role: ignored there;
+ *            kos_moe_layer: KOS_ERR_UNSUPPORTED. */
+typedef enum kos_policy { KOS_POLICY_DEFAULT = 0, KOS_POLICY_SWAPPED = 1 } kos_policy;
 
 /* Timeline of one traced call (kos_opts.trace).  The trace region holds
  * KOS_TRACE_LAUNCHES slots, one per kernel launch of the call (a fused call
@@ -465,6 +480,39 @@ kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
                            void* h, void* y_grouped, void* const* out_return,
                            const int64_t* return_caps, void* y,
                            const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole expert layer, forward direction, in ONE persistent launch:
+ * router -> permutation -> token movement -> grouped SwiGLU expert GEMMs ->
+ * results pushed back -> weighted fold [abstract: KOSMOS runs the whole
+ * expert layer, routing through the final weighted sum, in one launch per
+ * direction; explainer, "KOSMOS removes the manager"].
+ *
+ * Computes exactly what kos_moe_dispatch followed by kos_moe_combine
+ * computes, with the same arguments and outputs (see both): the launch
+ * boundary between them is replaced by ready counters -- the grouped
+ * SwiGLU tiles of a unit (256 grouped rows of one expert) start as soon as
+ * the unit's rows have landed, while other workgroups still move tokens.
+ *
+ * Inputs: x, logits, peer_send, peer_counts (as kos_moe_dispatch); w_gate,
+ * w_up, w_down, peer_return (as kos_moe_combine).  Outputs: topk_idx,
+ * topk_w, counts, perm, out_send (with send_caps), x_grouped (grouped_cap
+ * rows), grouped_offsets, row_src (as kos_moe_dispatch); h, y_grouped (at
+ * least grouped_cap rows), out_return (with return_caps), y (as
+ * kos_moe_combine).  Shapes and errors: those of both calls (H % 128 == 0,
+ * F % 64 == 0; capacities -> KOS_ERR_CAPACITY from kos_workspace_status,
+ * nothing written past a buffer).  opts->mode must be KOS_MODE_FUSED
+ * (KOS_ERR_UNSUPPORTED otherwise): the two calls are the baseline.
+ */
+kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* logits,
+                         const void* const* peer_send, const int32_t* peer_counts,
+                         const void* w_gate, const void* w_up, const void* w_down,
+                         const void* const* peer_return,
+                         int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* perm,
+                         void* const* out_send, const int64_t* send_caps,
+                         void* x_grouped, int64_t grouped_cap, int32_t* grouped_offsets, int32_t* row_src,
+                         void* h, void* y_grouped, void* const* out_return, const int64_t* return_caps,
+                         void* y, const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }
