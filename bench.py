@@ -276,6 +276,46 @@ def measured_traffic(op: str, workload: str):
         return None
 
 
+def _summary(path: str) -> dict:
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#")):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def measured_counters():
+    """What the committed rocprofv3 summaries of the current kernel sources
+    say: per kernel the matrix cores' busy share and the counted bf16 FLOPs
+    over the algorithmic ones (``*_mfma.txt``), and per communication-only
+    launch of the unfused baselines the bytes moved per second against the
+    HBM peak (``*_rates.txt``).  Summaries taken on other kernel sources are
+    left out."""
+    import glob
+    dig = source_digest()
+    out = {"mfma": {}, "unfused_comm_launches": {}}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_mfma.txt"))):
+        kv = _summary(path)
+        if kv.get("source_digest") != dig:
+            continue
+        base = os.path.basename(path)
+        op = next((o for o in ("ag_gemm", "gemm_rs", "moe_dispatch", "moe_combine", "moe_layer")
+                   if base.startswith(o + "_")), base)
+        out["mfma"][op] = {"busy_fraction": float(kv["mfma_busy_fraction"]),
+                           "counted_over_algorithmic_flops": float(kv["counted_over_algorithmic"]),
+                           "clock_mhz_counter_run": float(kv["clock_mhz"]), "file": os.path.basename(path)}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_rates.txt"))):
+        kv = _summary(path)
+        if kv.get("source_digest") != dig:
+            continue
+        out["unfused_comm_launches"][os.path.basename(path)[:-len("_rates.txt")]] = {
+            "gb_s": float(kv["algorithmic_gb_s"]), "frac_hbm_peak": float(kv["fraction_of_hbm_peak_8tb_s"]),
+            "duration_us": float(kv["duration_us"])}
+    return out
+
+
 def copy_calibration(torch):
     """Three plain elementwise passes over 1 GiB of bf16 (dst = -src: 1 GiB
     read, 1 GiB written, 16-byte vector accesses like the kernels'): the
@@ -757,6 +797,7 @@ def main():
     for n in names:
         per_op[n]["clock_mhz"] = clocks[n]
     extra = {"per_op": per_op, "moe_tokens_per_s": round(moe_tok_s, 1), "moe_grouped_rows": rows,
+             "counters": measured_counters(),
              "wall_ms_per_step": round(wall, 3), "caches_flushed": not args.no_flush,
              "source_digest": source_digest()}
     if args.copy_calibration:

@@ -109,14 +109,16 @@ def mfma(pmc_csv: str, trace_csv: str, kernel: str, op: str, workload: str, flop
     def per(counter):
         return [float(r["Counter_Value"]) for r in _readings(pmc_csv, counter) if kernel in r["Kernel_Name"]]
     busy, mops, gui = per("SQ_VALU_MFMA_BUSY_CYCLES"), per("SQ_INSTS_VALU_MFMA_MOPS_BF16"), per("GRBM_GUI_ACTIVE")
+    pdur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in _readings(pmc_csv, "GRBM_GUI_ACTIVE")
+            if kernel in r["Kernel_Name"]]
     dur = _durations(trace_csv, kernel)
-    if not busy or not mops or not gui or not dur:
+    if not busy or not mops or not gui or not dur or not pdur:
         raise SystemExit(f"kernel {kernel!r} not found in both runs")
-    b, m, g, d = (statistics.median(x) for x in (busy, mops, gui, dur))
+    b, m, g, d, pd = (statistics.median(x) for x in (busy, mops, gui, dur, pdur))
     # GRBM_GUI_ACTIVE counts GPU-busy cycles; summed over the 8 XCDs it reads
-    # 8x the clock times the duration
-    xcds = 8 if g / d > 3.5 else 1
-    clk_mhz = g / xcds / d * 1e3
+    # 8x the clock times the duration (the counter run's own duration)
+    xcds = 8 if g / pd > 3.5 else 1
+    clk_mhz = g / xcds / pd * 1e3
     simds = 256 * 4
     util = b / (g / xcds * simds)
     mflops = m * 512
@@ -126,7 +128,7 @@ def mfma(pmc_csv: str, trace_csv: str, kernel: str, op: str, workload: str, flop
         f"command_trace: {command.replace('--pmc PMC', '--kernel-trace')}",
         f"kernel: {kernel}",
         f"launches: {len(busy)} (pmc run), {len(dur)} (trace run); medians below",
-        f"duration_us: {d / 1e3:.1f}",
+        f"duration_us: {d / 1e3:.1f} (trace run); {pd / 1e3:.1f} (counter run)",
         f"grbm_gui_active_cycles: {g:.0f} (summed over {xcds} XCDs)",
         f"clock_mhz: {clk_mhz:.0f}",
         f"mfma_busy_simd_cycles: {b:.0f}",
@@ -140,7 +142,7 @@ def mfma(pmc_csv: str, trace_csv: str, kernel: str, op: str, workload: str, flop
 
 
 def rates(fetch_csv: str, write_csv: str, trace_csv: str, kernel: str, launches: int, which: int, label: str,
-          nbytes: float, command: str) -> str:
+          nbytes: float, digest: str, command: str) -> str:
     fr, wr = _readings(fetch_csv, "FETCH_SIZE"), _readings(write_csv, "WRITE_SIZE")
 
     def calib(rows):
@@ -172,6 +174,7 @@ def rates(fetch_csv: str, write_csv: str, trace_csv: str, kernel: str, launches:
         f"algorithmic_bytes: {nbytes:.0f}",
         f"algorithmic_gb_s: {nbytes / (d * 1e-9) / 1e9:.1f}",
         f"fraction_of_hbm_peak_8tb_s: {nbytes / (d * 1e-9) / 8e12:.3f}",
+        f"source_digest: {digest}",
     ]) + "\n"
 
 
@@ -197,7 +200,7 @@ def main(argv=None):
     r.add_argument("fetch_csv")
     r.add_argument("write_csv")
     r.add_argument("trace_csv")
-    for k in ("kernel", "label", "command", "out"):
+    for k in ("kernel", "label", "digest", "command", "out"):
         r.add_argument(f"--{k}", required=True)
     r.add_argument("--launches", type=int, required=True)
     r.add_argument("--which", type=int, required=True)
@@ -211,7 +214,7 @@ def main(argv=None):
         text = mfma(a.pmc_csv, a.trace_csv, a.kernel, a.op, a.workload, a.flops, a.digest, a.command)
     else:
         text = rates(a.fetch_csv, a.write_csv, a.trace_csv, a.kernel, a.launches, a.which, a.label, a.bytes,
-                     a.command)
+                     a.digest, a.command)
     with open(a.out, "w") as f:
         f.write(text)
     sys.stdout.write(text)
