@@ -18,7 +18,12 @@ order the pages describe them:
   token's row goes to the rank owning its expert and the result comes back
   [same paragraph; KOSMOS arXiv abstract];
 * the same two TP+SP collectives with MXFP8 operands [KOSMOS arXiv abstract],
-  the format taken from the OCP Microscaling specification v1.0.
+  the format taken from the OCP Microscaling specification v1.0;
+* the expert layer's backward direction [KOSMOS arXiv abstract, one launch
+  per direction]: the chain rule of the forward definition, written out
+  step by step (gradients of the pairs dispatched like the tokens, the
+  experts' data gradient, the results pushed back and summed, the router
+  gradient through the softmax over the selected logits).
 
 Arithmetic is float64 (NumPy/BLAS), which is exact for every integer-valued
 case and more accurate than the kernels' fp32 accumulation otherwise.  bf16
@@ -35,6 +40,9 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``expert_ffn`` is pinned only to a float64 brute-force loop and to closed-form
 special cases (there is no printed example), which fixes its definition but
 not a value from the pages.
+The backward functions are pinned in ``tests/test_oracle_bwd_pins.py`` by
+central finite differences of an unrounded forward written out there, and
+by special cases and the softmax invariant.
 """
 from __future__ import annotations
 
@@ -434,3 +442,182 @@ def moe_layer(x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return,
              pc, peer_return, world, rank)
     d.update(y_grouped=yg, out_return=out_return, y=y)
     return d
+
+
+# ---------------------------------------------------------------------------
+# expert layer, backward direction: the gradient of the layer's output with
+# respect to its input tokens and router logits [KOSMOS arXiv abstract: one
+# launch per direction of the expert layer]
+# ---------------------------------------------------------------------------
+#
+# The pages give no formula for the backward pass; it is the chain rule of
+# the forward definition above, read this way.  With dy = dL/dy (bf16 [T,H])
+# and y[t] = sum_j w[t,j] * res[t,j]:
+#   * each pair's output gradient dres[t,j] = w[t,j] * dy[t] travels to the
+#     rank of expert idx[t,j] as a bf16 row, in the forward's packed order;
+#   * the expert recomputes g = X.Wg and u = X.Wu from its forward input rows
+#     (only the grouped inputs are kept from the forward), then
+#     dH = dres . Wd^T, dU = dH * silu(g), dG = dH * u * silu'(g) (the
+#     forward's bf16 rounding of h passes the gradient unchanged), each
+#     rounded to bf16, and dX = dG . Wg^T + dU . Wu^T, rounded to bf16;
+#   * dX rows travel back to their source rank, which sums them:
+#     dx[t] = bf16(sum_j dX[t,j]) (the weight is already in dres);
+#   * the router gradient: dw[t,j] = <dy[t], res[t,j]> and, through the
+#     softmax over the k selected logits,
+#     dlogits[t, idx[t,j]] = w[t,j] * (dw[t,j] - sum_i w[t,i] * dw[t,i]),
+#     zero for the experts not selected.
+# Weight gradients are plain grouped GEMMs with no collective and are not
+# part of this path.  ``rounded=False`` keeps every intermediate in float64
+# (for the finite-difference pins).
+
+
+def dsilu(z: np.ndarray) -> np.ndarray:
+    """d silu(z) / dz = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _val(a, rounded):
+    return bf16_to_f64(a) if rounded else np.asarray(a, dtype=np.float64)
+
+
+def expert_ffn_bwd(x_bits, dy_rows, wg_bits, wu_bits, wd_bits, rounded: bool = True):
+    """Data gradient of the SwiGLU expert for rows X (bf16 [n,H]) and output
+    gradients dY ([n,H]: bf16 bits, or float64 when not rounded): returns
+    (dG, dU, dX) -- [n,F], [n,F], [n,H], bf16 bits when `rounded`."""
+    x = bf16_to_f64(x_bits)
+    wg, wu, wd = bf16_to_f64(wg_bits), bf16_to_f64(wu_bits), bf16_to_f64(wd_bits)
+    dy = _val(dy_rows, rounded)
+    g = x @ wg
+    u = x @ wu
+    dh = dy @ wd.T
+    du = dh * silu(g)
+    dg = dh * u * dsilu(g)
+    if rounded:
+        du, dg = round_bf16(du), round_bf16(dg)
+        dx = round_bf16(bf16_to_f64(dg) @ wg.T + bf16_to_f64(du) @ wu.T)
+    else:
+        dx = dg @ wg.T + du @ wu.T
+    return dg, du, dx
+
+
+def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world: int, rank: int,
+                  rounded: bool = True):
+    """The pairs' output gradients, placed like the forward dispatch places
+    the token rows: dres at packed position perm[t*k+j] is w[t,j] * dy[t]
+    (bf16); returns dict(send: rows for each destination d != rank in our
+    packed order, grouped: the rows of our local experts -- expert-major,
+    then source rank, then the source's packed order, the peers' rows taken
+    from ``peer_send_grad``)."""
+    dy = bf16_to_f64(dy_bits)
+    w = np.asarray(w, dtype=np.float64)
+    T, k = w.shape
+    E = len(offsets) - 1
+    el = E // world
+    token_of = np.empty(T * k, dtype=np.int64)
+    slot_of = np.empty(T * k, dtype=np.int64)
+    token_of[np.asarray(perm)] = np.arange(T * k) // k
+    slot_of[np.asarray(perm)] = np.arange(T * k) % k
+    packed = w[token_of, slot_of][:, None] * dy[token_of]
+    if rounded:
+        packed = round_bf16(packed)
+    so = send_offsets(offsets, world, el)
+    send = [None if d == rank else packed[so[d]:so[d + 1]] for d in range(world)]
+    pc = np.asarray(peer_counts, dtype=np.int64)
+    rows = []
+    for e in range(el):
+        ge = rank * el + e
+        for p in range(world):
+            if p == rank:
+                rows.append(packed[offsets[ge]:offsets[ge + 1]])
+            else:
+                lo, n = int(pc[p, :e].sum()), int(pc[p, e])
+                rows.append(np.asarray(peer_send_grad[p])[lo:lo + n])
+    H = dy.shape[1]
+    grouped = np.concatenate(rows, axis=0) if rows else np.zeros((0, H), packed.dtype)
+    return dict(send=send, grouped=grouped)
+
+
+def router_grad(dy_bits, idx, w, perm, offsets, y_grouped, grouped_offsets, peer_counts, peer_return,
+                world: int, rank: int, tokens=None):
+    """dlogits [len(tokens), E] (float64): through the softmax over the k
+    selected logits; res[t,j] is the forward result (our expert's output row
+    when the expert is local, else the row its rank returned)."""
+    dy = bf16_to_f64(dy_bits)
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    E = len(offsets) - 1
+    el = E // world
+    so = send_offsets(offsets, world, el)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    out = np.zeros((len(toks), E))
+    for n, t in enumerate(toks):
+        dw = np.zeros(k)
+        for j in range(k):
+            e = int(idx[t, j])
+            d = e // el
+            pos = int(perm[t * k + j])
+            if d == rank:
+                res = bf16_to_f64(y_grouped[local_row(e, pos, rank, el, offsets, grouped_offsets, peer_counts)])
+            else:
+                res = bf16_to_f64(peer_return[d][pos - so[d]])
+            dw[j] = float(dy[t] @ res)
+        wt = np.asarray(w[t], dtype=np.float64)
+        out[n, idx[t]] = wt * (dw - float(wt @ dw))
+    return out
+
+
+def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return,
+                  peer_send_grad, peer_return_grad, world: int, rank: int, k: int, rounded: bool = True):
+    """The whole expert layer's backward direction for one rank: the forward
+    routing and expert outputs (``moe_layer``), the pairs' gradients
+    dispatched, the experts' data gradients, the results pushed back and
+    summed per token, and the router gradient.  Returns a dict with the
+    forward's fields and send_grad, grouped_grad, dg, du, dx_grouped,
+    out_return_grad, dx, dlogits."""
+    f = moe_layer(x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return, world, rank, k)
+    g = dispatch_grad(dy_bits, f["w"], f["perm"], f["offsets"], peer_send_grad, peer_counts, world, rank,
+                      rounded)
+    go = f["grouped_offsets"]
+    n, H = f["grouped"].shape
+    F = np.asarray(wg).shape[2]
+    dt = np.uint16 if rounded else np.float64
+    dg, du, dxg = np.zeros((n, F), dt), np.zeros((n, F), dt), np.zeros((n, H), dt)
+    for e in range(len(go) - 1):
+        lo, hi = int(go[e]), int(go[e + 1])
+        if hi > lo:
+            dg[lo:hi], du[lo:hi], dxg[lo:hi] = expert_ffn_bwd(f["grouped"][lo:hi], g["grouped"][lo:hi], wg[e],
+                                                              wu[e], wd[e], rounded)
+    pc = np.asarray(peer_counts)
+    out_return = push(dxg, f["row_src"], world, rank, pc.sum(axis=1)) if rounded else None
+    ones = np.ones_like(np.asarray(f["w"], dtype=np.float32))
+    if rounded:
+        dx = fold(f["idx"], ones, f["perm"], f["offsets"], dxg, go, pc, peer_return_grad, world, rank)
+    else:
+        dx = _sum_pairs(f, dxg, go, pc, peer_return_grad, world, rank)
+    dl = router_grad(dy_bits, f["idx"], f["w"], f["perm"], f["offsets"], f["y_grouped"], go, pc, peer_return,
+                     world, rank)
+    f.update(send_grad=g["send"], grouped_grad=g["grouped"], dg=dg, du=du, dx_grouped=dxg,
+             out_return_grad=out_return, dx=dx, dlogits=dl)
+    return f
+
+
+def _sum_pairs(f, dxg, go, pc, peer_return_grad, world, rank):
+    """float64 sum over each token's pairs of their data gradients (the
+    unrounded fold)."""
+    idx = f["idx"]
+    T, k = idx.shape
+    E = len(f["offsets"]) - 1
+    el = E // world
+    so = send_offsets(f["offsets"], world, el)
+    out = np.zeros((T, dxg.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            d = e // el
+            pos = int(f["perm"][t * k + j])
+            if d == rank:
+                out[t] += dxg[local_row(e, pos, rank, el, f["offsets"], go, pc)]
+            else:
+                out[t] += np.asarray(peer_return_grad[d][pos - so[d]], dtype=np.float64)
+    return out
