@@ -28,6 +28,7 @@ EXPORTS = [
     "kos_last_error", "kos_device_cu_count", "kos_ag_gemm", "kos_gemm_rs",
     "kos_ag_gemm_mx", "kos_gemm_rs_mx", "kos_ag_gemm_wt", "kos_gemm_rs_wt",
     "kos_moe_dispatch", "kos_moe_combine", "kos_workspace_trace", "kos_ag_gemm_noalloc", "kos_moe_layer",
+    "kos_moe_layer_bwd",
 ]
 
 
@@ -101,6 +102,9 @@ def _load():
                                     P, c_int64, P, P, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_combine": (c_int32, [POINTER(MoeShape), P, P, P, c_int64, P, P, P, P, P, P, P, P,
                                       PP, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
+        "kos_moe_layer_bwd": (c_int32, [POINTER(MoeShape), P, P, P, P, P, P, P, c_int64, P, P, P, PP, P, P, P,
+                                        PP, PP, POINTER(c_int64), P, P, P, P, PP, PP, POINTER(c_int64), P, P,
+                                        POINTER(Opts), P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name, None)

@@ -388,3 +388,59 @@ def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_do
                             _p(w_down), arr["pr"], _p(topk_idx), _p(topk_w), _p(counts), _p(perm), arr["os"], scaps,
                             _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(h), _p(y_grouped), arr["or"],
                             rcaps, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, x_grouped, grouped_offsets,
+                  row_src, y_grouped, peer_return, w_gate, w_up, w_down, peer_send_grad, out_send_grad,
+                  dres_grouped, dg, du, dx_grouped, peer_return_grad, out_return_grad, dx, dlogits,
+                  ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+    """kos_moe_layer_bwd: the expert layer's data and router gradients in one
+    launch (see include/kos.h).  The forward's routing and grouped buffers
+    come in unchanged; grouped_cap is x_grouped's row count, and each
+    out_send_grad[d] / out_return_grad[p] buffer's row count is its
+    capacity."""
+    T, H, E, R, F = s.tokens, s.hidden, s.experts, s.world, s.ffn
+    E_loc = E // R
+    for name, lst in (("peer_return", peer_return), ("peer_send_grad", peer_send_grad),
+                      ("out_send_grad", out_send_grad), ("peer_return_grad", peer_return_grad),
+                      ("out_return_grad", out_return_grad)):
+        if len(lst) != R:
+            raise ValueError(f"{name} needs one entry per rank")
+    if T > 0:
+        _need(dy, torch.bfloat16, "dy", 2, (T, H))
+        _need(dx, torch.bfloat16, "dx", 2, (T, H))
+        _need(dlogits, torch.float32, "dlogits", 2, (T, E))
+    _need(peer_counts, torch.int32, "peer_counts", 2, (R, E_loc))
+    _check_tokens(s, topk_idx, topk_w, perm, counts)
+    _need(w_gate, torch.bfloat16, "w_gate", 3, (E_loc, H, F))
+    _need(w_up, torch.bfloat16, "w_up", 3, (E_loc, H, F))
+    _need(w_down, torch.bfloat16, "w_down", 3, (E_loc, F, H))
+    _need(x_grouped, torch.bfloat16, "x_grouped", 2, (None, H))
+    cap = x_grouped.shape[0]
+    _need(grouped_offsets, torch.int32, "grouped_offsets", 1, (E_loc + 1,))
+    _need(row_src, torch.int32, "row_src", 2, (None, 2))
+    _min_rows(row_src, cap, "row_src")
+    for name, t, width in (("y_grouped", y_grouped, H), ("dres_grouped", dres_grouped, H), ("dg", dg, F),
+                           ("du", du, F), ("dx_grouped", dx_grouped, H)):
+        _need(t, torch.bfloat16, name, 2, (None, width))
+        _min_rows(t, cap, name)
+    lists = (("peer_return", peer_return, True), ("peer_send_grad", peer_send_grad, True),
+             ("out_send_grad", out_send_grad, False), ("peer_return_grad", peer_return_grad, True),
+             ("out_return_grad", out_return_grad, False))
+    for p in range(R):
+        if p == s.rank:
+            continue
+        for name, lst, host_ok in lists:
+            if lst[p] is not None:
+                _need(lst[p], torch.bfloat16, f"{name}[{p}]", 2, (None, H), host_ok=host_ok)
+    arr = {n: ptr_array([None if p == s.rank else _p(t) for p, t in enumerate(lst)]) for n, lst, _ in lists}
+    scaps = (ctypes.c_int64 * R)(*[0 if p == s.rank or t is None else t.shape[0] for p, t in enumerate(out_send_grad)])
+    rcaps = (ctypes.c_int64 * R)(*[0 if p == s.rank or t is None else t.shape[0]
+                                   for p, t in enumerate(out_return_grad)])
+    o = o if o is not None else make_opts()
+    check(lib.kos_moe_layer_bwd(ctypes.byref(s), _p(dy), _p(topk_idx), _p(topk_w), _p(perm), _p(counts),
+                                _p(peer_counts), _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(y_grouped),
+                                arr["peer_return"], _p(w_gate), _p(w_up), _p(w_down), arr["peer_send_grad"],
+                                arr["out_send_grad"], scaps, _p(dres_grouped), _p(dg), _p(du), _p(dx_grouped),
+                                arr["peer_return_grad"], arr["out_return_grad"], rcaps, _p(dx), _p(dlogits),
+                                ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))

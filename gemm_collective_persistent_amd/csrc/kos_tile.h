@@ -148,9 +148,11 @@ struct BLayout {
 // A rows and of its B matrix, and per-lane byte offsets; every stage adds
 // k0*2 (A) or k0*ldb*2 (B) as a scalar offset.  Offsets stay below 2^31
 // (the entry points check the operand extents).
-template <class S, bool DUAL, bool COH_A = false>
+template <class S, bool DUAL, bool COH_A = false, bool SPLIT = false>
 struct LoadPlan {
   __amdgpu_buffer_rsrc_t ra, rb;
+  __amdgpu_buffer_rsrc_t ra2, rb2;             // SPLIT: the second A and B matrices, for k >= k1
+  int k1;
   uint32_t a_off[S::A_LOADS];
   uint32_t b_off[S::B_LOADS];
   int b_stride;                                // bytes per k row of B
@@ -165,8 +167,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
 
 // A rows are clamped to m_valid-1: rows past the valid ones only feed
 // accumulator rows that are never stored.
-template <class S, bool DUAL, bool COH_A>
-__device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const uint16_t* __restrict__ A, int64_t lda,
+template <class S, bool DUAL, bool COH_A, bool SPLIT>
+__device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A, SPLIT>& P, const uint16_t* __restrict__ A, int64_t lda,
                                            int m_valid, const BSrc& b, const WaveCtx& w) {
   using L = BLayout<S, DUAL>;
   const int lane = w.lane, wave = w.wave;
@@ -214,18 +216,23 @@ __device__ __forceinline__ void plan_loads(LoadPlan<S, DUAL, COH_A>& P, const ui
 constexpr int kCpolDevice = 16;
 
 // Issues this wave's direct loads (buffer -> LDS) of the stage at k0.
-template <class S, bool DUAL, bool COH_A>
-__device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A>& P, int k0) {
-  const int soa = k0 * 2;
-  const int sob = S::BNT ? k0 * 2 : k0 * P.b_stride;
+// SPLIT: stages at k0 >= k1 come from the second matrices, at k0 - k1.
+template <class S, bool DUAL, bool COH_A, bool SPLIT>
+__device__ __forceinline__ void stage_load(char* lds_stage, const LoadPlan<S, DUAL, COH_A, SPLIT>& P, int k0) {
+  const bool second = SPLIT && k0 >= P.k1;
+  const int ka = second ? k0 - P.k1 : k0;
+  const __amdgpu_buffer_rsrc_t ra = second ? P.ra2 : P.ra;
+  const __amdgpu_buffer_rsrc_t rb = second ? P.rb2 : P.rb;
+  const int soa = ka * 2;
+  const int sob = S::BNT ? ka * 2 : ka * P.b_stride;
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i)
     if (!S::A_HALF || P.a_on)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(P.ra, (lds_void*)(lds_stage + P.a_lds + i * S::A_WAVE_BYTES), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lds_stage + P.a_lds + i * S::A_WAVE_BYTES), 16,
                                                P.a_off[i], soa, 0, COH_A ? kCpolDevice : 0);
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(P.rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i], sob,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(lds_stage + P.b_lds + i * 1024), 16, P.b_off[i], sob,
                                              0, 0);
 }
 
@@ -341,9 +348,10 @@ __device__ __forceinline__ void sched_interleave() {
 // (kt+1, step 0).  `steady`: the look-ahead load is always issued (past the
 // end it re-reads the last stage: cache hits, never used), so the counts in
 // flight stay uniform and the loop body has no branches.
-template <class S, bool DUAL, bool COH_A, bool steady>
+template <class S, bool DUAL, bool COH_A, bool steady, bool SPLIT>
 __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0, Frags<S>& f1, int kt, int nk,
-                                       const LoadPlan<S, DUAL, COH_A>& P, char* cur, char* nxt, const WaveCtx& w) {
+                                       const LoadPlan<S, DUAL, COH_A, SPLIT>& P, char* cur, char* nxt,
+                                       const WaveCtx& w) {
 #if defined(__HIP_DEVICE_COMPILE__)   // device code only (the host pass never emits it)
   constexpr int ST = S::STAGES;
   constexpr int NM = S::TM * S::TN, ND = S::TM + (S::BNT ? 1 : 2) * S::TN;
@@ -359,12 +367,12 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
   }
   lds_barrier();
   if (steady) {
-    stage_load<S, DUAL, COH_A>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
+    stage_load<S, DUAL, COH_A, SPLIT>(cur, P, (kt + ST < nk ? kt + ST : nk - 1) * S::BK);
     frag_load<S, DUAL>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
     sched_interleave<NM, ND, S::LOADS>();
   } else {
-    if (kt + ST < nk) stage_load<S, DUAL, COH_A>(cur, P, (kt + ST) * S::BK);
+    if (kt + ST < nk) stage_load<S, DUAL, COH_A, SPLIT>(cur, P, (kt + ST) * S::BK);
     if (kt + 1 < nk) frag_load<S, DUAL>(f0, nxt, 0, w);
     frag_mfma<S>(acc, f1);
   }
@@ -374,9 +382,13 @@ __device__ __forceinline__ void k_iter(f32x16 (&acc)[S::TM][S::TN], Frags<S>& f0
 // Full K loop: acc = A[0:m_valid rows] . B over k in [0, K) (K a multiple of
 // 32).  Begins and ends with the LDS ring free.  RING: stage size of the
 // ring (at least the tile's; a kernel with two tile shapes passes the larger).
-template <class S, bool DUAL = false, bool COH_A = false, int RING = S::STAGE_BYTES>
+// SPLIT: the sum of two products over one K loop, acc = A[:, 0:K1] . B +
+// A2[:, 0:K-K1] . B2 (same strides; K1 a multiple of 32; B2 the second
+// matrix's first element as b.p0 is the first's).
+template <class S, bool DUAL = false, bool COH_A = false, int RING = S::STAGE_BYTES, bool SPLIT = false>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const uint16_t* __restrict__ A,
-                                              int64_t lda, int m_valid, const BSrc& b, int K) {
+                                              int64_t lda, int m_valid, const BSrc& b, int K,
+                                              const uint16_t* A2 = nullptr, const uint16_t* B2 = nullptr, int K1 = 0) {
   constexpr int ST = S::STAGES;
   static_assert(ST == 4, "the ring is unrolled for four stages");
 #pragma unroll
@@ -387,8 +399,13 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / S::BK;
   const WaveCtx w = wave_ctx();
-  LoadPlan<S, DUAL, COH_A> P;
-  plan_loads<S, DUAL, COH_A>(P, A, lda, m_valid, b, w);
+  LoadPlan<S, DUAL, COH_A, SPLIT> P;
+  plan_loads<S, DUAL, COH_A, SPLIT>(P, A, lda, m_valid, b, w);
+  if (SPLIT) {
+    P.ra2 = raw_rsrc(A2);
+    P.rb2 = raw_rsrc(B2);
+    P.k1 = K1;
+  }
   static_assert(S::STAGE_BYTES <= RING, "tile stage larger than the ring");
   char* r0 = ring<RING, 0>();
   char* r1 = ring<RING, 1>();
@@ -397,28 +414,28 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   KOS_WAITCNT(0, 0);
   lds_barrier();   // the ring is free (previous user done)
   if (nk >= ST && nk % ST == 0) {
-    stage_load<S, DUAL, COH_A>(r0, P, 0);
-    stage_load<S, DUAL, COH_A>(r1, P, 1 * S::BK);
-    stage_load<S, DUAL, COH_A>(r2, P, 2 * S::BK);
-    stage_load<S, DUAL, COH_A>(r3, P, 3 * S::BK);
+    stage_load<S, DUAL, COH_A, SPLIT>(r0, P, 0);
+    stage_load<S, DUAL, COH_A, SPLIT>(r1, P, 1 * S::BK);
+    stage_load<S, DUAL, COH_A, SPLIT>(r2, P, 2 * S::BK);
+    stage_load<S, DUAL, COH_A, SPLIT>(r3, P, 3 * S::BK);
     KOS_WAITCNT(3 * S::LOADS, 0);
     lds_barrier();
     Frags<S> f0, f1;
     frag_load<S, DUAL>(f0, r0, 0, w);
     for (int kt = 0; kt < nk; kt += ST) {
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt, nk, P, r0, r1, w);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
-      k_iter<S, DUAL, COH_A, true>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
+      k_iter<S, DUAL, COH_A, true, SPLIT>(acc, f0, f1, kt, nk, P, r0, r1, w);
+      k_iter<S, DUAL, COH_A, true, SPLIT>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
+      k_iter<S, DUAL, COH_A, true, SPLIT>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
+      k_iter<S, DUAL, COH_A, true, SPLIT>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
     }
     KOS_WAITCNT(0, 0);
     lds_barrier();
     return;
   }
-  stage_load<S, DUAL, COH_A>(r0, P, 0);
-  if (1 < nk) stage_load<S, DUAL, COH_A>(r1, P, 1 * S::BK);
-  if (2 < nk) stage_load<S, DUAL, COH_A>(r2, P, 2 * S::BK);
-  if (3 < nk) stage_load<S, DUAL, COH_A>(r3, P, 3 * S::BK);
+  stage_load<S, DUAL, COH_A, SPLIT>(r0, P, 0);
+  if (1 < nk) stage_load<S, DUAL, COH_A, SPLIT>(r1, P, 1 * S::BK);
+  if (2 < nk) stage_load<S, DUAL, COH_A, SPLIT>(r2, P, 2 * S::BK);
+  if (3 < nk) stage_load<S, DUAL, COH_A, SPLIT>(r3, P, 3 * S::BK);
   // stage 0 landed; up to three later stages may still fly
   if (nk >= 4) {
     KOS_WAITCNT(3 * S::LOADS, 0);
@@ -429,10 +446,10 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[S::TM][S::TN], const
   Frags<S> f0, f1;
   frag_load<S, DUAL>(f0, r0, 0, w);
   for (int kt = 0; kt < nk; kt += ST) {
-    k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt, nk, P, r0, r1, w);
-    if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
-    if (kt + 2 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
-    if (kt + 3 < nk) k_iter<S, DUAL, COH_A, false>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
+    k_iter<S, DUAL, COH_A, false, SPLIT>(acc, f0, f1, kt, nk, P, r0, r1, w);
+    if (kt + 1 < nk) k_iter<S, DUAL, COH_A, false, SPLIT>(acc, f0, f1, kt + 1, nk, P, r1, r2, w);
+    if (kt + 2 < nk) k_iter<S, DUAL, COH_A, false, SPLIT>(acc, f0, f1, kt + 2, nk, P, r2, r3, w);
+    if (kt + 3 < nk) k_iter<S, DUAL, COH_A, false, SPLIT>(acc, f0, f1, kt + 3, nk, P, r3, r0, w);
   }
   KOS_WAITCNT(0, 0);
   lds_barrier();
@@ -486,14 +503,17 @@ __device__ __forceinline__ lds_char* ring_lds(int i) {
 // global writes are whole cache lines (what device-coherent write-through
 // stores need to be cheap).  SWIGLU: the tile holds gate and up columns
 // (BSrc dual layout) and the BN/2 output columns are swiglu(gate, up).
-// COH: device-scope (sc1) stores.  Call right after tile_mainloop (the ring
-// is free); the next tile_mainloop waits for the ring.  dst is the same in
-// every thread.
-template <class S, int RING, bool COH, bool SWIGLU = false>
+// HALF = 0 or 1: a dual-layout tile whose gate (0) or up (1) blocks are
+// stored as the BN/2 output columns.  COH: device-scope (sc1) stores.  Call
+// right after tile_mainloop (the ring is free); the next tile_mainloop waits
+// for the ring.  dst is the same in every thread.
+template <class S, int RING, bool COH, bool SWIGLU = false, int HALF = -1>
 __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst, int64_t ld,
                                                 int m_valid) {
-  constexpr int OW = SWIGLU ? S::BN / 2 : S::BN;   // output columns
-  constexpr int OJ = SWIGLU ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
+  constexpr bool DUAL_OUT = SWIGLU || HALF >= 0;
+  static_assert(!(SWIGLU && HALF >= 0) && HALF <= 1, "one dual output at a time");
+  constexpr int OW = DUAL_OUT ? S::BN / 2 : S::BN;   // output columns
+  constexpr int OJ = DUAL_OUT ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
   constexpr int ROW_BYTES = OW * 2;
   constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
   constexpr int ROWS_PER_RING = RING / ROW_BYTES;
@@ -521,7 +541,9 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
+          v[e] = SWIGLU      ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e])
+                 : HALF >= 0 ? acc[i][j + (HALF > 0 ? S::TN / 2 : 0)][4 * g + e]
+                             : acc[i][j][4 * g + e];
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col & 7) * 2) =
             pack4_bf16(v);
         // one 32x32 block at a time: keeps the accumulator reads from being

@@ -514,6 +514,74 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
                          void* h, void* y_grouped, void* const* out_return, const int64_t* return_caps,
                          void* y, const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The expert layer, backward direction (data and router gradients), in ONE
+ * persistent launch [abstract: one launch per direction of the whole expert
+ * layer].  The pages give no backward formulas; this is the chain rule of
+ * the forward above, with y[t] = sum_j w[t,j] * res[t,j]:
+ *   movers    each pair's output gradient dres = bf16(w[t,j] * dy[t]) goes
+ *             where the forward sent the token row: into dres_grouped for
+ *             our own experts, into out_send_grad[d] (our packed order)
+ *             for rank d's; the rows peers send us (peer_send_grad) are
+ *             pulled into dres_grouped (grouped order of the forward)
+ *   tiles 1   per unit (256 grouped rows of one expert), 128-row half and
+ *             128 columns of F: recompute g = X.Wg and u = X.Wu from the
+ *             forward's grouped input, dH = dres . Wd^T, then
+ *             dU = bf16(dH * silu(g)), dG = bf16(dH * u * silu'(g))
+ *             (the forward's bf16 rounding of h passes gradients unchanged)
+ *   tiles 2   per unit and 256 columns of H, once the unit's tiles 1 are
+ *             done: dX = bf16(dG . Wg^T + dU . Wu^T)
+ *   pushes    dX rows of rows a peer sent us, back to it (out_return_grad,
+ *             the peer's packed order); two-way with the tiles
+ *   fold      dx[t] = bf16(sum_j dX(t,j)) (fp32, j ascending; remote rows
+ *             from peer_return_grad) and the router gradient
+ *             dlogits[t, idx[t,j]] = w_j * (dw_j - sum_i w_i * dw_i),
+ *             dw_j = <dy[t], res[t,j]> (fp32; res the forward's results:
+ *             y_grouped rows or peer_return rows), 0 for other experts.
+ * Weight gradients are plain grouped GEMMs with no collective: not here.
+ *
+ * dy           bf16 [T, H]
+ * topk_idx, topk_w, perm, counts, peer_counts, x_grouped, grouped_offsets,
+ * row_src, y_grouped, peer_return: the forward's (kos_moe_layer, or
+ *              kos_moe_dispatch + kos_moe_combine), read only
+ * w_gate, w_up bf16 [E_loc, H, F];  w_down bf16 [E_loc, F, H]
+ * peer_send_grad  host array[world] of bf16 [rows p sent us, H] (entry
+ *              `rank` ignored): the gradients of the rows p sent us, in
+ *              the order p sent them
+ * out_send_grad   host array[world] of out bf16 [send_caps[d], H]: our
+ *              pairs' gradients for rank d, in our packed order
+ * dres_grouped out bf16 [grouped_cap, H];  dg, du: out bf16 [grouped_cap, F]
+ * dx_grouped   out bf16 [grouped_cap, H]
+ * peer_return_grad host array[world] of bf16 [>= rows we sent d, H]: the
+ *              dX rows d returns for the rows we sent it
+ * out_return_grad  host array[world] of out bf16 [return_caps[p], H]
+ * dx           out bf16 [T, H];  dlogits: out fp32 [T, E] (every entry
+ *              written)
+ * A rank's buffers may be NULL where nothing travels (world == 1: the
+ * arrays themselves).  Errors, reported by kos_workspace_status with the
+ * kernel then doing nothing more: a NULL peer buffer that would be read or
+ * written, grouped offsets that disagree with counts + peer_counts or pass
+ * grouped_cap, routing that names rows outside the forward's (KOS_ERR_ARG
+ * or KOS_ERR_CAPACITY); send/return capacities below the rows that travel
+ * (KOS_ERR_CAPACITY).  Shapes: H % 256 == 0, F % 128 == 0, grouped_cap * H
+ * * 2 < 2^31 bytes (else KOS_ERR_SHAPE).  opts->mode must be
+ * KOS_MODE_FUSED with the default policy (KOS_ERR_UNSUPPORTED otherwise).
+ */
+kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy,
+                             const int32_t* topk_idx, const float* topk_w, const int32_t* perm,
+                             const int32_t* counts, const int32_t* peer_counts,
+                             const void* x_grouped, int64_t grouped_cap,
+                             const int32_t* grouped_offsets, const int32_t* row_src,
+                             const void* y_grouped, const void* const* peer_return,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* const* peer_send_grad,
+                             void* const* out_send_grad, const int64_t* send_caps,
+                             void* dres_grouped, void* dg, void* du, void* dx_grouped,
+                             const void* const* peer_return_grad,
+                             void* const* out_return_grad, const int64_t* return_caps,
+                             void* dx, float* dlogits,
+                             const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,6 +153,15 @@ MOE_TINY = MoeShape("moe_tiny_4r_t96_h256_e16_k4_f128", 6, 4, 96, 256, 16, 4,
 MOE_TINY_SKEW = MoeShape("moe_tiny_skew_4r_t160_h256_e16_k4_f192", 7, 4, 160,
                          256, 16, 4, 192, zipf_s=1.1)
 
+# the expert layer's backward direction (hidden a multiple of 256, ffn of
+# 128): several 256-row units per expert with ragged tails, top-10 (more
+# than eight pairs per token), one rank, and top-1
+MOE_BWD_MID = MoeShape("moe_bwd_mid_4r_t640_h512_e16_k4_f256_zipf1.1", 24, 4, 640, 512, 16, 4, 256,
+                       zipf_s=1.1)
+MOE_BWD_K10 = MoeShape("moe_bwd_k10_2r_t64_h256_e32_k10_f128", 25, 2, 64, 256, 32, 10, 128)
+MOE_BWD_1R = MoeShape("moe_bwd_1r_t96_h256_e8_k2_f128", 26, 1, 96, 256, 8, 2, 128)
+MOE_BWD_K1 = MoeShape("moe_bwd_k1_4r_t96_h256_e16_k1_f128", 27, 4, 96, 256, 16, 1, 128)
+
 
 # ---------------------------------------------------------------------------
 # seeded draws
@@ -160,6 +169,7 @@ MOE_TINY_SKEW = MoeShape("moe_tiny_skew_4r_t160_h256_e16_k4_f192", 7, 4, 160,
 
 # tensor ids (stable: part of the seed)
 T_A, T_W, T_PEER, T_X, T_LOGITS, T_WG, T_WU, T_WD, T_SEND, T_RET, T_PLOG, T_SA, T_SW = range(13)
+T_DY, T_SENDG, T_RETG = 13, 14, 15    # the expert layer's backward direction
 
 
 def _gen(wid: int, tid: int, rank: int, device) -> torch.Generator:
@@ -379,6 +389,30 @@ def moe_inputs(s: MoeShape, rank: int, device="cpu", with_weights=True):
     out["peer_return"] = peer_ret
     if with_weights:
         out.update(moe_weights(s, rank, device))
+    return out
+
+
+def moe_grad_inputs(s: MoeShape, rank: int, device="cpu"):
+    """What one rank's expert-layer backward reads besides the forward's
+    buffers: dy [T,H] bf16 N(0,1) (the layer output's gradient);
+    peer_send_grad[p] [n_p,H] bf16 N(0,1): the gradients of the rows p sent
+    us (n_p = what emulated_peer_counts says p sends), in p's order;
+    peer_return_grad[d] [max(peer_cap,1),H] bf16 N(0,1): the data gradients
+    d returns for the rows we sent it (only the first send-count rows are
+    read)."""
+    out = {"dy": normal((s.tokens, s.hidden), 1.0, s.wid, T_DY, rank, device)}
+    pc = emulated_peer_counts(s, rank, "cpu")
+    sg, rg = [], []
+    for p in range(s.world):
+        if p == rank:
+            sg.append(None)
+            rg.append(None)
+            continue
+        n_p = int(pc[p].sum())
+        sg.append(normal((max(n_p, 1), s.hidden), 1.0, s.wid, T_SENDG, p * 64 + rank, device)[:n_p])
+        rg.append(normal((max(s.peer_cap, 1), s.hidden), 1.0, s.wid, T_RETG, p * 64 + rank, device))
+    out["peer_send_grad"] = sg
+    out["peer_return_grad"] = rg
     return out
 
 

@@ -501,6 +501,15 @@ def expert_ffn_bwd(x_bits, dy_rows, wg_bits, wu_bits, wd_bits, rounded: bool = T
     return dg, du, dx
 
 
+def pair_grad(dy_bits, w, tokens, slots, rounded: bool = True):
+    """The output gradient of pairs (tokens[i], slots[i]): w[t,j] * dy[t]
+    (bf16 bits when rounded, else float64), one row per pair."""
+    t = np.asarray(tokens, dtype=np.int64)
+    g = np.asarray(w, dtype=np.float64)[t, np.asarray(slots, dtype=np.int64)][:, None] * bf16_to_f64(
+        np.asarray(dy_bits)[t])
+    return round_bf16(g) if rounded else g
+
+
 def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world: int, rank: int,
                   rounded: bool = True):
     """The pairs' output gradients, placed like the forward dispatch places
@@ -509,7 +518,6 @@ def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world:
     packed order, grouped: the rows of our local experts -- expert-major,
     then source rank, then the source's packed order, the peers' rows taken
     from ``peer_send_grad``)."""
-    dy = bf16_to_f64(dy_bits)
     w = np.asarray(w, dtype=np.float64)
     T, k = w.shape
     E = len(offsets) - 1
@@ -518,9 +526,7 @@ def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world:
     slot_of = np.empty(T * k, dtype=np.int64)
     token_of[np.asarray(perm)] = np.arange(T * k) // k
     slot_of[np.asarray(perm)] = np.arange(T * k) % k
-    packed = w[token_of, slot_of][:, None] * dy[token_of]
-    if rounded:
-        packed = round_bf16(packed)
+    packed = pair_grad(dy_bits, w, token_of, slot_of, rounded)
     so = send_offsets(offsets, world, el)
     send = [None if d == rank else packed[so[d]:so[d + 1]] for d in range(world)]
     pc = np.asarray(peer_counts, dtype=np.int64)
@@ -533,7 +539,7 @@ def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world:
             else:
                 lo, n = int(pc[p, :e].sum()), int(pc[p, e])
                 rows.append(np.asarray(peer_send_grad[p])[lo:lo + n])
-    H = dy.shape[1]
+    H = np.asarray(dy_bits).shape[1]
     grouped = np.concatenate(rows, axis=0) if rows else np.zeros((0, H), packed.dtype)
     return dict(send=send, grouped=grouped)
 
