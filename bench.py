@@ -146,8 +146,9 @@ def moe_block(torch, kos, KI, ws, flush, reps, shape, rank=0):
                                  rank_moe=rank)
     t_layer = per[0] + per[1]
     one = single_launch(torch, kos, KI, m, ws, flush, reps, shape, t_layer, rank)
+    bwd = moe_backward(torch, kos, KI, m, ws, flush, reps, shape, one["ms"], rank)
     return {
-        "single_launch": one,
+        "single_launch": one, "backward": bwd,
         "workload": shape.name, "rank": rank, "grouped_rows": rows,
         "ms": {"moe_dispatch": round(per[0], 4), "moe_combine": round(per[1], 4), "layer": round(t_layer, 4)},
         "tokens_per_s": round(shape.tokens / (t_layer * 1e-3), 1),
@@ -193,6 +194,171 @@ def single_launch(torch, kos, KI, m, ws, flush, reps, shape, two_ms, rank=0):
     t = time_ops(torch, [("moe_layer", fn)], reps, ws, flush)[0][0]
     return {"ms": round(t, 4), "two_launch_ms": round(two_ms, 4), "speedup_vs_two_launch": round(two_ms / t, 3),
             "tokens_per_s": round(shape.tokens / (t * 1e-3), 1)}
+
+
+def build_moe_grad(torch, KI, shape, m, rank=0):
+    """The backward's inputs (seeded: dy, the gradients peers send us and the
+    data gradients they return) and its output buffers, resident."""
+    dev = "cuda"
+    g = KI.moe_grad_inputs(shape, rank, dev)
+    cap = m["grouped"].shape[0]
+    H, F, T, E = shape.hidden, shape.ffn, shape.tokens, shape.experts
+    pc = m["peer_counts"].cpu()
+    g.update(
+        send=[None if p == rank else torch.empty((shape.peer_cap, H), dtype=torch.bfloat16, device=dev)
+              for p in range(shape.world)],
+        dres=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+        dg=torch.empty((cap, F), dtype=torch.bfloat16, device=dev),
+        du=torch.empty((cap, F), dtype=torch.bfloat16, device=dev),
+        dxg=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+        ret=[None if p == rank else torch.empty((max(int(pc[p].sum()), 1), H), dtype=torch.bfloat16, device=dev)
+             for p in range(shape.world)],
+        dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        dl=torch.empty((T, E), dtype=torch.float32, device=dev))
+    return g
+
+
+def bwd_op(kos, m, g, ws, shape, rank=0, trace=False):
+    """The expert layer's backward in one launch (kos_moe_layer_bwd), reading
+    the forward's buffers in `m` (kept from a forward call)."""
+    from gemm_collective_persistent_amd.api import moe_shape as mk_shape
+    shp = mk_shape(shape.world, rank, shape.tokens, shape.hidden, shape.experts, shape.topk, shape.ffn)
+    o = kos.opts(trace=trace)
+    return lambda: kos.moe_layer_bwd(shp, g["dy"], m["idx"], m["w"], m["perm"], m["counts"], m["peer_counts"],
+                                     m["grouped"], m["goff"], m["row_src"], m["yg"], m["peer_return"], m["wg"],
+                                     m["wu"], m["wd"], g["peer_send_grad"], g["send"], g["dres"], g["dg"], g["du"],
+                                     g["dxg"], g["peer_return_grad"], g["ret"], g["dx"], g["dl"], ws, o)
+
+
+def torch_bwd_baseline(torch, m, g, shape, rank=0):
+    """The same backward composed of PyTorch operations on the same GPU
+    (hipBLASLt GEMMs per expert, elementwise and indexing kernels): a
+    same-GPU library baseline.  Index maps are built once, untimed, from the
+    forward's routing; the returned closure computes dx and dlogits (and the
+    rows sent and returned) from the resident inputs."""
+    import numpy as np
+    T, k, E, H, R = shape.tokens, shape.topk, shape.experts, shape.hidden, shape.world
+    el = shape.e_local
+    dev = m["grouped"].device
+    idx = m["idx"].long()
+    perm = m["perm"].long()
+    counts = m["counts"].cpu().numpy().astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    so = [int(off[d * el]) for d in range(R + 1)]
+    go = m["goff"].cpu().numpy().astype(np.int64)
+    rs = m["row_src"][:int(go[-1])].cpu().numpy().astype(np.int64)
+    pc = m["peer_counts"].cpu().numpy().astype(np.int64)
+    # grouped row -> row of cat(our own local pairs' gradients, each peer's rows)
+    base = {rank: 0}
+    acc = so[rank + 1] - so[rank]
+    for p in range(R):
+        if p != rank:
+            base[p] = acc
+            acc += int(pc[p].sum())
+    gidx = torch.as_tensor(np.array([base[p] + i for p, i in rs], dtype=np.int64), device=dev)
+    push = {p: (torch.as_tensor(np.where(rs[:, 0] == p)[0], device=dev),
+                torch.as_tensor(rs[rs[:, 0] == p, 1], device=dev)) for p in range(R) if p != rank}
+    # every pair (t, j) -> local grouped row, or (rank d, row)
+    perm_np = m["perm"].cpu().numpy().astype(np.int64)
+    idx_np = m["idx"].cpu().numpy().astype(np.int64).reshape(-1)
+    dst = idx_np // el
+    before = pc[:rank].sum(axis=0)
+    loc = np.where(dst == rank)[0]
+    e_l = idx_np[loc] - rank * el
+    loc_rows = go[e_l] + before[e_l] + (perm_np[loc] - off[idx_np[loc]])
+    pairs_loc = (torch.as_tensor(loc, device=dev), torch.as_tensor(loc_rows, device=dev))
+    pairs_rem = {}
+    for d in range(R):
+        sel = np.where(dst == d)[0]
+        if d != rank and sel.size:
+            pairs_rem[d] = (torch.as_tensor(sel, device=dev), torch.as_tensor(perm_np[sel] - so[d], device=dev))
+    bounds = [(int(go[e]), int(go[e + 1])) for e in range(el)]
+    wg, wu, wd = m["wg"], m["wu"], m["wd"]
+    dy, w = g["dy"], m["w"]
+    xg, yg = m["grouped"], m["yg"]
+    dxg, dxp = g["dxg"], torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    res = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    packed = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = {}
+
+    def run():
+        # the pairs' gradients in packed order, sent and grouped
+        packed[perm] = (w.reshape(-1, 1) * dy.float().repeat_interleave(k, 0)).to(torch.bfloat16)
+        for d in range(R):
+            if d != rank and so[d + 1] > so[d]:
+                g["send"][d][:so[d + 1] - so[d]].copy_(packed[so[d]:so[d + 1]])
+        src = torch.cat([packed[so[rank]:so[rank + 1]]] + [g["peer_send_grad"][p] for p in range(R) if p != rank])
+        dres = src[gidx]
+        for e, (lo, hi) in enumerate(bounds):
+            if hi == lo:
+                continue
+            x = xg[lo:hi]
+            gg = (x @ wg[e]).float()
+            uu = (x @ wu[e]).float()
+            dh = (dres[lo:hi] @ wd[e].t()).float()
+            sg = torch.sigmoid(gg)
+            du = (dh * gg * sg).to(torch.bfloat16)
+            dgr = (dh * uu * sg * (1 + gg * (1 - sg))).to(torch.bfloat16)
+            torch.matmul(dgr, wg[e].t(), out=dxg[lo:hi])
+            dxg[lo:hi].addmm_(du, wu[e].t())
+        for p, (rows, dst_rows) in push.items():
+            g["ret"][p].index_copy_(0, dst_rows, dxg[rows])
+        # per token: the sum of its pairs' gradients and the router gradient
+        dxp[pairs_loc[0]] = dxg[pairs_loc[1]]
+        res[pairs_loc[0]] = yg[pairs_loc[1]]
+        for d, (sel, rows) in pairs_rem.items():
+            dxp[sel] = g["peer_return_grad"][d][rows]
+            res[sel] = m["peer_return"][d][rows]
+        out["dx"] = dxp.view(T, k, H).float().sum(1).to(torch.bfloat16)
+        dw = (res.view(T, k, H).float() * dy.float()[:, None, :]).sum(-1)
+        gl = w * (dw - (w * dw).sum(1, keepdim=True))
+        out["dl"] = torch.zeros((T, E), dtype=torch.float32, device=dev).scatter_(1, idx, gl)
+
+    return run, out
+
+
+def moe_backward(torch, kos, KI, m, ws, flush, reps, shape, fwd_ms, rank=0, baseline=True):
+    """The expert layer's backward direction in one launch on the forward's
+    buffers: time, executed and algorithmic TFLOP/s, the clock it ran at,
+    the idle-CU fraction, tokens/s of forward + backward, and the
+    PyTorch-composed baseline on the same inputs (with how closely its dx
+    and router gradient agree with the kernel's)."""
+    from gemm_collective_persistent_amd.timeline import summarize
+    g = build_moe_grad(torch, KI, shape, m, rank)
+    fn = bwd_op(kos, m, g, ws, shape, rank)
+    fn()
+    ws.status()
+    t = time_ops(torch, [("moe_layer_bwd", fn)], reps, ws, flush)[0][0]
+    rows = int(m["goff"][-1].item())
+    fl_exec = rows * 10.0 * shape.hidden * shape.ffn   # g, u recomputed; dH; dX
+    fl_alg = rows * 6.0 * shape.hidden * shape.ffn     # dH; dX
+    grid = int(kos.lib.kos_device_cu_count())
+    tl = traced_call(kos, ws, bwd_op(kos, m, g, ws, shape, rank, trace=True), grid, 1, flush)
+    clk = sum(ws.trace_clock_mhz) / len(ws.trace_clock_mhz)
+    summ = summarize(tl, workgroups=grid)
+    tf = fl_exec / (t * 1e-3) / 1e12
+    d = {"workload": shape.name, "rank": rank, "grouped_rows": rows, "ms": round(t, 4),
+         "tflops_executed": round(tf, 1), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
+         "tflops_algorithmic_no_recompute": round(fl_alg / (t * 1e-3) / 1e12, 1),
+         "clock_mhz": round(clk, 1), "pct_bf16_peak_at_clock": round(100 * tf / (PEAK_BF16_TFLOPS * clk / PEAK_CLOCK_MHZ), 1),
+         "idle_cu_fraction": summ["idle_frac"], "wait_fraction": summ["wait_frac"],
+         "tokens_per_s": round(shape.tokens / (t * 1e-3), 1),
+         "forward_ms": round(fwd_ms, 4),
+         "fwd_plus_bwd_tokens_per_s": round(shape.tokens / ((t + fwd_ms) * 1e-3), 1)}
+    if baseline:
+        run, out = torch_bwd_baseline(torch, m, g, shape, rank)
+        run()
+        torch.cuda.synchronize()
+        tb = time_ops(torch, [("torch_bwd", run)], reps, ws, flush)[0][0]
+
+        def rel(a, b):
+            a, b = a.float(), b.float()
+            return float((a - b).norm() / b.norm().clamp_min(1e-30))
+        d["torch_composed"] = {"ms": round(tb, 4), "speedup": round(tb / t, 3),
+                               "dx_rel_diff": float(f"{rel(out['dx'], g['dx']):.3g}"),
+                               "dlogits_rel_diff": float(f"{rel(out['dl'], g['dl']):.3g}"),
+                               "dlogits_norm": float(f"{float(g['dl'].norm()):.4g}")}
+    return d
 
 
 def policy_comparison(torch, kos, KI, inp, ws, moe_shape, flush, reps, fused_ms, unfused_ms, sweep, planned):
@@ -806,6 +972,10 @@ def main():
     t_two = per[names.index("moe_dispatch")] + per[names.index("moe_combine")]
     extra["moe_single_launch"] = single_launch(torch, kos, KI, inp["moe"], ws, flush, max(3, args.steps // 4),
                                                moe_shape, t_two)
+    # the expert layer's backward direction in one launch, on the forward
+    # buffers the single launch just left (the forward's routing and rows)
+    extra["moe_backward"] = moe_backward(torch, kos, KI, inp["moe"], ws, flush, max(3, args.steps // 4), moe_shape,
+                                         extra["moe_single_launch"]["ms"], baseline=not args.no_baselines)
     if not args.no_baselines:
         reps = max(3, args.steps // 4)
         ops_u = make_ops(kos, KI, inp, ws, moe_shape, mode=2)
