@@ -210,6 +210,7 @@ def build_moe_grad(torch, KI, shape, m, rank=0):
         dres=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
         dg=torch.empty((cap, F), dtype=torch.bfloat16, device=dev),
         du=torch.empty((cap, F), dtype=torch.bfloat16, device=dev),
+        dh=torch.empty((cap, F), dtype=torch.float32, device=dev),
         dxg=torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
         ret=[None if p == rank else torch.empty((max(int(pc[p].sum()), 1), H), dtype=torch.bfloat16, device=dev)
              for p in range(shape.world)],
@@ -227,7 +228,7 @@ def bwd_op(kos, m, g, ws, shape, rank=0, trace=False):
     return lambda: kos.moe_layer_bwd(shp, g["dy"], m["idx"], m["w"], m["perm"], m["counts"], m["peer_counts"],
                                      m["grouped"], m["goff"], m["row_src"], m["yg"], m["peer_return"], m["wg"],
                                      m["wu"], m["wd"], g["peer_send_grad"], g["send"], g["dres"], g["dg"], g["du"],
-                                     g["dxg"], g["peer_return_grad"], g["ret"], g["dx"], g["dl"], ws, o)
+                                     g["dh"], g["dxg"], g["peer_return_grad"], g["ret"], g["dx"], g["dl"], ws, o)
 
 
 def torch_bwd_baseline(torch, m, g, shape, rank=0):

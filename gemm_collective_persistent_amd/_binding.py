@@ -103,7 +103,7 @@ def _load():
         "kos_moe_combine": (c_int32, [POINTER(MoeShape), P, P, P, c_int64, P, P, P, P, P, P, P, P,
                                       PP, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_layer_bwd": (c_int32, [POINTER(MoeShape), P, P, P, P, P, P, P, c_int64, P, P, P, PP, P, P, P,
-                                        PP, PP, POINTER(c_int64), P, P, P, P, PP, PP, POINTER(c_int64), P, P,
+                                        PP, PP, POINTER(c_int64), P, P, P, P, P, PP, PP, POINTER(c_int64), P, P,
                                         POINTER(Opts), P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():

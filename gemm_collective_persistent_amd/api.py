@@ -392,7 +392,7 @@ def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_do
 
 def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, x_grouped, grouped_offsets,
                   row_src, y_grouped, peer_return, w_gate, w_up, w_down, peer_send_grad, out_send_grad,
-                  dres_grouped, dg, du, dx_grouped, peer_return_grad, out_return_grad, dx, dlogits,
+                  dres_grouped, dg, du, dh, dx_grouped, peer_return_grad, out_return_grad, dx, dlogits,
                   ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
     """kos_moe_layer_bwd: the expert layer's data and router gradients in one
     launch (see include/kos.h).  The forward's routing and grouped buffers
@@ -424,6 +424,8 @@ def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, 
                            ("du", du, F), ("dx_grouped", dx_grouped, H)):
         _need(t, torch.bfloat16, name, 2, (None, width))
         _min_rows(t, cap, name)
+    _need(dh, torch.float32, "dh", 2, (None, F))
+    _min_rows(dh, cap, "dh")
     lists = (("peer_return", peer_return, True), ("peer_send_grad", peer_send_grad, True),
              ("out_send_grad", out_send_grad, False), ("peer_return_grad", peer_return_grad, True),
              ("out_return_grad", out_return_grad, False))
@@ -441,6 +443,6 @@ def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, 
     check(lib.kos_moe_layer_bwd(ctypes.byref(s), _p(dy), _p(topk_idx), _p(topk_w), _p(perm), _p(counts),
                                 _p(peer_counts), _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(y_grouped),
                                 arr["peer_return"], _p(w_gate), _p(w_up), _p(w_down), arr["peer_send_grad"],
-                                arr["out_send_grad"], scaps, _p(dres_grouped), _p(dg), _p(du), _p(dx_grouped),
+                                arr["out_send_grad"], scaps, _p(dres_grouped), _p(dg), _p(du), _p(dh), _p(dx_grouped),
                                 arr["peer_return_grad"], arr["out_return_grad"], rcaps, _p(dx), _p(dlogits),
                                 ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))

@@ -21,10 +21,13 @@
 //            into the grouped gradient rows.  Each grouped row stored bumps
 //            rows_in[its unit].
 //   head[1]  tiles in the lagged consumer order of the combine: a unit's
-//            first-stage tiles (128-row half x 128 columns of F: recompute
-//            g, u; dH = dres . Wd^T; store dG, dU) wait for rows_in, its
-//            second-stage tiles (256 columns of H: dX = dG . Wg^T +
-//            dU . Wu^T) for the unit's first-stage tiles.  Between tiles a
+//            first-stage entries (FB = 256, or 128, columns of F each:
+//            dH = dres . Wd^T, kept in fp32 in the caller's dH buffer and
+//            read back by the same workgroup; then per 128 of those columns
+//            g and u recomputed in the SwiGLU tile, whose epilogue forms
+//            dG and dU) wait for rows_in, its second-stage tiles (256
+//            columns of H: dX = dG . Wg^T + dU . Wu^T, one split-K loop)
+//            for the unit's first-stage entries.  Between tiles a
 //            workgroup takes the push queue's head if it is ready.
 //   head[2]  pushes: dX rows of rows a peer sent us, back to it.
 //   head[3]  fold: per token, dx = bf16(sum of its pairs' dX) and the
@@ -38,8 +41,7 @@
 namespace kos {
 
 constexpr int kBwdUnit = 256;      // grouped rows per unit
-constexpr int kBwdHalf = 128;      // rows of a first-stage tile
-constexpr int kBwdFCols = 128;     // F columns of a first-stage tile
+constexpr int kBwdFCols = 128;     // F columns of a SwiGLU recompute tile
 constexpr int kBwdHCols = 256;     // H columns of a second-stage tile
 constexpr int kBwdMoveTokens = 8;  // our tokens per mover entry (one per wave)
 constexpr int kBwdMoveRows = 16;   // peer rows per mover entry
@@ -61,6 +63,7 @@ struct BwdParams {
   uint16_t* dres;                       // grouped pair gradients [cap, H]
   uint16_t* dg;                         // [cap, F]
   uint16_t* du;                         // [cap, F]
+  float* dh;                            // [cap, F] fp32
   float* dlogits;                       // [T, E]
   uint32_t* rows_in;                    // [u_max]; the counters start here
   uint32_t n_counters;                  // 3 * u_max
@@ -137,7 +140,7 @@ __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float w) {
 // then the wave scales dy's row by each pair's weight and stores it there.
 // Returns false (wave-uniform) on routing that names rows outside the
 // forward's.
-__device__ inline bool bwd_move_token(const BwdParams& b, const CombineMeta& M, int t) {
+__device__ __forceinline__ bool bwd_move_token(const BwdParams& b, const CombineMeta& M, int t) {
   const CombineParams& p = b.c;
   const int lane = threadIdx.x & 63;
   const int k = p.k;
@@ -192,7 +195,7 @@ __device__ inline bool bwd_move_token(const BwdParams& b, const CombineMeta& M, 
 
 // Mover entry past our tokens: a chunk of kBwdMoveRows gradient rows peer q
 // sent us, one row per wave at a time, into the grouped gradient rows.
-__device__ inline void bwd_move_peer(const BwdParams& b, const CombineMeta& M, const BwdLds& B, int i) {
+__device__ __forceinline__ void bwd_move_peer(const BwdParams& b, const CombineMeta& M, const BwdLds& B, int i) {
   const CombineParams& p = b.c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int q = 0;
@@ -211,45 +214,68 @@ __device__ inline void bwd_move_peer(const BwdParams& b, const CombineMeta& M, c
   }
 }
 
-// First-stage tile: rows [half*128, +m) of unit x, F columns [nf*128, +128).
-// SD: the SwiGLU-layout tile (gate and up blocks of the same columns); SH:
-// the dH tile, N x K weights (Wd rows), whose blocks line up with SD's gate
-// blocks element for element.
-template <class SD, class SH, int RING>
-__device__ __forceinline__ void bwd_tile1(const BwdParams& b, const Unit& x, int half, int nf,
-                                          f32x16 (&gu)[SD::TM][SD::TN], f32x16 (&dh)[SH::TM][SH::TN]) {
-  static_assert(SD::BM == SH::BM && SD::WGM == SH::WGM && SD::WGN == SH::WGN && SD::TM == SH::TM &&
-                    SD::TN == 2 * SH::TN && SD::BN == 2 * SH::BN && SH::BNT && !SD::BNT,
-                "the dH blocks must line up with the gate blocks");
+// First-stage entry: F columns [blk*FB, +FB) of unit x.  SH: the dH tile
+// (N x K weights: Wd rows); SD: the SwiGLU-layout tile (gate and up blocks
+// of the same 128 columns), whose epilogue reads dH back.
+template <class SH, class SD, int RING, int FB>
+__device__ __forceinline__ void bwd_stage1(const BwdParams& b, const Unit& x, int blk, f32x16 (&ah)[SH::TM][SH::TN],
+                                           f32x16 (&ad)[SD::TM][SD::TN]) {
+  static_assert(SH::BNT && !SD::BNT && SH::BM == SD::BM && SH::BN == FB && SD::BN == 2 * kBwdFCols &&
+                    FB % kBwdFCols == 0,
+                "dH tile of FB columns, SwiGLU tiles of 128");
   const CombineParams& p = b.c;
   const int64_t H = p.H, F = p.F;
-  const int64_t row0 = (int64_t)x.row0 + half * kBwdHalf;
-  const int m = min(kBwdHalf, x.m_valid - half * kBwdHalf);
+  const int64_t row0 = x.row0;
+  const int m = x.m_valid;
   const int64_t woff = (int64_t)x.el * H * F;
-  // g and u of the forward, recomputed (the grouped input is resident)
-  const BSrc bgu{p.wg + woff + (int64_t)nf * kBwdFCols, p.wu + woff + (int64_t)nf * kBwdFCols, F};
-  tile_mainloop<SD, true, false, RING>(gu, p.xg + row0 * H, H, m, bgu, p.H);
   // dH = dres . Wd^T; the gradient rows come from this launch's movers
-  const BSrc bd{p.wd + woff + (int64_t)nf * kBwdFCols * H, nullptr, H};
-  tile_mainloop<SH, false, true, RING>(dh, b.dres + row0 * H, H, m, bd, p.H);
-  // dU = dH * silu(g), dG = dH * u * silu'(g), silu'(g) = s (1 + g (1 - s)),
-  // s = 1 / (1 + e^-g); in place of g and u
-#pragma unroll
-  for (int i = 0; i < SD::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < SH::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float g = gu[i][j][r], u = gu[i][j + SH::TN][r], d = dh[i][j][r];
-        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-        gu[i][j][r] = d * u * (sg * (1.0f + g * (1.0f - sg)));
-        gu[i][j + SH::TN][r] = d * (g * sg);
-      }
-  // read by this launch's second-stage tiles: device-coherent stores
-  tile_store_rows<SD, RING, true, false, 0>(gu, b.dg + row0 * F + nf * kBwdFCols, F, m);
+  tile_mainloop<SH, false, true, RING>(ah, b.dres + row0 * H, H, m, BSrc{p.wd + woff + (int64_t)blk * FB * H, nullptr, H},
+                                       p.H);
+  float* dhp = b.dh + row0 * F + (int64_t)blk * FB;
+  const DevBuf db(dhp);
+  tile_foreach4<SH>(ah, [&](int r, int c, f32x4 v) {
+    if (r < m) db.st128((uint32_t)(r * F + c) * 4u, __builtin_bit_cast(u32x4, v));
+  });
   KOS_WAITCNT(0, 0);
-  lds_barrier();   // every wave has read the first store out of the ring
-  tile_store_rows<SD, RING, true, false, 1>(gu, b.du + row0 * F + nf * kBwdFCols, F, m);
+  lds_barrier();   // the whole dH block is stored before any wave reads it back
+#pragma unroll 1
+  for (int hf = 0; hf < FB / kBwdFCols; ++hf) {
+    const int64_t c0 = (int64_t)blk * FB + hf * kBwdFCols;
+    // g and u of the forward, recomputed (the grouped input is resident)
+    tile_mainloop<SD, true, false, RING>(ad, p.xg + row0 * H, H, m, BSrc{p.wg + woff + c0, p.wu + woff + c0, F}, p.H);
+    // dU = dH * silu(g), dG = dH * u * silu'(g), silu'(g) = s (1 + g (1 - s)),
+    // s = 1 / (1 + e^-g); in place of g and u.  Lane l holds, in block
+    // (i, j) of the gate half, rows wm*WM + i*32 + l%32 and four columns
+    // from wn*WN/2 + j*32 + 8*q + 4*(l/32) per group q.
+    {
+      const WaveCtx w = wave_ctx();
+      const int wm = w.wave / SD::WGN, wn = w.wave % SD::WGN;
+#pragma unroll
+      for (int i = 0; i < SD::TM; ++i) {
+        const int row = wm * SD::WM + i * 32 + (w.lane & 31);
+        const int rr = row < m ? row : m - 1;   // rows past the unit are computed, never stored
+#pragma unroll
+        for (int j = 0; j < SD::TN / 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wn * (SD::WN / 2) + j * 32 + q * 8 + (w.lane >> 5) * 4;
+            const f32x4 d = __builtin_bit_cast(f32x4, db.ld128((uint32_t)(rr * F + hf * kBwdFCols + col) * 4u));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float g = ad[i][j][4 * q + e], u = ad[i][j + SD::TN / 2][4 * q + e];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              ad[i][j][4 * q + e] = d[e] * u * (sg * (1.0f + g * (1.0f - sg)));
+              ad[i][j + SD::TN / 2][4 * q + e] = d[e] * (g * sg);
+            }
+            // one group at a time: keeps the loads of later groups from
+            // being hoisted here (each would hold four more registers)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+    }
+    // read by this launch's second-stage tiles: device-coherent stores
+    tile_store_rows_pair<SD, RING, true>(ad, b.dg + row0 * F + c0, b.du + row0 * F + c0, F, m);
+  }
 }
 
 // Second-stage tile: H columns [nh*256, +256) of unit x's dX.
@@ -320,7 +346,7 @@ __device__ __forceinline__ void pair_dots(int H, int k, uint64_t resp, const uin
 // second-stage tiles; remote: what its rank returned) and its forward
 // result.  Returns false (wave-uniform) on abort, time-out or bad routing.
 template <int KN, int CB>
-__device__ inline bool bwd_fold_token(const BwdParams& b, const CombineMeta& M, int t, uint32_t info) {
+__device__ __forceinline__ bool bwd_fold_token(const BwdParams& b, const CombineMeta& M, int t, uint32_t info) {
   const CombineParams& p = b.c;
   const int lane = threadIdx.x & 63;
   const int k = p.k;
@@ -390,16 +416,25 @@ __device__ inline bool bwd_fold_token(const BwdParams& b, const CombineMeta& M, 
   return true;
 }
 
-template <class S2, class S2T, class S2T2, class SD, class SH, class SDT, class SHT>
-__global__ __launch_bounds__(S2::NT, 1) void moe_layer_bwd_kernel(BwdParams args) {
-  static_assert(S2::BM == kBwdUnit && SD::BM == kBwdHalf && SDT::BM < kBwdHalf && S2T::BM < S2::BM &&
-                    S2T2::BM < S2T::BM,
-                "unit, half and tail tiles");
-  static_assert(S2::NT == S2T::NT && S2::NT == S2T2::NT && S2::NT == SD::NT && S2::NT == SH::NT &&
-                    S2::NT == SDT::NT && S2::NT == SHT::NT && S2::NT / 64 == kBwdMoveTokens,
+// The tiles of a unit's rows (BM = 256, or 128 / 64 for an expert's last
+// unit when its rows fit): dX (N x K weights), dH over FB columns of F
+// (N x K weights), g and u over 128 columns (SwiGLU layout).  Eight waves.
+template <int BM, int FB>
+struct BwdShapes {
+  using X = TileShape<BM, kBwdHCols, 4, 2, 4, true>;
+  using DH = TileShape<BM, FB, 4, 2, 4, true>;
+  using GU = TileShape<BM, 2 * kBwdFCols, 4, 2, 4>;
+};
+
+template <int FB>
+__global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
+  using B256 = BwdShapes<kBwdUnit, FB>;
+  using B128 = BwdShapes<128, FB>;
+  using B64 = BwdShapes<64, FB>;
+  static_assert(B256::X::NT == 512 && B256::DH::NT == 512 && B256::GU::NT == 512 && 512 / 64 == kBwdMoveTokens,
                 "one workgroup shape; a mover entry holds one token per wave");
-  constexpr int RING = S2::STAGE_BYTES;
-  static_assert(SD::STAGE_BYTES <= RING && SH::STAGE_BYTES <= RING, "the unit tile's stage is the largest");
+  constexpr int RING = B256::X::STAGE_BYTES;
+  static_assert(B256::DH::STAGE_BYTES <= RING && B256::GU::STAGE_BYTES <= RING, "the dX tile's stage is the largest");
   __shared__ CombineMeta M;
   __shared__ BwdLds B;
   __shared__ WgSlots slots;
@@ -437,13 +472,9 @@ __global__ __launch_bounds__(S2::NT, 1) void moe_layer_bwd_kernel(BwdParams args
   constexpr int kSlabs = kBwdUnit / kPushRows;
   const int n_push = U * kSlabs;
   if (ok) {
-    f32x16 acc[S2::TM][S2::TN];
-    f32x16 acc_t[S2T::TM][S2T::TN];
-    f32x16 acc_t2[S2T2::TM][S2T2::TN];
-    f32x16 gu[SD::TM][SD::TN];
-    f32x16 dh[SH::TM][SH::TN];
-    f32x16 gu_t[SDT::TM][SDT::TN];
-    f32x16 dh_t[SHT::TM][SHT::TN];
+    f32x16 ax[B256::X::TM][B256::X::TN], ax1[B128::X::TM][B128::X::TN], ax2[B64::X::TM][B64::X::TN];
+    f32x16 ah[B256::DH::TM][B256::DH::TN], ah1[B128::DH::TM][B128::DH::TN], ah2[B64::DH::TM][B64::DH::TN];
+    f32x16 ad[B256::GU::TM][B256::GU::TN], ad1[B128::GU::TM][B128::GU::TN], ad2[B64::GU::TM][B64::GU::TN];
     const int n_tiles = U * (p.G + p.D);
     for (;;) {
       for (;;) {   // push while the head of the push queue is ready
@@ -476,10 +507,9 @@ __global__ __launch_bounds__(S2::NT, 1) void moe_layer_bwd_kernel(BwdParams args
         }
         tr.put(KOS_TR_WAIT, j, t0);
         t0 = tr.now();
-        const int half = ct.nt & 1, nf = ct.nt >> 1;
-        const int m = x.m_valid - half * kBwdHalf;
-        if (m > SDT::BM) bwd_tile1<SD, SH, RING>(ps, x, half, nf, gu, dh);
-        else if (m > 0) bwd_tile1<SDT, SHT, RING>(ps, x, half, nf, gu_t, dh_t);
+        if (x.m_valid > 128) bwd_stage1<typename B256::DH, typename B256::GU, RING, FB>(ps, x, ct.nt, ah, ad);
+        else if (x.m_valid > 64) bwd_stage1<typename B128::DH, typename B128::GU, RING, FB>(ps, x, ct.nt, ah1, ad1);
+        else bwd_stage1<typename B64::DH, typename B64::GU, RING, FB>(ps, x, ct.nt, ah2, ad2);
         wg_publish(&t1_done[ct.u], 1u);
         tr.put(KOS_TR_TILE, j, t0);
       } else {
@@ -489,9 +519,9 @@ __global__ __launch_bounds__(S2::NT, 1) void moe_layer_bwd_kernel(BwdParams args
         }
         tr.put(KOS_TR_WAIT, j, t0);
         t0 = tr.now();
-        if (x.m_valid > S2T::BM) bwd_tile2<S2, RING>(ps, x, ct.nt, acc);
-        else if (x.m_valid > S2T2::BM) bwd_tile2<S2T, RING>(ps, x, ct.nt, acc_t);
-        else bwd_tile2<S2T2, RING>(ps, x, ct.nt, acc_t2);
+        if (x.m_valid > 128) bwd_tile2<typename B256::X, RING>(ps, x, ct.nt, ax);
+        else if (x.m_valid > 64) bwd_tile2<typename B128::X, RING>(ps, x, ct.nt, ax1);
+        else bwd_tile2<typename B64::X, RING>(ps, x, ct.nt, ax2);
         wg_publish(&t2_done[ct.u], 1u);
         tr.put(KOS_TR_TILE2, j, t0);
       }
@@ -538,13 +568,6 @@ __global__ __launch_bounds__(S2::NT, 1) void moe_layer_bwd_kernel(BwdParams args
   wg_exit(h, ps.rows_in, ps.n_counters, &slots);
 }
 
-using BwdTile2 = TileShape<256, 256, 4, 2, 4, true>;
-using BwdTile2T = TileShape<128, 256, 4, 2, 4, true>;
-using BwdTile2T2 = TileShape<64, 256, 4, 2, 4, true>;
-using BwdTile1G = TileShape<128, 256, 4, 2, 4>;
-using BwdTile1H = TileShape<128, 128, 4, 2, 4, true>;
-using BwdTile1GT = TileShape<64, 256, 4, 2, 4>;
-using BwdTile1HT = TileShape<64, 128, 4, 2, 4, true>;
 
 }  // namespace kos
 
@@ -557,7 +580,8 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
                                         const void* y_grouped, const void* const* peer_return, const void* w_gate,
                                         const void* w_up, const void* w_down, const void* const* peer_send_grad,
                                         void* const* out_send_grad, const int64_t* send_caps, void* dres_grouped,
-                                        void* dg, void* du, void* dx_grouped, const void* const* peer_return_grad,
+                                        void* dg, void* du, float* dh, void* dx_grouped,
+                                        const void* const* peer_return_grad,
                                         void* const* out_return_grad, const int64_t* return_caps, void* dx,
                                         float* dlogits, const kos_opts* opts, void* ws, size_t ws_bytes,
                                         void* stream) {
@@ -573,7 +597,7 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   const bool no_tokens = s->tokens == 0;
   if ((!no_tokens && (!dy || !topk_idx || !topk_w || !perm || !dx || !dlogits)) || !counts || !peer_counts ||
       !x_grouped || !grouped_offsets || !row_src || !y_grouped || !w_gate || !w_up || !w_down || !dres_grouped ||
-      !dg || !du || !dx_grouped)
+      !dg || !du || !dh || !dx_grouped)
     return fail(KOS_ERR_ARG, "null buffer");
   if (R > 1 && (!peer_return || !peer_send_grad || !out_send_grad || !send_caps || !peer_return_grad ||
                 !out_return_grad || !return_caps))
@@ -587,7 +611,8 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
       return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(dy) || !aligned16(x_grouped) || !aligned16(y_grouped) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(dres_grouped) || !aligned16(dg) || !aligned16(du) || !aligned16(dx_grouped) ||
+      !aligned16(w_down) || !aligned16(dres_grouped) || !aligned16(dg) || !aligned16(du) || !aligned16(dh) ||
+      !aligned16(dx_grouped) ||
       !aligned16(dx))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
@@ -639,7 +664,8 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   }
   p.yg = static_cast<uint16_t*>(dx_grouped);
   p.y = static_cast<uint16_t*>(dx);
-  p.G = 2 * (s->ffn / kBwdFCols);
+  const int FB = s->ffn % 256 == 0 ? 256 : kBwdFCols;   // F columns per first-stage entry
+  p.G = s->ffn / FB;
   p.D = s->hidden / kBwdHCols;
   p.L = (o.grid + p.G - 1) / p.G;
   p.u_max = (int32_t)((grouped_cap + kBwdUnit - 1) / kBwdUnit) + p.E_loc;
@@ -655,6 +681,7 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   b.dres = static_cast<uint16_t*>(dres_grouped);
   b.dg = static_cast<uint16_t*>(dg);
   b.du = static_cast<uint16_t*>(du);
+  b.dh = dh;
   b.dlogits = dlogits;
   uint32_t* base = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   b.rows_in = base;
@@ -662,8 +689,10 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   b.n_counters = 3 * (uint32_t)p.u_max;
   if ((size_t)b.n_counters > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
 
-  hipLaunchKernelGGL((moe_layer_bwd_kernel<BwdTile2, BwdTile2T, BwdTile2T2, BwdTile1G, BwdTile1H, BwdTile1GT,
-                                           BwdTile1HT>),
-                     dim3(o.grid), dim3(BwdTile2::NT), 0, static_cast<hipStream_t>(stream), b);
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (FB == 256)
+    hipLaunchKernelGGL(moe_layer_bwd_kernel<256>, dim3(o.grid), dim3(512), 0, strm, b);
+  else
+    hipLaunchKernelGGL(moe_layer_bwd_kernel<kBwdFCols>, dim3(o.grid), dim3(512), 0, strm, b);
   return launch_status("moe_layer_bwd launch");
 }

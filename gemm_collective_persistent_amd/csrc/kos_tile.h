@@ -503,17 +503,14 @@ __device__ __forceinline__ lds_char* ring_lds(int i) {
 // global writes are whole cache lines (what device-coherent write-through
 // stores need to be cheap).  SWIGLU: the tile holds gate and up columns
 // (BSrc dual layout) and the BN/2 output columns are swiglu(gate, up).
-// HALF = 0 or 1: a dual-layout tile whose gate (0) or up (1) blocks are
-// stored as the BN/2 output columns.  COH: device-scope (sc1) stores.  Call
-// right after tile_mainloop (the ring is free); the next tile_mainloop waits
-// for the ring.  dst is the same in every thread.
-template <class S, int RING, bool COH, bool SWIGLU = false, int HALF = -1>
+// COH: device-scope (sc1) stores.  Call right after tile_mainloop (the ring
+// is free); the next tile_mainloop waits for the ring.  dst is the same in
+// every thread.
+template <class S, int RING, bool COH, bool SWIGLU = false>
 __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst, int64_t ld,
                                                 int m_valid) {
-  constexpr bool DUAL_OUT = SWIGLU || HALF >= 0;
-  static_assert(!(SWIGLU && HALF >= 0) && HALF <= 1, "one dual output at a time");
-  constexpr int OW = DUAL_OUT ? S::BN / 2 : S::BN;   // output columns
-  constexpr int OJ = DUAL_OUT ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
+  constexpr int OW = SWIGLU ? S::BN / 2 : S::BN;   // output columns
+  constexpr int OJ = SWIGLU ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
   constexpr int ROW_BYTES = OW * 2;
   constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
   constexpr int ROWS_PER_RING = RING / ROW_BYTES;
@@ -541,9 +538,7 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = SWIGLU      ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e])
-                 : HALF >= 0 ? acc[i][j + (HALF > 0 ? S::TN / 2 : 0)][4 * g + e]
-                             : acc[i][j][4 * g + e];
+          v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col & 7) * 2) =
             pack4_bf16(v);
         // one 32x32 block at a time: keeps the accumulator reads from being
@@ -574,6 +569,83 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
 #pragma unroll
     for (int q = 0; q < BATCH; ++q) {
       const int row = (b0 + q) * ROWS_PER_PASS + t / CPR;
+      const int64_t off = ((int64_t)row * ld + c * 8) * 2;
+      if (row < m_valid) {
+        if constexpr (COH)
+          d.st128((uint32_t)off, v[q]);
+        else
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + off) = v[q];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Both halves of a dual-layout tile (gate blocks and up blocks, BN/2
+// columns each) as bf16 rows [0, m_valid) of dst0 and dst1, in one pass
+// through the LDS ring: the gate half takes ring rows [0, BM), the up half
+// rows [BM, 2 BM), laid out as in tile_store_rows; then every 16-byte chunk
+// of a row goes out with one store.  COH: device-scope (sc1) stores.  Call
+// right after tile_mainloop (the ring is free).
+template <class S, int RING, bool COH>
+__device__ __forceinline__ void tile_store_rows_pair(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst0,
+                                                     uint16_t* dst1, int64_t ld, int m_valid) {
+  constexpr int OW = S::BN / 2, OJ = S::TN / 2;
+  constexpr int ROW_BYTES = OW * 2;
+  constexpr int CPR = ROW_BYTES / 16;
+  constexpr int ROWS_PER_RING = RING / ROW_BYTES;
+  constexpr int ROWS_PER_PASS = S::NT / CPR;
+  static_assert(RING % ROW_BYTES == 0 && 4 * ROWS_PER_RING >= 2 * S::BM, "both halves must fit the ring");
+  static_assert((CPR & (CPR - 1)) == 0 && S::NT % CPR == 0, "power-of-two chunks per row");
+  static_assert(ROWS_PER_RING % 32 == 0 && ROWS_PER_RING % ROWS_PER_PASS == 0 && S::BM % ROWS_PER_PASS == 0,
+                "32-row groups and store passes stay inside one ring buffer and one half");
+  const WaveCtx w = wave_ctx();
+  const int lane = w.lane, wave = w.wave;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) {
+      const int row0 = hf * S::BM + wm * S::WM + i * 32;   // ring row of the 32-row group (uniform)
+      const int row = row0 + (lane & 31);
+      lds_char* base = ring_lds<RING>(row0 / ROWS_PER_RING) + (row % ROWS_PER_RING) * ROW_BYTES;
+#pragma unroll
+      for (int j = 0; j < OJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * (OW / S::WGN) + j * 32 + g * 8 + (lane >> 5) * 4;
+          const int chunk = (col >> 3) ^ (row & (CPR - 1));
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j + hf * OJ][4 * g + e];
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col & 7) * 2) =
+              pack4_bf16(v);
+          if (g == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  KOS_WAITCNT(0, 0);
+  lds_barrier();
+  const int t = wave * 64 + lane;
+  const int c = t % CPR;
+  constexpr int HALF_PASSES = S::BM / ROWS_PER_PASS, PASSES = 2 * HALF_PASSES;
+  constexpr int BATCH = HALF_PASSES < 8 ? HALF_PASSES : 8;
+  static_assert(HALF_PASSES % BATCH == 0, "whole batches, one half each");
+#pragma unroll
+  for (int b0 = 0; b0 < PASSES; b0 += BATCH) {
+    const bool up = b0 * ROWS_PER_PASS >= S::BM;   // uniform: a batch lies in one half
+    const DevBuf d(up ? dst1 : dst0);
+    uint16_t* dst = up ? dst1 : dst0;
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int r0 = (b0 + q) * ROWS_PER_PASS;
+      const int row = r0 + t / CPR;
+      v[q] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          ring_lds<RING>(r0 / ROWS_PER_RING) + (row % ROWS_PER_RING) * ROW_BYTES + ((c ^ (row & (CPR - 1))) * 16));
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int row = (b0 + q) * ROWS_PER_PASS + t / CPR - (up ? S::BM : 0);
       const int64_t off = ((int64_t)row * ld + c * 8) * 2;
       if (row < m_valid) {
         if constexpr (COH)

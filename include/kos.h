@@ -524,9 +524,10 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
  *             our own experts, into out_send_grad[d] (our packed order)
  *             for rank d's; the rows peers send us (peer_send_grad) are
  *             pulled into dres_grouped (grouped order of the forward)
- *   tiles 1   per unit (256 grouped rows of one expert), 128-row half and
- *             128 columns of F: recompute g = X.Wg and u = X.Wu from the
- *             forward's grouped input, dH = dres . Wd^T, then
+ *   tiles 1   per unit (256 grouped rows of one expert) and 256 columns of
+ *             F (128 when F % 256 != 0): dH = dres . Wd^T (fp32, kept in
+ *             dh), then per 128 of those columns g = X.Wg and u = X.Wu
+ *             recomputed from the forward's grouped input and
  *             dU = bf16(dH * silu(g)), dG = bf16(dH * u * silu'(g))
  *             (the forward's bf16 rounding of h passes gradients unchanged)
  *   tiles 2   per unit and 256 columns of H, once the unit's tiles 1 are
@@ -551,6 +552,7 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
  * out_send_grad   host array[world] of out bf16 [send_caps[d], H]: our
  *              pairs' gradients for rank d, in our packed order
  * dres_grouped out bf16 [grouped_cap, H];  dg, du: out bf16 [grouped_cap, F]
+ * dh           out fp32 [grouped_cap, F]
  * dx_grouped   out bf16 [grouped_cap, H]
  * peer_return_grad host array[world] of bf16 [>= rows we sent d, H]: the
  *              dX rows d returns for the rows we sent it
@@ -564,7 +566,8 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
  * grouped_cap, routing that names rows outside the forward's (KOS_ERR_ARG
  * or KOS_ERR_CAPACITY); send/return capacities below the rows that travel
  * (KOS_ERR_CAPACITY).  Shapes: H % 256 == 0, F % 128 == 0, grouped_cap * H
- * * 2 < 2^31 bytes (else KOS_ERR_SHAPE).  opts->mode must be
+ * * 2 < 2^31 bytes (else KOS_ERR_SHAPE).  All buffers 16-byte aligned
+ * (KOS_ERR_ALIGN).  opts->mode must be
  * KOS_MODE_FUSED with the default policy (KOS_ERR_UNSUPPORTED otherwise).
  */
 kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy,
@@ -576,7 +579,7 @@ kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy,
                              const void* w_gate, const void* w_up, const void* w_down,
                              const void* const* peer_send_grad,
                              void* const* out_send_grad, const int64_t* send_caps,
-                             void* dres_grouped, void* dg, void* du, void* dx_grouped,
+                             void* dres_grouped, void* dg, void* du, float* dh, void* dx_grouped,
                              const void* const* peer_return_grad,
                              void* const* out_return_grad, const int64_t* return_caps,
                              void* dx, float* dlogits,

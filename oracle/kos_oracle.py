@@ -510,6 +510,13 @@ def pair_grad(dy_bits, w, tokens, slots, rounded: bool = True):
     return round_bf16(g) if rounded else g
 
 
+def expert_dh(dy_rows, wd_bits, rounded: bool = True) -> np.ndarray:
+    """dH = dY . Wd^T (float64) for output-gradient rows dY ([n,H]: bf16
+    bits, or float64 when not rounded): the gradient at the expert's hidden
+    h, before the SwiGLU."""
+    return _val(dy_rows, rounded) @ bf16_to_f64(wd_bits).T
+
+
 def dispatch_grad(dy_bits, w, perm, offsets, peer_send_grad, peer_counts, world: int, rank: int,
                   rounded: bool = True):
     """The pairs' output gradients, placed like the forward dispatch places
@@ -579,7 +586,7 @@ def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, p
     routing and expert outputs (``moe_layer``), the pairs' gradients
     dispatched, the experts' data gradients, the results pushed back and
     summed per token, and the router gradient.  Returns a dict with the
-    forward's fields and send_grad, grouped_grad, dg, du, dx_grouped,
+    forward's fields and send_grad, grouped_grad, dh, dg, du, dx_grouped,
     out_return_grad, dx, dlogits."""
     f = moe_layer(x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return, world, rank, k)
     g = dispatch_grad(dy_bits, f["w"], f["perm"], f["offsets"], peer_send_grad, peer_counts, world, rank,
@@ -589,11 +596,13 @@ def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, p
     F = np.asarray(wg).shape[2]
     dt = np.uint16 if rounded else np.float64
     dg, du, dxg = np.zeros((n, F), dt), np.zeros((n, F), dt), np.zeros((n, H), dt)
+    dh = np.zeros((n, F))
     for e in range(len(go) - 1):
         lo, hi = int(go[e]), int(go[e + 1])
         if hi > lo:
             dg[lo:hi], du[lo:hi], dxg[lo:hi] = expert_ffn_bwd(f["grouped"][lo:hi], g["grouped"][lo:hi], wg[e],
                                                               wu[e], wd[e], rounded)
+            dh[lo:hi] = expert_dh(g["grouped"][lo:hi], wd[e], rounded)
     pc = np.asarray(peer_counts)
     out_return = push(dxg, f["row_src"], world, rank, pc.sum(axis=1)) if rounded else None
     ones = np.ones_like(np.asarray(f["w"], dtype=np.float32))
@@ -603,7 +612,7 @@ def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, p
         dx = _sum_pairs(f, dxg, go, pc, peer_return_grad, world, rank)
     dl = router_grad(dy_bits, f["idx"], f["w"], f["perm"], f["offsets"], f["y_grouped"], go, pc, peer_return,
                      world, rank)
-    f.update(send_grad=g["send"], grouped_grad=g["grouped"], dg=dg, du=du, dx_grouped=dxg,
+    f.update(send_grad=g["send"], grouped_grad=g["grouped"], dh=dh, dg=dg, du=du, dx_grouped=dxg,
              out_return_grad=out_return, dx=dx, dlogits=dl)
     return f
 

@@ -70,6 +70,7 @@ def _out_buffers(s, rank, pc, cap):
         dres=torch.full((cap, H), nan, dtype=torch.bfloat16, device=DEV),
         dg=torch.full((cap, F), nan, dtype=torch.bfloat16, device=DEV),
         du=torch.full((cap, F), nan, dtype=torch.bfloat16, device=DEV),
+        dh=torch.full((cap, F), nan, dtype=torch.float32, device=DEV),
         dxg=torch.full((cap, H), nan, dtype=torch.bfloat16, device=DEV),
         ret=[None if p == rank else torch.full((max(int(pc[p].sum()), 1), H), nan, dtype=torch.bfloat16,
                                                device=DEV) for p in range(s.world)],
@@ -81,7 +82,7 @@ def _out_buffers(s, rank, pc, cap):
 def run_bwd(kos, ws, s, rank, inp, gin, f, b, o=None, check=True):
     kos.moe_layer_bwd(_shape(s, rank), gin["dy"], f["idx"], f["w"], f["perm"], f["counts"], inp["peer_counts"],
                       f["grouped"], f["goff"], f["row_src"], f["yg"], inp["peer_return"], inp["wg"], inp["wu"],
-                      inp["wd"], gin["peer_send_grad"], b["send"], b["dres"], b["dg"], b["du"], b["dxg"],
+                      inp["wd"], gin["peer_send_grad"], b["send"], b["dres"], b["dg"], b["du"], b["dh"], b["dxg"],
                       gin["peer_return_grad"], b["ret"], b["dx"], b["dl"], ws, o)
     if check:
         ws.status()
@@ -106,6 +107,7 @@ def _check_all(s, rank, b, ref):
                              f"send_grad[{d}]")
     if n:
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dres"][:n])), O.bf16_to_f64(ref["grouped_grad"]), "dres")
+        assert_close(b["dh"][:n].cpu().numpy(), ref["dh"], "dH")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dg"][:n])), O.bf16_to_f64(ref["dg"]), "dG")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["du"][:n])), O.bf16_to_f64(ref["du"]), "dU")
         dxg = KI.bf16_bits(b["dxg"][:n])
@@ -252,6 +254,7 @@ def test_bwd_full_size_sampled(kos, ws):
         rows = sorted({lo, min(lo + 255, hi - 1), min(lo + 256, hi - 1), hi - 1})
         dres = np.stack([dres_row(r) for r in rows])
         dg, du, dxr = O.expert_ffn_bwd(ref["grouped"][rows], dres, wg[e], wu[e], wd[e])
+        assert_close(b["dh"][rows].cpu().numpy(), O.expert_dh(dres, wd[e]), f"dH e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dres"][rows])), O.bf16_to_f64(dres), f"dres e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dg"][rows])), O.bf16_to_f64(dg), f"dG e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["du"][rows])), O.bf16_to_f64(du), f"dU e{e}")

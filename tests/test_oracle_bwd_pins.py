@@ -63,6 +63,24 @@ def test_expert_ffn_bwd_matches_finite_differences():
         assert abs(fd - np.sum((X.T @ du) * V)) < 1e-6 * max(1.0, abs(fd))
 
 
+def test_dh_is_the_gradient_at_the_hidden():
+    """dU = dH * silu(g) with g = X.Wg: the unrounded dU over silu(g) is
+    expert_dh, and W_down's column scaling shows up in dH's column."""
+    rng = np.random.default_rng(102)
+    n, H, F = 4, 10, 6
+    x = _w(rng, (n, H), 1.0)
+    wg, wu, wd = _w(rng, (H, F), 0.4), _w(rng, (H, F), 0.4), _w(rng, (F, H), 0.4)
+    dy = rng.standard_normal((n, H))
+    _, du, _ = O.expert_ffn_bwd(x, dy, wg, wu, wd, rounded=False)
+    dh = O.expert_dh(dy, wd, rounded=False)
+    g = O.bf16_to_f64(x) @ O.bf16_to_f64(wg)
+    assert np.allclose(du, dh * O.silu(g), rtol=1e-12, atol=1e-12)
+    wd2 = wd.copy()
+    wd2[2] = O.round_bf16(2.0 * O.bf16_to_f64(wd[2]))
+    dh2 = O.expert_dh(dy, wd2, rounded=False)
+    assert np.allclose(dh2[:, 2], 2.0 * dh[:, 2]) and np.allclose(np.delete(dh2, 2, 1), np.delete(dh, 2, 1))
+
+
 def _case(rng, R, rank, T=18, H=8, E=8, k=2, F=6, rounded=False):
     """Our tokens, every rank's expert weights, and peers' rows consistent
     with those weights: rows a peer sends us are random, the rows it
