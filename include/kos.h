@@ -85,9 +85,11 @@ typedef enum kos_dtype { KOS_BF16 = 0, KOS_F32 = 1 } kos_dtype;
  *           (or GEMM then reduction), same tile code. */
 typedef enum kos_mode { KOS_MODE_FUSED = 0, KOS_MODE_FIXED = 1, KOS_MODE_UNFUSED = 2 } kos_mode;
 
-/* GEMM+reduce-scatter output order: band by band across every rank's chunk
- * (the consumer order), or one chunk after the other (the ablation the
- * explainer reports 1.41-1.45x slower) ["Role switching only works if"]. */
+/* GEMM+reduce-scatter output order: BAND finishes the first BM rows of
+ * every rank's chunk before any chunk's next BM rows (the consumer order:
+ * every reducer can start after the first band), ROW one chunk after the
+ * other (the ablation the explainer reports 1.41-1.45x slower) ["Role
+ * switching only works if"]. */
 typedef enum kos_rs_order { KOS_RS_BAND = 0, KOS_RS_ROW = 1 } kos_rs_order;
 
 typedef struct kos_opts {

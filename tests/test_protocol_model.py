@@ -100,8 +100,9 @@ def test_queue_orders_follow_the_pages(model):
     local copy; tiles of the local shard come first, then the remote shards
     in the movers' order ("Role switching only works if ...": local shard
     first, remote shards in consumption order).  Reduce-scatter band order
-    -- every chunk's band b before any band b+1 ("band by band across every
-    GPU's chunk"); row order -- one chunk after another.  Combine -- every
+    -- every chunk's band b before any band b+1 (the same paragraph's
+    consumer order for the reducers); row order -- one chunk after another.
+    Combine -- every
     down tile after all gate/up tiles of its unit, by about L units."""
     W, R, RB, M, NT = 4, 1, 2, 3, 5
     o = _order(model, f"ag {W} {R} {RB} {M} {NT}")
