@@ -15,10 +15,14 @@
 //
 // Scenarios are read from stdin, one per line:
 //   op grid world rank a b c mode crew fault spin
-//     op     ag | rs | combine
+//     op     ag | rs | combine | layer (the expert layer forward in one
+//            launch) | bwd (its backward in one launch)
 //     a b c  ag: row blocks per shard, slices per row block, column tiles
 //            rs: bands per chunk, column tiles, slabs per tile
 //            combine: units, gate/up tiles per unit, down tiles per unit
+//            layer / bwd: units, first-stage entries per unit (gate/up
+//            tiles; dH + SwiGLU recompute), second-stage tiles per unit
+//            (down tiles; dX)
 //     mode   fused | swapped (fused with the other switching policy: two-way
 //            all-gather and reduce-scatter, one-way combine) | fixed
 //     crew   workgroups that start communicating (fixed: only communicate)
@@ -35,6 +39,7 @@
 #include <cstring>
 #include <iostream>
 #include <memory>
+#include <numeric>
 #include <sstream>
 #include <string>
 #include <thread>
@@ -361,6 +366,138 @@ Result run_combine(const Scenario& s) {
   return r;
 }
 
+// ---- the expert layer in one launch (forward, and backward) ----------------
+// Movers deliver every unit's rows (two mover entries per unit, in an
+// order that completes the units out of order; in the forward, the first
+// `own` entries stand for our own tokens' entries, whose packed positions
+// the fold reads); a unit's first-stage entries wait for its rows, its
+// second-stage tiles for its first-stage entries; pushes are taken between
+// tiles when ready (two-way), the rest after the tiles; a fold block waits
+// for two units' second stage (and, forward, for every own-token mover
+// entry).  The forward starts with the router (R entries, counted) and the
+// per-expert scan (3 entries, each after every router entry), then a
+// barrier of every workgroup on the scan count before any mover entry.
+Result run_expert(const Scenario& s, bool layer) {
+  const int U = s.a, G = s.b, D = s.c;
+  const int L = (s.grid + G - 1) / G;
+  const int n_mv = 2 * U, n_own = layer ? U / 2 : 0, n_route = layer ? 5 : 0, n_scan = layer ? 3 : 0;
+  const int n_tile = U * (G + D), n_push = U, n_fold = U;
+  // counters: route, scan, own moved, rows_in[U], st1[U], st2[U]
+  Workspace ws(3 + 3 * U);
+  std::atomic<uint32_t>& c_route = ws.ctr[0];
+  std::atomic<uint32_t>& c_scan = ws.ctr[1];
+  std::atomic<uint32_t>& c_own = ws.ctr[2];
+  std::atomic<uint32_t>* rows_in = &ws.ctr[3];
+  std::atomic<uint32_t>* st1 = &ws.ctr[3 + U];
+  std::atomic<uint32_t>* st2 = &ws.ctr[3 + 2 * U];
+  std::vector<uint32_t> rows(2 * U, 0), h(U * G, 0), y(U * D, 0), scanned(n_scan, 0);
+  std::unique_ptr<std::atomic<int>[]> moved(new std::atomic<int>[n_mv]), done(new std::atomic<int>[n_tile]),
+      pushed(new std::atomic<int>[n_push]), folded(new std::atomic<int>[n_fold]);
+  for (int i = 0; i < n_mv; ++i) moved[i] = 0;
+  for (int i = 0; i < n_tile; ++i) done[i] = 0;
+  for (int i = 0; i < n_push; ++i) pushed[i] = 0;
+  for (int i = 0; i < n_fold; ++i) folded[i] = 0;
+  std::atomic<int> bad_data{0};
+  Faults f;
+  f.drop = s.fault == "drop";
+  f.kill = s.fault == "dead";
+  f.delay = s.fault == "delay";
+  int stride = 7;   // mover entry i fills row slot (i * stride) % n_mv: a permutation (stride coprime to n_mv)
+  while (std::gcd(stride, n_mv) != 1) stride += 2;
+  auto mv_slot = [&](int i) { return (int)(((long)i * stride) % n_mv); };
+  auto push = [&](int u) {
+    f.pace();
+    for (int nt = 0; nt < D; ++nt)
+      if (y[u * D + nt] != 10u * u + nt + 1) bad_data++;
+    pushed[u]++;
+  };
+  run_grid(s.grid, [&] {
+    ws.ticket.fetch_add(1);
+    bool ok = true;
+    if (layer) {
+      for (;;) {   // router entries
+        const uint32_t i = claim(ws, ws.head[0]);
+        if (i >= (uint32_t)n_route) break;
+        publish(c_route);
+      }
+      for (;;) {   // scan entries, each after every router entry
+        const uint32_t e = claim(ws, ws.head[1]);
+        if (e >= (uint32_t)n_scan) break;
+        if (!(ok = observe(ws, c_route, (uint32_t)n_route, s.spin))) break;
+        scanned[e] = 1;
+        publish(c_scan);
+      }
+      if (ok) ok = observe(ws, c_scan, (uint32_t)n_scan, s.spin);   // every workgroup: the layer's bookkeeping
+      for (int e = 0; e < n_scan && ok; ++e)
+        if (scanned[e] != 1) bad_data++;
+    }
+    for (bool first = true; ok; first = false) {   // movers
+      const uint32_t i = claim(ws, ws.head[2]);
+      if (i >= (uint32_t)n_mv) break;
+      if (first && f.die()) {   // claimed, never delivered, never departs normally
+        depart(ws, s.grid);
+        return;
+      }
+      f.pace();
+      const int slot = mv_slot((int)i), u = slot / 2;
+      rows[slot] = 1000u * u + slot % 2 + 1;
+      moved[i]++;
+      if (!f.skip_bump()) publish(rows_in[u]);
+      if ((int)i < n_own) publish(c_own);
+    }
+    for (; ok;) {   // tiles, two-way with pushes
+      for (;;) {
+        uint32_t hd = ws.head[4].load(std::memory_order_relaxed);
+        if (hd >= (uint32_t)n_push || st2[hd].load(std::memory_order_acquire) < (uint32_t)D) break;
+        if (!ws.head[4].compare_exchange_strong(hd, hd + 1, std::memory_order_relaxed)) continue;
+        push((int)hd);
+      }
+      const uint32_t j = claim(ws, ws.head[3]);
+      if (j >= (uint32_t)n_tile) break;
+      const kos::CombineTile t = kos::combine_tile_of((int)j, U, G, D, L, true, true);
+      if (!t.down) {
+        if (!(ok = observe(ws, rows_in[t.u], 2u, s.spin))) break;
+        for (int k = 0; k < 2; ++k)
+          if (rows[2 * t.u + k] != 1000u * t.u + k + 1) bad_data++;
+        h[t.u * G + t.nt] = 100u * t.u + t.nt + 1;
+        done[j]++;
+        publish(st1[t.u]);
+      } else {
+        if (!(ok = observe(ws, st1[t.u], (uint32_t)G, s.spin))) break;
+        for (int g = 0; g < G; ++g)
+          if (h[t.u * G + g] != 100u * t.u + g + 1) bad_data++;
+        y[t.u * D + t.nt] = 10u * t.u + t.nt + 1;
+        done[j]++;
+        publish(st2[t.u]);
+      }
+    }
+    for (; ok;) {   // pushes left over
+      const uint32_t i = claim(ws, ws.head[4]);
+      if (i >= (uint32_t)n_push) break;
+      if (!(ok = observe(ws, st2[i], (uint32_t)D, s.spin))) break;
+      push((int)i);
+    }
+    if (ok && layer) ok = observe(ws, c_own, (uint32_t)n_own, s.spin);
+    for (; ok;) {   // fold blocks: block b needs units b and U-1-b
+      const uint32_t i = claim(ws, ws.head[5]);
+      if (i >= (uint32_t)n_fold) break;
+      if (!observe(ws, st2[i], (uint32_t)D, s.spin) || !observe(ws, st2[U - 1 - i], (uint32_t)D, s.spin)) break;
+      if (y[i * D] != 10u * i + 1 || y[(U - 1 - i) * D] != 10u * (U - 1 - i) + 1) bad_data++;
+      folded[i]++;
+    }
+    depart(ws, s.grid);
+  });
+  Result r;
+  r.timeout = ws.status.load() != 0;
+  for (int i = 0; i < n_mv && !r.timeout; ++i) r.entries_ok &= moved[i] == 1;
+  for (int i = 0; i < n_tile && !r.timeout; ++i) r.entries_ok &= done[i] == 1;
+  for (int i = 0; i < n_push && !r.timeout; ++i) r.entries_ok &= pushed[i] == 1;
+  for (int i = 0; i < n_fold && !r.timeout; ++i) r.entries_ok &= folded[i] == 1;
+  r.data_ok = bad_data == 0;
+  r.reset_ok = all_zero(ws);
+  return r;
+}
+
 // "order <op> ..." lines print a queue's decoded entries, one per line, so
 // the tests can check the orders themselves:
 //   order ag W R RB M NT     moves "m shard rb sub", then tiles "t q shard rb nt"
@@ -418,7 +555,11 @@ int main() {
       std::printf("bad scenario: %s\n", line.c_str());
       return 2;
     }
-    Result r = s.op == "ag" ? run_ag(s) : s.op == "rs" ? run_rs(s) : run_combine(s);
+    Result r = s.op == "ag"      ? run_ag(s)
+               : s.op == "rs"    ? run_rs(s)
+               : s.op == "layer" ? run_expert(s, true)
+               : s.op == "bwd"   ? run_expert(s, false)
+                                 : run_combine(s);
     std::printf("status=%s entries=%s data=%s reset=%s\n", r.timeout ? "timeout" : "ok",
                 r.entries_ok ? "ok" : "bad", r.data_ok ? "ok" : "bad", r.reset_ok ? "ok" : "bad");
     std::fflush(stdout);

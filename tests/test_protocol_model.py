@@ -1,7 +1,8 @@
 """The queue / ready-counter protocol, modelled on the CPU with one thread per
 workgroup (tests/protocol_model/kos_protocol_model.cpp, built here with
 ThreadSanitizer): the kernels' own entry orders and role rules, every crew
-size, and forced faults.  Checks: no deadlock for any crew of one or more
+size, and forced faults; the expert layer's one-launch forward and
+backward protocols too.  Checks: no deadlock for any crew of one or more
 (every entry done exactly once, every read ordered after its write, the
 last workgroup out leaves the counters at zero), and a time-out -- not a
 hang -- when the protocol is broken (no mover at all, a dropped ready bump,
@@ -60,6 +61,29 @@ def test_every_crew_completes(model):
     out = run(model, lines)
     bad = [(l, o) for l, o in zip(lines, out) if o != OK]
     assert not bad, bad[:5]
+
+
+def test_expert_layer_one_launch_completes(model):
+    """The expert layer forward in one launch (router, scan, barrier,
+    movers, two-way tiles and pushes, fold) and its backward (movers,
+    first-stage entries, second-stage tiles, pushes, fold): every grid and
+    shape completes with every entry done once and every read after its
+    write."""
+    lines = []
+    for grid in (2, 3, 5, 8):
+        for op in ("layer", "bwd"):
+            for u, g, d in ((1, 1, 1), (5, 2, 3), (9, 3, 2), (14, 4, 5)):
+                lines.append(f"{op} {grid} 1 0 {u} {g} {d} fused 0 none 10000000")
+            lines.append(f"{op} {grid} 1 0 6 2 2 fused 0 delay 100000000")
+    assert run(model, lines) == [OK] * len(lines)
+
+
+def test_expert_layer_broken_protocol_times_out(model):
+    lines = ["layer 6 1 0 9 2 3 fused 0 drop 20000",   # one unit's row bump lost
+             "bwd 6 1 0 9 2 3 fused 0 drop 20000",
+             "layer 6 1 0 9 2 3 fused 0 dead 20000",   # a mover dies holding an entry
+             "bwd 6 1 0 9 2 3 fused 0 dead 20000"]
+    assert run(model, lines, timeout=120) == [TIMEOUT] * len(lines)
 
 
 def test_slow_communication_still_completes(model):
