@@ -42,7 +42,11 @@ special cases (there is no printed example), which fixes its definition but
 not a value from the pages.
 The backward functions are pinned in ``tests/test_oracle_bwd_pins.py`` by
 central finite differences of an unrounded forward written out there, and
-by special cases and the softmax invariant.
+by special cases and the softmax invariant; the variant that takes the
+forward's bf16 copies of g and u (``expert_gate_up``, ``saved=True``) by a
+brute-force sum on integer inputs, by equality with the recomputing
+backward where those copies are exact, and by bf16-sized distance to it
+otherwise.
 """
 from __future__ import annotations
 
@@ -481,15 +485,40 @@ def _val(a, rounded):
     return bf16_to_f64(a) if rounded else np.asarray(a, dtype=np.float64)
 
 
-def expert_ffn_bwd(x_bits, dy_rows, wg_bits, wu_bits, wd_bits, rounded: bool = True):
+def expert_gate_up(x_bits, wg_bits, wu_bits):
+    """The gate and up projections of rows X as a forward pass keeps them for
+    its backward pass: (bf16(X.Wg), bf16(X.Wu)), bf16 bits [n,F] each."""
+    x = bf16_to_f64(x_bits)
+    return round_bf16(x @ bf16_to_f64(wg_bits)), round_bf16(x @ bf16_to_f64(wu_bits))
+
+
+def grouped_gate_up(grouped, grouped_offsets, wg, wu):
+    """expert_gate_up over every local expert's rows (expert e: rows
+    [grouped_offsets[e], grouped_offsets[e+1]))."""
+    n = np.asarray(grouped).shape[0]
+    F = np.asarray(wg).shape[2]
+    g, u = np.zeros((n, F), np.uint16), np.zeros((n, F), np.uint16)
+    for e in range(len(grouped_offsets) - 1):
+        lo, hi = int(grouped_offsets[e]), int(grouped_offsets[e + 1])
+        if hi > lo:
+            g[lo:hi], u[lo:hi] = expert_gate_up(grouped[lo:hi], wg[e], wu[e])
+    return g, u
+
+
+def expert_ffn_bwd(x_bits, dy_rows, wg_bits, wu_bits, wd_bits, rounded: bool = True, saved: bool = False):
     """Data gradient of the SwiGLU expert for rows X (bf16 [n,H]) and output
     gradients dY ([n,H]: bf16 bits, or float64 when not rounded): returns
-    (dG, dU, dX) -- [n,F], [n,F], [n,H], bf16 bits when `rounded`."""
+    (dG, dU, dX) -- [n,F], [n,F], [n,H], bf16 bits when `rounded`.
+    saved: g and u are the bf16 values the forward kept (expert_gate_up)
+    rather than X.Wg and X.Wu themselves."""
     x = bf16_to_f64(x_bits)
     wg, wu, wd = bf16_to_f64(wg_bits), bf16_to_f64(wu_bits), bf16_to_f64(wd_bits)
     dy = _val(dy_rows, rounded)
-    g = x @ wg
-    u = x @ wu
+    if saved:
+        g, u = (bf16_to_f64(v) for v in expert_gate_up(x_bits, wg_bits, wu_bits))
+    else:
+        g = x @ wg
+        u = x @ wu
     dh = dy @ wd.T
     du = dh * silu(g)
     dg = dh * u * dsilu(g)
@@ -581,13 +610,15 @@ def router_grad(dy_bits, idx, w, perm, offsets, y_grouped, grouped_offsets, peer
 
 
 def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return,
-                  peer_send_grad, peer_return_grad, world: int, rank: int, k: int, rounded: bool = True):
+                  peer_send_grad, peer_return_grad, world: int, rank: int, k: int, rounded: bool = True,
+                  saved: bool = False):
     """The whole expert layer's backward direction for one rank: the forward
     routing and expert outputs (``moe_layer``), the pairs' gradients
     dispatched, the experts' data gradients, the results pushed back and
     summed per token, and the router gradient.  Returns a dict with the
     forward's fields and send_grad, grouped_grad, dh, dg, du, dx_grouped,
-    out_return_grad, dx, dlogits."""
+    out_return_grad, dx, dlogits.  saved: the experts' g and u are the
+    forward's bf16 copies (expert_ffn_bwd)."""
     f = moe_layer(x_bits, logits, wg, wu, wd, peer_send, peer_counts, peer_return, world, rank, k)
     g = dispatch_grad(dy_bits, f["w"], f["perm"], f["offsets"], peer_send_grad, peer_counts, world, rank,
                       rounded)
@@ -601,7 +632,7 @@ def moe_layer_bwd(dy_bits, x_bits, logits, wg, wu, wd, peer_send, peer_counts, p
         lo, hi = int(go[e]), int(go[e + 1])
         if hi > lo:
             dg[lo:hi], du[lo:hi], dxg[lo:hi] = expert_ffn_bwd(f["grouped"][lo:hi], g["grouped"][lo:hi], wg[e],
-                                                              wu[e], wd[e], rounded)
+                                                              wu[e], wd[e], rounded, saved)
             dh[lo:hi] = expert_dh(g["grouped"][lo:hi], wd[e], rounded)
     pc = np.asarray(peer_counts)
     out_return = push(dxg, f["row_src"], world, rank, pc.sum(axis=1)) if rounded else None

@@ -280,3 +280,68 @@ def test_rounded_stays_within_bf16_error_of_unrounded():
     got = O.bf16_to_f64(out["dx"])
     err = np.linalg.norm(got - ref["dx"]) / np.linalg.norm(ref["dx"])
     assert err < 2e-2
+
+
+def _ints(rng, shape):
+    """bf16 bits of values in {-1, 0, 1}."""
+    return O.round_bf16(rng.integers(-1, 2, shape).astype(np.float64))
+
+
+def test_gate_up_kept_by_the_forward():
+    """Rows and weights in {-1, 0, 1}: every X.Wg and X.Wu entry is an
+    integer of magnitude <= H = 16, exact in bf16, so the kept copies are the
+    brute-force sums themselves -- the gate from Wg, the up from Wu, each
+    expert's rows with its own weights."""
+    rng = np.random.default_rng(140)
+    n, H, F = 5, 16, 6
+    x = _ints(rng, (n, H))
+    wg, wu = _ints(rng, (2, H, F)), _ints(rng, (2, H, F))
+    X, G, U = O.bf16_to_f64(x), O.bf16_to_f64(wg), O.bf16_to_f64(wu)
+    g, u = O.grouped_gate_up(x, [0, 2, 5], wg, wu)
+    for r in range(n):
+        e = 0 if r < 2 else 1
+        for c in range(F):
+            sg = sum(X[r, h] * G[e, h, c] for h in range(H))
+            su = sum(X[r, h] * U[e, h, c] for h in range(H))
+            assert O.bf16_to_f64(g[r, c]) == sg and O.bf16_to_f64(u[r, c]) == su, (r, c)
+    assert not np.array_equal(g, u)
+
+
+def test_saved_backward_equals_recompute_when_g_u_are_exact():
+    """When X.Wg and X.Wu are exact in bf16 the kept copies are the values
+    themselves, so the saved-activation backward is bit-identical to the
+    recomputing one -- for one expert and for the whole layer."""
+    rng = np.random.default_rng(141)
+    n, H, F = 6, 16, 8
+    x = _ints(rng, (n, H))
+    wg, wu, wd = _ints(rng, (H, F)), _ints(rng, (H, F)), _w(rng, (F, H), 0.4)
+    dy = _w(rng, (n, H), 1.0)
+    a = O.expert_ffn_bwd(x, dy, wg, wu, wd, saved=False)
+    b = O.expert_ffn_bwd(x, dy, wg, wu, wd, saved=True)
+    assert all(np.array_equal(p, q) for p, q in zip(a, b))
+    assert np.any(O.bf16_to_f64(a[0])) and np.any(O.bf16_to_f64(a[1]))
+    c = _case(rng, 2, 1, H=16, rounded=True)
+    c["x"] = _ints(rng, c["x"].shape)
+    c["wg"], c["wu"] = _ints(rng, c["wg"].shape), _ints(rng, c["wu"].shape)
+    c["ps"] = [None if t is None else _ints(rng, t.shape) for t in c["ps"]]
+    full = _bwd(c)
+    kept = O.moe_layer_bwd(c["dy"], c["x"], c["lg"], c["wg"], c["wu"], c["wd"], c["ps"], c["pc"], c["pr"],
+                           c["psg"], c["prg"], c["R"], c["rank"], c["k"], True, saved=True)
+    for key in ("dg", "du", "dx_grouped", "dx", "dlogits"):
+        assert np.array_equal(full[key], kept[key]), key
+
+
+def test_saved_backward_stays_within_bf16_of_recompute():
+    """General values: the kept g and u carry one bf16 rounding, which moves
+    dG, dU and dX by about that much and no more."""
+    rng = np.random.default_rng(142)
+    c = _case(rng, 4, 2, rounded=True)
+    full = _bwd(c)
+    kept = O.moe_layer_bwd(c["dy"], c["x"], c["lg"], c["wg"], c["wu"], c["wd"], c["ps"], c["pc"], c["pr"],
+                           c["psg"], c["prg"], c["R"], c["rank"], c["k"], True, saved=True)
+    changed = False
+    for key in ("dg", "du", "dx_grouped"):
+        a, b = O.bf16_to_f64(full[key]), O.bf16_to_f64(kept[key])
+        changed |= not np.array_equal(a, b)
+        assert np.linalg.norm(a - b) <= 2e-2 * np.linalg.norm(a), key
+    assert changed
