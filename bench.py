@@ -176,14 +176,17 @@ def crew_sweep_moe(torch, kos, KI, inp, ws, shape, flush, reps, planned, rank):
     return out
 
 
-def layer_op(kos, m, ws, shape, rank=0, trace=False):
-    """The whole expert layer in one launch (kos_moe_layer) on resident inputs."""
+def layer_op(kos, m, ws, shape, rank=0, trace=False, save=False):
+    """The whole expert layer in one launch (kos_moe_layer) on resident inputs
+    (save: also keeping bf16 g and u in m["gs"], m["us"])."""
     from gemm_collective_persistent_amd.api import moe_shape as mk_shape
     shp = mk_shape(shape.world, rank, shape.tokens, shape.hidden, shape.experts, shape.topk, shape.ffn)
     o = kos.opts(trace=trace)
+    kw = dict(gate_save=m["gs"], up_save=m["us"]) if save else {}
     return lambda: kos.moe_layer(shp, m["x"], m["logits"], m["peer_send"], m["peer_counts"], m["wg"], m["wu"],
                                  m["wd"], m["peer_return"], m["idx"], m["w"], m["counts"], m["perm"], m["send"],
-                                 m["grouped"], m["goff"], m["row_src"], m["h"], m["yg"], m["ret"], m["y"], ws, o)
+                                 m["grouped"], m["goff"], m["row_src"], m["h"], m["yg"], m["ret"], m["y"], ws, o,
+                                 **kw)
 
 
 def single_launch(torch, kos, KI, m, ws, flush, reps, shape, two_ms, rank=0):
@@ -219,24 +222,34 @@ def build_moe_grad(torch, KI, shape, m, rank=0):
     return g
 
 
-def bwd_op(kos, m, g, ws, shape, rank=0, trace=False):
+def bwd_op(kos, m, g, ws, shape, rank=0, trace=False, saved=False):
     """The expert layer's backward in one launch (kos_moe_layer_bwd), reading
-    the forward's buffers in `m` (kept from a forward call)."""
+    the forward's buffers in `m` (kept from a forward call; saved: with the
+    g and u it kept, and no dH written)."""
     from gemm_collective_persistent_amd.api import moe_shape as mk_shape
     shp = mk_shape(shape.world, rank, shape.tokens, shape.hidden, shape.experts, shape.topk, shape.ffn)
     o = kos.opts(trace=trace)
+    kw = dict(gate_saved=m["gs"], up_saved=m["us"]) if saved else {}
     return lambda: kos.moe_layer_bwd(shp, g["dy"], m["idx"], m["w"], m["perm"], m["counts"], m["peer_counts"],
                                      m["grouped"], m["goff"], m["row_src"], m["yg"], m["peer_return"], m["wg"],
                                      m["wu"], m["wd"], g["peer_send_grad"], g["send"], g["dres"], g["dg"], g["du"],
-                                     g["dh"], g["dxg"], g["peer_return_grad"], g["ret"], g["dx"], g["dl"], ws, o)
+                                     None if saved else g["dh"], g["dxg"], g["peer_return_grad"], g["ret"], g["dx"],
+                                     g["dl"], ws, o, **kw)
 
 
-def torch_bwd_baseline(torch, m, g, shape, rank=0):
+def _rel(a, b):
+    """||a - b|| / ||b|| in fp32."""
+    a, b = a.float(), b.float()
+    return float((a - b).norm() / b.norm().clamp_min(1e-30))
+
+
+def torch_bwd_baseline(torch, m, g, shape, rank=0, saved=False):
     """The same backward composed of PyTorch operations on the same GPU
     (hipBLASLt GEMMs per expert, elementwise and indexing kernels): a
     same-GPU library baseline.  Index maps are built once, untimed, from the
     forward's routing; the returned closure computes dx and dlogits (and the
-    rows sent and returned) from the resident inputs."""
+    rows sent and returned) from the resident inputs.  saved: g and u are the
+    forward's kept copies (m["gs"], m["us"]) rather than two more GEMMs."""
     import numpy as np
     T, k, E, H, R = shape.tokens, shape.topk, shape.experts, shape.hidden, shape.world
     el = shape.e_local
@@ -293,9 +306,12 @@ def torch_bwd_baseline(torch, m, g, shape, rank=0):
         for e, (lo, hi) in enumerate(bounds):
             if hi == lo:
                 continue
-            x = xg[lo:hi]
-            gg = (x @ wg[e]).float()
-            uu = (x @ wu[e]).float()
+            if saved:
+                gg, uu = m["gs"][lo:hi].float(), m["us"][lo:hi].float()
+            else:
+                x = xg[lo:hi]
+                gg = (x @ wg[e]).float()
+                uu = (x @ wu[e]).float()
             dh = (dres[lo:hi] @ wd[e].t()).float()
             sg = torch.sigmoid(gg)
             du = (dh * gg * sg).to(torch.bfloat16)
@@ -351,14 +367,49 @@ def moe_backward(torch, kos, KI, m, ws, flush, reps, shape, fwd_ms, rank=0, base
         run()
         torch.cuda.synchronize()
         tb = time_ops(torch, [("torch_bwd", run)], reps, ws, flush)[0][0]
-
-        def rel(a, b):
-            a, b = a.float(), b.float()
-            return float((a - b).norm() / b.norm().clamp_min(1e-30))
         d["torch_composed"] = {"ms": round(tb, 4), "speedup": round(tb / t, 3),
-                               "dx_rel_diff": float(f"{rel(out['dx'], g['dx']):.3g}"),
-                               "dlogits_rel_diff": float(f"{rel(out['dl'], g['dl']):.3g}"),
+                               "dx_rel_diff": float(f"{_rel(out['dx'], g['dx']):.3g}"),
+                               "dlogits_rel_diff": float(f"{_rel(out['dl'], g['dl']):.3g}"),
                                "dlogits_norm": float(f"{float(g['dl'].norm()):.4g}")}
+    d["saved_activations"] = saved_backward(torch, kos, m, g, ws, flush, reps, shape, fwd_ms, t, rows, rank,
+                                            baseline)
+    return d
+
+
+def saved_backward(torch, kos, m, g, ws, flush, reps, shape, fwd_ms, bwd_ms, rows, rank=0, baseline=True):
+    """The forward keeps bf16 g and u (two more [rows, F] outputs) and the
+    backward reads them instead of recomputing them, writing no dH: the
+    forward's extra time, the backward's time and TFLOP/s (6 H F per row,
+    all of it algorithmic), forward + backward tokens/s, and the PyTorch
+    composition on the same kept values."""
+    cap, F = m["grouped"].shape[0], shape.ffn
+    m["gs"] = torch.empty((cap, F), dtype=torch.bfloat16, device="cuda")
+    m["us"] = torch.empty((cap, F), dtype=torch.bfloat16, device="cuda")
+    fs = layer_op(kos, m, ws, shape, rank, save=True)
+    fs()
+    ws.status()
+    tf = time_ops(torch, [("moe_layer_save", fs)], reps, ws, flush)[0][0]
+    fb = bwd_op(kos, m, g, ws, shape, rank, saved=True)
+    fb()
+    ws.status()
+    tb = time_ops(torch, [("moe_layer_bwd_saved", fb)], reps, ws, flush)[0][0]
+    fl = rows * 6.0 * shape.hidden * shape.ffn
+    tfl = fl / (tb * 1e-3) / 1e12
+    d = {"forward_ms": round(tf, 4), "forward_extra_ms": round(tf - fwd_ms, 4), "ms": round(tb, 4),
+         "tflops": round(tfl, 1), "pct_bf16_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1),
+         "speedup_vs_recompute": round(bwd_ms / tb, 3),
+         "kept_bytes": 2 * rows * F * 2,
+         "fwd_plus_bwd_tokens_per_s": round(shape.tokens / ((tf + tb) * 1e-3), 1),
+         "fwd_plus_bwd_speedup_vs_recompute": round((fwd_ms + bwd_ms) / (tf + tb), 3)}
+    if baseline:
+        run, out = torch_bwd_baseline(torch, m, g, shape, rank, saved=True)
+        run()
+        torch.cuda.synchronize()
+        tt = time_ops(torch, [("torch_bwd_saved", run)], reps, ws, flush)[0][0]
+        d["torch_composed"] = {"ms": round(tt, 4), "speedup": round(tt / tb, 3),
+                               "dx_rel_diff": float(f"{_rel(out['dx'], g['dx']):.3g}"),
+                               "dlogits_rel_diff": float(f"{_rel(out['dl'], g['dl']):.3g}")}
+    del m["gs"], m["us"]
     return d
 
 

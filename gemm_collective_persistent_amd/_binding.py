@@ -99,12 +99,13 @@ def _load():
         "kos_moe_dispatch": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, P, PP, POINTER(c_int64),
                                        P, c_int64, P, P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_layer": (c_int32, [POINTER(MoeShape), P, P, PP, P, P, P, P, PP, P, P, P, P, PP, POINTER(c_int64),
-                                    P, c_int64, P, P, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
+                                    P, c_int64, P, P, P, P, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P,
+                                    c_size_t, P]),
         "kos_moe_combine": (c_int32, [POINTER(MoeShape), P, P, P, c_int64, P, P, P, P, P, P, P, P,
-                                      PP, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
+                                      PP, P, P, P, P, PP, POINTER(c_int64), P, POINTER(Opts), P, c_size_t, P]),
         "kos_moe_layer_bwd": (c_int32, [POINTER(MoeShape), P, P, P, P, P, P, P, c_int64, P, P, P, PP, P, P, P,
-                                        PP, PP, POINTER(c_int64), P, P, P, P, P, PP, PP, POINTER(c_int64), P, P,
-                                        POINTER(Opts), P, c_size_t, P]),
+                                        P, P, PP, PP, POINTER(c_int64), P, P, P, P, P, PP, PP, POINTER(c_int64),
+                                        P, P, POINTER(Opts), P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name, None)

@@ -45,6 +45,16 @@ def _min_rows(t: torch.Tensor, rows: int, name: str):
         raise ValueError(f"{name}: {t.shape[0]} rows, needs at least {rows}")
 
 
+def _check_saved(g, u, cap: int, F: int):
+    """The optional saved gate/up activations: both or neither, bf16 [>= cap, F]."""
+    if (g is None) != (u is None):
+        raise ValueError("the saved gate and up activations are given together or not at all")
+    for name, t in (("gate", g), ("up", u)):
+        if t is not None:
+            _need(t, torch.bfloat16, name, 2, (None, F))
+            _min_rows(t, cap, name)
+
+
 class Workspace:
     """Device workspace of kos_workspace_bytes() bytes, zeroed once."""
 
@@ -300,11 +310,13 @@ def moe_dispatch(s: MoeShape, x, logits, peer_send, peer_counts, topk_idx, topk_
 
 def moe_combine(s: MoeShape, x_grouped, grouped_offsets, row_src, w_gate, w_up, w_down,
                 topk_idx, topk_w, counts, perm, peer_counts, peer_return, h, y_grouped,
-                out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+                out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None, *,
+                gate_save=None, up_save=None) -> None:
     """kos_moe_combine (see include/kos.h for every buffer's layout).  h and
     y_grouped must hold at least x_grouped's rows (the capacity); each
     out_return[p] must hold the rows p sent us, and peer_return[d] the rows
-    we sent d."""
+    we sent d.  gate_save / up_save (optional, together): bf16 [cap, F]
+    outputs for moe_layer_bwd."""
     T, H, E, R, F = s.tokens, s.hidden, s.experts, s.world, s.ffn
     E_loc = E // R
     if len(peer_return) != R or len(out_return) != R:
@@ -323,6 +335,7 @@ def moe_combine(s: MoeShape, x_grouped, grouped_offsets, row_src, w_gate, w_up, 
     _min_rows(h, cap, "h")
     _need(y_grouped, torch.bfloat16, "y_grouped", 2, (None, H))
     _min_rows(y_grouped, cap, "y_grouped")
+    _check_saved(gate_save, up_save, cap, F)
     if T > 0:
         _need(y, torch.bfloat16, "y", 2, (T, H))
     for p in range(R):
@@ -339,13 +352,15 @@ def moe_combine(s: MoeShape, x_grouped, grouped_offsets, row_src, w_gate, w_up, 
     check(lib.kos_moe_combine(ctypes.byref(s), _p(x_grouped), _p(grouped_offsets), _p(row_src),
                               cap, _p(w_gate), _p(w_up), _p(w_down), _p(topk_idx),
                               _p(topk_w), _p(counts), _p(perm), _p(peer_counts), pret, _p(h),
-                              _p(y_grouped), oret, rcaps, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes,
+                              _p(gate_save), _p(up_save), _p(y_grouped), oret, rcaps, _p(y),
+                              ctypes.byref(o), ws.ptr, ws.nbytes,
                               _stream(stream)))
 
 
 def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_down, peer_return,
               topk_idx, topk_w, counts, perm, out_send, x_grouped, grouped_offsets, row_src, h, y_grouped,
-              out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+              out_return, y, ws: Workspace, o: Optional[Opts] = None, stream=None, *,
+              gate_save=None, up_save=None) -> None:
     """kos_moe_layer: the whole expert layer in one launch -- what moe_dispatch
     followed by moe_combine computes, with the same buffers (see include/kos.h)."""
     T, H, E, R, F = s.tokens, s.hidden, s.experts, s.world, s.ffn
@@ -372,6 +387,7 @@ def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_do
     _min_rows(h, cap, "h")
     _need(y_grouped, torch.bfloat16, "y_grouped", 2, (None, H))
     _min_rows(y_grouped, cap, "y_grouped")
+    _check_saved(gate_save, up_save, cap, F)
     for p in range(R):
         if p == s.rank:
             continue
@@ -386,19 +402,23 @@ def moe_layer(s: MoeShape, x, logits, peer_send, peer_counts, w_gate, w_up, w_do
     o = o if o is not None else make_opts()
     check(lib.kos_moe_layer(ctypes.byref(s), _p(x), _p(logits), arr["ps"], _p(peer_counts), _p(w_gate), _p(w_up),
                             _p(w_down), arr["pr"], _p(topk_idx), _p(topk_w), _p(counts), _p(perm), arr["os"], scaps,
-                            _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(h), _p(y_grouped), arr["or"],
+                            _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(h), _p(gate_save),
+                            _p(up_save), _p(y_grouped), arr["or"],
                             rcaps, _p(y), ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))
 
 
 def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, x_grouped, grouped_offsets,
                   row_src, y_grouped, peer_return, w_gate, w_up, w_down, peer_send_grad, out_send_grad,
                   dres_grouped, dg, du, dh, dx_grouped, peer_return_grad, out_return_grad, dx, dlogits,
-                  ws: Workspace, o: Optional[Opts] = None, stream=None) -> None:
+                  ws: Workspace, o: Optional[Opts] = None, stream=None, *,
+                  gate_saved=None, up_saved=None) -> None:
     """kos_moe_layer_bwd: the expert layer's data and router gradients in one
     launch (see include/kos.h).  The forward's routing and grouped buffers
     come in unchanged; grouped_cap is x_grouped's row count, and each
     out_send_grad[d] / out_return_grad[p] buffer's row count is its
-    capacity."""
+    capacity.  gate_saved / up_saved (optional, together): the forward's
+    gate_save / up_save, used instead of recomputing g and u; dh may then be
+    None."""
     T, H, E, R, F = s.tokens, s.hidden, s.experts, s.world, s.ffn
     E_loc = E // R
     for name, lst in (("peer_return", peer_return), ("peer_send_grad", peer_send_grad),
@@ -424,8 +444,12 @@ def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, 
                            ("du", du, F), ("dx_grouped", dx_grouped, H)):
         _need(t, torch.bfloat16, name, 2, (None, width))
         _min_rows(t, cap, name)
-    _need(dh, torch.float32, "dh", 2, (None, F))
-    _min_rows(dh, cap, "dh")
+    _check_saved(gate_saved, up_saved, cap, F)
+    if dh is None and gate_saved is None:
+        raise ValueError("dh is needed unless the saved gate and up activations are given")
+    if dh is not None:
+        _need(dh, torch.float32, "dh", 2, (None, F))
+        _min_rows(dh, cap, "dh")
     lists = (("peer_return", peer_return, True), ("peer_send_grad", peer_send_grad, True),
              ("out_send_grad", out_send_grad, False), ("peer_return_grad", peer_return_grad, True),
              ("out_return_grad", out_return_grad, False))
@@ -442,7 +466,8 @@ def moe_layer_bwd(s: MoeShape, dy, topk_idx, topk_w, perm, counts, peer_counts, 
     o = o if o is not None else make_opts()
     check(lib.kos_moe_layer_bwd(ctypes.byref(s), _p(dy), _p(topk_idx), _p(topk_w), _p(perm), _p(counts),
                                 _p(peer_counts), _p(x_grouped), cap, _p(grouped_offsets), _p(row_src), _p(y_grouped),
-                                arr["peer_return"], _p(w_gate), _p(w_up), _p(w_down), arr["peer_send_grad"],
+                                arr["peer_return"], _p(w_gate), _p(w_up), _p(w_down), _p(gate_saved),
+                                _p(up_saved), arr["peer_send_grad"],
                                 arr["out_send_grad"], scaps, _p(dres_grouped), _p(dg), _p(du), _p(dh), _p(dx_grouped),
                                 arr["peer_return_grad"], arr["out_return_grad"], rcaps, _p(dx), _p(dlogits),
                                 ctypes.byref(o), ws.ptr, ws.nbytes, _stream(stream)))

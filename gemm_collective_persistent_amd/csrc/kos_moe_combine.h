@@ -28,6 +28,8 @@ struct CombineParams {
   const int32_t* peer_counts;
   const uint16_t* peer_return[8];
   uint16_t* h;
+  uint16_t* g_save;       // optional [cap, F] bf16: X.Wg and X.Wu as computed (for a backward pass)
+  uint16_t* u_save;
   uint16_t* yg;
   uint16_t* out_return[8];
   int64_t return_cap[8];  // rows out_return[p] holds
@@ -129,8 +131,9 @@ __device__ __forceinline__ void decode_tile(const CombineParams& p, int U, int j
 }
 
 // COH_X: the grouped input rows were written by this launch (the
-// single-launch layer's movers): read device-coherent.
-template <class S, int RING, bool COH_X = false>
+// single-launch layer's movers): read device-coherent.  SAVE: g and u are
+// also stored when p.g_save is set (false: never; the code is left out).
+template <class S, int RING, bool COH_X = false, bool SAVE = true>
 __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit& x, int nt, f32x16 (&acc)[S::TM][S::TN]) {
   constexpr int HN = S::BN / 2;    // h columns per tile
   const int64_t H = p.H, F = p.F;
@@ -138,6 +141,12 @@ __device__ __forceinline__ void gate_up_tile(const CombineParams& p, const Unit&
   tile_mainloop<S, true, COH_X, RING>(acc, p.xg + (int64_t)x.row0 * H, H, x.m_valid, b, p.H);
   // read by this launch's down tiles: device-coherent stores
   tile_store_rows<S, RING, true, true>(acc, p.h + (int64_t)x.row0 * F + (int64_t)nt * HN, F, x.m_valid);
+  if (SAVE && p.g_save) {   // the activations a backward pass reads instead of recomputing them
+    KOS_WAITCNT(0, 0);
+    lds_barrier();   // every wave has read the h tile out of the ring
+    const int64_t off = (int64_t)x.row0 * F + (int64_t)nt * HN;
+    tile_store_rows_pair<S, RING, false>(acc, p.g_save + off, p.u_save + off, F, x.m_valid);
+  }
 }
 
 // COH: h was written by this launch's gate/up tiles (read device-coherent).

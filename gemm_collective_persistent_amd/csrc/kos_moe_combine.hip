@@ -171,7 +171,8 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
                                       const void* w_up, const void* w_down, const int32_t* topk_idx,
                                       const float* topk_w, const int32_t* counts, const int32_t* perm,
                                       const int32_t* peer_counts, const void* const* peer_return, void* h,
-                                      void* y_grouped, void* const* out_return, const int64_t* return_caps,
+                                      void* gate_save, void* up_save, void* y_grouped,
+                                      void* const* out_return, const int64_t* return_caps,
                                       void* y, const kos_opts* opts,
                                       void* ws, size_t ws_bytes, void* stream) {
   if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
@@ -198,8 +199,10 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
     if (!aligned16(peer_return[q]) || !aligned16(out_return[q])) return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(x_grouped) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(h) ||
-      !aligned16(y_grouped) || !aligned16(y))
+      !aligned16(y_grouped) || !aligned16(y) || !aligned16(gate_save) || !aligned16(up_save))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  if ((gate_save == nullptr) != (up_save == nullptr))
+    return fail(KOS_ERR_ARG, "gate_save and up_save are given together or not at all");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
   // the tiles address one expert's weights through 32-bit buffer offsets
   if ((int64_t)s->hidden * s->ffn * 2 >= (int64_t(1) << 31))
@@ -240,6 +243,8 @@ extern "C" kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grou
     p.return_cap[q] = q == r ? 0 : return_caps[q];
   }
   p.h = static_cast<uint16_t*>(h);
+  p.g_save = static_cast<uint16_t*>(gate_save);
+  p.u_save = static_cast<uint16_t*>(up_save);
   p.yg = static_cast<uint16_t*>(y_grouped);
   p.y = static_cast<uint16_t*>(y);
   const int BMt = big ? CombineTileBig::BM : CombineTileSmall::BM;

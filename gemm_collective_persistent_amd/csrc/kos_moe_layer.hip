@@ -82,7 +82,8 @@ __device__ __forceinline__ bool layer_meta(const CombineParams& p, const Dispatc
   return s->ok != 0;
 }
 
-template <class S, class ST, class ST2>
+// SAVE: the gate/up tiles also keep g and u (gate_save, up_save given).
+template <class S, class ST, class ST2, bool SAVE>
 __global__ __launch_bounds__(S::NT, 1) void moe_layer_kernel(LayerParams args) {
   constexpr int BM = S::BM, NW = S::NT / 64;
   constexpr int MT = NW;                           // our tokens per mover entry: one per wave
@@ -204,9 +205,9 @@ __global__ __launch_bounds__(S::NT, 1) void moe_layer_kernel(LayerParams args) {
         }
         tr.put(KOS_TR_WAIT, j, t0);
         t0 = tr.now();
-        if (tail2) gate_up_tile<ST2, RB, true>(p, x, nt, acc_t2);
-        else if (tail) gate_up_tile<ST, RB, true>(p, x, nt, acc_t);
-        else gate_up_tile<S, RB, true>(p, x, nt, acc);
+        if (tail2) gate_up_tile<ST2, RB, true, SAVE>(p, x, nt, acc_t2);
+        else if (tail) gate_up_tile<ST, RB, true, SAVE>(p, x, nt, acc_t);
+        else gate_up_tile<S, RB, true, SAVE>(p, x, nt, acc);
         wg_publish(&gu_done[u], 1u);
         tr.put(KOS_TR_TILE, j, t0);
       } else {
@@ -275,9 +276,10 @@ extern "C" kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const
                                     const void* const* peer_return, int32_t* topk_idx, float* topk_w,
                                     int32_t* counts, int32_t* perm, void* const* out_send,
                                     const int64_t* send_caps, void* x_grouped, int64_t grouped_cap,
-                                    int32_t* grouped_offsets, int32_t* row_src, void* h, void* y_grouped,
-                                    void* const* out_return, const int64_t* return_caps, void* y,
-                                    const kos_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+                                    int32_t* grouped_offsets, int32_t* row_src, void* h, void* gate_save,
+                                    void* up_save, void* y_grouped, void* const* out_return,
+                                    const int64_t* return_caps, void* y, const kos_opts* opts, void* ws,
+                                    size_t ws_bytes, void* stream) {
   if (!s) return fail(KOS_ERR_ARG, "shape is NULL");
   const int R = s->world, r = s->rank;
   if (R < 1 || R > 8) return fail(KOS_ERR_ARG, "world %d outside [1, 8]", R);
@@ -303,8 +305,10 @@ extern "C" kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const
       return fail(KOS_ERR_ALIGN, "peer buffer not aligned");
   }
   if (!aligned16(x) || !aligned16(x_grouped) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      !aligned16(h) || !aligned16(y_grouped) || !aligned16(y))
+      !aligned16(h) || !aligned16(y_grouped) || !aligned16(y) || !aligned16(gate_save) || !aligned16(up_save))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
+  if ((gate_save == nullptr) != (up_save == nullptr))
+    return fail(KOS_ERR_ARG, "gate_save and up_save are given together or not at all");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
   if ((int64_t)s->hidden * s->ffn * 2 >= (int64_t(1) << 31))
     return fail(KOS_ERR_SHAPE, "one expert's weight (hidden x ffn bf16) must be smaller than 2 GiB");
@@ -385,6 +389,8 @@ extern "C" kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const
     p.return_cap[q] = q == r ? 0 : return_caps[q];
   }
   p.h = static_cast<uint16_t*>(h);
+  p.g_save = static_cast<uint16_t*>(gate_save);
+  p.u_save = static_cast<uint16_t*>(up_save);
   p.yg = static_cast<uint16_t*>(y_grouped);
   p.y = static_cast<uint16_t*>(y);
   const int BMt = big ? CombineTileBig::BM : CombineTileSmall::BM;
@@ -406,11 +412,18 @@ extern "C" kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const
   if ((size_t)lp.n_counters > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  if (big)
-    hipLaunchKernelGGL((moe_layer_kernel<CombineTileBig, CombineTailBig, CombineTail2Big>), dim3(o.grid),
+  const bool save = gate_save != nullptr;
+  if (big && save)
+    hipLaunchKernelGGL((moe_layer_kernel<CombineTileBig, CombineTailBig, CombineTail2Big, true>), dim3(o.grid),
                        dim3(CombineTileBig::NT), 0, strm, lp);
-  else
-    hipLaunchKernelGGL((moe_layer_kernel<CombineTileSmall, CombineTailSmall, CombineTailSmall>), dim3(o.grid),
+  else if (big)
+    hipLaunchKernelGGL((moe_layer_kernel<CombineTileBig, CombineTailBig, CombineTail2Big, false>), dim3(o.grid),
+                       dim3(CombineTileBig::NT), 0, strm, lp);
+  else if (save)
+    hipLaunchKernelGGL((moe_layer_kernel<CombineTileSmall, CombineTailSmall, CombineTailSmall, true>), dim3(o.grid),
                        dim3(CombineTileSmall::NT), 0, strm, lp);
+  else
+    hipLaunchKernelGGL((moe_layer_kernel<CombineTileSmall, CombineTailSmall, CombineTailSmall, false>),
+                       dim3(o.grid), dim3(CombineTileSmall::NT), 0, strm, lp);
   return launch_status("moe_layer launch");
 }

@@ -28,7 +28,9 @@
 //            dG and dU) wait for rows_in, its second-stage tiles (256
 //            columns of H: dX = dG . Wg^T + dU . Wu^T, one split-K loop)
 //            for the unit's first-stage entries.  Between tiles a
-//            workgroup takes the push queue's head if it is ready.
+//            workgroup takes the push queue's head if it is ready.  When
+//            the forward kept g and u (bf16), a first-stage entry is the dH
+//            tile alone, its epilogue reading them (no recomputation).
 //   head[2]  pushes: dX rows of rows a peer sent us, back to it.
 //   head[3]  fold: per token, dx = bf16(sum of its pairs' dX) and the
 //            router gradient through the softmax over the selected logits.
@@ -63,7 +65,9 @@ struct BwdParams {
   uint16_t* dres;                       // grouped pair gradients [cap, H]
   uint16_t* dg;                         // [cap, F]
   uint16_t* du;                         // [cap, F]
-  float* dh;                            // [cap, F] fp32
+  float* dh;                            // [cap, F] fp32 (optional with g_in)
+  const uint16_t* g_in;                 // optional [cap, F] bf16: the forward's X.Wg and X.Wu
+  const uint16_t* u_in;
   float* dlogits;                       // [T, E]
   uint32_t* rows_in;                    // [u_max]; the counters start here
   uint32_t n_counters;                  // 3 * u_max
@@ -278,6 +282,82 @@ __device__ __forceinline__ void bwd_stage1(const BwdParams& b, const Unit& x, in
   }
 }
 
+// First-stage entry with the forward's g and u at hand (bf16, as the
+// forward's tiles kept them): F columns [blk*FB, +FB) of unit x,
+// dH = dres . Wd^T in registers (stored to dh when given), then dU and dG
+// from the saved g and u, each through the LDS ring in a pass of its own
+// (dH stays in the accumulators; the second pass reads g and u again, from
+// the cache).
+template <class SH, int RING, int FB>
+__device__ __forceinline__ void bwd_stage1_saved(const BwdParams& b, const Unit& x, int blk,
+                                                 f32x16 (&ah)[SH::TM][SH::TN]) {
+  static_assert(SH::BNT && SH::BN == FB, "dH tile of FB columns (N x K weights: Wd rows)");
+  const CombineParams& p = b.c;
+  const int64_t H = p.H, F = p.F;
+  const int64_t row0 = x.row0;
+  const int m = x.m_valid;
+  const int64_t c0 = (int64_t)blk * FB;
+  const int64_t woff = (int64_t)x.el * H * F;
+  tile_mainloop<SH, false, true, RING>(ah, b.dres + row0 * H, H, m, BSrc{p.wd + woff + c0 * H, nullptr, H}, p.H);
+  if (b.dh) {
+    float* dhp = b.dh + row0 * F + c0;
+    tile_foreach4<SH>(ah, [&](int r, int c, f32x4 v) {
+      if (r < m) *reinterpret_cast<f32x4*>(dhp + r * F + c) = v;
+    });
+  }
+  const WaveCtx w = wave_ctx();
+  const int wm = w.wave / SH::WGN, wn = w.wave % SH::WGN;
+  const uint16_t* gp = b.g_in + row0 * F + c0;
+  const uint16_t* up = b.u_in + row0 * F + c0;
+  // the lane's g and u pieces of one 32-row block of the tile, loaded
+  // together when the block's first group is reached (one wait per block)
+  u32x2 gs[SH::TN][4], us[SH::TN][4];
+  auto load_block = [&](int i, bool with_u) {
+    const int row = wm * SH::WM + i * 32 + (w.lane & 31);
+    const int64_t rr = row < m ? row : m - 1;   // rows past the unit are computed, never stored
+#pragma unroll
+    for (int j = 0; j < SH::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * SH::WN + j * 32 + q * 8 + (w.lane >> 5) * 4;
+        gs[j][q] = *reinterpret_cast<const u32x2*>(gp + rr * F + col);
+        if (with_u) us[j][q] = *reinterpret_cast<const u32x2*>(up + rr * F + col);
+      }
+  };
+  auto unpack = [](u32x2 v, float (&f)[4]) {
+    f[0] = __builtin_bit_cast(float, v.x << 16);
+    f[1] = __builtin_bit_cast(float, v.x & 0xFFFF0000u);
+    f[2] = __builtin_bit_cast(float, v.y << 16);
+    f[3] = __builtin_bit_cast(float, v.y & 0xFFFF0000u);
+  };
+  // dU = dH * silu(g), silu(g) = g s, s = 1 / (1 + e^-g)
+  tile_store_rows_fn<SH, RING, true, FB>(b.du + row0 * F + c0, F, m, [&](int i, int j, int q) {
+    if (j == 0 && q == 0) load_block(i, false);
+    float g[4];
+    unpack(gs[j][q], g);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = ah[i][j][4 * q + e] * (g[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e])));
+    return v;
+  });
+  KOS_WAITCNT(0, 0);
+  lds_barrier();   // every wave has read dU out of the ring
+  // dG = dH * u * silu'(g), silu'(g) = s (1 + g (1 - s))
+  tile_store_rows_fn<SH, RING, true, FB>(b.dg + row0 * F + c0, F, m, [&](int i, int j, int q) {
+    if (j == 0 && q == 0) load_block(i, true);
+    float g[4], u[4];
+    unpack(gs[j][q], g);
+    unpack(us[j][q], u);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g[e]));
+      v[e] = ah[i][j][4 * q + e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+    }
+    return v;
+  });
+}
+
 // Second-stage tile: H columns [nh*256, +256) of unit x's dX.
 template <class S, int RING>
 __device__ __forceinline__ void bwd_tile2(const BwdParams& b, const Unit& x, int nh, f32x16 (&acc)[S::TM][S::TN]) {
@@ -426,7 +506,9 @@ struct BwdShapes {
   using GU = TileShape<BM, 2 * kBwdFCols, 4, 2, 4>;
 };
 
-template <int FB>
+// SAVED: the first stage reads the forward's kept g and u (g_in, u_in)
+// instead of recomputing them.
+template <int FB, bool SAVED>
 __global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
   using B256 = BwdShapes<kBwdUnit, FB>;
   using B128 = BwdShapes<128, FB>;
@@ -507,9 +589,15 @@ __global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
         }
         tr.put(KOS_TR_WAIT, j, t0);
         t0 = tr.now();
-        if (x.m_valid > 128) bwd_stage1<typename B256::DH, typename B256::GU, RING, FB>(ps, x, ct.nt, ah, ad);
-        else if (x.m_valid > 64) bwd_stage1<typename B128::DH, typename B128::GU, RING, FB>(ps, x, ct.nt, ah1, ad1);
-        else bwd_stage1<typename B64::DH, typename B64::GU, RING, FB>(ps, x, ct.nt, ah2, ad2);
+        if constexpr (SAVED) {
+          if (x.m_valid > 128) bwd_stage1_saved<typename B256::DH, RING, FB>(ps, x, ct.nt, ah);
+          else if (x.m_valid > 64) bwd_stage1_saved<typename B128::DH, RING, FB>(ps, x, ct.nt, ah1);
+          else bwd_stage1_saved<typename B64::DH, RING, FB>(ps, x, ct.nt, ah2);
+        } else {
+          if (x.m_valid > 128) bwd_stage1<typename B256::DH, typename B256::GU, RING, FB>(ps, x, ct.nt, ah, ad);
+          else if (x.m_valid > 64) bwd_stage1<typename B128::DH, typename B128::GU, RING, FB>(ps, x, ct.nt, ah1, ad1);
+          else bwd_stage1<typename B64::DH, typename B64::GU, RING, FB>(ps, x, ct.nt, ah2, ad2);
+        }
         wg_publish(&t1_done[ct.u], 1u);
         tr.put(KOS_TR_TILE, j, t0);
       } else {
@@ -578,7 +666,8 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
                                         const int32_t* peer_counts, const void* x_grouped, int64_t grouped_cap,
                                         const int32_t* grouped_offsets, const int32_t* row_src,
                                         const void* y_grouped, const void* const* peer_return, const void* w_gate,
-                                        const void* w_up, const void* w_down, const void* const* peer_send_grad,
+                                        const void* w_up, const void* w_down, const void* gate_saved,
+                                        const void* up_saved, const void* const* peer_send_grad,
                                         void* const* out_send_grad, const int64_t* send_caps, void* dres_grouped,
                                         void* dg, void* du, float* dh, void* dx_grouped,
                                         const void* const* peer_return_grad,
@@ -597,8 +686,10 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   const bool no_tokens = s->tokens == 0;
   if ((!no_tokens && (!dy || !topk_idx || !topk_w || !perm || !dx || !dlogits)) || !counts || !peer_counts ||
       !x_grouped || !grouped_offsets || !row_src || !y_grouped || !w_gate || !w_up || !w_down || !dres_grouped ||
-      !dg || !du || !dh || !dx_grouped)
+      !dg || !du || (!dh && !gate_saved) || !dx_grouped)
     return fail(KOS_ERR_ARG, "null buffer");
+  if ((gate_saved == nullptr) != (up_saved == nullptr))
+    return fail(KOS_ERR_ARG, "gate_saved and up_saved are given together or not at all");
   if (R > 1 && (!peer_return || !peer_send_grad || !out_send_grad || !send_caps || !peer_return_grad ||
                 !out_return_grad || !return_caps))
     return fail(KOS_ERR_ARG, "a peer array is NULL");
@@ -612,8 +703,7 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   }
   if (!aligned16(dy) || !aligned16(x_grouped) || !aligned16(y_grouped) || !aligned16(w_gate) || !aligned16(w_up) ||
       !aligned16(w_down) || !aligned16(dres_grouped) || !aligned16(dg) || !aligned16(du) || !aligned16(dh) ||
-      !aligned16(dx_grouped) ||
-      !aligned16(dx))
+      !aligned16(dx_grouped) || !aligned16(dx) || !aligned16(gate_saved) || !aligned16(up_saved))
     return fail(KOS_ERR_ALIGN, "buffers must be 16-byte aligned");
   if (grouped_cap < 0 || grouped_cap > (int64_t(1) << 31) - 1) return fail(KOS_ERR_ARG, "bad grouped_cap");
   // tiles address one expert's weights and the grouped rows through 32-bit
@@ -682,6 +772,8 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   b.dg = static_cast<uint16_t*>(dg);
   b.du = static_cast<uint16_t*>(du);
   b.dh = dh;
+  b.g_in = static_cast<const uint16_t*>(gate_saved);
+  b.u_in = static_cast<const uint16_t*>(up_saved);
   b.dlogits = dlogits;
   uint32_t* base = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountersOffset);
   b.rows_in = base;
@@ -690,9 +782,14 @@ extern "C" kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy, 
   if ((size_t)b.n_counters > kMaxCounters) return fail(KOS_ERR_SHAPE, "grouped_cap too large for the workspace");
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  if (FB == 256)
-    hipLaunchKernelGGL(moe_layer_bwd_kernel<256>, dim3(o.grid), dim3(512), 0, strm, b);
+  const bool saved = gate_saved != nullptr;
+  if (FB == 256 && saved)
+    hipLaunchKernelGGL((moe_layer_bwd_kernel<256, true>), dim3(o.grid), dim3(512), 0, strm, b);
+  else if (FB == 256)
+    hipLaunchKernelGGL((moe_layer_bwd_kernel<256, false>), dim3(o.grid), dim3(512), 0, strm, b);
+  else if (saved)
+    hipLaunchKernelGGL((moe_layer_bwd_kernel<kBwdFCols, true>), dim3(o.grid), dim3(512), 0, strm, b);
   else
-    hipLaunchKernelGGL(moe_layer_bwd_kernel<kBwdFCols>, dim3(o.grid), dim3(512), 0, strm, b);
+    hipLaunchKernelGGL((moe_layer_bwd_kernel<kBwdFCols, false>), dim3(o.grid), dim3(512), 0, strm, b);
   return launch_status("moe_layer_bwd launch");
 }

@@ -497,24 +497,25 @@ __device__ __forceinline__ lds_char* ring_lds(int i) {
   return i == 0 ? b0 : i == 1 ? b1 : i == 2 ? b2 : b3;
 }
 
-// Stores the tile as bf16 rows [0, m_valid) of dst (row stride ld elements)
-// through the LDS ring: every lane writes its four-column pieces into LDS,
-// then each group of lanes stores whole rows with 16-byte stores, so the
-// global writes are whole cache lines (what device-coherent write-through
-// stores need to be cheap).  SWIGLU: the tile holds gate and up columns
-// (BSrc dual layout) and the BN/2 output columns are swiglu(gate, up).
-// COH: device-scope (sc1) stores.  Call right after tile_mainloop (the ring
-// is free); the next tile_mainloop waits for the ring.  dst is the same in
-// every thread.
-template <class S, int RING, bool COH, bool SWIGLU = false>
-__device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst, int64_t ld,
-                                                int m_valid) {
-  constexpr int OW = SWIGLU ? S::BN / 2 : S::BN;   // output columns
-  constexpr int OJ = SWIGLU ? S::TN / 2 : S::TN;   // 32-column output blocks per wave
+// Stores BM x OW bf16 values as rows [0, m_valid) of dst (row stride ld
+// elements) through the LDS ring.  fn(i, j, q) gives the calling lane's four
+// fp32 values of row wm*WM + i*32 + lane%32, columns wn*(OW/WGN) + j*32 +
+// 8q + 4*(lane/32) + [0, 4), for i < TM, j < OW/(32 WGN), q < 4 (the
+// accumulator layout of a 32x32 block; fn may update the accumulators it
+// reads).  Every lane writes its four-column pieces into LDS, then each
+// group of lanes stores whole rows with 16-byte stores, so the global writes
+// are whole cache lines (what device-coherent write-through stores need to
+// be cheap).  COH: device-scope (sc1) stores.  Call right after
+// tile_mainloop (the ring is free); the next tile_mainloop waits for the
+// ring.  dst is the same in every thread.
+template <class S, int RING, bool COH, int OW, class Fn>
+__device__ __forceinline__ void tile_store_rows_fn(uint16_t* dst, int64_t ld, int m_valid, Fn&& fn) {
+  constexpr int OJ = OW / 32 / S::WGN;             // 32-column output blocks per wave
   constexpr int ROW_BYTES = OW * 2;
   constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
   constexpr int ROWS_PER_RING = RING / ROW_BYTES;
   constexpr int ROWS_PER_PASS = S::NT / CPR;
+  static_assert(OW % (32 * S::WGN) == 0, "whole 32-column blocks per wave");
   static_assert(RING % ROW_BYTES == 0 && 4 * ROWS_PER_RING >= S::BM, "the tile must fit the ring");
   static_assert((CPR & (CPR - 1)) == 0 && S::NT % CPR == 0, "power-of-two chunks per row");
   static_assert(ROWS_PER_RING % 32 == 0 && ROWS_PER_RING % ROWS_PER_PASS == 0,
@@ -535,10 +536,7 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
       for (int g = 0; g < 4; ++g) {
         const int col = wn * (OW / S::WGN) + j * 32 + g * 8 + (lane >> 5) * 4;
         const int chunk = (col >> 3) ^ (row & (CPR - 1));
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
+        const f32x4 v = fn(i, j, g);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col & 7) * 2) =
             pack4_bf16(v);
         // one 32x32 block at a time: keeps the accumulator reads from being
@@ -579,6 +577,21 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Stores the tile as bf16 rows [0, m_valid) of dst (tile_store_rows_fn).
+// SWIGLU: the tile holds gate and up columns (BSrc dual layout) and the BN/2
+// output columns are swiglu(gate, up).
+template <class S, int RING, bool COH, bool SWIGLU = false>
+__device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN], uint16_t* dst, int64_t ld,
+                                                int m_valid) {
+  tile_store_rows_fn<S, RING, COH, SWIGLU ? S::BN / 2 : S::BN>(dst, ld, m_valid, [&](int i, int j, int g) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = SWIGLU ? swiglu(acc[i][j][4 * g + e], acc[i][j + S::TN / 2][4 * g + e]) : acc[i][j][4 * g + e];
+    return v;
+  });
 }
 
 // Both halves of a dual-layout tile (gate blocks and up blocks, BN/2

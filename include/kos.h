@@ -453,6 +453,11 @@ kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, const float* 
  *              `rank` ignored): results d returns, in our packed order
  * h            out bf16 [grouped_cap, F] (the SwiGLU hidden, kept for
  *              inspection);  y_grouped: out bf16 [grouped_cap, H]
+ * gate_save, up_save  optional out bf16 [grouped_cap, F]: bf16(X_e . Wg_e)
+ *              and bf16(X_e . Wu_e) as the tiles computed them, for a
+ *              backward pass that reads them instead of recomputing them
+ *              (kos_moe_layer_bwd); both NULL (nothing written) or both
+ *              given (else KOS_ERR_ARG)
  * out_return   host array[world] of out bf16 [return_caps[p], H]: the
  *              results of the rows p sent us, in p's packed order
  * return_caps  host array[world]: rows out_return[p] holds (entry `rank`
@@ -479,7 +484,8 @@ kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
                            const int32_t* counts, const int32_t* perm,
                            const int32_t* peer_counts,
                            const void* const* peer_return,
-                           void* h, void* y_grouped, void* const* out_return,
+                           void* h, void* gate_save, void* up_save,
+                           void* y_grouped, void* const* out_return,
                            const int64_t* return_caps, void* y,
                            const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
@@ -499,9 +505,9 @@ kos_status kos_moe_combine(const kos_moe_shape* s, const void* x_grouped,
  * Inputs: x, logits, peer_send, peer_counts (as kos_moe_dispatch); w_gate,
  * w_up, w_down, peer_return (as kos_moe_combine).  Outputs: topk_idx,
  * topk_w, counts, perm, out_send (with send_caps), x_grouped (grouped_cap
- * rows), grouped_offsets, row_src (as kos_moe_dispatch); h, y_grouped (at
- * least grouped_cap rows), out_return (with return_caps), y (as
- * kos_moe_combine).  Shapes and errors: those of both calls (H % 128 == 0,
+ * rows), grouped_offsets, row_src (as kos_moe_dispatch); h, the optional
+ * gate_save and up_save, y_grouped (at least grouped_cap rows), out_return
+ * (with return_caps), y (as kos_moe_combine).  Shapes and errors: those of both calls (H % 128 == 0,
  * F % 64 == 0; capacities -> KOS_ERR_CAPACITY from kos_workspace_status,
  * nothing written past a buffer).  opts->mode must be KOS_MODE_FUSED
  * (KOS_ERR_UNSUPPORTED otherwise): the two calls are the baseline.
@@ -513,7 +519,8 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
                          int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* perm,
                          void* const* out_send, const int64_t* send_caps,
                          void* x_grouped, int64_t grouped_cap, int32_t* grouped_offsets, int32_t* row_src,
-                         void* h, void* y_grouped, void* const* out_return, const int64_t* return_caps,
+                         void* h, void* gate_save, void* up_save, void* y_grouped,
+                         void* const* out_return, const int64_t* return_caps,
                          void* y, const kos_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -531,7 +538,9 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
  *             dh), then per 128 of those columns g = X.Wg and u = X.Wu
  *             recomputed from the forward's grouped input and
  *             dU = bf16(dH * silu(g)), dG = bf16(dH * u * silu'(g))
- *             (the forward's bf16 rounding of h passes gradients unchanged)
+ *             (the forward's bf16 rounding of h passes gradients unchanged);
+ *             with gate_saved / up_saved given, g and u are those bf16
+ *             values instead (no recomputation: dH and the epilogue only)
  *   tiles 2   per unit and 256 columns of H, once the unit's tiles 1 are
  *             done: dX = bf16(dG . Wg^T + dU . Wu^T)
  *   pushes    dX rows of rows a peer sent us, back to it (out_return_grad,
@@ -548,13 +557,17 @@ kos_status kos_moe_layer(const kos_moe_shape* s, const void* x, const float* log
  * row_src, y_grouped, peer_return: the forward's (kos_moe_layer, or
  *              kos_moe_dispatch + kos_moe_combine), read only
  * w_gate, w_up bf16 [E_loc, H, F];  w_down bf16 [E_loc, F, H]
+ * gate_saved, up_saved  bf16 [grouped_cap, F]: the forward's gate_save and
+ *              up_save outputs, or both NULL to recompute g and u (one
+ *              without the other: KOS_ERR_ARG)
  * peer_send_grad  host array[world] of bf16 [rows p sent us, H] (entry
  *              `rank` ignored): the gradients of the rows p sent us, in
  *              the order p sent them
  * out_send_grad   host array[world] of out bf16 [send_caps[d], H]: our
  *              pairs' gradients for rank d, in our packed order
  * dres_grouped out bf16 [grouped_cap, H];  dg, du: out bf16 [grouped_cap, F]
- * dh           out fp32 [grouped_cap, F]
+ * dh           out fp32 [grouped_cap, F]; with gate_saved it may be NULL
+ *              (then not written)
  * dx_grouped   out bf16 [grouped_cap, H]
  * peer_return_grad host array[world] of bf16 [>= rows we sent d, H]: the
  *              dX rows d returns for the rows we sent it
@@ -579,6 +592,7 @@ kos_status kos_moe_layer_bwd(const kos_moe_shape* s, const void* dy,
                              const int32_t* grouped_offsets, const int32_t* row_src,
                              const void* y_grouped, const void* const* peer_return,
                              const void* w_gate, const void* w_up, const void* w_down,
+                             const void* gate_saved, const void* up_saved,
                              const void* const* peer_send_grad,
                              void* const* out_send_grad, const int64_t* send_caps,
                              void* dres_grouped, void* dg, void* du, float* dh, void* dx_grouped,

@@ -124,23 +124,77 @@ def test_combine_checks_and_return_capacities(api):
     b = _moe_buffers(s, rank, [0, 1, 1, 1], [0, 9, 2, 40])
 
     def call(**over):
-        a = {**b, **over}
+        a = {**b, "gate_save": None, "up_save": None, **over}
         api.moe_combine(shp, a["x_grouped"], a["grouped_offsets"], a["row_src"], a["wg"], a["wu"], a["wd"],
                         a["topk_idx"], a["topk_w"], a["counts"], a["perm"], a["peer_counts"], a["peer_return"],
-                        a["h"], a["yg"], a["out_return"], a["y"], _Ws())
+                        a["h"], a["yg"], a["out_return"], a["y"], _Ws(), gate_save=a["gate_save"],
+                        up_save=a["up_save"])
 
     call()
     name, args = api._rec.calls[-1]
     assert name == "kos_moe_combine"
-    caps = args[17]
+    caps = args[19]
     assert [caps[p] for p in range(1, s.world)] == [9, 2, 40]
+    assert args[15] is None and args[16] is None
     cap = b["x_grouped"].shape[0]
+    g, u = bf(cap, s.ffn), bf(cap + 3, s.ffn)
+    call(gate_save=g, up_save=u)
+    args = api._rec.calls[-1][1]
+    assert args[14] == b["h"].data_ptr() and args[15] == g.data_ptr() and args[16] == u.data_ptr()
+    assert args[17] == b["yg"].data_ptr()
     for key, bad in (("h", bf(cap - 1, s.ffn)), ("yg", bf(cap - 1, s.hidden)), ("wd", bf(s.e_local, s.hidden, s.ffn)),
                      ("y", bf(s.tokens + 1, s.hidden)), ("h", bf(cap, s.ffn + 64))):
         with pytest.raises(ValueError):
             call(**{key: bad})
     with pytest.raises(ValueError, match="topk_w"):
         call(topk_w=f32(s.tokens, s.topk + 1))
+    with pytest.raises(ValueError, match="together"):
+        call(gate_save=g)
+    for bad in (bf(cap - 1, s.ffn), bf(cap, s.ffn + 64), f32(cap, s.ffn)):
+        with pytest.raises((ValueError, TypeError)):
+            call(gate_save=g, up_save=bad)
+
+
+def test_layer_and_backward_pass_the_saved_activations(api):
+    s, rank = KI.MOE_TINY, 0
+    shp = api.moe_shape(s.world, rank, s.tokens, s.hidden, s.experts, s.topk, s.ffn)
+    b = _moe_buffers(s, rank, [0, 1, 1, 1], [0, 9, 2, 40])
+    cap = b["x_grouped"].shape[0]
+    g, u = bf(cap, s.ffn), bf(cap, s.ffn)
+    api.moe_layer(shp, b["x"], b["logits"], b["peer_send"], b["peer_counts"], b["wg"], b["wu"], b["wd"],
+                  b["peer_return"], b["topk_idx"], b["topk_w"], b["counts"], b["perm"], b["out_send"],
+                  b["x_grouped"], b["grouped_offsets"], b["row_src"], b["h"], b["yg"], b["out_return"], b["y"],
+                  _Ws(), gate_save=g, up_save=u)
+    name, args = api._rec.calls[-1]
+    assert name == "kos_moe_layer"
+    assert args[19] == b["h"].data_ptr() and args[20] == g.data_ptr() and args[21] == u.data_ptr()
+    assert args[22] == b["yg"].data_ptr()
+    T, H, F = s.tokens, s.hidden, s.ffn
+    grads = dict(dy=bf(T, H), dres=bf(cap, H), dg=bf(cap, F), du=bf(cap, F), dh=f32(cap, F), dxg=bf(cap, H),
+                 dx=bf(T, H), dl=f32(T, s.experts),
+                 psg=[None if p == rank else bf(3, H) for p in range(s.world)],
+                 osg=[None if p == rank else bf(7, H) for p in range(s.world)],
+                 prg=[None if p == rank else bf(5, H) for p in range(s.world)],
+                 org=[None if p == rank else bf(9, H) for p in range(s.world)])
+
+    def bwd(dh, **kw):
+        api.moe_layer_bwd(shp, grads["dy"], b["topk_idx"], b["topk_w"], b["perm"], b["counts"], b["peer_counts"],
+                          b["x_grouped"], b["grouped_offsets"], b["row_src"], b["yg"], b["peer_return"], b["wg"],
+                          b["wu"], b["wd"], grads["psg"], grads["osg"], grads["dres"], grads["dg"], grads["du"], dh,
+                          grads["dxg"], grads["prg"], grads["org"], grads["dx"], grads["dl"], _Ws(), **kw)
+        return api._rec.calls[-1][1]
+
+    args = bwd(grads["dh"])
+    assert args[16] is None and args[17] is None and args[24] == grads["dh"].data_ptr()
+    args = bwd(None, gate_saved=g, up_saved=u)
+    assert args[15] == b["wd"].data_ptr() and args[16] == g.data_ptr() and args[17] == u.data_ptr()
+    assert args[24] is None
+    with pytest.raises(ValueError, match="dh"):
+        bwd(None)
+    with pytest.raises(ValueError, match="together"):
+        bwd(grads["dh"], up_saved=u)
+    with pytest.raises(ValueError):
+        bwd(grads["dh"], gate_saved=g, up_saved=bf(cap, F + 64))
 
 
 def test_kos_error_carries_the_status():

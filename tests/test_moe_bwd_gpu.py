@@ -7,7 +7,9 @@ gradients sent and grouped, dG, dU, dX, the token gradients and the
 router gradient within the floating-point bar (zero exactly where an
 expert was not selected), the pushed rows bit copies of dX at the
 forward's provenance.  One small case chains the GPU forward into the
-backward.  Full DeepSeek-V3 shape: the GPU forward feeds the backward;
+backward.  The saved-activation variant (the forward's bf16 g and u read
+instead of recomputed, dh optional) against the oracle's variant, on the
+small cases, chained, and at full size.  Full DeepSeek-V3 shape: the GPU forward feeds the backward;
 sampled grouped rows, tokens and sent rows against the oracle evaluated
 row by row, every pushed row against the grouped dX.  Bad arguments forced
 from the host end in a reported error, with the kernel exiting normally."""
@@ -80,21 +82,24 @@ def _out_buffers(s, rank, pc, cap):
 
 
 def run_bwd(kos, ws, s, rank, inp, gin, f, b, o=None, check=True):
+    """f["gs"], f["us"] (optional): the forward's kept g and u, used instead
+    of recomputing them."""
     kos.moe_layer_bwd(_shape(s, rank), gin["dy"], f["idx"], f["w"], f["perm"], f["counts"], inp["peer_counts"],
                       f["grouped"], f["goff"], f["row_src"], f["yg"], inp["peer_return"], inp["wg"], inp["wu"],
                       inp["wd"], gin["peer_send_grad"], b["send"], b["dres"], b["dg"], b["du"], b["dh"], b["dxg"],
-                      gin["peer_return_grad"], b["ret"], b["dx"], b["dl"], ws, o)
+                      gin["peer_return_grad"], b["ret"], b["dx"], b["dl"], ws, o, gate_saved=f.get("gs"),
+                      up_saved=f.get("us"))
     if check:
         ws.status()
     torch.cuda.synchronize()
 
 
-def _oracle_bwd(s, rank, inp, gin):
+def _oracle_bwd(s, rank, inp, gin, saved=False):
     pc = inp["peer_counts"].cpu().numpy()
     wg, wu, wd = (KI.bf16_bits(inp[k]) for k in ("wg", "wu", "wd"))
     return O.moe_layer_bwd(KI.bf16_bits(gin["dy"]), KI.bf16_bits(inp["x"]), inp["logits"].cpu().numpy(), wg, wu,
                            wd, _bits(inp["peer_send"]), pc, _bits(inp["peer_return"]), _bits(gin["peer_send_grad"]),
-                           _bits(gin["peer_return_grad"]), s.world, rank, s.topk)
+                           _bits(gin["peer_return_grad"]), s.world, rank, s.topk, saved=saved)
 
 
 def _check_all(s, rank, b, ref):
@@ -107,7 +112,8 @@ def _check_all(s, rank, b, ref):
                              f"send_grad[{d}]")
     if n:
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dres"][:n])), O.bf16_to_f64(ref["grouped_grad"]), "dres")
-        assert_close(b["dh"][:n].cpu().numpy(), ref["dh"], "dH")
+        if b["dh"] is not None:
+            assert_close(b["dh"][:n].cpu().numpy(), ref["dh"], "dH")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dg"][:n])), O.bf16_to_f64(ref["dg"]), "dG")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["du"][:n])), O.bf16_to_f64(ref["du"]), "dU")
         dxg = KI.bf16_bits(b["dxg"][:n])
@@ -151,21 +157,61 @@ def test_bwd_small_vs_oracle(kos, ws, s, rank):
         assert torch.equal(b[key][:m], b2[key][:m]), key
 
 
-def test_forward_then_backward_on_the_gpu(kos, ws):
-    """The GPU forward's buffers feed the backward directly."""
-    from test_moe_layer_gpu import run_layer
-    s, rank = KI.MOE_BWD_MID, 2
-    say(f"[moe fwd+bwd] {s.name} rank={rank}")
+SAVED = [(KI.MOE_TINY, 1, True), (KI.MOE_BWD_MID, 1, False), (KI.MOE_BWD_K10, 1, True), (KI.MOE_BWD_1R, 0, False),
+         (KI.MOE_BWD_K1, 2, True), (EDGE_T0, 2, False)]
+
+
+@pytest.mark.parametrize("s,rank,with_dh", SAVED, ids=[f"{s.name}-r{r}-dh{int(d)}" for s, r, d in SAVED])
+def test_bwd_saved_small_vs_oracle(kos, ws, s, rank, with_dh):
+    """The forward's kept bf16 g and u (here the oracle's) instead of the
+    recomputation, against the oracle's saved-activation backward; dh
+    written when given, untouched otherwise."""
+    say(f"[moe bwd saved] {s.name} rank={rank} dh={with_dh}")
     inp = KI.moe_inputs(s, rank, DEV)
     gin = KI.moe_grad_inputs(s, rank, DEV)
-    fw = run_layer(kos, ws, s, rank, inp)
+    ref = _oracle_bwd(s, rank, inp, gin, saved=True)
+    pc = inp["peer_counts"].cpu().numpy()
+    cap = int(pc.sum()) + s.tokens * min(s.topk, s.e_local) + 37
+    f = _fwd_from_oracle(s, rank, ref, cap)
+    n = int(ref["grouped_offsets"][-1])
+    wg, wu = KI.bf16_bits(inp["wg"]), KI.bf16_bits(inp["wu"])
+    g, u = O.grouped_gate_up(ref["grouped"], ref["grouped_offsets"], wg, wu)
+    f["gs"] = torch.zeros((cap, s.ffn), dtype=torch.bfloat16, device=DEV)
+    f["us"] = torch.zeros((cap, s.ffn), dtype=torch.bfloat16, device=DEV)
+    if n:
+        f["gs"][:n] = KI.from_bf16_bits(g, DEV)
+        f["us"][:n] = KI.from_bf16_bits(u, DEV)
+    b = _out_buffers(s, rank, pc, cap)
+    if not with_dh:
+        b["dh"] = None
+    run_bwd(kos, ws, s, rank, inp, gin, f, b)
+    _check_all(s, rank, b, ref)
+    if n:   # the kept values decide: the recomputing oracle is not what ran
+        unsaved = _oracle_bwd(s, rank, inp, gin)
+        assert not np.array_equal(unsaved["dg"], ref["dg"])
+
+
+@pytest.mark.parametrize("saved", [False, True])
+def test_forward_then_backward_on_the_gpu(kos, ws, saved):
+    """The GPU forward's buffers feed the backward directly (saved: with the
+    g and u the forward kept, and no dh)."""
+    from test_moe_layer_gpu import run_layer
+    s, rank = KI.MOE_BWD_MID, 2
+    say(f"[moe fwd+bwd] {s.name} rank={rank} saved={saved}")
+    inp = KI.moe_inputs(s, rank, DEV)
+    gin = KI.moe_grad_inputs(s, rank, DEV)
+    fw = run_layer(kos, ws, s, rank, inp, save=saved)
     pc = inp["peer_counts"].cpu().numpy()
     cap = fw["grouped"].shape[0]
     f = dict(idx=fw["idx"], w=fw["w"], perm=fw["perm"], counts=fw["counts"], goff=fw["goff"], row_src=fw["row_src"],
              grouped=fw["grouped"], yg=fw["yg"])
+    if saved:
+        f.update(gs=fw["gs"], us=fw["us"])
     b = _out_buffers(s, rank, pc, cap)
+    if saved:
+        b["dh"] = None
     run_bwd(kos, ws, s, rank, inp, gin, f, b)
-    _check_all(s, rank, b, _oracle_bwd(s, rank, inp, gin))
+    _check_all(s, rank, b, _oracle_bwd(s, rank, inp, gin, saved=saved))
 
 
 def test_bad_arguments_are_reported(kos, ws):
@@ -199,20 +245,26 @@ def test_bad_arguments_are_reported(kos, ws):
     _check_all(s, rank, b, ref)
 
 
-def test_bwd_full_size_sampled(kos, ws):
+@pytest.mark.parametrize("saved", [False, True])
+def test_bwd_full_size_sampled(kos, ws, saved):
     """DeepSeek-V3 shape, rank 5: the GPU forward, then the backward;
-    sampled outputs against the oracle row by row."""
+    sampled outputs against the oracle row by row (saved: the forward keeps
+    g and u, the backward reads them and writes no dh)."""
     from test_moe_layer_gpu import run_layer
     s, rank = KI.MOE_DSV3, 5
-    say(f"[moe bwd full] {s.name} rank={rank}")
+    say(f"[moe bwd full] {s.name} rank={rank} saved={saved}")
     inp = KI.moe_inputs(s, rank, DEV)
     gin = KI.moe_grad_inputs(s, rank, DEV)
-    fw = run_layer(kos, ws, s, rank, inp)
+    fw = run_layer(kos, ws, s, rank, inp, save=saved)
     pc = inp["peer_counts"].cpu().numpy()
     cap = fw["grouped"].shape[0]
     f = dict(idx=fw["idx"], w=fw["w"], perm=fw["perm"], counts=fw["counts"], goff=fw["goff"], row_src=fw["row_src"],
              grouped=fw["grouped"], yg=fw["yg"])
+    if saved:
+        f.update(gs=fw["gs"], us=fw["us"])
     b = _out_buffers(s, rank, pc, cap)
+    if saved:
+        b["dh"] = None
     run_bwd(kos, ws, s, rank, inp, gin, f, b)
     say("[moe bwd full] kernel done; oracle on samples")
     ref = O.dispatch(KI.bf16_bits(inp["x"]), inp["logits"].cpu().numpy(), _bits(inp["peer_send"]), pc, s.world,
@@ -253,8 +305,9 @@ def test_bwd_full_size_sampled(kos, ws):
             continue
         rows = sorted({lo, min(lo + 255, hi - 1), min(lo + 256, hi - 1), hi - 1})
         dres = np.stack([dres_row(r) for r in rows])
-        dg, du, dxr = O.expert_ffn_bwd(ref["grouped"][rows], dres, wg[e], wu[e], wd[e])
-        assert_close(b["dh"][rows].cpu().numpy(), O.expert_dh(dres, wd[e]), f"dH e{e}")
+        dg, du, dxr = O.expert_ffn_bwd(ref["grouped"][rows], dres, wg[e], wu[e], wd[e], saved=saved)
+        if b["dh"] is not None:
+            assert_close(b["dh"][rows].cpu().numpy(), O.expert_dh(dres, wd[e]), f"dH e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dres"][rows])), O.bf16_to_f64(dres), f"dres e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["dg"][rows])), O.bf16_to_f64(dg), f"dG e{e}")
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["du"][rows])), O.bf16_to_f64(du), f"dU e{e}")
@@ -289,7 +342,7 @@ def test_bwd_full_size_sampled(kos, ws):
         rows = [r for r, _, _ in lst]
         xr = ref["grouped"][rows]
         dres = O.pair_grad(dy, w, [t for _, t, _ in lst], [j for _, _, j in lst])
-        dxg_s[rows] = O.expert_ffn_bwd(xr, dres, wg[e], wu[e], wd[e])[2]
+        dxg_s[rows] = O.expert_ffn_bwd(xr, dres, wg[e], wu[e], wd[e], saved=saved)[2]
         yg_s[rows] = O.expert_ffn(xr, wg[e], wu[e], wd[e])
     prg = _bits(gin["peer_return_grad"])
     pr = _bits(inp["peer_return"])

@@ -54,6 +54,8 @@ def _buffers(s, rank, pc):
         goff=torch.full((s.e_local + 1,), -1, dtype=torch.int32, device=dev),
         row_src=torch.full((cap, 2), -1, dtype=torch.int32, device=dev),
         h=torch.full((cap, F), nan, dtype=torch.bfloat16, device=dev),
+        gs=torch.full((cap, F), nan, dtype=torch.bfloat16, device=dev),
+        us=torch.full((cap, F), nan, dtype=torch.bfloat16, device=dev),
         yg=torch.full((cap, H), nan, dtype=torch.bfloat16, device=dev),
         ret=[None if p == rank else torch.full((max(int(pc[p].sum()), 1), H), nan, dtype=torch.bfloat16,
                                                device=dev) for p in range(s.world)],
@@ -61,18 +63,20 @@ def _buffers(s, rank, pc):
     )
 
 
-def run_layer(kos, ws, s, rank, inp, o=None):
+def run_layer(kos, ws, s, rank, inp, o=None, save=False):
+    """save: the layer also keeps bf16 g and u (b["gs"], b["us"])."""
     pc = inp["peer_counts"].cpu().numpy()
     b = _buffers(s, rank, pc)
     kos.moe_layer(_shape(s, rank), inp["x"], inp["logits"], inp["peer_send"], inp["peer_counts"], inp["wg"],
                   inp["wu"], inp["wd"], inp["peer_return"], b["idx"], b["w"], b["counts"], b["perm"], b["send"],
-                  b["grouped"], b["goff"], b["row_src"], b["h"], b["yg"], b["ret"], b["y"], ws, o)
+                  b["grouped"], b["goff"], b["row_src"], b["h"], b["yg"], b["ret"], b["y"], ws, o,
+                  gate_save=b["gs"] if save else None, up_save=b["us"] if save else None)
     ws.status()
     torch.cuda.synchronize()
     return b
 
 
-def run_two_launch(kos, ws, s, rank, inp):
+def run_two_launch(kos, ws, s, rank, inp, save=False):
     pc = inp["peer_counts"].cpu().numpy()
     b = _buffers(s, rank, pc)
     shp = _shape(s, rank)
@@ -80,7 +84,7 @@ def run_two_launch(kos, ws, s, rank, inp):
                      b["counts"], b["perm"], b["send"], b["grouped"], b["goff"], b["row_src"], ws)
     kos.moe_combine(shp, b["grouped"], b["goff"], b["row_src"], inp["wg"], inp["wu"], inp["wd"], b["idx"], b["w"],
                     b["counts"], b["perm"], inp["peer_counts"], inp["peer_return"], b["h"], b["yg"], b["ret"],
-                    b["y"], ws)
+                    b["y"], ws, gate_save=b["gs"] if save else None, up_save=b["us"] if save else None)
     ws.status()
     torch.cuda.synchronize()
     return b
@@ -127,9 +131,10 @@ SMALL = [(KI.MOE_TINY, 0), (KI.MOE_TINY, 3), (KI.MOE_TINY_SKEW, 0), (KI.MOE_TINY
 
 @pytest.mark.parametrize("s,rank", SMALL, ids=[f"{s.name}-r{r}" for s, r in SMALL])
 def test_layer_small_vs_oracle(kos, ws, s, rank):
+    """With the bf16 g and u kept as well (checked against the oracle)."""
     say(f"[moe layer] {s.name} rank={rank}")
     inp = KI.moe_inputs(s, rank, "cuda")
-    b = run_layer(kos, ws, s, rank, inp)
+    b = run_layer(kos, ws, s, rank, inp, save=True)
     pc = inp["peer_counts"].cpu().numpy()
     wg, wu, wd = (KI.bf16_bits(inp[k]) for k in ("wg", "wu", "wd"))
     peer_send = [None if t is None else KI.bf16_bits(t) for t in inp["peer_send"]]
@@ -146,6 +151,9 @@ def test_layer_small_vs_oracle(kos, ws, s, rank):
             if hi > lo:
                 href[lo:hi] = O.expert_hidden(ref["grouped"][lo:hi], wg[e], wu[e])
         assert_close(O.bf16_to_f64(KI.bf16_bits(b["h"][:n])), O.bf16_to_f64(href), "h")
+        gref, uref = O.grouped_gate_up(ref["grouped"], go, wg, wu)
+        assert_close(O.bf16_to_f64(KI.bf16_bits(b["gs"][:n])), O.bf16_to_f64(gref), "kept g")
+        assert_close(O.bf16_to_f64(KI.bf16_bits(b["us"][:n])), O.bf16_to_f64(uref), "kept u")
         ygpu = KI.bf16_bits(b["yg"][:n])
         assert_close(O.bf16_to_f64(ygpu), O.bf16_to_f64(ref["y_grouped"]), "y_grouped")
         _check_pushes(s, rank, b, ref, ygpu)
@@ -186,12 +194,14 @@ def test_layer_rejects_other_modes(kos, ws):
 UNIT_ROWS = 256
 
 
-@pytest.mark.parametrize("shape", [KI.MOE_DSV3, KI.MOE_QWEN3])
-def test_layer_full_size(kos, ws, shape):
+@pytest.mark.parametrize("shape,save", [(KI.MOE_DSV3, True), (KI.MOE_QWEN3, False)])
+def test_layer_full_size(kos, ws, shape, save):
+    """save: the kept g and u as well -- bit-identical between the two
+    paths, the sampled units' against the oracle."""
     rank = 0
-    say(f"[moe layer full] {shape.name}")
+    say(f"[moe layer full] {shape.name} save={save}")
     inp = KI.moe_inputs(shape, rank, "cuda")
-    b = run_layer(kos, ws, shape, rank, inp)
+    b = run_layer(kos, ws, shape, rank, inp, save=save)
     peer_send = [None if t is None else KI.bf16_bits(t) for t in inp["peer_send"]]
     pc = inp["peer_counts"].cpu().numpy()
     ref = O.dispatch(KI.bf16_bits(inp["x"]), inp["logits"].cpu().numpy(), peer_send, pc, shape.world, rank,
@@ -202,9 +212,12 @@ def test_layer_full_size(kos, ws, shape):
     ygpu = KI.bf16_bits(b["yg"][:n])
     _check_pushes(shape, rank, b, ref, ygpu)
     say(f"[moe layer full] {shape.name}: dispatch part bit-exact; two-launch path")
-    two = run_two_launch(kos, ws, shape, rank, inp)
+    two = run_two_launch(kos, ws, shape, rank, inp, save=save)
     assert np.array_equal(KI.bf16_bits(two["yg"][:n]), ygpu), "expert outputs differ from the two-launch path"
     assert np.array_equal(KI.bf16_bits(two["y"]), KI.bf16_bits(b["y"])), "folded tokens differ from the two-launch path"
+    if save:
+        for key in ("gs", "us"):
+            assert torch.equal(two[key][:n].view(torch.int16), b[key][:n].view(torch.int16)), key
     del two
     El = shape.e_local
     for e in range(El):
@@ -216,6 +229,12 @@ def test_layer_full_size(kos, ws, shape):
         yref = O.expert_ffn(ref["grouped"][rows], KI.bf16_bits(inp["wg"][e]), KI.bf16_bits(inp["wu"][e]),
                             KI.bf16_bits(inp["wd"][e]))
         assert_close(O.bf16_to_f64(ygpu[rows]), O.bf16_to_f64(yref), f"expert {e} first/last units")
+        if save:
+            gref, uref = O.expert_gate_up(ref["grouped"][rows], KI.bf16_bits(inp["wg"][e]),
+                                          KI.bf16_bits(inp["wu"][e]))
+            idx = torch.as_tensor(rows, device="cuda")
+            assert_close(O.bf16_to_f64(KI.bf16_bits(b["gs"][idx])), O.bf16_to_f64(gref), f"expert {e} kept g")
+            assert_close(O.bf16_to_f64(KI.bf16_bits(b["us"][idx])), O.bf16_to_f64(uref), f"expert {e} kept u")
     say(f"[moe layer full] {shape.name}: units checked; 512 tokens end to end")
     pret = [None if t is None else KI.bf16_bits(t) for t in inp["peer_return"]]
     rng = np.random.default_rng(9)
