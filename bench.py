@@ -519,7 +519,8 @@ def measured_counters():
         if kv.get("source_digest") != dig:
             continue
         base = os.path.basename(path)
-        op = next((o for o in ("ag_gemm", "gemm_rs", "moe_dispatch", "moe_combine", "moe_layer_bwd", "moe_layer")
+        op = next((o for o in ("ag_gemm", "gemm_rs", "moe_dispatch", "moe_combine", "moe_layer_bwd_saved",
+                               "moe_layer_bwd", "moe_layer_save", "moe_layer")
                    if base.startswith(o + "_")), base)
         out["mfma"][op] = {"busy_fraction": float(kv["mfma_busy_fraction"]),
                            "counted_over_algorithmic_flops": float(kv["counted_over_algorithmic"]),

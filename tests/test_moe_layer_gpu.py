@@ -254,3 +254,35 @@ def test_layer_full_size(kos, ws, shape, save):
     yref = O.fold(ref["idx"], ref["w"], ref["perm"], ref["offsets"], yg_sparse, go, pc, pret, shape.world, rank,
                   tokens=toks)
     assert_close(O.bf16_to_f64(KI.bf16_bits(b["y"])[toks]), O.bf16_to_f64(yref), "512 folded tokens end to end")
+
+
+def test_kept_activations_in_every_mode(kos, ws):
+    """The combine keeps the same bf16 g and u whichever way it runs: fused,
+    with a fixed crew and as separate launches -- bit-identical, and against
+    the oracle."""
+    s, rank = KI.MOE_TINY_SKEW, 2
+    say(f"[moe kept g/u, modes] {s.name} rank={rank}")
+    inp = KI.moe_inputs(s, rank, "cuda")
+    pc = inp["peer_counts"].cpu().numpy()
+    shp = _shape(s, rank)
+    got = {}
+    for label, o in (("fused", None), ("fixed", kos.opts(mode=1, n_movers=3)), ("unfused", kos.opts(mode=2))):
+        b = _buffers(s, rank, pc)
+        kos.moe_dispatch(shp, inp["x"], inp["logits"], inp["peer_send"], inp["peer_counts"], b["idx"], b["w"],
+                         b["counts"], b["perm"], b["send"], b["grouped"], b["goff"], b["row_src"], ws)
+        kos.moe_combine(shp, b["grouped"], b["goff"], b["row_src"], inp["wg"], inp["wu"], inp["wd"], b["idx"],
+                        b["w"], b["counts"], b["perm"], inp["peer_counts"], inp["peer_return"], b["h"], b["yg"],
+                        b["ret"], b["y"], ws, o, gate_save=b["gs"], up_save=b["us"])
+        ws.status()
+        torch.cuda.synchronize()
+        n = int(b["goff"][-1].item())
+        got[label] = (b["grouped"][:n].clone(), b["goff"].cpu().numpy(), b["gs"][:n].clone(), b["us"][:n].clone(),
+                      b["yg"][:n].clone())
+    for label in ("fixed", "unfused"):
+        for i, what in ((2, "g"), (3, "u"), (4, "y_grouped")):
+            assert torch.equal(got[label][i].view(torch.int16), got["fused"][i].view(torch.int16)), (label, what)
+    grouped, go = KI.bf16_bits(got["fused"][0]), got["fused"][1]
+    wg, wu = KI.bf16_bits(inp["wg"]), KI.bf16_bits(inp["wu"])
+    gref, uref = O.grouped_gate_up(grouped, go, wg, wu)
+    assert_close(O.bf16_to_f64(KI.bf16_bits(got["fused"][2])), O.bf16_to_f64(gref), "kept g")
+    assert_close(O.bf16_to_f64(KI.bf16_bits(got["fused"][3])), O.bf16_to_f64(uref), "kept u")
