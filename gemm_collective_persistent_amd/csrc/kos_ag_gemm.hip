@@ -369,8 +369,17 @@ static kos_status ag_gemm_run(const AgCall& a) {
   // workgroups keep enough requests in flight to fill the link.
   if ((st = resolve_opts(a.opts, dev, CrewDefaults{kCrewHalfGrid, 16, 16, 8}, &o)) != KOS_OK) return st;
 
-  int bm = 256, bn = 256;   // the MX tile
-  if (!a.mx) pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
+  int bm = 256, bn = 256;
+  if (a.mx) {
+    // 256 x 192 MX tiles where they take fewer rounds of the grid, counted
+    // in tile columns (the QKV shard: 256 tiles of 192 columns fill every
+    // compute unit once, 256-column tiles only 192 of them)
+    const int64_t rounds256 = (world * (m_local / 256) * (n / 256) + o.grid - 1) / o.grid;
+    const int64_t rounds192 = (world * (m_local / 256) * (n / 192) + o.grid - 1) / o.grid;
+    if (n % 192 == 0 && rounds192 * 192 < rounds256 * 256) bn = 192;
+  } else {
+    pick_ag_tile(world, m_local, n, o.grid, &bm, &bn);
+  }
   const int64_t row_bytes = a.mx ? k : 2 * k;
 
   AgParams p{};
@@ -428,8 +437,9 @@ static kos_status ag_gemm_run(const AgCall& a) {
 
   const int grid = o.grid;
   auto launch = [&](const AgParams& q) {
-    return a.mx ? launch_ag<TileShapeMX<256, 256>>(q, grid, s)
-                : a.wt ? launch_ag_tile<true>(bm, bn, q, grid, s) : launch_ag_tile<false>(bm, bn, q, grid, s);
+    if (a.mx)
+      return bn == 192 ? launch_ag<TileShapeMX<256, 192, 4, 2>>(q, grid, s) : launch_ag<TileShapeMX<256, 256>>(q, grid, s);
+    return a.wt ? launch_ag_tile<true>(bm, bn, q, grid, s) : launch_ag_tile<false>(bm, bn, q, grid, s);
   };
   if (o.mode == KOS_MODE_UNFUSED && nothing_to_move) {
     AgParams gm = p;           // the GEMM alone

@@ -29,7 +29,9 @@
 //   SA: [2][BM] x 4 bytes, SB: [2][BN] x 4 bytes: per step, each row's two
 //       scales in bytes 0 and 1 of its word (a direct LDS load of 2 bytes per
 //       lane fills one 4-byte word per lane, upper half zero; checked on the
-//       hardware).
+//       hardware).  Tiles whose 64-row scale groups do not divide among the
+//       waves (256 x 192 on eight waves: seven groups) end with a padding
+//       slot that the spare waves' loads fill and nothing reads.
 //
 // Scale layout in memory (the MX operands' contract): K/64 slabs, slab s
 // holding, for every row r of the operand, the scales of blocks 2s and 2s+1
@@ -61,20 +63,25 @@ struct TileShapeMX {
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_BYTES = BM * PAIR_K, B_BYTES = BN * PAIR_K;   // one byte per element
+  // scales: 64-row groups, 2 bytes per lane, SC_LOADS groups per wave and
+  // step; when the groups do not divide among the waves, the waves left over
+  // (SC_PAD of them) load A's first group into a slot nobody reads, so that
+  // every wave issues the same number of loads (the waits count them)
+  static constexpr int SC_GROUPS = (BM + BN) / 64;
+  static constexpr int SC_LOADS = (SC_GROUPS + NW - 1) / NW;
+  static constexpr int SC_PAD = SC_LOADS * NW - SC_GROUPS;
   static constexpr int SA_OFF = A_BYTES + B_BYTES;                     // [2][BM] words
   static constexpr int SB_OFF = SA_OFF + 2 * BM * 4;                   // [2][BN] words
-  static constexpr int PAIR_BYTES = SB_OFF + 2 * BN * 4;
+  static constexpr int PAD_OFF = SB_OFF + 2 * BN * 4;                  // [2][64] words, padding loads
+  static constexpr int PAIR_BYTES = PAD_OFF + (SC_PAD ? 2 * 256 : 0);
   static constexpr int LDS_BYTES = 2 * PAIR_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / NW;                  // 1 KiB loads per wave per pair
   static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-  // scales: 64-row groups, 2 bytes per lane, SC_LOADS groups per wave and step
-  static constexpr int SC_GROUPS = (BM + BN) / 64;
-  static constexpr int SC_LOADS = SC_GROUPS / NW;
   static constexpr int LOADS = A_LOADS + B_LOADS + 2 * SC_LOADS;     // per wave and pair
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sides are multiples of 64");
   static_assert(A_LOADS >= 1 && A_BYTES == A_LOADS * 1024 * NW, "whole A loads per wave");
   static_assert(B_LOADS >= 1 && B_BYTES == B_LOADS * 1024 * NW, "whole B loads per wave");
-  static_assert(SC_LOADS >= 1 && SC_GROUPS == SC_LOADS * NW, "whole scale loads per wave");
+  static_assert(SC_PAD == 0 || SC_LOADS == 1, "padding waves load one group");
   static_assert((BM / 64) % SC_LOADS == 0, "a wave's scale groups lie on one operand");
   static_assert(TM >= 1 && TM <= 4 && TN >= 1, "one to four row blocks per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -133,14 +140,16 @@ __device__ __forceinline__ void mx_plan(MxPlan<S, COH_A>& P, const MxSrc& a, int
     P.b_off[i] = (uint32_t)(nr * b.ld + c * 16);
   }
   // Scales: 64-row groups, A rows first; a wave's groups all lie on one
-  // operand.  Rows past the valid ones re-read the last valid row.
+  // operand.  Rows past the valid ones re-read the last valid row.  A
+  // padding wave re-reads A's first group into the padding slot.
   const int g0 = wave * S::SC_LOADS;
-  const bool on_a = g0 < S::BM / 64;
-  const int gl = on_a ? g0 : g0 - S::BM / 64;
+  const bool pad = g0 >= S::SC_GROUPS;
+  const bool on_a = pad || g0 < S::BM / 64;
+  const int gl = pad ? 0 : on_a ? g0 : g0 - S::BM / 64;
   const int valid = on_a ? m_valid : n_valid;
   P.rsc = raw_rsrc(on_a ? a.s : b.s);
-  P.sc_lds = (on_a ? S::SA_OFF : S::SB_OFF) + gl * 256;
-  P.sc_rows4 = (on_a ? S::BM : S::BN) * 4;
+  P.sc_lds = pad ? S::PAD_OFF : (on_a ? S::SA_OFF : S::SB_OFF) + gl * 256;
+  P.sc_rows4 = pad ? 256 : (on_a ? S::BM : S::BN) * 4;
   P.sc_slab = (int)(on_a ? a.slab : b.slab);
 #pragma unroll
   for (int i = 0; i < S::SC_LOADS; ++i) {

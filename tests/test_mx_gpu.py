@@ -72,6 +72,19 @@ def test_ag_mx_tiny_integer_exact(kos, ws, rank, mode):
     assert np.array_equal(_np(c), cref)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_ag_mx_192_column_tiles_integer_exact(kos, ws, mode):
+    """n = 768 on four ranks: 256 x 192 MX tiles fill more compute units than
+    256 x 256 ones (16 tiles against 12), so they are the ones that run."""
+    s = KI.AgShape("ag_mx_4r_1024x512x768", 18, 4, 256, 512, 768)
+    say(f"[ag mx 192-column tiles] mode={mode}")
+    inp, g, gs, c = _run_ag(kos, ws, s, 2, True, torch.float32, kos.opts(mode=mode, n_movers=2))
+    gref, gsref, cref = _ag_oracle(inp, 2, "f32")
+    assert np.array_equal(_np(g), gref)
+    assert np.array_equal(_nat(gs), gsref)
+    assert np.array_equal(_np(c), cref)
+
+
 def test_ag_mx_tiny_bf16_out(kos, ws):
     say("[ag mx tiny bf16 out]")
     inp, g, gs, c = _run_ag(kos, ws, KI.AG_TINY_MX, 1, False, torch.bfloat16, kos.opts())
