@@ -12,7 +12,7 @@ algorithmic GEMM FLOPs (AG + RS + expert FFN) / step time, in TFLOP/s; the
 MoE layer's tokens/s and each op's own TFLOP/s are reported beside it.
 
 Also reported: the same-GPU baselines (unfused launches, best fixed crew),
-the GEMM throughput on 224 of 256 compute units, the roofline of the
+the GEMM's throughput with 224 of the 256 compute units building, the roofline of the
 dominant kernel, and the CPU oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
@@ -723,8 +723,8 @@ def ag_pinned(torch, kos, KI, inp, ws, reps, flush):
 
 def planned_crews(KI, moe_shape, rows, grid):
     """The split a per-call cost model would plan (the explainer's kitchen
-    paragraph: a split predicted before each call, which the paper measured
-    slower than a plain fixed one): the crew that finishes its bytes at the
+    paragraph: a split predicted before each call, which did worse than an
+    untuned fixed crew in the paper's measurements): the crew that finishes its bytes at the
     published HBM rate when the builders finish their FLOPs at the published
     MFMA rate, M = grid * t_bytes / (t_bytes + t_flops).  Bytes per op: AG
     the gather (peer shards read + written, local shard copied); RS the

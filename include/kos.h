@@ -87,7 +87,7 @@ typedef enum kos_mode { KOS_MODE_FUSED = 0, KOS_MODE_FIXED = 1, KOS_MODE_UNFUSED
 
 /* GEMM+reduce-scatter output order: BAND finishes the first BM rows of
  * every rank's chunk before any chunk's next BM rows (the consumer order:
- * every reducer can start after the first band), ROW one chunk after the
+ * no reducer waits beyond the first band), ROW one chunk after the
  * other (the ablation the explainer reports 1.41-1.45x slower) ["Role
  * switching only works if"]. */
 typedef enum kos_rs_order { KOS_RS_BAND = 0, KOS_RS_ROW = 1 } kos_rs_order;
@@ -294,8 +294,8 @@ kos_status kos_gemm_rs(int32_t world, int32_t rank, int64_t m, int64_t k, int64_
 /*
  * The same two collectives with the weight stored transposed, W^T [n, k]
  * (row j holds output column j's k values): the data-gradient GEMMs of the
- * backward pass [abstract: KOSMOS fuses every TP+SP collective of a
- * transformer layer; explainer, "Start with the problem"].  The backward of
+ * backward pass [abstract: each TP+SP collective of a layer is fused with
+ * its GEMM; explainer, "Start with the problem"].  The backward of
  * an all-gather+GEMM (Y = AG(X) . W) is a GEMM+reduce-scatter of dY . W^T;
  * the backward of a GEMM+reduce-scatter (Y = RS(X . W)) is an
  * all-gather+GEMM of dY with W^T -- both with the forward weight as it is

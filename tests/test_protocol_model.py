@@ -119,8 +119,8 @@ def _order(model, spec):
 
 def test_queue_orders_follow_the_pages(model):
     """The orders the kernels decode their queues with (kos_order.h):
-    all-gather -- movers bring the remote shards in the order the tiles
-    consume them (rank+1, rank+2, ...), whole row blocks at a time, then the
+    all-gather -- movers copy remote shards in tile-consumption order
+    (rank+1, rank+2, ...), whole row blocks at a time, then the
     local copy; tiles of the local shard come first, then the remote shards
     in the movers' order ("Role switching only works if ...": local shard
     first, remote shards in consumption order).  Reduce-scatter band order
