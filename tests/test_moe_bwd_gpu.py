@@ -245,13 +245,16 @@ def test_bad_arguments_are_reported(kos, ws):
     _check_all(s, rank, b, ref)
 
 
-@pytest.mark.parametrize("saved", [False, True])
-def test_bwd_full_size_sampled(kos, ws, saved):
-    """DeepSeek-V3 shape, rank 5: the GPU forward, then the backward;
-    sampled outputs against the oracle row by row (saved: the forward keeps
-    g and u, the backward reads them and writes no dh)."""
+FULL = [(KI.MOE_DSV3, 5, False), (KI.MOE_DSV3, 5, True), (KI.MOE_QWEN3, 0, True)]
+
+
+@pytest.mark.parametrize("s,rank,saved", FULL, ids=[f"{s.name}-r{r}-saved{int(v)}" for s, r, v in FULL])
+def test_bwd_full_size_sampled(kos, ws, s, rank, saved):
+    """DeepSeek-V3 shape (rank 5) and the Qwen3 shape with skewed routing
+    (rank 0, the most loaded): the GPU forward, then the backward; sampled
+    outputs against the oracle row by row (saved: the forward keeps g and
+    u, the backward reads them and writes no dh)."""
     from test_moe_layer_gpu import run_layer
-    s, rank = KI.MOE_DSV3, 5
     say(f"[moe bwd full] {s.name} rank={rank} saved={saved}")
     inp = KI.moe_inputs(s, rank, DEV)
     gin = KI.moe_grad_inputs(s, rank, DEV)
