@@ -112,3 +112,46 @@ def test_mx_and_wt_argument_validation():
     # transposed weights: the bf16 rules
     assert _rs(kos, "wt", k=100) == KOS_ERR_SHAPE
     assert _rs(kos, "wt", w=None) == KOS_ERR_ARG
+
+
+def _moe_call(kos, name, **over):
+    """kos_moe_layer / kos_moe_combine / kos_moe_layer_bwd with one world-1
+    rank and fake (never dereferenced) pointers: only the host checks run."""
+    lib = kos.lib
+    from gemm_collective_persistent_amd._binding import MoeShape
+    s = MoeShape(1, 0, 64, 256, 8, 2, 256, 0)
+    f = 0x10000
+    a = dict(g=None, u=None, dh=f, gate=None, up=None)
+    a.update(over)
+    P = ctypes.c_void_p
+    o = kos.opts()
+    ws, wsb = P(f), lib.kos_workspace_bytes()
+    one = kos._binding.ptr_array([None])
+    caps = (ctypes.c_int64 * 1)(0)
+    if name == "layer":
+        return lib.kos_moe_layer(ctypes.byref(s), P(f), P(f), one, P(f), P(f), P(f), P(f), one, P(f), P(f), P(f),
+                                 P(f), one, caps, P(f), 1024, P(f), P(f), P(f), P(a["g"]), P(a["u"]), P(f), one,
+                                 caps, P(f), ctypes.byref(o), ws, wsb, None)
+    if name == "combine":
+        return lib.kos_moe_combine(ctypes.byref(s), P(f), P(f), P(f), 1024, P(f), P(f), P(f), P(f), P(f), P(f),
+                                   P(f), P(f), one, P(f), P(a["g"]), P(a["u"]), P(f), one, caps, P(f),
+                                   ctypes.byref(o), ws, wsb, None)
+    return lib.kos_moe_layer_bwd(ctypes.byref(s), P(f), P(f), P(f), P(f), P(f), P(f), P(f), 1024, P(f), P(f), P(f),
+                                 one, P(f), P(f), P(f), P(a["gate"]), P(a["up"]), one, one, caps, P(f), P(f), P(f),
+                                 P(a["dh"]), P(f), one, one, caps, P(f), P(f), ctypes.byref(o), ws, wsb, None)
+
+
+def test_kept_activation_argument_validation():
+    """The optional kept g and u: both or neither, 16-byte aligned; the
+    backward needs dh only when it recomputes them."""
+    import gemm_collective_persistent_amd as kos
+    from gemm_collective_persistent_amd._binding import KOS_ERR_ALIGN, KOS_ERR_ARG
+    for name in ("layer", "combine"):
+        assert _moe_call(kos, name, g=0x20000) == KOS_ERR_ARG, name
+        assert _moe_call(kos, name, u=0x20000) == KOS_ERR_ARG, name
+        assert b"together" in kos.lib.kos_last_error(), name
+        assert _moe_call(kos, name, g=0x20008, u=0x20000) == KOS_ERR_ALIGN, name
+    assert _moe_call(kos, "bwd", dh=None) == KOS_ERR_ARG
+    assert _moe_call(kos, "bwd", gate=0x20000) == KOS_ERR_ARG
+    assert b"together" in kos.lib.kos_last_error()
+    assert _moe_call(kos, "bwd", gate=0x20000, up=0x20004) == KOS_ERR_ALIGN
