@@ -361,7 +361,8 @@ def moe_backward(torch, kos, KI, m, ws, flush, reps, shape, fwd_ms, rank=0, base
          "idle_cu_fraction": summ["idle_frac"], "wait_fraction": summ["wait_frac"],
          "tokens_per_s": round(shape.tokens / (t * 1e-3), 1),
          "forward_ms": round(fwd_ms, 4),
-         "fwd_plus_bwd_tokens_per_s": round(shape.tokens / ((t + fwd_ms) * 1e-3), 1)}
+         "fwd_plus_bwd_tokens_per_s": round(shape.tokens / ((t + fwd_ms) * 1e-3), 1),
+         "traffic": measured_traffic("moe_layer_bwd", shape.name)}
     if baseline:
         run, out = torch_bwd_baseline(torch, m, g, shape, rank)
         run()
@@ -400,7 +401,8 @@ def saved_backward(torch, kos, m, g, ws, flush, reps, shape, fwd_ms, bwd_ms, row
          "speedup_vs_recompute": round(bwd_ms / tb, 3),
          "kept_bytes": 2 * rows * F * 2,
          "fwd_plus_bwd_tokens_per_s": round(shape.tokens / ((tf + tb) * 1e-3), 1),
-         "fwd_plus_bwd_speedup_vs_recompute": round((fwd_ms + bwd_ms) / (tf + tb), 3)}
+         "fwd_plus_bwd_speedup_vs_recompute": round((fwd_ms + bwd_ms) / (tf + tb), 3),
+         "traffic": measured_traffic("moe_layer_bwd_saved", shape.name)}
     if baseline:
         run, out = torch_bwd_baseline(torch, m, g, shape, rank, saved=True)
         run()
