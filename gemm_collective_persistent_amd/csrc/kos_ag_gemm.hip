@@ -193,9 +193,9 @@ __global__ __launch_bounds__(S::NT, 1) void ag_gemm_kernel(AgParams args) {
       if (p.c_f32) {
         float* C = reinterpret_cast<float*>(p.c) + row0 * N + col0;
         tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<f32x4*>(&C[r * N + c]) = v; });
-      } else {
-        uint16_t* C = reinterpret_cast<uint16_t*>(p.c) + row0 * N + col0;
-        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<u32x2*>(&C[r * N + c]) = pack4_bf16(v); });
+      } else {   // whole rows of the tile through the (now free) LDS ring
+        tile_store_out<S, ring_bytes<S>(), false, uint16_t, ring_bufs<S>()>(
+            acc, reinterpret_cast<uint16_t*>(p.c) + row0 * N + col0, N, BM);
       }
       tr.put(KOS_TR_TILE, j, t0);
     }

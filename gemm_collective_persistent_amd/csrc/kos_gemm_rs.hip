@@ -188,14 +188,12 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
         tile_mainloop<S>(acc, reinterpret_cast<const uint16_t*>(p.a) + row0 * K, K, BM, b, p.k);
       }
       float* P = p.partial + row0 * N + (int64_t)col * BN;
+      // whole rows of the tile through the (now free) LDS ring
       if (chunk == p.rank) {   // read by this launch's reducers: device-coherent stores
-        const DevBuf pb(P);
-        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) {
-          pb.st128((uint32_t)(r * N + c) * 4u, __builtin_bit_cast(u32x4, v));
-        });
+        tile_store_out<S, ring_bytes<S>(), true, float, ring_bufs<S>()>(acc, P, N, BM);
         wg_publish(&p.ready[band * p.tiles_n + col], 1u);
       } else {
-        tile_foreach4<S>(acc, [&](int r, int c, f32x4 v) { *reinterpret_cast<f32x4*>(&P[r * N + c]) = v; });
+        tile_store_out<S, ring_bytes<S>(), false, float, ring_bufs<S>()>(acc, P, N, BM);
       }
       tr.put(KOS_TR_TILE, j, t0);
     }

@@ -594,6 +594,136 @@ __device__ __forceinline__ void tile_store_rows(const f32x16 (&acc)[S::TM][S::TN
   });
 }
 
+// Ring buffer i (i < NBUF, uniform) of a kernel whose ring has NBUF buffers
+// of RING bytes; buffers past NBUF are never instantiated.
+template <int RING, int NBUF>
+__device__ __forceinline__ lds_char* ring_buf(int i) {
+  static_assert(NBUF == 2 || NBUF == 4, "rings of two or four buffers");
+  if constexpr (NBUF == 2) {
+    lds_char* b0 = (lds_char*)ring<RING, 0>();
+    lds_char* b1 = (lds_char*)ring<RING, 1>();
+    return i == 0 ? b0 : b1;
+  } else {
+    return ring_lds<RING>(i);
+  }
+}
+
+// Rounds a tile store takes: the fewest (1, 2 or 4) whose rows fill NBUF
+// ring buffers, or fewer, with whole 32-row groups (0: none fits).
+template <int BM, int ROW_BYTES, int RING, int NBUF>
+constexpr int store_rounds() {
+  for (int r = 1; r <= 4; r *= 2) {
+    const int rr = BM / r, nb = rr / 32 < NBUF ? rr / 32 : NBUF;
+    if (BM % r == 0 && rr % 32 == 0 && nb > 0 && rr % nb == 0 && (rr / nb) % 32 == 0 && (rr / nb) * ROW_BYTES <= RING)
+      return r;
+  }
+  return 0;
+}
+
+// Stores the whole BM x BN tile as rows [0, m_valid) of dst (row stride ld
+// elements of T: bf16 as uint16_t, or float), through the LDS ring, so that
+// the global writes are whole 16-byte chunks of rows, consecutive lanes on
+// consecutive chunks (whole cache lines), for any BN with a multiple of 8
+// chunks per row.  When the tile is larger than the ring it goes out in
+// rounds: round r takes every wave's 32-row blocks [r*TM/R, (r+1)*TM/R), so
+// each round frees part of every wave's accumulators.  A round's rows are
+// spread evenly over the ring buffers (RPB each), and a store pass never
+// leaves its buffer, so every LDS address has a uniform base.  Chunk c of a
+// ring row x sits at c ^ (x & SW), SW+1 the largest power of two (up to 32)
+// dividing the chunks per row: the 32 rows a write instruction touches fall
+// on different banks, and the chunk stays inside its row.  COH:
+// device-scope (sc1) stores.  BM rows of ld elements stay below 2 GiB.  Call
+// right after the K loop (the ring is free); the next K loop waits for the
+// ring.
+template <class S, int RING, bool COH, class T, int NBUF = 4>
+__device__ __forceinline__ void tile_store_out(const f32x16 (&acc)[S::TM][S::TN], T* dst, int64_t ld, int m_valid) {
+  constexpr int ESZ = sizeof(T);
+  static_assert(ESZ == 2 || ESZ == 4, "bf16 or fp32 output");
+  constexpr int EPC = 16 / ESZ;                       // elements per 16-byte chunk
+  constexpr int ROW_BYTES = S::BN * ESZ;
+  constexpr int CPR = ROW_BYTES / 16;                 // chunks per row
+  constexpr int LOWBIT = CPR & -CPR;
+  constexpr int SW = (LOWBIT < 32 ? LOWBIT : 32) - 1;
+  constexpr int ROUNDS = store_rounds<S::BM, ROW_BYTES, RING, NBUF>();
+  static_assert(ROUNDS > 0, "the tile's rows do not fit the ring in whole 32-row groups");
+  constexpr int RR = S::BM / ROUNDS;                  // rows per round
+  constexpr int NB = RR / 32 < NBUF ? RR / 32 : NBUF; // ring buffers used
+  constexpr int RPB = RR / NB;                        // rows per buffer
+  constexpr int TMR = S::TM / ROUNDS;                 // 32-row blocks per wave and round
+  constexpr int RWM = S::WM / ROUNDS;                 // rows per wave and round
+  constexpr int PPB = RPB * CPR / S::NT;              // store passes per buffer
+  constexpr int PASSES = NB * PPB;
+  constexpr int BATCH = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : PASSES % 4 == 0 ? 4 : PASSES % 3 == 0 ? 3
+                        : PASSES % 2 == 0 ? 2 : 1;    // passes per batch
+  static_assert(CPR % 8 == 0, "whole groups of eight chunks per row");
+  static_assert(S::TM % ROUNDS == 0 && RWM % 32 == 0, "whole 32-row blocks per wave and round");
+  static_assert(RPB * CPR % S::NT == 0, "whole store passes per buffer");
+  static_assert(S::TN * 32 * S::WGN == S::BN, "whole 32-column blocks per wave");
+  const WaveCtx w = wave_ctx();
+  const int lane = w.lane, wave = w.wave;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int t = wave * 64 + lane;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wave_uniform((const void*)dst)), (short)0, 0x7fffffff,
+                                        kRawBufferWord3);
+  const uint32_t ldb = (uint32_t)(ld * ESZ);
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (rd > 0) {
+      KOS_WAITCNT(0, 0);   // the previous round's ring reads are done
+      lds_barrier();
+    }
+#pragma unroll
+    for (int ii = 0; ii < TMR; ++ii) {
+      const int i = rd * TMR + ii;
+      const int x0 = wm * RWM + ii * 32;             // ring row of the 32-row block (uniform)
+      const int x = x0 + (lane & 31);
+      lds_char* base = ring_buf<RING, NBUF>(x0 / RPB) + (x % RPB) * ROW_BYTES;
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * S::WN + j * 32 + g * 8 + (lane >> 5) * 4;
+          const int chunk = (col / EPC) ^ (x & SW);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          if constexpr (ESZ == 2)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(base + chunk * 16 + (col % EPC) * 2) =
+                pack4_bf16(v);
+          else
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(base + chunk * 16) = v;
+          if (g == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    KOS_WAITCNT(0, 0);
+    lds_barrier();
+#pragma unroll
+    for (int b0 = 0; b0 < PASSES; b0 += BATCH) {
+      u32x4 v[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int ps = b0 + q, bf = ps / PPB;        // buffer bf: compile-time
+        const int y = (ps % PPB) * S::NT + t;
+        const int xb = y / CPR, c = y % CPR, x = bf * RPB + xb;
+        v[q] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            ring_buf<RING, NBUF>(bf) + xb * ROW_BYTES + ((c ^ (x & SW)) * 16));
+      }
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int ps = b0 + q, bf = ps / PPB;
+        const int y = (ps % PPB) * S::NT + t;
+        const int x = bf * RPB + y / CPR, c = y % CPR;
+        const int row = (x / RWM) * S::WM + rd * RWM + x % RWM;
+        if (row < m_valid)
+          __builtin_amdgcn_raw_buffer_store_b128(v[q], rs, (uint32_t)row * ldb + (uint32_t)c * 16u, 0,
+                                                 COH ? kCpolSc1 : 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Both halves of a dual-layout tile (gate blocks and up blocks, BN/2
 // columns each) as bf16 rows [0, m_valid) of dst0 and dst1, in one pass
 // through the LDS ring: the gate half takes ring rows [0, BM), the up half

@@ -339,4 +339,18 @@ __device__ __forceinline__ void tile_mainloop_mx(f32x16 (&acc)[S::TM][S::TN], co
   lds_barrier();
 }
 
+// The LDS ring of a tile shape's K loop (bf16 or MX): buffer size and
+// count, for the staged tile stores that reuse it.
+template <class S>
+constexpr int ring_bytes() {
+  if constexpr (S::MX)
+    return S::PAIR_BYTES;
+  else
+    return S::STAGE_BYTES;
+}
+template <class S>
+constexpr int ring_bufs() {
+  return S::MX ? 2 : 4;
+}
+
 }  // namespace kos
