@@ -676,21 +676,34 @@ def cu_subset_gemm(torch, kos, inp, ws, reps, flush):
     """Plain GEMM throughput on 224 of the 256 compute units relative to all
     256, on the QKV GEMM (4096 x 8192 x 3072: exactly 256 tiles, so 224
     workgroups need a second round) and on a large square GEMM (8192^3:
-    1024 tiles) -- the explainer's worked example reports about 93%."""
+    1024 tiles) -- the explainer's worked example reports about 93%.  Beside
+    it, the vendor library's GEMM on the same operands (torch.matmul, i.e.
+    hipBLASLt): a reference for the tile itself."""
     res = {}
     ag = inp["ag"]
     big = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
-    cases = {"qkv_4096x8192x3072": (ag["g"], ag["w"]), "square_8192": (big, big)}
-    for name, (a, w) in cases.items():
+    rs = inp["rs"]
+    cases = {"qkv_4096x8192x3072": (ag["g"], ag["w"], True), "square_8192": (big, big, True),
+             "mlp_down_4096x3584x8192": (rs["a"], rs["w"], False)}
+    for name, (a, w, subset) in cases.items():
         c = torch.empty((a.shape[0], w.shape[1]), dtype=torch.bfloat16, device="cuda")
         t = {}
-        for grid in (256, 224):
+        for grid in (256, 224) if subset else (256,):
             o = kos.opts(mode=2, grid=grid)
             fn = lambda: kos.ag_gemm(a, [None], w, a, c, 0, ws, o)  # noqa: E731
             fn()
             t[grid] = time_ops(torch, [("gemm", fn)], reps, ws, flush)[0][0]
-        res[name] = {"ms_256": round(t[256], 4), "ms_224": round(t[224], 4),
-                     "throughput_224_vs_256": round(t[256] / t[224], 3)}
+        vend = lambda: torch.matmul(a, w, out=c)  # noqa: E731
+        for _ in range(3):   # the library picks and loads its kernel on the first calls
+            vend()
+        tv = time_ops(torch, [("hipblaslt", vend)], reps, ws, flush)[0][0]
+        fl = 2.0 * a.shape[0] * a.shape[1] * w.shape[1]
+        d = {"ms_256": round(t[256], 4), "tflops": round(fl / (t[256] * 1e-3) / 1e12, 1),
+             "hipblaslt_ms": round(tv, 4), "hipblaslt_tflops": round(fl / (tv * 1e-3) / 1e12, 1),
+             "vs_hipblaslt": round(tv / t[256], 3)}
+        if subset:
+            d.update(ms_224=round(t[224], 4), throughput_224_vs_256=round(t[256] / t[224], 3))
+        res[name] = d
     del big
     return res
 
