@@ -79,7 +79,7 @@ typedef enum kos_dtype { KOS_BF16 = 0, KOS_F32 = 1 } kos_dtype;
  *   FUSED   one persistent launch; roles switch as readiness dictates.
  *   FIXED   one persistent launch; a fixed crew of `n_movers` workgroups
  *           only communicates (or only reduces), the rest only compute:
- *           the "manager who assigns the crew at opening time" baseline
+ *           a split chosen once, before the call, and never revised
  *           [explainer, "Picture a restaurant kitchen" paragraph].
  *   UNFUSED two launches: the whole collective step, then the whole GEMM
  *           (or GEMM then reduction), same tile code. */
@@ -117,8 +117,9 @@ typedef struct kos_opts {
 } kos_opts;
 
 /* Role-switching policy under KOS_MODE_FUSED [explainer, "KOSMOS removes
- * the manager": one-way switching in the all-gather and reduce-scatter
- * kernels, two-way in the expert combine; "How do the policies compare?"].
+ * the manager": roles change in one direction only for the two TP+SP
+ * collectives, in both directions for the expert combine; "How do the
+ * policies compare?"].
  *   DEFAULT  the pages' choice per op: kos_ag_gemm one-way (movers become
  *            builders), kos_gemm_rs one-way (builders become reducers),
  *            kos_moe_combine and kos_moe_layer two-way (push a ready result,
