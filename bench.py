@@ -189,14 +189,26 @@ def layer_op(kos, m, ws, shape, rank=0, trace=False, save=False):
                                  **kw)
 
 
-def single_launch(torch, kos, KI, m, ws, flush, reps, shape, two_ms, rank=0):
+def single_launch(torch, kos, KI, m, ws, flush, reps, shape, two_ms, rank=0, baseline=True):
     """The expert layer in one launch, router to fold (kos_moe_layer), against
-    the two launches (dispatch, then combine) on the same inputs."""
+    the two launches (dispatch, then combine) on the same inputs, and (with
+    `baseline`) against the same forward composed of PyTorch operations."""
     fn = layer_op(kos, m, ws, shape, rank)
     fn()
     t = time_ops(torch, [("moe_layer", fn)], reps, ws, flush)[0][0]
-    return {"ms": round(t, 4), "two_launch_ms": round(two_ms, 4), "speedup_vs_two_launch": round(two_ms / t, 3),
-            "tokens_per_s": round(shape.tokens / (t * 1e-3), 1)}
+    d = {"ms": round(t, 4), "two_launch_ms": round(two_ms, 4), "speedup_vs_two_launch": round(two_ms / t, 3),
+         "tokens_per_s": round(shape.tokens / (t * 1e-3), 1)}
+    if baseline:
+        fn()
+        ws.status()
+        run, out = torch_fwd_baseline(torch, m, shape, rank)
+        run()
+        torch.cuda.synchronize()
+        tb = time_ops(torch, [("torch_fwd", run)], reps, ws, flush)[0][0]
+        d["torch_composed"] = {"ms": round(tb, 4), "speedup_two_launch": round(tb / two_ms, 3),
+                               "speedup_one_launch": round(tb / t, 3),
+                               "y_rel_diff": float(f"{_rel(out['y'], m['y']):.3g}")}
+    return d
 
 
 def build_moe_grad(torch, KI, shape, m, rank=0):
@@ -243,13 +255,12 @@ def _rel(a, b):
     return float((a - b).norm() / b.norm().clamp_min(1e-30))
 
 
-def torch_bwd_baseline(torch, m, g, shape, rank=0, saved=False):
-    """The same backward composed of PyTorch operations on the same GPU
-    (hipBLASLt GEMMs per expert, elementwise and indexing kernels): a
-    same-GPU library baseline.  Index maps are built once, untimed, from the
-    forward's routing; the returned closure computes dx and dlogits (and the
-    rows sent and returned) from the resident inputs.  saved: g and u are the
-    forward's kept copies (m["gs"], m["us"]) rather than two more GEMMs."""
+def _moe_maps(torch, m, shape, rank=0):
+    """Index maps of one forward's routing, for the PyTorch-composed
+    baselines (built once, untimed): grouped row -> row of cat(our own local
+    pairs' rows in packed order, each peer's rows); the rows to push back per
+    peer; every pair -> its local grouped row or (rank, row) of what that rank
+    returns."""
     import numpy as np
     T, k, E, H, R = shape.tokens, shape.topk, shape.experts, shape.hidden, shape.world
     el = shape.e_local
@@ -262,7 +273,7 @@ def torch_bwd_baseline(torch, m, g, shape, rank=0, saved=False):
     go = m["goff"].cpu().numpy().astype(np.int64)
     rs = m["row_src"][:int(go[-1])].cpu().numpy().astype(np.int64)
     pc = m["peer_counts"].cpu().numpy().astype(np.int64)
-    # grouped row -> row of cat(our own local pairs' gradients, each peer's rows)
+    # grouped row -> row of cat(our own local pairs' rows, each peer's rows)
     base = {rank: 0}
     acc = so[rank + 1] - so[rank]
     for p in range(R):
@@ -287,6 +298,73 @@ def torch_bwd_baseline(torch, m, g, shape, rank=0, saved=False):
         if d != rank and sel.size:
             pairs_rem[d] = (torch.as_tensor(sel, device=dev), torch.as_tensor(perm_np[sel] - so[d], device=dev))
     bounds = [(int(go[e]), int(go[e + 1])) for e in range(el)]
+    return dict(idx=idx, perm=perm, so=so, gidx=gidx, push=push, pairs_loc=pairs_loc, pairs_rem=pairs_rem,
+                bounds=bounds)
+
+
+def torch_fwd_baseline(torch, m, shape, rank=0):
+    """The same forward (router to fold) composed of PyTorch operations on
+    the same GPU (hipBLASLt GEMMs per expert, elementwise and indexing
+    kernels): a same-GPU library baseline.  The routing (top-k and softmax)
+    is computed in the timed closure; the index maps of the permutation are
+    built once, untimed, from the routing the kernels produced (the same
+    routing, top-k being deterministic on these logits).  Returns the closure
+    and a dict that receives y."""
+    T, k, H, R = shape.tokens, shape.topk, shape.hidden, shape.world
+    mp = _moe_maps(torch, m, shape, rank)
+    perm, so, gidx = mp["perm"], mp["so"], mp["gidx"]
+    push, pairs_loc, pairs_rem, bounds = mp["push"], mp["pairs_loc"], mp["pairs_rem"], mp["bounds"]
+    dev = m["grouped"].device
+    wg, wu, wd, x = m["wg"], m["wu"], m["wd"], m["x"]
+    rows = int(m["goff"][-1].item())
+    yg = torch.empty((max(rows, 1), H), dtype=torch.bfloat16, device=dev)
+    packed = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    res = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    send = {d: torch.empty((max(so[d + 1] - so[d], 1), H), dtype=torch.bfloat16, device=dev)
+            for d in range(R) if d != rank}
+    ret = {p: torch.empty((max(int(r.numel()), 1), H), dtype=torch.bfloat16, device=dev) for p, (r, _) in push.items()}
+    pair_tok = torch.arange(T * k, device=dev) // k
+    out = {}
+
+    def run():
+        vals = torch.topk(m["logits"], k, dim=1).values
+        w = torch.softmax(vals, dim=1)
+        # every pair's row in packed (expert-major) order, sent or kept
+        packed[perm] = x[pair_tok]
+        for d in send:
+            if so[d + 1] > so[d]:
+                send[d][:so[d + 1] - so[d]].copy_(packed[so[d]:so[d + 1]])
+        src = torch.cat([packed[so[rank]:so[rank + 1]]] + [m["peer_send"][p] for p in range(R) if p != rank])
+        xg = src[gidx]
+        for e, (lo, hi) in enumerate(bounds):
+            if hi == lo:
+                continue
+            xe = xg[lo:hi]
+            h = (torch.nn.functional.silu((xe @ wg[e]).float()) * (xe @ wu[e]).float()).to(torch.bfloat16)
+            torch.matmul(h, wd[e], out=yg[lo:hi])
+        for p, (rws, dst_rows) in push.items():
+            ret[p].index_copy_(0, dst_rows, yg[rws])
+        # per token: the weighted sum of its pairs' results
+        res[pairs_loc[0]] = yg[pairs_loc[1]]
+        for d, (sel, rws) in pairs_rem.items():
+            res[sel] = m["peer_return"][d][rws]
+        out["y"] = (res.view(T, k, H).float() * w[:, :, None]).sum(1).to(torch.bfloat16)
+
+    return run, out
+
+
+def torch_bwd_baseline(torch, m, g, shape, rank=0, saved=False):
+    """The same backward composed of PyTorch operations on the same GPU
+    (hipBLASLt GEMMs per expert, elementwise and indexing kernels): a
+    same-GPU library baseline.  Index maps are built once, untimed, from the
+    forward's routing; the returned closure computes dx and dlogits (and the
+    rows sent and returned) from the resident inputs.  saved: g and u are the
+    forward's kept copies (m["gs"], m["us"]) rather than two more GEMMs."""
+    T, k, E, H, R = shape.tokens, shape.topk, shape.experts, shape.hidden, shape.world
+    mp = _moe_maps(torch, m, shape, rank)
+    idx, perm, so, gidx = mp["idx"], mp["perm"], mp["so"], mp["gidx"]
+    push, pairs_loc, pairs_rem, bounds = mp["push"], mp["pairs_loc"], mp["pairs_rem"], mp["bounds"]
+    dev = m["grouped"].device
     wg, wu, wd = m["wg"], m["wu"], m["wd"]
     dy, w = g["dy"], m["w"]
     xg, yg = m["grouped"], m["yg"]
@@ -1039,7 +1117,7 @@ def main():
     # the expert layer in one launch, router to fold, beside the two launches
     t_two = per[names.index("moe_dispatch")] + per[names.index("moe_combine")]
     extra["moe_single_launch"] = single_launch(torch, kos, KI, inp["moe"], ws, flush, max(3, args.steps // 4),
-                                               moe_shape, t_two)
+                                               moe_shape, t_two, baseline=not args.no_baselines)
     # the expert layer's backward direction in one launch, on the forward
     # buffers the single launch just left (the forward's routing and rows)
     extra["moe_backward"] = moe_backward(torch, kos, KI, inp["moe"], ws, flush, max(3, args.steps // 4), moe_shape,
