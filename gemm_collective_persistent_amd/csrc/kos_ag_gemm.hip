@@ -343,6 +343,7 @@ static kos_status ag_gemm_run(const AgCall& a) {
   if (m_local * world > (int64_t(1) << 30) || k > (1 << 20) || n > (1 << 20))
     return fail(KOS_ERR_SHAPE, "sizes too large");
   // the tiles address W (bf16) and the scale slabs through 32-bit offsets
+  // (n <= 2^20 keeps a tile's 256 output rows, fp32, below 1 GiB of offsets)
   if (!a.mx && k * n * 2 >= (int64_t(1) << 31)) return fail(KOS_ERR_SHAPE, "w (bf16) must be smaller than 2 GiB");
   if (a.mx && (k / 64) * 2 * std::max<int64_t>(m_local * world, n) >= (int64_t(1) << 31))
     return fail(KOS_ERR_SHAPE, "MX scale arrays must be smaller than 2 GiB");
