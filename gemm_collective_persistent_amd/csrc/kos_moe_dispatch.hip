@@ -23,14 +23,15 @@
 //                goes to the send buffer of e's rank, or straight into the
 //                grouped input when e is local -- then kMoveRows-row chunks of
 //                each peer's rows, pulled into the grouped input.  Entries
-//                are small (about 0.5 MB of traffic) so that the workgroups
-//                run out of them together.
+//                are small (at most about 1 MB of traffic: one of our tokens, or two peer
+//                rows, per wave) so that the workgroups run out of them
+//                together.
 #include "kos_host.h"
 #include "kos_moe_dispatch.h"
 
 namespace kos {
 
-constexpr int kMoveTokens = 4;    // our tokens per mover entry (one per wave)
+constexpr int kMoveTokens = 8;    // our tokens per mover entry (one per wave)
 
 template <int NT>
 __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args) {
@@ -174,7 +175,7 @@ extern "C" kos_status kos_moe_dispatch(const kos_moe_shape* s, const void* x, co
   p.base = reinterpret_cast<int32_t*>(scratch + mask_bytes);
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  constexpr int NT = 256;
+  constexpr int NT = 512;   // eight waves: two rows in flight per SIMD while moving
   if (o.mode == KOS_MODE_UNFUSED) {
     DispatchParams a = p;   // launch 1: router + scan
     a.do_route = 1;
