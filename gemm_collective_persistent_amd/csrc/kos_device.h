@@ -241,6 +241,14 @@ struct Tracer {
     }
     ++n;
   }
+  // Same, for a piece of work the whole workgroup shares whose waves may end
+  // at different times: the record ends when the last wave is done (a
+  // barrier, taken only when tracing).
+  __device__ __forceinline__ void put_wg(uint32_t kind, uint32_t entry, uint64_t t0) {
+    if (!row) return;
+    __syncthreads();
+    put(kind, entry, t0);
+  }
   // The header (start, lifetime, arrival ticket, the accelerator complex die
   // (XCD) the workgroup runs on, the record count) and the clock record
   // (shader-clock cycles over the same lifetime).

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(S::NT, 1) void gemm_rs_kernel(RsParams args) {
   auto do_reduce = [&](uint32_t i, uint64_t t0) {
     const RsReduce re = rs_reduce_of((int)i, p.tiles_n, SLABS);
     reduce_entry<BN>(p, (int64_t)re.band * BM + re.slab * kSlabRows, re.col);
-    tr.put(KOS_TR_REDUCE, i, t0);
+    tr.put_wg(KOS_TR_REDUCE, i, t0);
   };
 
   // ---- builder role -----------------------------------------------------

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
           if (got == kNoEntry) break;
           const uint64_t t0 = tr.now();
           push_slab(p, M, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
-          tr.put(KOS_TR_PUSH, got, t0);
+          tr.put_wg(KOS_TR_PUSH, got, t0);
         }
       }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_combine_kernel(CombineParams arg
         t0 = tr.now();
       }
       push_slab(p, M, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
-      tr.put(KOS_TR_PUSH, i, t0);
+      tr.put_wg(KOS_TR_PUSH, i, t0);
     }
   }
 

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NT, 1) void moe_dispatch_kernel(DispatchParams args
       if (i >= (uint32_t)n_entries) break;
       const uint64_t t0 = tr.now();
       move_entry<kMoveTokens, false>(p, L, (int)i, [](int, int) {});
-      tr.put(KOS_TR_MOVE, i, t0);
+      tr.put_wg(KOS_TR_MOVE, i, t0);
     }
   }
   tr.finish(ticket);

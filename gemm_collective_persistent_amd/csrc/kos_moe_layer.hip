@@ -155,7 +155,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_layer_kernel(LayerParams args) {
       });
       // our tokens' packed positions (perm) are read by the fold
       if ((int)i < d.nblk * (kMoeTokBlock / MT)) wg_publish(own_moved, 1u);
-      tr.put(KOS_TR_MOVE, i, t0);
+      tr.put_wg(KOS_TR_MOVE, i, t0);
     }
   }
 
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_layer_kernel(LayerParams args) {
         if (got == kNoEntry) break;
         const uint64_t t0 = tr.now();
         push_slab<true>(p, M, unit_of<BM>(M, p.E_loc, (int)got / kPushSlabs), (int)got % kPushSlabs);
-        tr.put(KOS_TR_PUSH, got, t0);
+        tr.put_wg(KOS_TR_PUSH, got, t0);
       }
       const uint32_t j = wg_claim(&h->head[3], h, &slots);
       if (j >= (uint32_t)n_entries) break;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(S::NT, 1) void moe_layer_kernel(LayerParams args) {
       tr.put(KOS_TR_WAIT, i, t0);
       t0 = tr.now();
       push_slab<true>(p, M, unit_of<BM>(M, p.E_loc, u), (int)i % kPushSlabs);
-      tr.put(KOS_TR_PUSH, i, t0);
+      tr.put_wg(KOS_TR_PUSH, i, t0);
     }
   }
 

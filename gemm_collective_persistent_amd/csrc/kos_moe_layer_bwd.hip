@@ -545,7 +545,7 @@ __global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
       } else {
         bwd_move_peer(ps, M, B, (int)i);
       }
-      tr.put(KOS_TR_MOVE, i, t0);
+      tr.put_wg(KOS_TR_MOVE, i, t0);
     }
   }
 
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
         if (got == kNoEntry) break;
         const uint64_t t0 = tr.now();
         push_slab(p, M, unit_of<kBwdUnit>(M, p.E_loc, (int)got / kSlabs), (int)got % kSlabs);
-        tr.put(KOS_TR_PUSH, got, t0);
+        tr.put_wg(KOS_TR_PUSH, got, t0);
       }
       const uint32_t j = wg_claim(&h->head[1], h, &slots);
       if (j >= (uint32_t)n_tiles) break;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void moe_layer_bwd_kernel(BwdParams args) {
       tr.put(KOS_TR_WAIT, i, t0);
       t0 = tr.now();
       push_slab(p, M, unit_of<kBwdUnit>(M, p.E_loc, u), (int)i % kSlabs);
-      tr.put(KOS_TR_PUSH, i, t0);
+      tr.put_wg(KOS_TR_PUSH, i, t0);
     }
   }
 
