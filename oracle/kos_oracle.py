@@ -37,9 +37,9 @@ are stated at each function.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (brute force, closed forms, invariants).
-``expert_ffn`` is pinned only to a float64 brute-force loop and to closed-form
-special cases (there is no printed example), which fixes its definition but
-not a value from the pages.
+``expert_ffn`` is pinned by a float64 brute-force loop on random inputs and by
+a closed-form case of selection weights (gate and up roles, indices, the
+SiLU's asymmetry); the pages print no worked example to pin a value to.
 The backward functions are pinned in ``tests/test_oracle_bwd_pins.py`` by
 central finite differences of an unrounded forward written out there, and
 by special cases and the softmax invariant; the variant that takes the

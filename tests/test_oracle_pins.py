@@ -332,6 +332,36 @@ def test_ffn_vs_float64_loop():
     assert np.array_equal(O.expert_hidden(x, wg, wu), O.round_bf16(h))
 
 
+def test_ffn_selection_closed_form():
+    """Selection weights reduce the expert to arithmetic checkable by hand:
+    gate column f reads input column a[f] times 40, up column f reads input
+    column b[f], down output column c reads hidden column d[c].  With inputs
+    of +-1, silu(+40) = 40 to 1e-15 and silu(-40) = 0 to 1e-15, so
+    y[t, c] = 40 * x[t, b[d[c]]] where x[t, a[d[c]]] = +1 and ~0 where it is
+    -1.  Swapping the gate and up roles, an index or the operand order fails
+    this (silu(+-1) * 40 is neither 40 nor ~0)."""
+    rng = np.random.default_rng(21)
+    n, H, F = 6, 7, 4
+    a = [5, 0, 3, 6]          # gate source column of hidden f
+    b = [2, 4, 1, 0]          # up source column of hidden f
+    d = [3, 1, 0, 2, 2, 1, 3]  # hidden column feeding output column c
+    xs = rng.choice([-1.0, 1.0], size=(n, H))
+    wg, wu, wd = np.zeros((H, F)), np.zeros((H, F)), np.zeros((F, H))
+    for f in range(F):
+        wg[a[f], f] = 40.0
+        wu[b[f], f] = 1.0
+    for c in range(H):
+        wd[d[c], c] = 1.0
+    y = O.bf16_to_f64(O.expert_ffn(O.round_bf16(xs), O.round_bf16(wg), O.round_bf16(wu), O.round_bf16(wd)))
+    for t in range(n):
+        for c in range(H):
+            f = d[c]
+            if xs[t, a[f]] > 0:
+                assert y[t, c] == 40.0 * xs[t, b[f]], (t, c)
+            else:
+                assert abs(y[t, c]) < 1e-15, (t, c)
+
+
 def test_ffn_zero_up_gives_zero():
     rng = np.random.default_rng(14)
     x = O.round_bf16(rng.standard_normal((4, 8)))
