@@ -352,7 +352,15 @@ def test_ffn_selection_closed_form():
         wu[b[f], f] = 1.0
     for c in range(H):
         wd[d[c], c] = 1.0
-    y = O.bf16_to_f64(O.expert_ffn(O.round_bf16(xs), O.round_bf16(wg), O.round_bf16(wu), O.round_bf16(wd)))
+    x16, wg16, wu16, wd16 = O.round_bf16(xs), O.round_bf16(wg), O.round_bf16(wu), O.round_bf16(wd)
+    y = O.bf16_to_f64(O.expert_ffn(x16, wg16, wu16, wd16))
+    h = O.bf16_to_f64(O.expert_hidden(x16, wg16, wu16))
+    for t in range(n):
+        for f in range(F):
+            if xs[t, a[f]] > 0:
+                assert h[t, f] == 40.0 * xs[t, b[f]], (t, f)
+            else:
+                assert abs(h[t, f]) < 1e-15, (t, f)
     for t in range(n):
         for c in range(H):
             f = d[c]
