@@ -23,9 +23,9 @@
 //                goes to the send buffer of e's rank, or straight into the
 //                grouped input when e is local -- then kMoveRows-row chunks of
 //                each peer's rows, pulled into the grouped input.  Entries
-//                are small (at most about 1 MB of traffic: one of our tokens, or two peer
-//                rows, per wave) so that the workgroups run out of them
-//                together.
+//                are small (at most about 1 MB of traffic: one of our
+//                tokens, or two peer rows, per wave) so that the workgroups
+//                run out of them together.
 #include "kos_host.h"
 #include "kos_moe_dispatch.h"
 
