@@ -45,6 +45,7 @@ struct DispatchLds {
   int32_t cum[8][kMoeMaxLocal + 1];     // per-source prefix over local experts
   int32_t before[8][kMoeMaxLocal];      // rows of sources < p, per local expert
   int32_t go[kMoeMaxLocal + 1];         // grouped offsets
+  int32_t go_over;                      // the grouped rows exceed grouped_cap
   int32_t own_entries;                  // mover entries of our own tokens
   int32_t n_entries;                    // all mover entries
   int32_t chunk_base[9];                // first entry of each source's rows
@@ -204,15 +205,33 @@ __device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& 
     L.pc[p.rank][el] = L.off[ge + 1] - L.off[ge];
   }
   __syncthreads();
-  for (int el = threadIdx.x; el < p.E_loc; el += blockDim.x) {
-    int run = 0;
-    for (int q = 0; q < p.world; ++q) {
-      L.before[q][el] = run;
-      run += L.pc[q][el];
+  // one lane per local expert (E_loc <= 64): the rows of the sources before
+  // q, then the grouped offsets as a wave-wide exclusive prefix of the
+  // experts' totals, in 64 bits so that the capacity check sees any overflow
+  // (a single thread walking every (expert, source) pair took ~10 us)
+  if (threadIdx.x < 64) {
+    const int el = threadIdx.x;
+    int64_t run = 0;
+    if (el < p.E_loc)
+      for (int q = 0; q < p.world; ++q) {
+        L.before[q][el] = (int32_t)run;
+        run += L.pc[q][el];
+      }
+    int64_t incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(incl, d);
+      if (el >= d) incl += o;
+    }
+    if (el < p.E_loc) L.go[el] = (int32_t)(incl - run);
+    if (el == p.E_loc - 1) {
+      L.go[p.E_loc] = (int32_t)incl;
+      L.go_over = incl > p.grouped_cap ? 1 : 0;
     }
   }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    bool over = false;
+    bool over = L.go_over != 0;
     bool null_send = false;
     for (int d = 0; d < p.world; ++d) {
       if (d == p.rank) continue;
@@ -220,14 +239,7 @@ __device__ __forceinline__ bool load_meta(const DispatchParams& p, DispatchLds& 
       if (sent > p.send_cap[d]) over = true;
       if (sent > 0 && p.out_send[d] == nullptr) null_send = true;   // rows for a NULL buffer
     }
-    int64_t go = 0;
-    for (int el = 0; el < p.E_loc; ++el) {
-      L.go[el] = (int32_t)go;
-      for (int q = 0; q < p.world; ++q) go += L.pc[q][el];
-    }
-    L.go[p.E_loc] = (int32_t)go;
-    if (go > p.grouped_cap) over = true;
-    if (over) raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)go);
+    if (over) raise_error(p.ws, KOS_ERR_CAPACITY, (uint32_t)L.go[p.E_loc]);
     if (null_send) raise_error(p.ws, KOS_ERR_ARG, 0x00B00000u);
     slots->ok = over || null_send ? 0 : 1;
   }
