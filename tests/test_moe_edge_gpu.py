@@ -1,7 +1,7 @@
 """Expert layer edge cases on the GPU against the oracle: a ragged token
 count, top-1 routing, widths that take the small (128 x 128) tile, expert
 counts that are not multiples of 64, a single rank (no peers), top-k = all
-experts, and an empty batch."""
+experts, one and 64 local experts per rank, and an empty batch."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +18,10 @@ EDGE = [
     KI.MoeShape("moe_edge_1r_t33_h256_e8_k3_f128", 41, 1, 33, 256, 8, 3, 128),
     KI.MoeShape("moe_edge_2r_t40_h128_e4_k4_f192", 42, 2, 40, 128, 4, 4, 192),
     KI.MoeShape("moe_edge_3r_t0_h256_e6_k2_f128", 43, 3, 0, 256, 6, 2, 128),
+    # one local expert per rank, and the most a rank may hold (64: every lane
+    # of the wave that sums the grouped offsets)
+    KI.MoeShape("moe_edge_4r_t48_h128_e4_k2_f64", 46, 4, 48, 128, 4, 2, 64),
+    KI.MoeShape("moe_edge_2r_t80_h128_e128_k6_f64", 47, 2, 80, 128, 128, 6, 64),
 ]
 
 
